@@ -1,0 +1,395 @@
+"""Pins for the CPU oracle: each test ties an oracle function to something
+other than the oracle itself (a published table, a closed form, a library
+routine, brute force, or a value derived by hand in the test's docstring).
+
+CPU only; no GPU and no HIP library involved.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+from scipy.integrate import quad
+from scipy.stats import norm as normal_dist
+
+import oracle as o
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+F32 = np.float32
+
+
+def _read_max_table():
+    table = {}
+    with open(os.path.join(GOLDEN, "max1960_lloyd_max_normal.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            parts = line.split()
+            table[(int(parts[0]), parts[1])] = [float(v) for v in parts[2:]]
+    return table
+
+
+# ---------------------------------------------------------------- transform
+
+def test_wht_equals_sylvester_hadamard():
+    """The ascending butterfly is the Sylvester-Hadamard matrix (scipy)."""
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((5, 128))
+    H = scipy.linalg.hadamard(128).astype(np.float64)
+    np.testing.assert_allclose(o.wht_butterfly(x), x @ H.T, rtol=0, atol=1e-12)
+
+
+def test_wht_involution_norm_and_impulse():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal(128)
+    y = o.wht_butterfly(x)
+    np.testing.assert_allclose(o.wht_butterfly(y), 128 * x, atol=1e-11)
+    assert abs(np.dot(y, y) - 128 * np.dot(x, x)) < 1e-9
+    e0 = np.zeros(128); e0[0] = 1
+    assert np.all(o.wht_butterfly(e0) == 1.0)
+
+
+def test_wht_float32_ascending_stage_order():
+    """Hand-derived float32 rounding that only the ascending order produces.
+
+    u0 = 1, u1 = -2^-24, u64 = 2^-24, rest 0 (float32).
+    Ascending (h=1 first): out[0] = fl(fl(1 - 2^-24) + 2^-24) = 1 exactly,
+    whereas h=64 first would give fl(fl(1 + 2^-24) - 2^-24) = 1 - 2^-24
+    (the tie 1 + 2^-24 rounds to even, i.e. to 1).
+    out[1] = u0 - u1 + u64: ascending gives fl(fl(1 + 2^-24) + 2^-24) = 1,
+    while the exact (float64) value is 1 + 2^-23.
+    """
+    u = np.zeros(128, dtype=F32)
+    u[0] = 1.0
+    u[1] = -(2.0 ** -24)
+    u[64] = 2.0 ** -24
+    out = o.wht_butterfly(u)
+    assert out.dtype == F32
+    assert out[0] == F32(1.0)
+    assert out[1] == F32(1.0)
+    assert float(o.wht_butterfly(u.astype(np.float64))[1]) == 1.0 + 2.0 ** -23
+
+
+def test_sum_squares_tree_order():
+    """x0 = 1, x1..x127 = 2^-13 (squares 2^-26), float32, neighbouring pairs.
+
+    Level 1: 1 + 2^-26 -> 1; other pairs 2^-25.  Level 2: 1 + 2^-25 -> 1;
+    others 2^-24.  Level 3: 1 + 2^-24 is a tie -> 1 (even); others 2^-23.
+    Level 4: 1 + 2^-23 exact; level 5 adds 2^-22 -> 1 + 3*2^-23; level 6
+    adds 2^-21 -> 1 + 7*2^-23; level 7 adds 2^-20 -> 1 + 15*2^-23.
+    A left-to-right sum would stay at 1; the exact sum is 1 + 15.875*2^-23.
+    """
+    x = np.full(128, 2.0 ** -13, dtype=F32)
+    x[0] = 1.0
+    assert o.sum_squares_tree(x) == F32(1.0 + 15 * 2.0 ** -23)
+
+
+# ---------------------------------------------------------------- codebook
+
+@pytest.mark.parametrize("levels", [4, 8, 16])
+def test_lloyd_max_matches_max_1960(levels):
+    tab = _read_max_table()
+    lv = o.lloyd_max_normal(levels)
+    pos = lv[levels // 2:]
+    np.testing.assert_allclose(pos, tab[(levels, "out")], rtol=0, atol=6e-4)
+    edges = 0.5 * (lv[1:] + lv[:-1])
+    np.testing.assert_allclose(edges[levels // 2:], tab[(levels, "edge")], rtol=0, atol=6e-4)
+    t = np.concatenate(([-np.inf], edges, [np.inf]))
+    mse = sum(quad(lambda z, c=c: (z - c) ** 2 * normal_dist.pdf(z), a, b)[0]
+              for c, a, b in zip(lv, t[:-1], t[1:]))
+    # the table prints about four significant figures (its last digit is not
+    # always exact for the 16-level case), hence a relative 5e-4
+    assert abs(mse - tab[(levels, "mse")][0]) < 5e-4 * tab[(levels, "mse")][0]
+
+
+def test_lloyd_max_two_levels_closed_form():
+    """One-bit Lloyd-Max quantizer of N(0,1): +-sqrt(2/pi)."""
+    lv = o.lloyd_max_normal(2)
+    np.testing.assert_allclose(lv, [-np.sqrt(2 / np.pi), np.sqrt(2 / np.pi)], atol=1e-12)
+
+
+@pytest.mark.parametrize("levels", [4, 8, 16])
+def test_lloyd_max_fixed_point_by_quadrature(levels):
+    """Each level is the conditional mean of its cell, by numerical integration."""
+    lv = o.lloyd_max_normal(levels)
+    t = np.concatenate(([-np.inf], 0.5 * (lv[1:] + lv[:-1]), [np.inf]))
+    for c, a, b in zip(lv, t[:-1], t[1:]):
+        num = quad(lambda z: z * normal_dist.pdf(z), a, b, epsabs=1e-14, epsrel=1e-13)[0]
+        den = quad(normal_dist.pdf, a, b, epsabs=1e-14, epsrel=1e-13)[0]
+        assert abs(num / den - c) < 1e-8
+    np.testing.assert_array_equal(lv, -lv[::-1])
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_stored_codebook_is_fp16_of_lloyd_max(bits):
+    """Stored magnitudes are float16 values within half an fp16 ulp of the
+    quadrature-checked Lloyd-Max levels, and thresholds are exact midpoints."""
+    m = o.code_magnitudes(bits)
+    lv = o.lloyd_max_normal(2 ** bits)[2 ** (bits - 1):]
+    assert np.all(m.astype(np.float16).astype(np.float32) == m)
+    ulp = np.spacing(m.astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(m.astype(np.float64) - lv) <= 0.5 * ulp)
+    t = o.mag_thresholds(bits)
+    assert np.all(t.astype(np.float64) * 2 == m[1:].astype(np.float64) + m[:-1])
+    v = o.code_values(bits)
+    half = 2 ** (bits - 1)
+    np.testing.assert_array_equal(v[:half], m)
+    np.testing.assert_array_equal(v[half:], -m)
+
+
+def test_splitmix64_published_outputs():
+    with open(os.path.join(GOLDEN, "splitmix64_seed0.txt")) as f:
+        want = [int(l, 16) for l in f if l.strip() and not l.startswith("#")]
+    assert o.splitmix64(0, 3) == want
+    s = o.sign_flips()
+    w0, w1 = want[0], want[1]
+    assert all(s[d] == bool((w0 >> d) & 1) for d in range(64))
+    assert all(s[64 + d] == bool((w1 >> d) & 1) for d in range(64))
+
+
+# ---------------------------------------------------------------- quantizer
+
+def _fp64_rotated_unit(x):
+    """y = H (s . x) / ||x|| in float64 through scipy's Hadamard matrix."""
+    H = scipy.linalg.hadamard(128).astype(np.float64)
+    s = o.sign_flips()
+    x = x.astype(np.float64)
+    u = np.where(s, -x, x)
+    return (u @ H.T) / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_quantizer_is_nearest_level_brute_force(bits):
+    """Codes equal the brute-force nearest stored level of the float64 y,
+    except where y is within 1e-5 of a decision threshold."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((400, 128)).astype(F32) * F32(3.0)
+    codes, _ = o.quantize_groups(x, bits)
+    y = _fp64_rotated_unit(x)
+    vals = o.code_values(bits).astype(np.float64)
+    dist = np.abs(y[..., None] - vals[None, None, :])
+    best = np.argmin(dist, axis=-1)
+    near = np.min(np.abs(np.abs(y)[..., None] - o.mag_thresholds(bits)[None, None, :]), axis=-1) < 1e-5
+    near |= np.abs(y) < 1e-5
+    assert np.all((best == codes) | near)
+    assert near.mean() < 0.01
+
+
+@pytest.mark.parametrize("bits,qs_star", [(2, 1), (3, 1), (4, 3)])
+def test_quantizer_impulse_closed_form(bits, qs_star):
+    """x = alpha e_j gives y = sign(alpha) s_j H[:, j], so |y| = 1 everywhere:
+    every code has the magnitude index of the level nearest 1 and
+    x_hat = level * fp16(|alpha|) * sign(alpha) * e_j."""
+    s = o.sign_flips()
+    H = scipy.linalg.hadamard(128)
+    level = o.code_magnitudes(bits)[qs_star]
+    for j, alpha in [(0, -3.0), (5, 2.5), (127, -0.1)]:
+        x = np.zeros(128, F32)
+        x[j] = alpha
+        codes, n16 = o.quantize_groups(x, bits)
+        assert float(n16) == float(np.float16(abs(alpha)))
+        assert np.all(codes & (2 ** (bits - 1) - 1) == qs_star)
+        sign_y = np.sign(alpha) * (-1 if s[j] else 1) * H[:, j]
+        assert np.all((codes >> (bits - 1)) == (sign_y < 0))
+        xh = o.dequant(codes, n16, bits)
+        want = np.zeros(128)
+        want[j] = float(level) * float(np.float16(abs(alpha))) * np.sign(alpha)
+        np.testing.assert_allclose(xh, want, atol=1e-12)
+    # the worked number for turbo3, alpha = -3: 0.7558594 * 3
+    if bits == 3:
+        x = np.zeros(128, F32); x[0] = -3.0
+        c, n = o.quantize_groups(x, 3)
+        assert abs(o.dequant(c, n, 3)[0] + 2.267578125) < 1e-12
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_quantizer_symmetries(bits):
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((300, 128)).astype(F32)
+    c, n = o.quantize_groups(x, bits)
+    cn, nn = o.quantize_groups(-x, bits)
+    top = 1 << (bits - 1)
+    np.testing.assert_array_equal(cn, c ^ top)          # no y is exactly 0 here
+    np.testing.assert_array_equal(nn, n)
+    c4, n4 = o.quantize_groups(x * F32(4.0), bits)      # power-of-two scaling is exact
+    np.testing.assert_array_equal(c4, c)
+    np.testing.assert_array_equal(n4.astype(np.float32), n.astype(np.float32) * 4)
+
+
+def test_quantizer_zero_and_norm():
+    c, n = o.quantize_groups(np.zeros((2, 128), F32), 3)
+    assert np.all(c == 0) and np.all(n == 0)
+    x = np.zeros(128, F32); x[0] = 3; x[1] = 4
+    _, n = o.quantize_groups(x, 3)
+    assert float(n) == 5.0
+
+
+def test_quantizer_keeps_denormals():
+    """x = 2^-70: each square 2^-140 is a float32 subnormal.  Without
+    flushing, the tree sum is 2^-133 exactly (it would be 0 with flushing),
+    the norm is float32(2^-66.5) and the codes are those of the same group
+    scaled by 2^70 (power-of-two scaling is exact)."""
+    x = np.full((1, 128), 2.0 ** -70, F32)
+    x[0, ::3] *= -1
+    assert o.sum_squares_tree(x)[0] == F32(2.0 ** -133)
+    c, n = o.quantize_groups(x, 3)
+    c_big, _ = o.quantize_groups(x * F32(2.0 ** 70), 3)
+    np.testing.assert_array_equal(c, c_big)
+    assert float(n[0]) == 0.0          # 2^-66.5 is below the float16 range
+
+
+@pytest.mark.parametrize("bits,dist", [(2, 0.1175), (3, 0.03455), (4, 0.009501)])
+def test_quantizer_distortion_near_lloyd_max(bits, dist):
+    """Relative MSE on iid normal groups sits just below the scalar Lloyd-Max
+    distortion (rotated coordinates of a sphere are lighter-tailed)."""
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((20000, 128)).astype(F32)
+    c, n = o.quantize_groups(x, bits)
+    xh = o.dequant(c, n, bits)
+    rel = np.sum((xh - x) ** 2) / np.sum(x.astype(np.float64) ** 2)
+    assert 0.93 * dist < rel < 1.01 * dist
+
+
+# ---------------------------------------------------------------- packing
+
+def test_pack_hand_example_turbo3():
+    """codes 1,2,3,4,5,6,7,0 as 3-bit little-endian fields: the integer
+    1 + 2*8 + 3*8^2 + 4*8^3 + 5*8^4 + 6*8^5 + 7*8^6 = 0x1F58D1, i.e. bytes
+    D1 58 1F, followed by zero bytes."""
+    codes = np.zeros(128, np.uint8)
+    codes[:8] = [1, 2, 3, 4, 5, 6, 7, 0]
+    p = o.pack_codes(codes, 3)
+    assert p.shape == (48,)
+    assert list(p[:3]) == [0xD1, 0x58, 0x1F]
+    assert not p[3:].any()
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_pack_roundtrip_and_sizes(bits):
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 2 ** bits, (7, 3, 128)).astype(np.uint8)
+    p = o.pack_codes(codes, bits)
+    assert p.shape == (7, 3, 16 * bits)
+    np.testing.assert_array_equal(o.unpack_codes(p, bits), codes)
+    assert o.group_bytes(bits) + 2 == {2: 34, 3: 50, 4: 66}[bits]
+
+
+def test_turbo2_compression_is_7_5x():
+    """128 fp16 values (256 B) against 32 code bytes + one fp16 norm."""
+    assert round(256 / (o.group_bytes(2) + 2), 1) == 7.5
+
+
+# ---------------------------------------------------------------- dequant / cache
+
+def test_rotated_domain_inner_products():
+    """<H(s.q)/sqrt(128), w_hat> equals <q, x_hat> (orthonormal transform)."""
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((10, 128)).astype(F32)
+    q = rng.standard_normal(128)
+    c, n = o.quantize_groups(x, 3)
+    w = o.dequant_rotated(c, n, 3)
+    xh = o.dequant(c, n, 3)
+    s = o.sign_flips()
+    qr = o.wht_butterfly(np.where(s, -q, q)) / np.sqrt(128)
+    np.testing.assert_allclose(w @ qr, xh @ q, atol=1e-12)
+
+
+def test_set_rows_scatter_semantics():
+    rng = np.random.default_rng(7)
+    cache = o.new_cache(3, 256, 2, 10)
+    src = rng.standard_normal((3, 2, 256)).astype(F32)
+    o.set_rows(cache, src, np.array([7, 0, 4]))
+    for r, cell in enumerate([7, 0, 4]):
+        for h in range(2):
+            for g in range(2):
+                c, n = o.quantize_groups(src[r, h, g * 128:(g + 1) * 128], 3)
+                np.testing.assert_array_equal(cache["codes"][h, cell, g], o.pack_codes(c, 3))
+                assert cache["norms"][h, cell, g] == n
+    untouched = [1, 2, 3, 5, 6, 8, 9]
+    assert not cache["codes"][:, untouched].any()
+    assert not cache["norms"][:, untouched].astype(np.float32).any()
+
+
+# ---------------------------------------------------------------- attention
+
+def _sdpa_fp64(q, k, v, scale, q_pos0):
+    import torch
+    n_rows, n_q, d = q.shape
+    n_kv, L, _ = k.shape
+    rep = n_q // n_kv
+    qt = torch.from_numpy(q).permute(1, 0, 2)
+    kt = torch.from_numpy(np.repeat(k, rep, axis=0))
+    vt = torch.from_numpy(np.repeat(v, rep, axis=0))
+    mask = torch.from_numpy(np.arange(L)[None, :] <= (q_pos0 + np.arange(n_rows))[:, None])
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale)
+    return out.permute(1, 0, 2).numpy()
+
+
+@pytest.mark.parametrize("n_rows,L,q_pos0,n_q,n_kv", [(1, 37, 36, 8, 2), (5, 40, 35, 4, 4),
+                                                       (6, 6, 0, 2, 1), (3, 1024, 1021, 16, 8)])
+def test_attention_matches_sdpa(n_rows, L, q_pos0, n_q, n_kv):
+    rng = np.random.default_rng(8)
+    d = 64
+    q = rng.standard_normal((n_rows, n_q, d))
+    k = rng.standard_normal((n_kv, L, d))
+    v = rng.standard_normal((n_kv, L, d))
+    got = o.attention(q, k, v, 0.125, q_pos0, block=2)
+    np.testing.assert_allclose(got, _sdpa_fp64(q, k, v, 0.125, q_pos0), atol=1e-12)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(9)
+    k = rng.standard_normal((1, 9, 16)); v = rng.standard_normal((1, 9, 16))
+    q = rng.standard_normal((3, 2, 16))
+    out = o.attention(q, k[:, :1], v[:, :1], 0.3, 0)          # one key
+    np.testing.assert_allclose(out[0, 0], v[0, 0], atol=1e-15)
+    out = o.attention(np.zeros((1, 1, 16)), k, v, 1.0, 8)   # q = 0: mean of values
+    np.testing.assert_allclose(out[0, 0], v[0].mean(axis=0), atol=1e-14)
+    out = o.attention(q, k, v, 0.3, 0)                      # row 0 sees key 0 only
+    np.testing.assert_allclose(out[0, 1], v[0, 0], atol=1e-15)
+
+
+def test_decode_prefill_use_dequantized_cache():
+    """attn_decode / attn_prefill are attention over dequant_cache rows."""
+    rng = np.random.default_rng(10)
+    kc = o.new_cache(3, 128, 2, 20); vc = o.new_cache(3, 128, 2, 20)
+    kk = rng.standard_normal((20, 2, 128)).astype(F32)
+    vv = rng.standard_normal((20, 2, 128)).astype(F32)
+    o.set_rows(kc, kk, np.arange(20)); o.set_rows(vc, vv, np.arange(20))
+    q = rng.standard_normal((4, 128))
+    k = o.dequant_cache(kc, 17); v = o.dequant_cache(vc, 17)
+    np.testing.assert_allclose(o.attn_decode(kc, vc, 17, q, 0.1),
+                               _sdpa_fp64(q[None], k, v, 0.1, 16)[0], atol=1e-12)
+    qp = rng.standard_normal((5, 4, 128))
+    np.testing.assert_allclose(o.attn_prefill(kc, vc, 17, qp, 12, 0.1),
+                               _sdpa_fp64(qp, k, v, 0.1, 12), atol=1e-12)
+    # dequantized rows are close to the originals (3-bit: ~3.5% relative MSE)
+    err = np.sum((k - kk[:17].transpose(1, 0, 2)) ** 2) / np.sum(kk[:17].astype(np.float64) ** 2)
+    assert err < 0.05
+
+
+# ---------------------------------------------------------------- int8
+
+def test_int8_brute_force_and_page_invariance():
+    from quantized_kv_cache_tq_amd import inputs
+    a = inputs.int8_prompt(seed=3, ctx=96, n_q=5, n_q_heads=2, n_kv=1, d=8)
+    b = inputs.int8_prompt(seed=3, ctx=96, n_q=5, n_q_heads=2, n_kv=1, d=8, identity_pages=True)
+    q0 = 96 - 5
+    got = o.attn_int8_prompt(a["q"], a["k8"], a["v8"], a["k_scale"], a["v_scale"],
+                             a["page_table"], 96, q0, 0.35)
+    got_id = o.attn_int8_prompt(b["q"], b["k8"], b["v8"], b["k_scale"], b["v_scale"],
+                                b["page_table"], 96, q0, 0.35)
+    np.testing.assert_array_equal(got, got_id)
+    assert not np.array_equal(a["page_table"], b["page_table"])
+    # brute force in pure Python over the logical copies
+    kl = a["k8_logical"].astype(np.float64) * a["ks_logical"].astype(np.float64)[..., None]
+    vl = a["v8_logical"].astype(np.float64) * a["vs_logical"].astype(np.float64)[..., None]
+    for i in range(5):
+        for h in range(2):
+            sc = [0.35 * sum(float(a["q"][i, h, t]) * kl[j, 0, t] for t in range(8))
+                  for j in range(q0 + i + 1)]
+            m = max(sc)
+            w = [np.exp(s - m) for s in sc]
+            ref = [sum(w[j] * vl[j, 0, t] for j in range(len(w))) / sum(w) for t in range(8)]
+            np.testing.assert_allclose(got[i, h], ref, atol=1e-12)
