@@ -1,0 +1,205 @@
+/*
+ * tq.h -- C ABI of libtq.so: attention over a TurboQuant-compressed KV cache
+ * on one AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *   [PR36]    llama-cpp-turboquant pull request 36: (a) SET_ROWS butterfly on
+ *             warp shuffles, (b) asymmetric-K head-dim fix, (c) decode
+ *             Q x centroid lookup table, (d) four VEC flash-attention changes.
+ *   [PR28]    "HIP/turbo3: graph-safe decode + inline-dequant TILE prefill on
+ *             gfx1201 (RDNA4)".
+ *   [QSA1821] "#1821 qsa_prompt_attn: int8 K/V prefetched in registers and
+ *             sharing one buffer (Turing / sm_75)".
+ *
+ * General rules for every entry point:
+ *   - Pointers are DEVICE pointers unless marked [host].  The caller owns every
+ *     buffer; the library never allocates, frees or memsets device memory, so
+ *     every call may be recorded into a HIP graph (the failure of [PR28]
+ *     "Graph-safe decode" was an allocation during stream capture).
+ *   - All argument checks run on the host before any HIP call; a rejected
+ *     call returns a negative tq_status and enqueues nothing.  TQ_OK means the
+ *     work was enqueued on `stream`; faults surface at the caller's
+ *     synchronization.  TQ_ERR_HIP reports a failed launch.
+ *   - Calls that share an output or workspace buffer on the same device must
+ *     be ordered by the caller (same stream or events).
+ *   - No call reads or writes memory outside the extents stated here for
+ *     valid arguments.  Values in device buffers that the host cannot check
+ *     (cell indices, page-table entries) are bounds-checked in the kernels:
+ *     an out-of-range cell index drops that row, an out-of-range page entry
+ *     masks that page's keys; results are then unspecified but no access
+ *     leaves the stated extents.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A hipStream_t (NULL = the legacy null stream). */
+typedef struct ihipStream_t *tq_stream_t;
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARG = -1, /* a null/misaligned pointer or an out-of-contract size */
+  TQ_ERR_UNSUPPORTED = -2, /* a valid request this build has no kernel for */
+  TQ_ERR_WORKSPACE = -3,   /* workspace pointer null/misaligned or too small */
+  TQ_ERR_HIP = -4          /* the HIP runtime reported an error */
+} tq_status;
+
+/* Cache element types ([PR36] (c)/(d) results table: turbo2, turbo3, turbo4):
+ * b = 2, 3, 4 bits per element, 2^b reconstruction levels. */
+typedef enum { TQ_TURBO2 = 2, TQ_TURBO3 = 3, TQ_TURBO4 = 4 } tq_type;
+
+/* Element type of a query tensor. */
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
+
+/*
+ * One compressed cache (the K cache or the V cache of one layer).
+ *
+ * Every head_dim-wide row of every kv head is cut into G = head_dim/128
+ * groups of 128 elements ([PR36] (a): 7 butterfly stages, h = 1..64; a
+ * 192-wide head is padded to 256 in [PR36] (b)).  Each group stores
+ *   - 16*b code bytes: one little-endian bit stream in which element e's
+ *     b-bit code occupies stream bits b*e .. b*e+b-1, low bit first (stream
+ *     bit k is bit k%8 of byte k/8).  A code is a (b-1)-bit magnitude index
+ *     ("qs") with the sign bit on top (set = negative); 8 elements take 3
+ *     bytes for turbo3, as the "2 qs bytes + 1 signs byte" of [PR36] (c);
+ *   - one float16 norm (the group's L2 norm), so a turbo2 group is 34 bytes
+ *     against 256 for float16, the 7.5x of [PR36] (d).
+ * Planes (head-major, so one kv head's cells are contiguous):
+ *   codes : uint8  [n_kv_heads][n_cells][G][16*b]   16-byte aligned
+ *   norms : uint16 [n_kv_heads][n_cells][G]         float16 bits, 4-byte aligned
+ */
+typedef struct {
+  int32_t type;       /* tq_type */
+  int32_t head_dim;   /* multiple of 128, >= 128 */
+  int32_t n_kv_heads; /* >= 1 */
+  int32_t reserved;   /* must be 0 */
+  int64_t n_cells;    /* capacity in cells (tokens), >= 1 */
+  uint8_t *codes;     /* device */
+  uint16_t *norms;    /* device */
+} tq_cache;
+
+const char *tq_version(void);
+const char *tq_status_str(int status);
+
+/* [host] Byte sizes of the two planes of a cache with these dimensions. */
+tq_status tq_cache_plane_bytes(int type, int32_t head_dim, int32_t n_kv_heads, int64_t n_cells,
+                               size_t *codes_bytes /*[host]*/, size_t *norms_bytes /*[host]*/);
+
+/*
+ * [host] The fixed parameters of the code ([PR36] (c) gives only the number of
+ * levels; these are chosen values, identical for K, V and Q):
+ *   code_values[2^b]       reconstruction level of each code: +-magnitude, the
+ *                          magnitudes being the Lloyd-Max levels of N(0,1)
+ *                          rounded to float16;
+ *   mag_thresholds[2^(b-1)-1]  midpoints between neighbouring magnitudes;
+ *   sign_words[2]          the random sign flip: element d of a group is
+ *                          negated iff bit d%64 of sign_words[d/64] is set
+ *                          (the first two SplitMix64 outputs from state 0).
+ * Any output pointer may be NULL.
+ */
+tq_status tq_codebook(int type, float *code_values /*[host]*/, float *mag_thresholds /*[host]*/,
+                      uint64_t *sign_words /*[host]*/);
+
+/*
+ * SET_ROWS ([PR36] (a)): quantize n_rows rows into the cache cells cell_idx[r].
+ *   src      float32 [n_rows][n_kv_heads][head_dim], 16-byte aligned
+ *   cell_idx int64 [n_rows], each in [0, n_cells); duplicates give an
+ *            unspecified one of the rows; out-of-range rows are dropped.
+ * Per 128-element group x, in IEEE float32 without fused multiply-add:
+ *   n2 = sum of x_d^2 added in the butterfly's pairing order (partials at
+ *   distance 1, 2, 4, .., 64); norm = sqrt(n2) correctly rounded, stored as
+ *   float16 (nearest-even); u = sign flip of x; seven butterfly stages
+ *   h = 1, 2, .., 64 in that order, the lower element of each pair taking
+ *   a + b and the upper a - b ([PR36] (a)); y = u * (1/norm) (0 if norm is
+ *   not > 0); sign bit = (y < 0); qs = #{k : |y| > mag_thresholds[k]}.
+ * The written bytes and norms are a pure function of the source values.
+ * n_rows == 0 is a no-op.
+ */
+tq_status tq_set_rows(const tq_cache *dst, const float *src, const int64_t *cell_idx,
+                      int64_t n_rows, tq_stream_t stream);
+
+/*
+ * Decode attention: one query row over cells [0, kv_len) ([PR36] (c),(d):
+ * decode over a turbo cache, the single-column flash-attention case;
+ * [PR28] "Graph-safe decode").
+ *   q    [n_q_heads][head_dim], float32 or bfloat16 (q_dtype), 16-byte aligned
+ *   out  float32 [n_q_heads][head_dim], 16-byte aligned
+ * Computes, for q head h and kv head g = h / (n_q_heads / n_kv_heads):
+ *   out[h] = sum_j softmax_j(scale * <q[h], k_hat_j>) v_hat_j,
+ * with k_hat, v_hat the dequantized rows: x_hat = s (.) H w / sqrt(128) per
+ * group, w_d = code_values[code_d] * norm / sqrt(128), H the 128-point
+ * Sylvester-Hadamard matrix.  (The kernels work in the rotated domain,
+ * rotating q in and the output back out.)
+ * Requires k and v of the same type, head_dim and n_kv_heads,
+ * 1 <= kv_len <= n_cells, n_q_heads a multiple of n_kv_heads with at most 8
+ * q heads per kv head, and head_dim == 128 in this build.
+ * sparse_v_tau must be 0 in this build (skipping value rows with small
+ * weights, [PR36] (d) item 3, returns TQ_ERR_UNSUPPORTED).
+ * The workspace holds per-split partial results; its size comes from
+ * tq_attn_decode_workspace for the same arguments on the same device.
+ */
+tq_status tq_attn_decode_workspace(const tq_cache *k, int64_t kv_len, int32_t n_q_heads,
+                                   size_t *bytes /*[host]*/);
+tq_status tq_attn_decode(const tq_cache *k, const tq_cache *v, int64_t kv_len, const void *q,
+                         int q_dtype, int32_t n_q_heads, float scale, float sparse_v_tau,
+                         float *out, void *workspace, size_t workspace_bytes, tq_stream_t stream);
+
+/*
+ * Prefill / speculative-verify attention: n_rows query rows
+ * ([PR28] "Inline-dequant TILE prefill": multi-row batches that read the
+ * turbo cache directly, dequantizing as the tiles are loaded).
+ *   q    [n_rows][n_q_heads][head_dim], float32 or bfloat16, 16-byte aligned
+ *   out  float32 [n_rows][n_q_heads][head_dim], 16-byte aligned
+ * Query row r sits at position q_pos0 + r and sees cells j <= q_pos0 + r
+ * (causal, aligned so that the last row sees q_pos0 + n_rows - 1 keys + 1).
+ * Same formula and head mapping as decode.  Requires
+ * 0 <= q_pos0, q_pos0 + n_rows <= kv_len <= n_cells; n_rows == 0 is a no-op.
+ * This build supports turbo3 with head_dim 256 and at most 8 q heads per
+ * kv head (others: TQ_ERR_UNSUPPORTED, as [PR28] "Scope / honesty" limits
+ * its fast path to that case).
+ */
+tq_status tq_attn_prefill_workspace(const tq_cache *k, int64_t n_rows, int32_t n_q_heads,
+                                    int64_t kv_len, size_t *bytes /*[host]*/);
+tq_status tq_attn_prefill(const tq_cache *k, const tq_cache *v, int64_t kv_len, const void *q,
+                          int q_dtype, int64_t n_rows, int32_t n_q_heads, int64_t q_pos0,
+                          float scale, float *out, void *workspace, size_t workspace_bytes,
+                          tq_stream_t stream);
+
+/*
+ * Paged int8 prompt attention ([QSA1821] What / Change).
+ *   q          float32 [n_q][n_q_heads][head_dim], 16-byte aligned
+ *   k, v       int8 [n_phys_pages*32][n_kv_heads][head_dim], 16-byte aligned
+ *   k_scale, v_scale  float16 bits [n_phys_pages*32][n_kv_heads], 4-byte aligned
+ *   page_table int32 [ceil(ctx_len/32)]: logical 32-cell chunk i is stored at
+ *              physical chunk page_table[i] (0 <= entry < n_phys_pages)
+ *   out        float32 [n_q][n_q_heads][head_dim], 16-byte aligned
+ * Logical cell j is physical row page_table[j/32]*32 + j%32; its key is
+ * k[row][g][:] * k_scale[row][g] (symmetric, no zero point), likewise v.
+ * Query i sits at position q_pos0 + i and sees logical cells
+ * j <= q_pos0 + i; same softmax formula and head mapping as decode.
+ * The result depends only on the logical order, never on where the chunks
+ * sit physically ([QSA1821] Change: same bytes, same arithmetic, same bits).
+ * Requires 0 <= q_pos0, q_pos0 + n_q <= ctx_len, head_dim == 128 and at most
+ * 16 q heads per kv head in this build.
+ */
+tq_status tq_attn_int8_prompt_workspace(int64_t n_q, int32_t n_q_heads, int32_t n_kv_heads,
+                                        int32_t head_dim, int64_t ctx_len,
+                                        size_t *bytes /*[host]*/);
+tq_status tq_attn_int8_prompt(const float *q, int64_t n_q, int32_t n_q_heads, const int8_t *k,
+                              const int8_t *v, const uint16_t *k_scale, const uint16_t *v_scale,
+                              int32_t n_kv_heads, int32_t head_dim, const int32_t *page_table,
+                              int64_t n_phys_pages, int64_t ctx_len, int64_t q_pos0, float scale,
+                              float *out, void *workspace, size_t workspace_bytes,
+                              tq_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

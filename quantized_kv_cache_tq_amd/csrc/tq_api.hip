@@ -1,0 +1,232 @@
+// tq_api.hip -- host side of the C ABI declared in include/tq.h: argument
+// validation, workspace sizing and kernel dispatch.  Nothing here allocates
+// device memory; every check happens before the first HIP call.
+#include <string.h>
+
+#include "tq_common.h"
+#include "tq_launch.h"
+
+using namespace tq;
+
+namespace {
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool valid_type(int t) { return t == TQ_TURBO2 || t == TQ_TURBO3 || t == TQ_TURBO4; }
+
+tq_status check_cache(const tq_cache *c) {
+  if (!c) return TQ_ERR_INVALID_ARG;
+  if (!valid_type(c->type) || c->head_dim < kGroup || c->head_dim % kGroup != 0 ||
+      c->n_kv_heads < 1 || c->n_cells < 1 || c->reserved != 0)
+    return TQ_ERR_INVALID_ARG;
+  if (!c->codes || !c->norms || !aligned(c->codes, 16) || !aligned(c->norms, 4))
+    return TQ_ERR_INVALID_ARG;
+  return TQ_OK;
+}
+
+tq_status check_pair(const tq_cache *k, const tq_cache *v) {
+  tq_status s = check_cache(k);
+  if (s != TQ_OK) return s;
+  s = check_cache(v);
+  if (s != TQ_OK) return s;
+  if (k->type != v->type || k->head_dim != v->head_dim || k->n_kv_heads != v->n_kv_heads)
+    return TQ_ERR_INVALID_ARG;
+  return TQ_OK;
+}
+
+tq_status from_hip(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *tq_version(void) { return "libtq 0.1.0 (gfx950)"; }
+
+const char *tq_status_str(int status) {
+  switch (status) {
+    case TQ_OK: return "ok";
+    case TQ_ERR_INVALID_ARG: return "invalid argument";
+    case TQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case TQ_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case TQ_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+tq_status tq_cache_plane_bytes(int type, int32_t head_dim, int32_t n_kv_heads, int64_t n_cells,
+                               size_t *codes_bytes, size_t *norms_bytes) {
+  if (!valid_type(type) || head_dim < kGroup || head_dim % kGroup || n_kv_heads < 1 ||
+      n_cells < 1)
+    return TQ_ERR_INVALID_ARG;
+  const size_t groups = (size_t)n_kv_heads * (size_t)n_cells * (size_t)(head_dim / kGroup);
+  if (codes_bytes) *codes_bytes = groups * 16u * (size_t)type;
+  if (norms_bytes) *norms_bytes = groups * 2u;
+  return TQ_OK;
+}
+
+tq_status tq_codebook(int type, float *code_values, float *mag_thresholds, uint64_t *sign_words) {
+  if (!valid_type(type)) return TQ_ERR_INVALID_ARG;
+  const int n = 1 << type;
+  for (int c = 0; c < n; ++c) {
+    if (!code_values) break;
+    code_values[c] = type == 2 ? code_value<2>(c) : type == 3 ? code_value<3>(c) : code_value<4>(c);
+  }
+  for (int k = 1; k < n / 2; ++k) {
+    if (!mag_thresholds) break;
+    mag_thresholds[k - 1] =
+        type == 2 ? threshold<2>(k) : type == 3 ? threshold<3>(k) : threshold<4>(k);
+  }
+  if (sign_words) {
+    sign_words[0] = kSignWord0;
+    sign_words[1] = kSignWord1;
+  }
+  return TQ_OK;
+}
+
+tq_status tq_set_rows(const tq_cache *dst, const float *src, const int64_t *cell_idx,
+                      int64_t n_rows, tq_stream_t stream) {
+  tq_status s = check_cache(dst);
+  if (s != TQ_OK) return s;
+  if (n_rows < 0) return TQ_ERR_INVALID_ARG;
+  if (n_rows == 0) return TQ_OK;
+  if (!src || !cell_idx || !aligned(src, 16) || !aligned(cell_idx, 8)) return TQ_ERR_INVALID_ARG;
+  return from_hip(launch_set_rows(*dst, src, cell_idx, n_rows, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------- decode
+
+static tq_status decode_check(const tq_cache *k, int64_t kv_len, int32_t n_q_heads) {
+  tq_status s = check_cache(k);
+  if (s != TQ_OK) return s;
+  if (kv_len < 1 || kv_len > k->n_cells) return TQ_ERR_INVALID_ARG;
+  if (n_q_heads < 1 || n_q_heads % k->n_kv_heads) return TQ_ERR_INVALID_ARG;
+  if (k->head_dim != 128 || n_q_heads / k->n_kv_heads > 8) return TQ_ERR_UNSUPPORTED;
+  return TQ_OK;
+}
+
+tq_status tq_attn_decode_workspace(const tq_cache *k, int64_t kv_len, int32_t n_q_heads,
+                                   size_t *bytes) {
+  tq_status s = decode_check(k, kv_len, n_q_heads);
+  if (s != TQ_OK) return s;
+  if (!bytes) return TQ_ERR_INVALID_ARG;
+  DecodePlan p;
+  if (plan_decode(*k, kv_len, n_q_heads, &p) != hipSuccess) return TQ_ERR_HIP;
+  *bytes = p.workspace_bytes;
+  return TQ_OK;
+}
+
+tq_status tq_attn_decode(const tq_cache *k, const tq_cache *v, int64_t kv_len, const void *q,
+                         int q_dtype, int32_t n_q_heads, float scale, float sparse_v_tau,
+                         float *out, void *workspace, size_t workspace_bytes,
+                         tq_stream_t stream) {
+  tq_status s = check_pair(k, v);
+  if (s != TQ_OK) return s;
+  s = decode_check(k, kv_len, n_q_heads);
+  if (s != TQ_OK) return s;
+  if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return TQ_ERR_INVALID_ARG;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
+  if (!(scale == scale) || !(sparse_v_tau == sparse_v_tau) || sparse_v_tau < 0.f)
+    return TQ_ERR_INVALID_ARG;
+  if (sparse_v_tau != 0.f) return TQ_ERR_UNSUPPORTED;
+  DecodePlan p;
+  if (plan_decode(*k, kv_len, n_q_heads, &p) != hipSuccess) return TQ_ERR_HIP;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.workspace_bytes)
+    return TQ_ERR_WORKSPACE;
+  return from_hip(launch_decode(*k, *v, kv_len, q, q_dtype, n_q_heads, scale, out, workspace, p,
+                                (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------- prefill
+
+static tq_status prefill_check(const tq_cache *k, int64_t n_rows, int32_t n_q_heads,
+                               int64_t kv_len) {
+  tq_status s = check_cache(k);
+  if (s != TQ_OK) return s;
+  if (n_rows < 0 || kv_len < 1 || kv_len > k->n_cells) return TQ_ERR_INVALID_ARG;
+  if (n_q_heads < 1 || n_q_heads % k->n_kv_heads) return TQ_ERR_INVALID_ARG;
+  if (k->type != TQ_TURBO3 || k->head_dim != 256 || n_q_heads / k->n_kv_heads > 8)
+    return TQ_ERR_UNSUPPORTED;
+  return TQ_OK;
+}
+
+tq_status tq_attn_prefill_workspace(const tq_cache *k, int64_t n_rows, int32_t n_q_heads,
+                                    int64_t kv_len, size_t *bytes) {
+  tq_status s = prefill_check(k, n_rows, n_q_heads, kv_len);
+  if (s != TQ_OK) return s;
+  if (!bytes) return TQ_ERR_INVALID_ARG;
+  PrefillPlan p;
+  if (plan_prefill(*k, n_rows, n_q_heads, kv_len, &p) != hipSuccess) return TQ_ERR_HIP;
+  *bytes = p.workspace_bytes;
+  return TQ_OK;
+}
+
+tq_status tq_attn_prefill(const tq_cache *k, const tq_cache *v, int64_t kv_len, const void *q,
+                          int q_dtype, int64_t n_rows, int32_t n_q_heads, int64_t q_pos0,
+                          float scale, float *out, void *workspace, size_t workspace_bytes,
+                          tq_stream_t stream) {
+  tq_status s = check_pair(k, v);
+  if (s != TQ_OK) return s;
+  s = prefill_check(k, n_rows, n_q_heads, kv_len);
+  if (s != TQ_OK) return s;
+  if (q_pos0 < 0 || q_pos0 + n_rows > kv_len) return TQ_ERR_INVALID_ARG;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
+  if (!(scale == scale)) return TQ_ERR_INVALID_ARG;
+  if (n_rows == 0) return TQ_OK;
+  if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return TQ_ERR_INVALID_ARG;
+  PrefillPlan p;
+  if (plan_prefill(*k, n_rows, n_q_heads, kv_len, &p) != hipSuccess) return TQ_ERR_HIP;
+  if (p.workspace_bytes && (!workspace || !aligned(workspace, 256) ||
+                            workspace_bytes < p.workspace_bytes))
+    return TQ_ERR_WORKSPACE;
+  return from_hip(launch_prefill(*k, *v, kv_len, q, q_dtype, n_rows, n_q_heads, q_pos0, scale,
+                                 out, workspace, p, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------- int8 prompt
+
+static tq_status int8_check(int64_t n_q, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                            int64_t ctx_len) {
+  if (n_q < 0 || ctx_len < 1 || n_kv_heads < 1 || n_q_heads < 1 || n_q_heads % n_kv_heads)
+    return TQ_ERR_INVALID_ARG;
+  if (head_dim < 1) return TQ_ERR_INVALID_ARG;
+  if (head_dim != 128 || n_q_heads / n_kv_heads > 16) return TQ_ERR_UNSUPPORTED;
+  return TQ_OK;
+}
+
+tq_status tq_attn_int8_prompt_workspace(int64_t n_q, int32_t n_q_heads, int32_t n_kv_heads,
+                                        int32_t head_dim, int64_t ctx_len, size_t *bytes) {
+  tq_status s = int8_check(n_q, n_q_heads, n_kv_heads, head_dim, ctx_len);
+  if (s != TQ_OK) return s;
+  if (!bytes) return TQ_ERR_INVALID_ARG;
+  Int8Plan p;
+  if (plan_int8(n_q, n_q_heads, n_kv_heads, ctx_len, &p) != hipSuccess) return TQ_ERR_HIP;
+  *bytes = p.workspace_bytes;
+  return TQ_OK;
+}
+
+tq_status tq_attn_int8_prompt(const float *q, int64_t n_q, int32_t n_q_heads, const int8_t *k,
+                              const int8_t *v, const uint16_t *k_scale, const uint16_t *v_scale,
+                              int32_t n_kv_heads, int32_t head_dim, const int32_t *page_table,
+                              int64_t n_phys_pages, int64_t ctx_len, int64_t q_pos0, float scale,
+                              float *out, void *workspace, size_t workspace_bytes,
+                              tq_stream_t stream) {
+  tq_status s = int8_check(n_q, n_q_heads, n_kv_heads, head_dim, ctx_len);
+  if (s != TQ_OK) return s;
+  if (q_pos0 < 0 || q_pos0 + n_q > ctx_len || n_phys_pages < 1) return TQ_ERR_INVALID_ARG;
+  if (!(scale == scale)) return TQ_ERR_INVALID_ARG;
+  if (n_q == 0) return TQ_OK;
+  if (!q || !k || !v || !k_scale || !v_scale || !page_table || !out) return TQ_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(k_scale, 4) ||
+      !aligned(v_scale, 4) || !aligned(page_table, 4) || !aligned(out, 16))
+    return TQ_ERR_INVALID_ARG;
+  Int8Plan p;
+  if (plan_int8(n_q, n_q_heads, n_kv_heads, ctx_len, &p) != hipSuccess) return TQ_ERR_HIP;
+  if (p.workspace_bytes && (!workspace || !aligned(workspace, 256) ||
+                            workspace_bytes < p.workspace_bytes))
+    return TQ_ERR_WORKSPACE;
+  return from_hip(launch_int8(q, n_q, n_q_heads, k, v, k_scale, v_scale, n_kv_heads, page_table,
+                              n_phys_pages, ctx_len, q_pos0, scale, out, workspace, p,
+                              (hipStream_t)stream));
+}
+
+}  // extern "C"

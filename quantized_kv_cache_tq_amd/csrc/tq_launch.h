@@ -1,0 +1,58 @@
+// tq_launch.h -- launch plans and launchers behind the C ABI (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+// Number of compute units of the current device (cached per device).
+hipError_t device_cu_count(int *n_cu);
+
+hipError_t launch_set_rows(const tq_cache &c, const float *src, const int64_t *cell_idx,
+                           int64_t n_rows, hipStream_t stream);
+
+struct DecodePlan {
+  int tiles_per_wave;    // 16-key tiles per wave
+  int keys_per_split;    // 64 * tiles_per_wave (4 waves per workgroup)
+  int n_split;           // workgroups per kv head
+  size_t workspace_bytes;
+};
+hipError_t plan_decode(const tq_cache &k, int64_t kv_len, int32_t n_q_heads, DecodePlan *p);
+hipError_t launch_decode(const tq_cache &k, const tq_cache &v, int64_t kv_len, const void *q,
+                         int q_dtype, int32_t n_q_heads, float scale, float *out, void *workspace,
+                         const DecodePlan &p, hipStream_t stream);
+
+struct PrefillPlan {
+  int rows_per_tile;     // query rows per workgroup
+  int n_row_tiles;
+  int keys_per_split;    // key range per workgroup (multiple of the key tile)
+  int max_splits;        // splits of the longest row tile
+  size_t workspace_bytes;
+};
+hipError_t plan_prefill(const tq_cache &k, int64_t n_rows, int32_t n_q_heads, int64_t kv_len,
+                        PrefillPlan *p);
+hipError_t launch_prefill(const tq_cache &k, const tq_cache &v, int64_t kv_len, const void *q,
+                          int q_dtype, int64_t n_rows, int32_t n_q_heads, int64_t q_pos0,
+                          float scale, float *out, void *workspace, const PrefillPlan &p,
+                          hipStream_t stream);
+
+struct Int8Plan {
+  int queries_per_tile;
+  int n_q_tiles;
+  int keys_per_split;
+  int n_split;
+  size_t workspace_bytes;
+};
+hipError_t plan_int8(int64_t n_q, int32_t n_q_heads, int32_t n_kv_heads, int64_t ctx_len,
+                     Int8Plan *p);
+hipError_t launch_int8(const float *q, int64_t n_q, int32_t n_q_heads, const int8_t *k,
+                       const int8_t *v, const uint16_t *k_scale, const uint16_t *v_scale,
+                       int32_t n_kv_heads, const int32_t *page_table, int64_t n_phys_pages,
+                       int64_t ctx_len, int64_t q_pos0, float scale, float *out, void *workspace,
+                       const Int8Plan &p, hipStream_t stream);
+
+}  // namespace tq
