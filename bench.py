@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Benchmark of the TurboQuant KV-cache attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one pass over every hot-path kernel, on synthetic inputs already
+resident in HBM:
+  1. tq_set_rows: quantize one 32768-row K and V cache (4 kv heads, d 128,
+     turbo3, outlier channels);
+  2. tq_attn_decode: one decode token across LAYERS layers, each layer
+     attending over its own 32768-cell turbo3 cache (32 q / 4 kv heads,
+     bf16 q); the LAYERS caches (>256 MB in total) are cycled so every call
+     streams its cache from HBM, and the calls are replayed from a HIP graph;
+  3. tq_attn_prefill: 2048 causal rows, 16 q / 8 kv heads, d 256, turbo3;
+  4. tq_attn_int8_prompt: 2048 queries x 40000 cells, 8 q / 1 kv head, d 128.
+Each phase is timed with HIP events on the stream its kernels run on; the
+step time is their sum.  `value` is the decode leg's KV bytes (algorithmic:
+packed codes + norms of every key and kv head) per second.
+
+Prints ONE JSON line.  The CPU baseline runs the oracle (oracle/) on a
+bounded sample of the decode workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "decode KV GB/s (% HBM peak) at 32K + prefill tokens/s (% MFMA peak)"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak
+FP32_PEAK_TFLOPS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=24)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default="", help="comma list of legs: set_rows,decode,prefill,int8")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Leg:
+    """Times one phase with HIP events on torch's current stream."""
+
+    def __init__(self, name):
+        import torch
+        self.name = name
+        self.pairs = []
+        self.torch = torch
+
+    def run(self, fn, record=True):
+        if not record:
+            fn()
+            return
+        a = self.torch.cuda.Event(enable_timing=True)
+        b = self.torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.pairs.append((a, b))
+
+    def mean_ms(self):
+        if not self.pairs:
+            return None
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                          "(multi-GPU sharding is a design note, not implemented)"}))
+        sys.exit(2)
+    import torch
+    from quantized_kv_cache_tq_amd import binding as b
+    from quantized_kv_cache_tq_amd import inputs
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(3)
+    b.load_library()
+    only = set(filter(None, args.only.split(",")))
+    want = lambda leg: not only or leg in only
+    dev = torch.device("cuda:0")
+    t_wall0 = time.time()
+
+    # ---------------- decode workload (32 q / 4 kv heads, d 128, 32K, turbo3)
+    log("[bench] generating the 32K decode workload")
+    q_np, k_np, v_np = inputs.outlier_decode(seed=0)
+    KV, NKV, D, NQ = k_np.shape[0], k_np.shape[1], k_np.shape[2], q_np.shape[0]
+    k_src = torch.from_numpy(k_np).to(dev)
+    v_src = torch.from_numpy(v_np).to(dev)
+    idx = torch.arange(KV, dtype=torch.int64, device=dev)
+    q_dec = torch.from_numpy(q_np).to(torch.bfloat16).to(dev)
+    L = args.layers
+    kcs = [b.new_cache(3, D, NKV, KV) for _ in range(L)]
+    vcs = [b.new_cache(3, D, NKV, KV) for _ in range(L)]
+    b.tq_set_rows(kcs[0], k_src, idx)
+    b.tq_set_rows(vcs[0], v_src, idx)
+    for i in range(1, L):
+        kcs[i].codes.copy_(kcs[0].codes); kcs[i].norms.copy_(kcs[0].norms)
+        vcs[i].codes.copy_(vcs[0].codes); vcs[i].norms.copy_(vcs[0].norms)
+    torch.cuda.synchronize()
+    scale_dec = 1.0 / math.sqrt(D)
+    ws_bytes = b.tq_attn_decode_workspace(kcs[0], KV, NQ)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    outs = [torch.empty((NQ, D), dtype=torch.float32, device=dev) for _ in range(L)]
+    kv_bytes_per_call = 2 * NKV * KV * (48 + 2)      # packed codes + fp16 norm, K and V
+
+    def decode_all():
+        for i in range(L):
+            b.tq_attn_decode(kcs[i], vcs[i], KV, q_dec, scale_dec, out=outs[i], workspace=ws)
+
+    graph = None
+    if want("decode"):
+        decode_all()                       # warm, outside capture
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            decode_all()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            decode_all()
+        torch.cuda.synchronize()
+
+    # ---------------- prefill workload (2048 rows, 16 q / 8 kv heads, d 256)
+    prefill = None
+    if want("prefill"):
+        try:
+            pq, pk, pv = inputs.prefill(seed=0, rows=2048)
+            R, PNQ, PD = pq.shape
+            PNKV = pk.shape[1]
+            pkc, pvc = b.new_cache(3, PD, PNKV, R), b.new_cache(3, PD, PNKV, R)
+            pidx = torch.arange(R, dtype=torch.int64, device=dev)
+            b.tq_set_rows(pkc, torch.from_numpy(pk).to(dev), pidx)
+            b.tq_set_rows(pvc, torch.from_numpy(pv).to(dev), pidx)
+            pqt = torch.from_numpy(pq).to(torch.bfloat16).to(dev)
+            pws = torch.empty(max(256, b.tq_attn_prefill_workspace(pkc, R, PNQ, R)), dtype=torch.uint8,
+                              device=dev)
+            pout = torch.empty((R, PNQ, PD), dtype=torch.float32, device=dev)
+            pscale = 1.0 / math.sqrt(PD)
+            fn = lambda: b.tq_attn_prefill(pkc, pvc, R, pqt, 0, pscale, out=pout, workspace=pws)
+            fn()
+            torch.cuda.synchronize()
+            flops = 4.0 * PD * PNQ * (R * (R + 1) / 2)
+            prefill = dict(fn=fn, rows=R, flops=flops)
+        except b.TQError as e:
+            log(f"[bench] prefill leg skipped: {e}")
+
+    # ---------------- int8 prompt workload (2048 q x 40000 cells)
+    int8 = None
+    if want("int8"):
+        try:
+            d8 = inputs.int8_prompt(seed=0, ctx=40000)
+            t = {k_: torch.from_numpy(v_).to(dev) for k_, v_ in d8.items() if not k_.endswith("logical")}
+            n_q8, nqh8, dd8 = d8["q"].shape
+            ctx8 = 40000
+            q08 = ctx8 - n_q8
+            ws8 = torch.empty(max(256, b.tq_attn_int8_prompt_workspace(n_q8, nqh8, 1, dd8, ctx8)),
+                              dtype=torch.uint8, device=dev)
+            out8 = torch.empty((n_q8, nqh8, dd8), dtype=torch.float32, device=dev)
+            fn8 = lambda: b.tq_attn_int8_prompt(t["q"], t["k8"], t["v8"], t["k_scale"], t["v_scale"],
+                                                t["page_table"], ctx8, q08, 1.0 / math.sqrt(dd8),
+                                                out=out8, workspace=ws8)
+            fn8()
+            torch.cuda.synchronize()
+            pairs = sum(min(ctx8, q08 + i + 1) for i in range(n_q8))
+            int8 = dict(fn=fn8, flops=4.0 * dd8 * nqh8 * pairs, ctx=ctx8, n_q=n_q8)
+        except b.TQError as e:
+            log(f"[bench] int8 leg skipped: {e}")
+
+    # ---------------- timed steps
+    legs = {n: Leg(n) for n in ("set_rows", "decode", "prefill", "int8")}
+
+    def step(record):
+        if want("set_rows"):
+            j = step.i % L
+            legs["set_rows"].run(lambda: (b.tq_set_rows(kcs[j], k_src, idx),
+                                          b.tq_set_rows(vcs[j], v_src, idx)), record)
+        if graph is not None:
+            legs["decode"].run(graph.replay, record)
+        if prefill is not None:
+            legs["prefill"].run(prefill["fn"], record)
+        if int8 is not None:
+            legs["int8"].run(int8["fn"], record)
+        step.i += 1
+    step.i = 0
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / max(1, args.steps)
+    log("[bench] timed region done")
+
+    res = {}
+    ms = {n: legs[n].mean_ms() for n in legs}
+    step_ms = sum(v_ for v_ in ms.values() if v_ is not None)
+    out = {"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+           "data": "synthetic",
+           "config": {"workload": f"turbo3 decode: 32 q / 4 kv heads, head_dim 128, kv 32768, bf16 q, "
+                                  f"{L} layers' caches per step; + set_rows of one 32768-row cache, "
+                                  f"turbo3 causal prefill 2048 rows (16 q / 8 kv, d 256), "
+                                  f"int8 prompt 2048 q x 40000 ctx",
+                      "global_batch": 1, "seq_len": KV, "parallelism": "none (1 GPU)"},
+           "wall_ms_per_step": round(wall_ms, 4)}
+    if ms["decode"] is not None:
+        per_call_us = ms["decode"] * 1e3 / L
+        gbps = kv_bytes_per_call / (per_call_us * 1e-6) / 1e9
+        out["value"] = round(gbps, 2)
+        out["decode"] = {"us_per_call": round(per_call_us, 3), "kv_bytes_per_call": kv_bytes_per_call,
+                         "GBps": round(gbps, 2), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                         "layers_per_step": L}
+        out["roofline"] = {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
+                           "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                           "kernel": "decode call (decode_split_kernel<3,4> + decode_merge_kernel)"}
+    if ms["set_rows"] is not None:
+        per_cache_us = ms["set_rows"] * 1e3
+        nbytes = 2 * (KV * NKV * D * 4 + KV * NKV * 50)
+        out["set_rows"] = {"us_per_32k_KV_pair": round(per_cache_us, 2), "bytes": nbytes,
+                           "GBps": round(nbytes / (per_cache_us * 1e-6) / 1e9, 1)}
+    if ms["prefill"] is not None:
+        t_s = ms["prefill"] * 1e-3
+        tflops = prefill["flops"] / t_s / 1e12
+        out["prefill"] = {"rows": prefill["rows"], "us": round(ms["prefill"] * 1e3, 2),
+                          "tokens_per_s": round(prefill["rows"] / t_s, 1),
+                          "TFLOPs": round(tflops, 2), "frac_mfma_f16_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)}
+    if ms["int8"] is not None:
+        t_s = ms["int8"] * 1e-3
+        tflops = int8["flops"] / t_s / 1e12
+        out["int8_prompt"] = {"ctx": int8["ctx"], "n_q": int8["n_q"], "ms": round(ms["int8"], 4),
+                              "TFLOPs": round(tflops, 2),
+                              "frac_mfma_f16_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                              "frac_fp32_peak": round(tflops / FP32_PEAK_TFLOPS, 4)}
+
+    # ---------------- CPU baseline: the oracle on a bounded sample
+    if not args.no_cpu_baseline and want("decode"):
+        log("[bench] cpu baseline (oracle decode, 2 calls at the 32K shape)")
+        import oracle as o
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            cores = 1
+        okc, ovc = o.new_cache(3, D, NKV, KV), o.new_cache(3, D, NKV, KV)
+        o.set_rows(okc, k_np, np.arange(KV))
+        o.set_rows(ovc, v_np, np.arange(KV))
+        reps = 2
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            ref = o.attn_decode(okc, ovc, KV, q_np.astype(np.float64), scale_dec)
+        dt = (time.perf_counter() - t0) / reps
+        got = outs[0].cpu().numpy()
+        out["cpu_baseline"] = {"value": round(kv_bytes_per_call / dt / 1e9, 6), "unit": "GB/s",
+                               "cores": cores, "kind": "oracle",
+                               "sample": f"{reps} decode calls at the 32K/GQA-8 turbo3 shape "
+                                         f"(numpy: unpack, dequantize, float64 attention); "
+                                         f"{dt:.2f} s per call"}
+        out["parity_check"] = {"decode_max_abs_vs_oracle": float(np.abs(got - ref).max())}
+    out["wall_s_total"] = round(time.time() - t_wall0, 1)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

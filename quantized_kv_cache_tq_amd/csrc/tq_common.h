@@ -48,41 +48,142 @@ __host__ __device__ constexpr float code_value(int c) {
                         : magnitude<B>(c & ((1 << (B - 1)) - 1));
 }
 
+// float16 bit pattern of a float that is an exact normal float16 value.
+__host__ __device__ constexpr uint16_t f16_bits_exact(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const uint32_t sign = (u >> 16) & 0x8000u;
+  const uint32_t e = ((u >> 23) & 0xffu) - 127u + 15u;
+  return (uint16_t)(sign | (e << 10) | ((u >> 13) & 0x3ffu));
+}
+template <int B>
+__host__ __device__ constexpr bool levels_are_f16() {
+  for (int i = 0; i < (1 << (B - 1)); ++i) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, magnitude<B>(i));
+    if (u & 0x1fffu) return false;
+  }
+  return true;
+}
+static_assert(levels_are_f16<2>() && levels_are_f16<3>() && levels_are_f16<4>(),
+              "levels must be exact float16 values");
+
+// Level table for the attention kernels: entry idx decodes the U codes
+// packed in idx (code u in bits [B*u, B*u+B)) to U float16 levels, two per
+// dword (code 2p in the low half).  U = 4 for 2- and 3-bit codes (8/12-bit
+// index), U = 2 for 4-bit codes (8-bit index).
+template <int B>
+struct UnitCfg {
+  static constexpr int U = (B == 4) ? 2 : 4;
+  static constexpr int IBITS = U * B;
+  static constexpr int N = 1 << IBITS;
+  static constexpr int DW = U / 2;
+  static constexpr int WORDS = N * DW;
+};
+template <int B>
+struct alignas(16) LevelTable {
+  uint32_t w[UnitCfg<B>::WORDS];
+  constexpr LevelTable() : w{} {
+    using C = UnitCfg<B>;
+    for (int idx = 0; idx < C::N; ++idx)
+      for (int p = 0; p < C::DW; ++p) {
+        const int c0 = (idx >> (B * (2 * p))) & ((1 << B) - 1);
+        const int c1 = (idx >> (B * (2 * p + 1))) & ((1 << B) - 1);
+        w[idx * C::DW + p] = (uint32_t)f16_bits_exact(code_value<B>(c0)) |
+                             ((uint32_t)f16_bits_exact(code_value<B>(c1)) << 16);
+      }
+  }
+};
+
 // The fixed random sign flip: element d negated iff bit d%64 of word d/64 is
 // set (the first two SplitMix64 outputs from state 0).
 constexpr uint64_t kSignWord0 = 0xe220a8397b1dcdafull;
 constexpr uint64_t kSignWord1 = 0x6e789e6aa1b965f4ull;
 
-// ---------------------------------------------------------------- wave helpers
-
-__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
-  return __shfl_xor(v, mask, 64);
+__device__ __forceinline__ uint32_t sign_bit_of(int d) {
+  return (uint32_t)((d < 64 ? kSignWord0 >> d : kSignWord1 >> (d - 64)) & 1u);
 }
 
-// In-place unnormalized 128-point Walsh-Hadamard transform of one group held
-// by one wave, lane j owning elements j (a) and j + 64 (b).  Stages
-// h = 1, 2, .., 64 in ascending order; in each pair the lower element gets
-// lower + upper and the upper one lower - upper.  Each stage is a single
-// IEEE float32 add or subtract of the same two operands, so the result is
-// bit-identical to any other schedule of the same stages.
-__device__ __forceinline__ void wht128_wave(float &a, float &b, int lane) {
-#pragma clang fp contract(off)
-#pragma unroll
-  for (int h = 1; h < 64; h <<= 1) {
-    const float pa = shfl_xor_f(a, h);
-    const float pb = shfl_xor_f(b, h);
-    const bool upper = (lane & h) != 0;
-    a = upper ? (pa - a) : (a + pa);
-    b = upper ? (pb - b) : (b + pb);
+// ---------------------------------------------------------------- lane exchanges
+
+// v from lane (lane ^ H).  H = 1, 2: DPP quad permutes; H = 4: half-row
+// mirror (lane ^ 7) then quad reverse (^ 3); H = 8: row rotate by 8;
+// H = 16: ds_swizzle in xor mode (within 32 lanes); H = 32: ds_bpermute.
+template <int H>
+__device__ __forceinline__ float xor_lane(float v) {
+  const int x = __float_as_int(v);
+  int r;
+  if constexpr (H == 1) {
+    r = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);
+  } else if constexpr (H == 2) {
+    r = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);
+  } else if constexpr (H == 4) {
+    const int m = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);
+    r = __builtin_amdgcn_update_dpp(0, m, 0x1B, 0xF, 0xF, false);
+  } else if constexpr (H == 8) {
+    r = __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false);
+  } else if constexpr (H == 16) {
+    r = __builtin_amdgcn_ds_swizzle(x, 0x401F);
+  } else {
+    static_assert(H == 32, "xor_lane: H must be a power of two <= 32");
+    r = __shfl_xor(x, 32, 64);
   }
-  const float s = a + b;
-  const float d = a - b;
-  a = s;
-  b = d;
+  return __int_as_float(r);
 }
 
 __device__ __forceinline__ float flip_sign(float x, uint32_t negate) {
   return __uint_as_float(__float_as_uint(x) ^ (negate << 31));
+}
+
+// One butterfly stage between lanes at distance H/... : the lower element of
+// each pair takes lower + partner, the upper one partner - upper.
+template <int H>
+__device__ __forceinline__ float bfly_lane(float v, bool upper) {
+#pragma clang fp contract(off)
+  const float p = xor_lane<H>(v);
+  return upper ? (p - v) : (v + p);
+}
+
+// Unnormalized 128-point Walsh-Hadamard transform of one group held by 32
+// lanes of a wave (lanes 0-31 or 32-63), lane j = lane & 31 owning elements
+// 4j .. 4j+3 in u[0..3].  Stages h = 1, 2 are in-register, h = 4 .. 64 are
+// exchanges with lane j ^ (h/4); in every pair the lower element becomes
+// lower + upper and the upper one lower - upper, stages in ascending h.
+// Each stage is one IEEE float32 add or subtract of the same two operands, so
+// the result equals any other schedule of the same stages bit for bit.
+__device__ __forceinline__ void wht128_half(float (&u)[4], int j) {
+#pragma clang fp contract(off)
+  float a0 = u[0] + u[1], a1 = u[0] - u[1];
+  float a2 = u[2] + u[3], a3 = u[2] - u[3];
+  u[0] = a0 + a2;
+  u[2] = a0 - a2;
+  u[1] = a1 + a3;
+  u[3] = a1 - a3;
+#define TQ_STAGE(H)                                          \
+  {                                                          \
+    const bool up = (j & (H)) != 0;                          \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) u[i] = bfly_lane<H>(u[i], up); \
+  }
+  TQ_STAGE(1)
+  TQ_STAGE(2)
+  TQ_STAGE(4)
+  TQ_STAGE(8)
+  TQ_STAGE(16)
+#undef TQ_STAGE
+}
+
+// Sum of squares of the group held as in wht128_half, in the butterfly's
+// pairing order (neighbours first, then distances 2, 4, .., 64); the result
+// is the same in all 32 lanes.
+__device__ __forceinline__ float sum_squares_half(const float (&x)[4]) {
+#pragma clang fp contract(off)
+  const float s01 = x[0] * x[0] + x[1] * x[1];
+  const float s23 = x[2] * x[2] + x[3] * x[3];
+  float s = s01 + s23;
+  s = s + xor_lane<1>(s);
+  s = s + xor_lane<2>(s);
+  s = s + xor_lane<4>(s);
+  s = s + xor_lane<8>(s);
+  s = s + xor_lane<16>(s);
+  return s;
 }
 
 template <typename T>

@@ -3,103 +3,104 @@
 //
 // [PR36] (a), the llama-cpp-turboquant SET_ROWS butterfly commit, describes
 // the kernel as a sign flip and a 128-point butterfly (h = 1..64) per group;
-// the earlier CUDA kernel spread a group over several 32-wide warps and used
-// block barriers for h = 32 and 64.  On CDNA4 one wave64 holds a whole group
-// (lane j owns elements j and j + 64): stages h = 1..32 are cross-lane
-// exchanges inside the wave and stage h = 64 is in-register, so no barrier is
-// needed anywhere in the transform.
+// the CUDA kernel spread a group over several 32-wide warps and kept block
+// barriers for h = 32 and 64.  On CDNA4 half a wave64 holds a whole group:
+// lane j owns elements 4j..4j+3 (one 16-byte load), stages h = 1 and 2 are
+// in-register and h = 4..64 are DPP / swizzle exchanges inside the 32 lanes,
+// so no barrier or LDS round trip is needed anywhere in the transform.  Each
+// wave quantizes 2 x kRounds groups and issues all their loads first, so
+// enough bytes are in flight to stream from HBM.
 //
 // Bit-exact contract (float32, no contraction): see tq_set_rows in tq.h.
 #include "tq_common.h"
 
 namespace tq {
 
-constexpr int kSetRowsWaves = 4;  // groups per workgroup (one wave each)
+constexpr int kSrWaves = 4;
+constexpr int kSrRounds = 4;                              // groups per half-wave
+constexpr int kSrGroupsPerBlock = kSrWaves * 2 * kSrRounds;
 
 template <int B>
-__global__ __launch_bounds__(64 * kSetRowsWaves) void set_rows_kernel(
+__global__ __launch_bounds__(64 * kSrWaves) void set_rows_kernel(
     uint8_t *__restrict__ codes, uint16_t *__restrict__ norms, const float *__restrict__ src,
     const int64_t *__restrict__ cell_idx, int64_t n_rows, int32_t n_kv, int32_t n_groups_per_head,
     int64_t n_cells) {
 #pragma clang fp contract(off)
-  __shared__ uint8_t lds_codes[kSetRowsWaves][kGroup];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, j = lane & 31;
   const int64_t groups_per_row = (int64_t)n_kv * n_groups_per_head;
   const int64_t total = n_rows * groups_per_row;
-  const int64_t gi = (int64_t)blockIdx.x * kSetRowsWaves + wave;
-  const bool active = gi < total;  // uniform per wave
+  const int64_t gbase = ((int64_t)blockIdx.x * kSrWaves + wave) * (2 * kSrRounds) + half;
 
-  int64_t row = 0, cell = -1;
-  int head = 0, grp = 0;
-  float a = 0.f, b = 0.f;
-  if (active) {
-    row = gi / groups_per_row;
-    const int64_t rem = gi - row * groups_per_row;
-    head = (int)(rem / n_groups_per_head);
-    grp = (int)(rem - (int64_t)head * n_groups_per_head);
-    cell = cell_idx[row];
-    const float *x = src + gi * kGroup;
-    a = x[lane];
-    b = x[lane + 64];
-  }
-
-  // 1. sum of squares in the butterfly's pairing order: partials at distance
-  //    1, 2, .., 32 across lanes, then the two halves (distance 64).
-  float sa = a * a;
-  float sb = b * b;
+  // issue every load first
+  float4 x[kSrRounds];
+  int64_t cell[kSrRounds];
 #pragma unroll
-  for (int h = 1; h < 64; h <<= 1) {
-    sa = sa + shfl_xor_f(sa, h);
-    sb = sb + shfl_xor_f(sb, h);
-  }
-  const float n2 = sa + sb;
-  const float norm = __builtin_sqrtf(n2);  // correctly rounded (no afn)
-  const float inv = norm > 0.f ? 1.0f / norm : 0.f;  // correctly rounded division
-
-  // 2. sign flip, 3. butterfly, 4. unit-variance coordinates
-  const uint32_t neg_a = (uint32_t)(kSignWord0 >> lane) & 1u;
-  const uint32_t neg_b = (uint32_t)(kSignWord1 >> lane) & 1u;
-  float ua = flip_sign(a, neg_a);
-  float ub = flip_sign(b, neg_b);
-  wht128_wave(ua, ub, lane);
-  const float ya = ua * inv;
-  const float yb = ub * inv;
-
-  // 5. nearest stored level: sign bit + magnitude index
-  const float aa = __builtin_fabsf(ya);
-  const float ab = __builtin_fabsf(yb);
-  int qa = 0, qb = 0;
-#pragma unroll
-  for (int k = 1; k < (1 << (B - 1)); ++k) {
-    qa += aa > threshold<B>(k) ? 1 : 0;
-    qb += ab > threshold<B>(k) ? 1 : 0;
-  }
-  const int ca = qa | ((ya < 0.f ? 1 : 0) << (B - 1));
-  const int cb = qb | ((yb < 0.f ? 1 : 0) << (B - 1));
-
-  // 6. pack: element e's code at stream bits B*e .. B*e+B-1
-  lds_codes[wave][lane] = (uint8_t)ca;
-  lds_codes[wave][lane + 64] = (uint8_t)cb;
-  __syncthreads();
-  if (!active || cell < 0 || cell >= n_cells) return;
-  constexpr int kWords = 4 * B;  // 16*B bytes per group
-  const int64_t slot = ((int64_t)head * n_cells + cell) * n_groups_per_head + grp;
-  if (lane < kWords) {
-    const int bit0 = 32 * lane;
-    const int e0 = bit0 / B;
-    const int e1 = (bit0 + 31) / B;
-    uint32_t word = 0;
-    for (int e = e0; e <= e1; ++e) {
-      const uint32_t c = lds_codes[wave][e];
-      const int pos = B * e - bit0;
-      word |= pos >= 0 ? (c << pos) : (c >> (-pos));
+  for (int r = 0; r < kSrRounds; ++r) {
+    const int64_t gi = gbase + 2 * r;
+    if (gi < total) {
+      x[r] = reinterpret_cast<const float4 *>(src + gi * kGroup)[j];
+      cell[r] = cell_idx[gi / groups_per_row];
+    } else {
+      x[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+      cell[r] = -1;
     }
-    reinterpret_cast<uint32_t *>(codes + slot * (16 * B))[lane] = word;
   }
-  if (lane == 0) {
-    const _Float16 h16 = (_Float16)norm;
-    norms[slot] = __builtin_bit_cast(uint16_t, h16);
+  uint32_t neg[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) neg[i] = sign_bit_of(4 * j + i);
+
+#pragma unroll
+  for (int r = 0; r < kSrRounds; ++r) {
+    const int64_t gi = gbase + 2 * r;
+    float u[4] = {x[r].x, x[r].y, x[r].z, x[r].w};
+    // 1. norm: sum of squares in the butterfly's pairing order
+    const float n2 = sum_squares_half(u);
+    const float norm = __builtin_sqrtf(n2);             // correctly rounded
+    const float inv = norm > 0.f ? 1.0f / norm : 0.f;   // correctly rounded
+    // 2. sign flip, 3. butterfly, 4. unit-variance coordinates, 5. codes
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = flip_sign(u[i], neg[i]);
+    wht128_half(u, j);
+    uint32_t field = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float y = u[i] * inv;
+      const float a = __builtin_fabsf(y);
+      uint32_t qs = 0;
+#pragma unroll
+      for (int k = 1; k < (1 << (B - 1)); ++k) qs += a > threshold<B>(k) ? 1u : 0u;
+      const uint32_t c = qs | ((y < 0.f ? 1u : 0u) << (B - 1));
+      field |= c << (B * i);
+    }
+    // 6. pack: lane j's 4B-bit field sits at stream bit 4B*j; lane w < 4B
+    //    assembles output dword w from the (at most KMAX) fields it overlaps.
+    constexpr int FB = 4 * B;
+    constexpr int KMAX = (B == 4) ? 2 : 4;
+    const int w = j;
+    const int j0 = (32 * w) / FB;
+    const int j1 = (32 * w + 31) / FB;
+    uint32_t word = 0;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      const int jj = j0 + k;
+      const int srcl = (half << 5) + (jj < 32 ? jj : 31);
+      const uint32_t f = (uint32_t)__shfl((int)field, srcl, 64);
+      const int pos = FB * jj - 32 * w;
+      if (jj <= j1) word |= pos >= 0 ? (f << pos) : (f >> (-pos));
+    }
+    const int64_t c = cell[r];
+    if (gi < total && c >= 0 && c < n_cells) {
+      const int64_t rem = gi % groups_per_row;
+      const int head = (int)(rem / n_groups_per_head);
+      const int grp = (int)(rem - (int64_t)head * n_groups_per_head);
+      const int64_t slot = ((int64_t)head * n_cells + c) * n_groups_per_head + grp;
+      if (w < FB) reinterpret_cast<uint32_t *>(codes + slot * (16 * B))[w] = word;
+      if (j == 0) {
+        const _Float16 h16 = (_Float16)norm;
+        norms[slot] = __builtin_bit_cast(uint16_t, h16);
+      }
+    }
   }
 }
 
@@ -107,9 +108,9 @@ hipError_t launch_set_rows(const tq_cache &c, const float *src, const int64_t *c
                            int64_t n_rows, hipStream_t stream) {
   const int32_t gph = c.head_dim / kGroup;
   const int64_t total = n_rows * (int64_t)c.n_kv_heads * gph;
-  const int64_t blocks = ceil_div<int64_t>(total, kSetRowsWaves);
+  const int64_t blocks = ceil_div<int64_t>(total, kSrGroupsPerBlock);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  dim3 grid((unsigned)blocks), block(64 * kSetRowsWaves);
+  dim3 grid((unsigned)blocks), block(64 * kSrWaves);
   switch (c.type) {
     case TQ_TURBO2:
       hipLaunchKernelGGL(set_rows_kernel<2>, grid, block, 0, stream, c.codes, c.norms, src,
