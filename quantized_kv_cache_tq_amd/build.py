@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIB_DIR, "libtq.so")
-SOURCES = ["tq_api.hip", "tq_set_rows.hip", "tq_decode.hip", "tq_prefill.hip"]
+SOURCES = ["tq_api.hip", "tq_set_rows.hip", "tq_decode.hip", "tq_prefill.hip", "tq_int8.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -1,0 +1,108 @@
+"""GPU parity of tq_attn_prefill (turbo3, head_dim 256) against the float64
+oracle; bar: max-abs <= 2e-3 and relative L2 <= 1e-3.
+
+The grid mirrors the correctness check of the "HIP/turbo3: graph-safe decode
++ inline-dequant TILE prefill" page (section Correctness: turbo3, 256-wide
+heads, batches of 3, 4, 6 rows (speculative verify) and 64, 128, 256 rows
+(prefill) against 512 and 1024 keys), with the rows aligned to the end of the
+keys.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle as o
+from quantized_kv_cache_tq_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(q, k, v, kv_len, q_pos0, q_bf16=True, what=""):
+    import torch
+    from quantized_kv_cache_tq_amd import binding as b
+    from gpu_util import assert_attention_close, bf16_cuda, cuda
+    n_rows, n_q, d = q.shape
+    n_cells, n_kv, _ = k.shape
+    idx = np.arange(n_cells)
+    kc, vc = b.new_cache(3, d, n_kv, n_cells), b.new_cache(3, d, n_kv, n_cells)
+    b.tq_set_rows(kc, cuda(k), cuda(idx))
+    b.tq_set_rows(vc, cuda(v), cuda(idx))
+    ok, ov = o.new_cache(3, d, n_kv, n_cells), o.new_cache(3, d, n_kv, n_cells)
+    o.set_rows(ok, k, idx)
+    o.set_rows(ov, v, idx)
+    scale = 1.0 / math.sqrt(d)
+    print(f"[prefill] {what} rows={n_rows} heads={n_q}/{n_kv} kv={kv_len} q0={q_pos0}", flush=True)
+    qt = bf16_cuda(q) if q_bf16 else cuda(q)
+    got = b.tq_attn_prefill(kc, vc, kv_len, qt, q_pos0, scale)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    want = o.attn_prefill(ok, ov, kv_len, q.astype(np.float64), q_pos0, scale)
+    return assert_attention_close(got, want, what=what), got
+
+
+@pytest.mark.parametrize("kv", [512, 1024])
+@pytest.mark.parametrize("nb", [3, 4, 6, 64, 128, 256])
+def test_backend_ops_grid(nb, kv):
+    q, k, v = inputs.prefill(seed=nb * 7 + kv, rows=nb, kv_len=kv)
+    _run(q, k, v, kv, kv - nb, what="grid")
+
+
+@pytest.mark.parametrize("rows", [512, 2048])
+def test_causal_prefill(rows):
+    q, k, v = inputs.prefill(seed=0, rows=rows)
+    (ma, rl), _ = _run(q, k, v, rows, 0, what="causal")
+    print(f"    max_abs={ma:.3g} rel_l2={rl:.3g}")
+
+
+def test_causal_prefill_4096_sampled_rows():
+    """4096 rows at full size; the oracle checks a sample of rows (first,
+    last, and a random set) so it finishes in seconds."""
+    import torch
+    from quantized_kv_cache_tq_amd import binding as b
+    from gpu_util import assert_attention_close, bf16_cuda, cuda
+    rows = 4096
+    q, k, v = inputs.prefill(seed=0, rows=rows)
+    d = 256
+    idx = np.arange(rows)
+    kc, vc = b.new_cache(3, d, 8, rows), b.new_cache(3, d, 8, rows)
+    b.tq_set_rows(kc, cuda(k), cuda(idx))
+    b.tq_set_rows(vc, cuda(v), cuda(idx))
+    got = b.tq_attn_prefill(kc, vc, rows, bf16_cuda(q), 0, 1 / 16.0)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    ok, ov = o.new_cache(3, d, 8, rows), o.new_cache(3, d, 8, rows)
+    o.set_rows(ok, k, idx)
+    o.set_rows(ov, v, idx)
+    kd, vd = o.dequant_cache(ok, rows), o.dequant_cache(ov, rows)
+    rng = np.random.default_rng(1)
+    sample = np.unique(np.concatenate([[0, 1, 63, 64, rows - 1], rng.integers(0, rows, 40)]))
+    for r in sample:
+        want = o.attention(q[r:r + 1].astype(np.float64), kd, vd, 1 / 16.0, r)
+        assert_attention_close(got[r:r + 1], want, what=f"row {r}")
+
+
+def test_spec_verify_three_rows():
+    q, k, v = inputs.prefill(seed=5, rows=3, kv_len=1024)
+    _run(q, k, v, 1024, 1021, what="spec-verify")
+
+
+@pytest.mark.parametrize("n_q,n_kv", [(8, 8), (16, 4), (16, 2), (8, 1)])
+def test_gqa_variants(n_q, n_kv):
+    q, k, v = inputs.prefill(seed=6, rows=100, kv_len=300, n_q=n_q, n_kv=n_kv)
+    _run(q, k, v, 300, 200, what=f"gqa {n_q}/{n_kv}")
+
+
+@pytest.mark.parametrize("rows,kv,q0", [(1, 1, 0), (1, 77, 76), (33, 33, 0), (65, 200, 100),
+                                        (97, 97, 0), (130, 700, 570), (31, 640, 0)])
+def test_ragged(rows, kv, q0):
+    q, k, v = inputs.prefill(seed=rows + kv, rows=rows, kv_len=kv)
+    _run(q, k, v, kv, q0, q_bf16=False, what="ragged f32-q")
+
+
+def test_prefill_deterministic():
+    q, k, v = inputs.prefill(seed=9, rows=200, kv_len=200)
+    _, a = _run(q, k, v, 200, 0, what="det-1")
+    _, b_ = _run(q, k, v, 200, 0, what="det-2")
+    np.testing.assert_array_equal(a, b_)
