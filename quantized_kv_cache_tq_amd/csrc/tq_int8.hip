@@ -1,18 +1,423 @@
-// tq_int8.hip -- placeholder until the int8 prompt-attention kernel lands.
+// tq_int8.hip -- prompt attention over a paged int8 K/V cache.
+//
+// [QSA1821] What / Change: the Turing kernel walks 32-cell chunks whose int8
+// K and V rows are scattered in memory, prefetching the next chunk while the
+// current one computes.  On CDNA4 the same walk becomes 64-key tiles (two
+// pages) gathered through the page table straight into LDS, converted to
+// float16 on the way (int8 is exact in float16), and multiplied on the matrix
+// cores:
+//   S^T[key][qrow] = K[key][:] . Q[qrow][:]      (then x k_scale[key])
+//   O^T[d][qrow]  += V^T[d][key] P^T[key][qrow]   (P already x v_scale[key])
+// The float32 query and P are each split into a high and a low float16 part
+// (x = hi + lo to ~22 bits) and both parts go through the matrix cores, so the
+// result stays within float32-level error of the exact attention.
+// The output depends only on the logical key order: physical page placement
+// changes which bytes are read, never the arithmetic.
+//
+// Workgroup: 64 qrows (64/n_rep queries x n_rep heads of one kv head), four
+// waves = 2 qrow halves x 2 key halves of each tile, merged at the end.  For
+// few queries the key range is split over workgroups and merged by a second
+// kernel.
 #include "tq_common.h"
 #include "tq_launch.h"
 
 namespace tq {
 
-hipError_t plan_int8(int64_t, int32_t, int32_t, int64_t, Int8Plan *p) {
-  *p = Int8Plan{};
-  return hipErrorNotSupported;
+namespace i8 {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kD = 128;
+constexpr int kQRows = 64;
+constexpr int kKT = 64;              // keys per tile (two 32-cell pages)
+constexpr int kPage = 32;
+constexpr int kKsStride = kD + 8;    // halves per K row
+constexpr int kVtStride = kKT + 8;   // halves per V^T row
+constexpr int kPartStride = kD + 4;  // o[128], m, l, pad
+
+struct Args {
+  const float *q;
+  const int8_t *k;
+  const int8_t *v;
+  const uint16_t *ks;
+  const uint16_t *vs;
+  const int32_t *pt;
+  float *out;
+  float *ws;
+  int64_t n_q, ctx_len, q_pos0, n_phys_pages;
+  int n_q_heads, n_kv, n_rep, bq, n_split, tiles_per_split;
+  float qscale;
+};
+
+__device__ __forceinline__ int64_t lmin(int64_t a, int64_t b) { return a < b ? a : b; }
+
+// float16 pair (x0, x1) of two signed bytes placed in the low bytes of the
+// two halves of w (high bytes zero): 0x6400 | (b ^ 0x80) is 1024 + b + 128,
+// exactly representable, so subtracting 1152 leaves b exactly.
+__device__ __forceinline__ uint32_t bytes_to_half2(uint32_t w) {
+  const half2_t h = __builtin_bit_cast(half2_t, w ^ 0x64806480u);
+  const half2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  return __builtin_bit_cast(uint32_t, h - bias);
 }
 
-hipError_t launch_int8(const float *, int64_t, int32_t, const int8_t *, const int8_t *,
-                       const uint16_t *, const uint16_t *, int32_t, const int32_t *, int64_t,
-                       int64_t, int64_t, float, float *, void *, const Int8Plan &, hipStream_t) {
-  return hipErrorNotSupported;
+__device__ __forceinline__ float half_to_float(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+struct TileRaw {
+  u32x4_t k[2];       // K: key t>>2, bytes 32*(t&3) .. +31
+  uint32_t v[4][2];   // V: keys 4*(t&15)+i, bytes 8*(t>>4) .. +7
+  uint16_t scl;       // scale: t < 64 -> K of key t, 64 <= t < 128 -> V of key t-64
+  bool page_ok;       // this thread's V/K keys' pages exist
+};
+
+// Physical row of logical key j (j < ctx_len); ok = page entry in range.
+__device__ __forceinline__ int64_t phys_row(const Args &a, int64_t j, bool &ok) {
+  const int64_t pg = a.pt[j >> 5];
+  ok = pg >= 0 && pg < a.n_phys_pages;
+  return (ok ? pg : 0) * kPage + (j & (kPage - 1));
+}
+
+__device__ __forceinline__ void load_tile(const Args &a, int g, int64_t kt, int tid, TileRaw &r) {
+  const int64_t last = a.ctx_len - 1;
+  bool ok;
+  {
+    const int64_t j = lmin(kt * kKT + (tid >> 2), last);
+    const int64_t row = phys_row(a, j, ok);
+    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(a.k + (row * a.n_kv + g) * kD + 32 * (tid & 3));
+    r.k[0] = src[0];
+    r.k[1] = src[1];
+  }
+  {
+    const int db = tid >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t j = lmin(kt * kKT + 4 * (tid & 15) + i, last);
+      const int64_t row = phys_row(a, j, ok);
+      const u32x2_t w = *reinterpret_cast<const u32x2_t *>(a.v + (row * a.n_kv + g) * kD + 8 * db);
+      r.v[i][0] = w.x;
+      r.v[i][1] = w.y;
+    }
+  }
+  {
+    const int64_t j = lmin(kt * kKT + (tid & 63), last);
+    const int64_t row = phys_row(a, j, ok);
+    r.page_ok = ok;
+    r.scl = (tid < 64) ? a.ks[row * a.n_kv + g] : a.vs[row * a.n_kv + g];
+  }
+}
+
+__device__ __forceinline__ void store_tile(const Args &a, int64_t kt, int tid, const TileRaw &r,
+                                           _Float16 *ksm, _Float16 *vt, float *sk, float *sv,
+                                           int *kval) {
+  {
+    // 32 K bytes -> 32 halves; byte pairs (2m, 2m+1) of dword m/2
+    uint32_t h[16];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x = r.k[c][w];
+        h[8 * c + 2 * w] = bytes_to_half2(__builtin_amdgcn_perm(0u, x, 0x0c010c00u));
+        h[8 * c + 2 * w + 1] = bytes_to_half2(__builtin_amdgcn_perm(0u, x, 0x0c030c02u));
+      }
+    u32x4_t *dst = reinterpret_cast<u32x4_t *>(ksm + (tid >> 2) * kKsStride + 32 * (tid & 3));
+#pragma unroll
+    for (int v = 0; v < 4; ++v) dst[v] = u32x4_t{h[4 * v], h[4 * v + 1], h[4 * v + 2], h[4 * v + 3]};
+  }
+  {
+    // 4 keys x 8 d -> V^T rows d = 8*db + e: (key0, key1) and (key2, key3) pairs
+    const int db = tid >> 4;
+    _Float16 *base = vt + (8 * db) * kVtStride + 4 * (tid & 15);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int w = e >> 2, b = e & 3;
+      const uint32_t sel = 0x0c000c00u | ((uint32_t)(4 + b) << 16) | (uint32_t)b;
+      const uint32_t p01 = bytes_to_half2(__builtin_amdgcn_perm(r.v[1][w], r.v[0][w], sel));
+      const uint32_t p23 = bytes_to_half2(__builtin_amdgcn_perm(r.v[3][w], r.v[2][w], sel));
+      *reinterpret_cast<u32x2_t *>(base + e * kVtStride) = u32x2_t{p01, p23};
+    }
+  }
+  if (tid < 2 * kKT) {
+    const int64_t j = kt * kKT + (tid & 63);
+    const bool ok = j < a.ctx_len && r.page_ok;
+    const float s = ok ? half_to_float(r.scl) : 0.f;
+    if (tid < kKT) {
+      sk[tid] = s;
+      kval[tid] = ok ? 1 : 0;
+    } else {
+      sv[tid - kKT] = s;
+    }
+  }
+}
+
+__device__ __forceinline__ void split_hl(float x, _Float16 &hi, _Float16 &lo) {
+  hi = (_Float16)x;
+  lo = (_Float16)(x - (float)hi);
+}
+
+__global__ __launch_bounds__(kThreads) void int8_prompt_kernel(Args a) {
+  constexpr int kArenaHalves = kKT * kKsStride + kD * kVtStride;
+  static_assert(kArenaHalves * 2 >= 2 * 4 * 16 * 64 * 4, "merge buffer must fit");
+  __shared__ __align__(16) _Float16 arena[kArenaHalves];
+  __shared__ __align__(16) float sk[kKT], sv[kKT];
+  __shared__ float mstat[2][32], lstat[2][32];
+  __shared__ int kval[kKT];   // key exists (in context, page in range)
+  _Float16 *ksm = arena;
+  _Float16 *vt = arena + kKT * kKsStride;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qhalf = wave & 1, khalf = wave >> 1;
+  const int qt = blockIdx.x, split = blockIdx.y, g = blockIdx.z;
+  const int ql = lane & 31, hl = lane >> 5;
+  const int qrow = 32 * qhalf + ql;
+  const int head_local = qrow / a.bq, row_local = qrow % a.bq;
+  const int head = g * a.n_rep + head_local;
+  const int64_t q0 = (int64_t)qt * a.bq;
+  const int64_t qi = q0 + row_local;                         // this column's query
+  const int64_t qi_c = lmin(qi, a.n_q - 1);
+  const int64_t last_q = lmin(q0 + a.bq, a.n_q) - 1;
+  const int64_t kend = lmin(a.ctx_len, a.q_pos0 + last_q + 1);
+  const int64_t n_kt_all = ceil_div<int64_t>(kend, kKT);
+  const int64_t kt0 = (int64_t)split * a.tiles_per_split;
+  const int64_t kt1 = lmin(kt0 + a.tiles_per_split, n_kt_all);
+  const int64_t pos = a.q_pos0 + qi_c;
+
+  // query operand: d = 16t + 8hl + i, high and low float16 parts
+  half8_t qhi[8], qlo[8];
+  {
+    const float *qr = a.q + (qi_c * a.n_q_heads + head) * kD + 8 * hl;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float4 f0 = *reinterpret_cast<const float4 *>(qr + 16 * t);
+      const float4 f1 = *reinterpret_cast<const float4 *>(qr + 16 * t + 4);
+      const float x[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        _Float16 h, l;
+        split_hl(x[i] * a.qscale, h, l);
+        qhi[t][i] = h;
+        qlo[t][i] = l;
+      }
+    }
+  }
+
+  f32x16_t o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) o[dt][rr] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  TileRaw raw;
+  if (kt0 < kt1) load_tile(a, g, kt0, tid, raw);
+  for (int64_t kt = kt0; kt < kt1; ++kt) {
+    store_tile(a, kt, tid, raw, ksm, vt, sk, sv, kval);
+    if (kt + 1 < kt1) load_tile(a, g, kt + 1, tid, raw);
+    __syncthreads();
+
+    f32x16_t s;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) s[rr] = 0.f;
+    const _Float16 *krow = ksm + (32 * khalf + ql) * kKsStride + 8 * hl;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const half8_t av = *reinterpret_cast<const half8_t *>(krow + 16 * t);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qhi[t], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qlo[t], s, 0, 0, 0);
+    }
+    const int64_t kbase = kt * kKT + 32 * khalf;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int kk = 8 * (rr >> 2) + 4 * hl + (rr & 3);
+      float v = s[rr] * sk[32 * khalf + kk];
+      if (kbase + kk > pos || !kval[32 * khalf + kk]) v = -INFINITY;  // causal / no such key
+      s[rr] = v;
+      tmax = fmaxf(tmax, v);
+    }
+    tmax = fmaxf(tmax, xor_lane<32>(tmax));
+    const float m_new = fmaxf(m_run, tmax);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    half8_t phi[2], plo[2];
+    float psum = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int kk = 8 * (rr >> 2) + 4 * hl + (rr & 3);
+      const float p = __builtin_amdgcn_exp2f(s[rr] - m_use);
+      psum += p;
+      _Float16 h, l;
+      split_hl(p * sv[32 * khalf + kk], h, l);
+      phi[rr >> 3][rr & 7] = h;
+      plo[rr >> 3][rr & 7] = l;
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) o[dt][rr] *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const _Float16 *vrow = vt + (32 * dt + ql) * kVtStride + 32 * khalf + 4 * hl;
+#pragma unroll
+      for (int ga = 0; ga < 2; ++ga) {
+        const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vrow + 16 * ga);
+        const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vrow + 16 * ga + 8);
+        const half8_t av = __builtin_bit_cast(half8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, phi[ga], o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, plo[ga], o[dt], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- merge the key halves
+  l_run += xor_lane<32>(l_run);
+  float *mbuf = reinterpret_cast<float *>(arena);
+  if (khalf == 1) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) mbuf[((qhalf * 4 + dt) * 16 + rr) * 64 + lane] = o[dt][rr];
+    if (hl == 0) {
+      mstat[qhalf][ql] = m_run;
+      lstat[qhalf][ql] = l_run;
+    }
+  }
+  __syncthreads();
+  if (khalf != 0) return;
+  const float m2 = mstat[qhalf][ql], l2 = lstat[qhalf][ql];
+  const float M = fmaxf(m_run, m2);
+  const float f1 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+  const float f2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
+  const float L = l_run * f1 + l2 * f2;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr)
+      o[dt][rr] = o[dt][rr] * f1 + mbuf[((qhalf * 4 + dt) * 16 + rr) * 64 + lane] * f2;
+  if (qi >= a.n_q) return;
+  // O^T register rr of tile dt <-> d = 32dt + 8(rr/4) + 4hl + rr%4
+  if (a.n_split == 1) {
+    const float r = 1.0f / L;
+    float *orow = a.out + (qi * a.n_q_heads + head) * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq)
+        *reinterpret_cast<float4 *>(orow + 32 * dt + 8 * rq + 4 * hl) =
+            make_float4(o[dt][4 * rq] * r, o[dt][4 * rq + 1] * r, o[dt][4 * rq + 2] * r,
+                        o[dt][4 * rq + 3] * r);
+  } else {
+    float *prow = a.ws + ((qi * a.n_q_heads + head) * (int64_t)a.n_split + split) * kPartStride;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq)
+        *reinterpret_cast<float4 *>(prow + 32 * dt + 8 * rq + 4 * hl) =
+            make_float4(o[dt][4 * rq], o[dt][4 * rq + 1], o[dt][4 * rq + 2], o[dt][4 * rq + 3]);
+    if (hl == 0) *reinterpret_cast<float2 *>(prow + kD) = make_float2(M, L);
+  }
+}
+
+// Merge split partials of one output row (query, head): 32 lanes x 4 elements.
+__global__ __launch_bounds__(64) void int8_merge_kernel(const float *__restrict__ ws, int n_split,
+                                                        int64_t n_rows, float *__restrict__ out) {
+  const int64_t row = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 5);
+  const int j = threadIdx.x & 31;
+  if (row >= n_rows) return;
+  const float *p = ws + row * n_split * kPartStride;
+  float mg = -INFINITY, L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < n_split; ++s) {
+    const float2 ml = *reinterpret_cast<const float2 *>(p + s * kPartStride + kD);
+    if (ml.x == -INFINITY) continue;
+    const float4 v = reinterpret_cast<const float4 *>(p + s * kPartStride)[j];
+    const float mn = fmaxf(mg, ml.x);
+    const float al = __builtin_amdgcn_exp2f(mg - mn);
+    const float w = __builtin_amdgcn_exp2f(ml.x - mn);
+    L = L * al + w * ml.y;
+    acc.x = acc.x * al + w * v.x;
+    acc.y = acc.y * al + w * v.y;
+    acc.z = acc.z * al + w * v.z;
+    acc.w = acc.w * al + w * v.w;
+    mg = mn;
+  }
+  const float r = 1.0f / L;
+  reinterpret_cast<float4 *>(out + row * kD)[j] = make_float4(acc.x * r, acc.y * r, acc.z * r, acc.w * r);
+}
+
+}  // namespace i8
+
+hipError_t plan_int8(int64_t n_q, int32_t n_q_heads, int32_t n_kv_heads, int64_t ctx_len,
+                     Int8Plan *p) {
+  const int n_rep = n_q_heads / n_kv_heads;
+  if (n_rep < 1 || i8::kQRows % n_rep != 0) return hipErrorNotSupported;
+  int n_cu = 0;
+  hipError_t e = device_cu_count(&n_cu);
+  if (e != hipSuccess) return e;
+  p->queries_per_tile = i8::kQRows / n_rep;
+  const int64_t q_tiles = ceil_div<int64_t>(n_q, p->queries_per_tile);
+  if (q_tiles > 0x7fffffff) return hipErrorInvalidValue;
+  p->n_q_tiles = (int)q_tiles;
+  const int64_t max_tiles = ceil_div<int64_t>(ctx_len, i8::kKT);
+  int64_t n_split = 1;
+  const int64_t wgs = q_tiles * n_kv_heads;
+  if (wgs < n_cu) n_split = ceil_div<int64_t>(n_cu, wgs);
+  if (n_split > max_tiles) n_split = max_tiles;
+  if (n_split > 65535) n_split = 65535;
+  const int64_t tps = ceil_div<int64_t>(max_tiles, n_split);
+  n_split = ceil_div<int64_t>(max_tiles, tps);
+  p->keys_per_split = (int)(tps * i8::kKT);
+  p->n_split = (int)n_split;
+  p->workspace_bytes = n_split > 1 ? (((size_t)n_q * n_q_heads * n_split * i8::kPartStride *
+                                       sizeof(float)) + 255) & ~(size_t)255
+                                   : 0;
+  return hipSuccess;
+}
+
+hipError_t launch_int8(const float *q, int64_t n_q, int32_t n_q_heads, const int8_t *k,
+                       const int8_t *v, const uint16_t *k_scale, const uint16_t *v_scale,
+                       int32_t n_kv_heads, const int32_t *page_table, int64_t n_phys_pages,
+                       int64_t ctx_len, int64_t q_pos0, float scale, float *out, void *workspace,
+                       const Int8Plan &p, hipStream_t stream) {
+  i8::Args a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.ks = k_scale;
+  a.vs = v_scale;
+  a.pt = page_table;
+  a.out = out;
+  a.ws = reinterpret_cast<float *>(workspace);
+  a.n_q = n_q;
+  a.ctx_len = ctx_len;
+  a.q_pos0 = q_pos0;
+  a.n_phys_pages = n_phys_pages;
+  a.n_q_heads = n_q_heads;
+  a.n_kv = n_kv_heads;
+  a.n_rep = n_q_heads / n_kv_heads;
+  a.bq = p.queries_per_tile;
+  a.n_split = p.n_split;
+  a.tiles_per_split = p.keys_per_split / i8::kKT;
+  a.qscale = scale * 1.4426950408889634f;  // log2 domain
+  if (n_kv_heads > 65535) return hipErrorInvalidValue;
+  dim3 grid((unsigned)p.n_q_tiles, (unsigned)p.n_split, (unsigned)n_kv_heads);
+  hipLaunchKernelGGL(i8::int8_prompt_kernel, grid, dim3(i8::kThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.n_split == 1) return e;
+  const int64_t rows = n_q * n_q_heads;
+  hipLaunchKernelGGL(i8::int8_merge_kernel, dim3((unsigned)ceil_div<int64_t>(rows, 2)), dim3(64), 0,
+                     stream, a.ws, p.n_split, rows, out);
+  return hipGetLastError();
 }
 
 }  // namespace tq
