@@ -45,7 +45,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=24)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="", help="comma list of legs: set_rows,decode,prefill,int8")
+    ap.add_argument("--only", default="",
+                    help="comma list of legs: set_rows,decode,prefill,int8 (default: all); "
+                         "'copy' adds a 256 MiB device copy used to calibrate HBM counters")
     return ap.parse_args()
 
 
@@ -186,8 +188,16 @@ def main():
         except b.TQError as e:
             log(f"[bench] int8 leg skipped: {e}")
 
+    # ---------------- calibration copy (not part of a step; only with --only copy):
+    # a plain device-to-device copy of known size, for scaling HBM counters
+    copy = None
+    if "copy" in only:
+        csrc = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        cdst = torch.empty_like(csrc)
+        copy = dict(fn=lambda: cdst.copy_(csrc), nbytes=csrc.numel())
+
     # ---------------- timed steps
-    legs = {n: Leg(n) for n in ("set_rows", "decode", "prefill", "int8")}
+    legs = {n: Leg(n) for n in ("set_rows", "decode", "prefill", "int8", "copy")}
 
     def step(record):
         if want("set_rows"):
@@ -200,6 +210,8 @@ def main():
             legs["prefill"].run(prefill["fn"], record)
         if int8 is not None:
             legs["int8"].run(int8["fn"], record)
+        if copy is not None:
+            legs["copy"].run(copy["fn"], record)
         step.i += 1
     step.i = 0
 
@@ -217,7 +229,7 @@ def main():
 
     res = {}
     ms = {n: legs[n].mean_ms() for n in legs}
-    step_ms = sum(v_ for v_ in ms.values() if v_ is not None)
+    step_ms = sum(v_ for n_, v_ in ms.items() if v_ is not None and n_ != "copy")
     out = {"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "f16",
@@ -256,6 +268,11 @@ def main():
                               "TFLOPs": round(tflops, 2),
                               "frac_mfma_f16_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
                               "frac_fp32_peak": round(tflops / FP32_PEAK_TFLOPS, 4)}
+
+    if ms["copy"] is not None:
+        out["calibration_copy"] = {"bytes_read": copy["nbytes"], "bytes_written": copy["nbytes"],
+                                   "us": round(ms["copy"] * 1e3, 2),
+                                   "GBps_read_plus_write": round(2 * copy["nbytes"] / (ms["copy"] * 1e-3) / 1e9, 1)}
 
     # ---------------- CPU baseline: the oracle on a bounded sample
     if not args.no_cpu_baseline and want("decode"):
