@@ -162,7 +162,7 @@ __device__ __forceinline__ void split_hl(float x, _Float16 &hi, _Float16 &lo) {
   lo = (_Float16)(x - (float)hi);
 }
 
-__global__ __launch_bounds__(kThreads) void int8_prompt_kernel(Args a) {
+__global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
   constexpr int kArenaHalves = kKT * kKsStride + kD * kVtStride;
   static_assert(kArenaHalves * 2 >= 2 * 4 * 16 * 64 * 4, "merge buffer must fit");
   __shared__ __align__(16) _Float16 arena[kArenaHalves];
@@ -232,13 +232,14 @@ __global__ __launch_bounds__(kThreads) void int8_prompt_kernel(Args a) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qhi[t], s, 0, 0, 0);
       s = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qlo[t], s, 0, 0, 0);
     }
-    const int64_t kbase = kt * kKT + 32 * khalf;
+    const int64_t lim64 = pos - (kt * kKT + 32 * khalf);   // keys past lim are masked
+    const int lim = lim64 > 64 ? 64 : (int)lim64;
     float tmax = -INFINITY;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const int kk = 8 * (rr >> 2) + 4 * hl + (rr & 3);
       float v = s[rr] * sk[32 * khalf + kk];
-      if (kbase + kk > pos || !kval[32 * khalf + kk]) v = -INFINITY;  // causal / no such key
+      if (kk > lim || !kval[32 * khalf + kk]) v = -INFINITY;  // causal / no such key
       s[rr] = v;
       tmax = fmaxf(tmax, v);
     }
@@ -260,10 +261,14 @@ __global__ __launch_bounds__(kThreads) void int8_prompt_kernel(Args a) {
       plo[rr >> 3][rr & 7] = l;
     }
     l_run = l_run * alpha + psum;
+    // rescale only when some column's running max moved (rare after the
+    // first tiles); alpha == 1 leaves the accumulators unchanged
+    if (__any(alpha != 1.0f)) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) o[dt][rr] *= alpha;
+    }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       const _Float16 *vrow = vt + (32 * dt + ql) * kVtStride + 32 * khalf + 4 * hl;
@@ -371,7 +376,8 @@ hipError_t plan_int8(int64_t n_q, int32_t n_q_heads, int32_t n_kv_heads, int64_t
   const int64_t max_tiles = ceil_div<int64_t>(ctx_len, i8::kKT);
   int64_t n_split = 1;
   const int64_t wgs = q_tiles * n_kv_heads;
-  if (wgs < n_cu) n_split = ceil_div<int64_t>(n_cu, wgs);
+  // two resident workgroups per compute unit: one computes while the other waits
+  if (wgs < 2LL * n_cu) n_split = ceil_div<int64_t>(2LL * n_cu, wgs);
   if (n_split > max_tiles) n_split = max_tiles;
   if (n_split > 65535) n_split = 65535;
   const int64_t tps = ceil_div<int64_t>(max_tiles, n_split);

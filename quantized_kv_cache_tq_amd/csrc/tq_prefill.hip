@@ -142,39 +142,69 @@ template <int B>
 __device__ __forceinline__ void store_tile(const Args &a, int kt, int tid, const TileRaw<B> &r,
                                            const uint32_t *lut, _Float16 *ks, _Float16 *vt,
                                            float *nk, float *nv) {
+  using C = UnitCfg<B>;
   {
-    uint32_t h[32];
-    decode_run<B, 64>(r.k, lut, h);
+    // K: 64 elements of key t>>2 -> ks row, 8 halves (16 bytes) at a time
     u32x4_t *dst = reinterpret_cast<u32x4_t *>(ks + (tid >> 2) * kKsStride + 64 * (tid & 3));
 #pragma unroll
-    for (int v = 0; v < 8; ++v) dst[v] = u32x4_t{h[4 * v], h[4 * v + 1], h[4 * v + 2], h[4 * v + 3]};
+    for (int v = 0; v < 8; ++v) {
+      uint32_t h[4];
+#pragma unroll
+      for (int e = 0; e < 8 / C::U; ++e) {
+        const int u = v * (8 / C::U) + e;
+        const uint32_t idx = bits_at(r.k, u * C::IBITS, C::IBITS);
+        if constexpr (C::DW == 2) {
+          const u32x2_t w = *reinterpret_cast<const u32x2_t *>(lut + idx * 2);
+          h[2 * e] = w.x;
+          h[2 * e + 1] = w.y;
+        } else {
+          h[e] = lut[idx];
+        }
+      }
+      dst[v] = u32x4_t{h[0], h[1], h[2], h[3]};
+    }
   }
   {
+    // V: 4 keys x 16 elements -> V^T rows d = 16*db + j, one decode unit
+    // (U elements) of all four keys at a time
     const int db = tid >> 4, m = db & 7;
     const int sh = (16 * B * m) & 31;
-    uint32_t pr[4][8];
+    uint32_t run[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t run[2];
       if (B == 2) {
-        run[0] = r.v[i][0];
-        run[1] = 0;
+        run[i][0] = r.v[i][0];
+        run[i][1] = 0;
       } else {
-        run[0] = __builtin_amdgcn_alignbit(r.v[i][1], r.v[i][0], sh);
-        run[1] = sh ? (r.v[i][1] >> sh) : r.v[i][1];
+        run[i][0] = __builtin_amdgcn_alignbit(r.v[i][1], r.v[i][0], sh);
+        run[i][1] = sh ? (r.v[i][1] >> sh) : r.v[i][1];
       }
-      decode_run<B, 16>(run, lut, pr[i]);
     }
-    // transpose 4 keys x 16 d into V^T rows: d = 16*db + 2p (+1)
     _Float16 *base = vt + (16 * db) * kVtStride + 4 * (tid & 15);
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const u32x2_t e = {__builtin_amdgcn_perm(pr[1][p], pr[0][p], 0x05040100u),
-                         __builtin_amdgcn_perm(pr[3][p], pr[2][p], 0x05040100u)};
-      const u32x2_t o = {__builtin_amdgcn_perm(pr[1][p], pr[0][p], 0x07060302u),
-                         __builtin_amdgcn_perm(pr[3][p], pr[2][p], 0x07060302u)};
-      *reinterpret_cast<u32x2_t *>(base + (2 * p) * kVtStride) = e;
-      *reinterpret_cast<u32x2_t *>(base + (2 * p + 1) * kVtStride) = o;
+    for (int u = 0; u < 16 / C::U; ++u) {
+      uint32_t pr[4][C::DW];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t idx = bits_at(run[i], u * C::IBITS, C::IBITS);
+        if constexpr (C::DW == 2) {
+          const u32x2_t w = *reinterpret_cast<const u32x2_t *>(lut + idx * 2);
+          pr[i][0] = w.x;
+          pr[i][1] = w.y;
+        } else {
+          pr[i][0] = lut[idx];
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < C::DW; ++p) {
+        const int d = u * C::U + 2 * p;  // elements d, d+1 of the 16
+        const u32x2_t e = {__builtin_amdgcn_perm(pr[1][p], pr[0][p], 0x05040100u),
+                           __builtin_amdgcn_perm(pr[3][p], pr[2][p], 0x05040100u)};
+        const u32x2_t o = {__builtin_amdgcn_perm(pr[1][p], pr[0][p], 0x07060302u),
+                           __builtin_amdgcn_perm(pr[3][p], pr[2][p], 0x07060302u)};
+        *reinterpret_cast<u32x2_t *>(base + d * kVtStride) = e;
+        *reinterpret_cast<u32x2_t *>(base + (d + 1) * kVtStride) = o;
+      }
     }
   }
   {
@@ -310,15 +340,17 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
         const half8_t av = *reinterpret_cast<const half8_t *>(krow + 16 * t);
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qb[t], s1, 0, 0, 0);
       }
-      // register rr <-> key 8(rr/4) + 4hl + rr%4 of this wave's half
-      const int64_t kbase = (int64_t)kt * kKT + 32 * khalf;
+      // register rr <-> key 8(rr/4) + 4hl + rr%4 of this wave's half; keys
+      // past lim = pos - (first key of the half) are masked
+      const int64_t lim64 = pos - ((int64_t)kt * kKT + 32 * khalf);
+      const int lim = lim64 > 64 ? 64 : (int)lim64;
       float tmax = -INFINITY;
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
         const int kk = 8 * (rr >> 2) + 4 * hl + (rr & 3);
         const float2 nn = *reinterpret_cast<const float2 *>(nk + 2 * (32 * khalf + kk));
         float v = s[rr] * nn.x + s1[rr] * nn.y;
-        if (kbase + kk > pos) v = -INFINITY;
+        if (kk > lim) v = -INFINITY;
         s[rr] = v;
         tmax = fmaxf(tmax, v);
       }
@@ -339,10 +371,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
         pb1[rr >> 3][rr & 7] = (_Float16)(p * nn.y);
       }
       l_run = l_run * alpha + psum;
+      // rescale only when some column's running max moved (rare after the
+      // first tiles); alpha == 1 leaves the accumulators unchanged
+      if (__any(alpha != 1.0f)) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) o[dt][rr] *= alpha;
+      }
 
       // ---- O^T += V^T P^T; k-slot (hl, i) of group ga <-> key 16ga + 8(i>>2) + 4hl + (i&3)
 #pragma unroll
