@@ -40,6 +40,8 @@ constexpr int kPage = 32;
 constexpr int kKsStride = kD + 8;    // halves per K row
 constexpr int kVtStride = kKT + 8;   // halves per V^T row
 constexpr int kPartStride = kD + 4;  // o[128], m, l, pad
+constexpr float kPTop = 15.f;         // P = p * scale stays below 2^kPTop
+constexpr float kPSet = 9.f;          // a moved reference puts the tile's top at 2^kPSet
 
 struct Args {
   const float *q;
@@ -115,7 +117,7 @@ __device__ __forceinline__ void load_tile(const Args &a, int g, int64_t kt, int 
 
 __device__ __forceinline__ void store_tile(const Args &a, int64_t kt, int tid, const TileRaw &r,
                                            _Float16 *ksm, _Float16 *vt, float *sk, float *sv,
-                                           int *kval) {
+                                           float *ve, int *kval) {
   {
     // 32 K bytes -> 32 halves; byte pairs (2m, 2m+1) of dword m/2
     uint32_t h[16];
@@ -153,6 +155,7 @@ __device__ __forceinline__ void store_tile(const Args &a, int64_t kt, int tid, c
       kval[tid] = ok ? 1 : 0;
     } else {
       sv[tid - kKT] = s;
+      ve[tid - kKT] = (float)__builtin_amdgcn_frexp_expf(s);   // s < 2^ve
     }
   }
 }
@@ -167,6 +170,7 @@ __global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
   static_assert(kArenaHalves * 2 >= 2 * 4 * 16 * 64 * 4, "merge buffer must fit");
   __shared__ __align__(16) _Float16 arena[kArenaHalves];
   __shared__ __align__(16) float sk[kKT], sv[kKT];
+  __shared__ __align__(16) float ve[kKT];   // binary exponent of each V scale
   __shared__ float mstat[2][32], lstat[2][32];
   __shared__ int kval[kKT];   // key exists (in context, page in range)
   _Float16 *ksm = arena;
@@ -189,23 +193,38 @@ __global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
   const int64_t kt1 = lmin(kt0 + a.tiles_per_split, n_kt_all);
   const int64_t pos = a.q_pos0 + qi_c;
 
-  // query operand: d = 16t + 8hl + i, high and low float16 parts
+  // query operand: d = 16t + 8hl + i, high and low float16 parts of
+  // q * qscale * 2^qexp, the power of two putting the row's largest element
+  // just under 2^14 (both parts clear of float16 overflow and subnormals);
+  // the scores are scaled back by 2^-qexp
   half8_t qhi[8], qlo[8];
+  int qexp;
   {
     const float *qr = a.q + (qi_c * a.n_q_heads + head) * kD + 8 * hl;
+    float x[8][8];
+    float amax = 0.f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const float4 f0 = *reinterpret_cast<const float4 *>(qr + 16 * t);
       const float4 f1 = *reinterpret_cast<const float4 *>(qr + 16 * t + 4);
-      const float x[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+      const float y[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        x[t][i] = y[i] * a.qscale;
+        amax = fmaxf(amax, fabsf(x[t][i]));
+      }
+    }
+    amax = fmaxf(amax, xor_lane<32>(amax));
+    qexp = 14 - __builtin_amdgcn_frexp_expf(amax);   // amax * 2^qexp < 2^14
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         _Float16 h, l;
-        split_hl(x[i] * a.qscale, h, l);
+        split_hl(__builtin_amdgcn_ldexpf(x[t][i], qexp), h, l);
         qhi[t][i] = h;
         qlo[t][i] = l;
       }
-    }
   }
 
   f32x16_t o[4];
@@ -218,7 +237,7 @@ __global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
   TileRaw raw;
   if (kt0 < kt1) load_tile(a, g, kt0, tid, raw);
   for (int64_t kt = kt0; kt < kt1; ++kt) {
-    store_tile(a, kt, tid, raw, ksm, vt, sk, sv, kval);
+    store_tile(a, kt, tid, raw, ksm, vt, sk, sv, ve, kval);
     if (kt + 1 < kt1) load_tile(a, g, kt + 1, tid, raw);
     __syncthreads();
 
@@ -234,17 +253,24 @@ __global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
     }
     const int64_t lim64 = pos - (kt * kKT + 32 * khalf);   // keys past lim are masked
     const int lim = lim64 > 64 ? 64 : (int)lim64;
-    float tmax = -INFINITY;
+    // m_run is a reference, not the running maximum: p = exp2(s - m_run)
+    // and P = p * (V scale) goes to float16 as a high and a low part.  With
+    // e the binary exponent of a key's V scale, P < 2^(s + e - m_run); the
+    // reference moves only when some key would reach 2^kPTop, and then to put
+    // the tile's top at 2^kPSet.  So P never overflows, its parts stay clear
+    // of float16 subnormals, and the accumulators are rescaled rarely.
+    // Softmax does not depend on the reference.
+    float tref = -INFINITY;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const int kk = 8 * (rr >> 2) + 4 * hl + (rr & 3);
-      float v = s[rr] * sk[32 * khalf + kk];
+      float v = __builtin_amdgcn_ldexpf(s[rr], -qexp) * sk[32 * khalf + kk];
       if (kk > lim || !kval[32 * khalf + kk]) v = -INFINITY;  // causal / no such key
       s[rr] = v;
-      tmax = fmaxf(tmax, v);
+      tref = fmaxf(tref, v + ve[32 * khalf + kk]);
     }
-    tmax = fmaxf(tmax, xor_lane<32>(tmax));
-    const float m_new = fmaxf(m_run, tmax);
+    tref = fmaxf(tref, xor_lane<32>(tref));
+    const float m_new = tref > m_run + kPTop ? tref - kPSet : m_run;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     m_run = m_new;
@@ -261,8 +287,6 @@ __global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
       plo[rr >> 3][rr & 7] = l;
     }
     l_run = l_run * alpha + psum;
-    // rescale only when some column's running max moved (rare after the
-    // first tiles); alpha == 1 leaves the accumulators unchanged
     if (__any(alpha != 1.0f)) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)

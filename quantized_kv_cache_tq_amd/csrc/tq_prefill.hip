@@ -40,6 +40,8 @@ constexpr int kQRows = 64;          // qrows per workgroup
 constexpr int kKT = 64;             // keys per tile
 constexpr int kKsStride = kD + 8;   // halves per K row (and per staged query row)
 constexpr int kVtStride = kKT + 8;  // halves per V^T row
+constexpr float kPTop = 15.f;       // P = p * norm stays below 2^kPTop
+constexpr float kPSet = 9.f;        // a moved reference puts the tile's top at 2^kPSet
 
 __device__ const LevelTable<2> kLevels2;
 __device__ const LevelTable<3> kLevels3;
@@ -141,7 +143,7 @@ __device__ __forceinline__ void load_tile(const Args &a, int64_t head_base, int 
 template <int B>
 __device__ __forceinline__ void store_tile(const Args &a, int kt, int tid, const TileRaw<B> &r,
                                            const uint32_t *lut, _Float16 *ks, _Float16 *vt,
-                                           float *nk, float *nv) {
+                                           float *nk, float *nv, float *ve) {
   using C = UnitCfg<B>;
   {
     // K: 64 elements of key t>>2 -> ks row, 8 halves (16 bytes) at a time
@@ -210,8 +212,14 @@ __device__ __forceinline__ void store_tile(const Args &a, int kt, int tid, const
   {
     const int64_t key = (int64_t)kt * kKT + ((tid & 127) >> 1);
     const float n = key < a.kv_len ? half_to_float(r.nrm) : 0.f;
-    if (tid < 2 * kKT) nk[tid] = n;        // nk[key * 2 + group]
-    else nv[tid - 2 * kKT] = n;
+    const float n2 = fmaxf(n, xor_lane<1>(n));   // larger norm of the key's two groups
+    if (tid < 2 * kKT) {
+      nk[tid] = n;                         // nk[key * 2 + group]
+    } else {
+      nv[tid - 2 * kKT] = n;
+      // binary exponent of the larger V norm: both norms are < 2^ve
+      if (!(tid & 1)) ve[(tid - 2 * kKT) >> 1] = (float)__builtin_amdgcn_frexp_expf(n2);
+    }
   }
 }
 
@@ -230,6 +238,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
   _Float16 *vt = arena + kKT * kKsStride;
   __shared__ __align__(16) float nk[2 * kKT];   // [key][group]
   __shared__ __align__(16) float nv[2 * kKT];
+  __shared__ __align__(16) float ve[kKT];       // V-norm exponent per key
   __shared__ float mstat[2][32], lstat[2][32];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -320,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
     TileRaw<B> raw;
     load_tile<B>(a, head_base, 0, tid, raw);
     for (int kt = 0; kt < n_kt; ++kt) {
-      store_tile<B>(a, kt, tid, raw, lut, ks, vt, nk, nv);
+      store_tile<B>(a, kt, tid, raw, lut, ks, vt, nk, nv, ve);
       if (kt + 1 < n_kt) load_tile<B>(a, head_base, kt + 1, tid, raw);
       __syncthreads();
 
@@ -344,7 +353,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
       // past lim = pos - (first key of the half) are masked
       const int64_t lim64 = pos - ((int64_t)kt * kKT + 32 * khalf);
       const int lim = lim64 > 64 ? 64 : (int)lim64;
-      float tmax = -INFINITY;
+      // m_run is a reference, not the running maximum: p = exp2(s - m_run)
+      // and P = p * (V norm) goes to float16.  With e the binary exponent of
+      // a key's larger V norm, P < 2^(s + e - m_run); the reference moves
+      // only when some key would reach 2^kPTop, and then to put the tile's
+      // top at 2^kPSet.  So P never overflows, stays clear of float16
+      // subnormals, and the accumulators are rescaled rarely.  Softmax does
+      // not depend on the reference.
+      float tref = -INFINITY;
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
         const int kk = 8 * (rr >> 2) + 4 * hl + (rr & 3);
@@ -352,14 +368,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
         float v = s[rr] * nn.x + s1[rr] * nn.y;
         if (kk > lim) v = -INFINITY;
         s[rr] = v;
-        tmax = fmaxf(tmax, v);
+        tref = fmaxf(tref, v + ve[32 * khalf + kk]);
       }
-      tmax = fmaxf(tmax, xor_lane<32>(tmax));
-      const float m_new = fmaxf(m_run, tmax);
+      tref = fmaxf(tref, xor_lane<32>(tref));
+      const float m_new = tref > m_run + kPTop ? tref - kPSet : m_run;
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
       m_run = m_new;
-      half8_t pb[2], pb1[2];   // p * V-norm of group 0 / group 1
+      half8_t pb[2], pb1[2];   // P of group 0 / group 1
       float psum = 0.f;
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
@@ -371,8 +387,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
         pb1[rr >> 3][rr & 7] = (_Float16)(p * nn.y);
       }
       l_run = l_run * alpha + psum;
-      // rescale only when some column's running max moved (rare after the
-      // first tiles); alpha == 1 leaves the accumulators unchanged
       if (__any(alpha != 1.0f)) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)

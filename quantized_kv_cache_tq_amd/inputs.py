@@ -75,19 +75,23 @@ def _int8_rows(rows: np.ndarray):
 
 
 def int8_prompt(seed: int = 0, ctx: int = 40000, n_q: int = 2048, n_q_heads: int = 8,
-                n_kv: int = 1, d: int = 128, page: int = 32, identity_pages: bool = False):
+                n_kv: int = 1, d: int = 128, page: int = 32, identity_pages: bool = False,
+                k_mult: float = 1.0, v_mult: float = 1.0):
     """Paged int8 prompt-attention inputs.
 
     K_f, V_f = N(0,1) [ctx, n_kv, d] in logical order -> int8 with per-row
     float16 scales; page table = rng.permutation(n_chunks) (logical chunk i is
     stored at physical chunk pt[i]); Q = N(0,1) [n_q, n_q_heads, d] float32.
     Returns q, k8, v8, k_scale, v_scale (physical order), page_table, logical
-    copies (k8_log, v8_log, ks_log, vs_log) for reference.
+    copies (k8_log, v8_log, ks_log, vs_log) for reference.  k_mult / v_mult
+    scale K_f / V_f before the int8 conversion (large-magnitude cases).
     """
     assert ctx % page == 0
     rng = np.random.default_rng(seed)
     kf = normal(rng, (ctx, n_kv, d))
     vf = normal(rng, (ctx, n_kv, d))
+    kf = (kf * np.float32(k_mult)).astype(np.float32)
+    vf = (vf * np.float32(v_mult)).astype(np.float32)
     n_chunks = ctx // page
     pt = rng.permutation(n_chunks).astype(np.int32)
     if identity_pages:

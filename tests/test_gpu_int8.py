@@ -94,3 +94,12 @@ def test_page_placement_does_not_change_bits():
 def test_int8_deterministic():
     d = inputs.int8_prompt(seed=8, ctx=2048, n_q=64)
     np.testing.assert_array_equal(_gpu(d, 2048, 2048 - 64), _gpu(d, 2048, 2048 - 64))
+
+
+def test_large_scales_and_sharp_scores():
+    """V rows scaled by 1e5 (float16 scales near 3000) and K by 4: p * scale
+    overflows float16 once p exceeds about 20, so tiles whose score maximum
+    rises take the exact-maximum path; compared at unit V scale."""
+    d = inputs.int8_prompt(seed=11, ctx=2048, n_q=256, v_mult=1e5, k_mult=4.0)
+    got, want = _gpu(d, 2048, 2048 - 256), _oracle(d, 2048, 2048 - 256)
+    _check(got / 1e5, want / 1e5, "large scales")
