@@ -93,6 +93,83 @@ struct alignas(16) LevelTable {
   }
 };
 
+// float16 bits of magnitudes 2k and 2k+1 (low, high half).
+template <int B>
+__host__ __device__ constexpr uint32_t mag_word(int k) {
+  return (uint32_t)f16_bits_exact(magnitude<B>(2 * k)) |
+         ((2 * k + 1 < (1 << (B - 1))) ? (uint32_t)f16_bits_exact(magnitude<B>(2 * k + 1)) << 16 : 0u);
+}
+
+// float16 levels of codes c0 (low half) and c1 (high half): the magnitudes
+// are picked by v_perm_b32 from the constant magnitude words (byte selector
+// 2q, 2q+1 per half), then the sign bits are applied.
+template <int B>
+__device__ __forceinline__ uint32_t level_pair(uint32_t c0, uint32_t c1) {
+  constexpr uint32_t QM = (1u << (B - 1)) - 1u;
+  const uint32_t sgn = ((c0 >> (B - 1)) << 15) | ((c1 >> (B - 1)) << 31);
+  const uint32_t q0 = c0 & QM & 3u, q1 = c1 & QM & 3u;
+  const uint32_t sel = 0x01000100u + (q0 | (q1 << 16)) * 0x202u;
+  if constexpr (B == 2) {
+    return __builtin_amdgcn_perm(mag_word<2>(0), mag_word<2>(0), sel) ^ sgn;
+  } else if constexpr (B == 3) {
+    return __builtin_amdgcn_perm(mag_word<3>(1), mag_word<3>(0), sel) ^ sgn;
+  } else {
+    const uint32_t lo = __builtin_amdgcn_perm(mag_word<4>(1), mag_word<4>(0), sel);
+    const uint32_t hi = __builtin_amdgcn_perm(mag_word<4>(3), mag_word<4>(2), sel);
+    const uint32_t m = ((c0 & 4u) ? 0xffffu : 0u) | ((c1 & 4u) ? 0xffff0000u : 0u);
+    return ((hi & m) | (lo & ~m)) ^ sgn;
+  }
+}
+
+// Writes the level table (the layout of LevelTable<B>) to shared memory
+// with NT threads; computed from the magnitudes, no global memory read.
+template <int B, int NT>
+__device__ __forceinline__ void build_level_table(uint32_t *lut, int tid) {
+  using C = UnitCfg<B>;
+  constexpr uint32_t CM = (1u << B) - 1u;
+#pragma unroll
+  for (int j = 0; j < (C::N + NT - 1) / NT; ++j) {
+    const uint32_t e = (uint32_t)tid + (uint32_t)NT * j;
+    if (C::N % NT == 0 || e < (uint32_t)C::N) {
+      if constexpr (C::DW == 2) {
+        const uint32_t lo = level_pair<B>(e & CM, (e >> B) & CM);
+        const uint32_t hi = level_pair<B>((e >> (2 * B)) & CM, (e >> (3 * B)) & CM);
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<u32x2_t *>(lut + 2 * e) = u32x2_t{lo, hi};
+      } else {
+        lut[e] = level_pair<B>(e & CM, (e >> B) & CM);
+      }
+    }
+  }
+}
+
+// Pair table for the decode kernels: entry e (the 2B-bit concatenation of
+// two codes, first code in the low bits) holds their two float16 levels
+// (first in the low half).  It is stored in 64 copies with copy c of entry e
+// at dword 64e + c, and lane l of a wave always reads copy l: whatever the
+// indices, the 64 lanes of one lookup touch 64 consecutive banks' worth of
+// distinct dwords (no bank conflicts), unlike a single-copy table whose
+// random lookups pile onto the same banks.
+template <int B>
+struct PairCfg {
+  static constexpr int BITS = 2 * B;
+  static constexpr int N = 1 << BITS;
+  static constexpr int WORDS = N * 64;
+};
+
+template <int B, int NT>
+__device__ __forceinline__ void build_pair_table(uint32_t *tab, int tid) {
+  using P = PairCfg<B>;
+  constexpr uint32_t CM = (1u << B) - 1u;
+  static_assert(P::WORDS % NT == 0 && NT % 64 == 0, "pair table fill");
+#pragma unroll
+  for (int j = 0; j < P::WORDS / NT; ++j) {
+    // entry (tid + NT j) / 64 is the same for a whole wave
+    const uint32_t e = (uint32_t)__builtin_amdgcn_readfirstlane((tid >> 6) + (NT / 64) * j);
+    tab[tid + NT * j] = level_pair<B>(e & CM, e >> B);
+  }
+}
+
 // The fixed random sign flip: element d negated iff bit d%64 of word d/64 is
 // set (the first two SplitMix64 outputs from state 0).
 constexpr uint64_t kSignWord0 = 0xe220a8397b1dcdafull;
@@ -106,7 +183,7 @@ __device__ __forceinline__ uint32_t sign_bit_of(int d) {
 
 // v from lane (lane ^ H).  H = 1, 2: DPP quad permutes; H = 4: half-row
 // mirror (lane ^ 7) then quad reverse (^ 3); H = 8: row rotate by 8;
-// H = 16: ds_swizzle in xor mode (within 32 lanes); H = 32: ds_bpermute.
+// H = 16: ds_swizzle in xor mode (within 32 lanes); H = 32: v_permlane32_swap.
 template <int H>
 __device__ __forceinline__ float xor_lane(float v) {
   const int x = __float_as_int(v);
@@ -124,9 +201,23 @@ __device__ __forceinline__ float xor_lane(float v) {
     r = __builtin_amdgcn_ds_swizzle(x, 0x401F);
   } else {
     static_assert(H == 32, "xor_lane: H must be a power of two <= 32");
-    r = __shfl_xor(x, 32, 64);
+    // v_permlane32_swap(a, b) trades a's upper 32 lanes for b's lower 32:
+    // with a = b = x the first result holds x[l & 31], the second x[l | 32]
+    const auto p = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+    r = (int)((threadIdx.x & 32) ? p[0] : p[1]);
   }
   return __int_as_float(r);
+}
+
+// Sum and maximum of v over the lane pair (l, l ^ 32); both lanes get the
+// same bits (the operands meet in the same order).
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 
 __device__ __forceinline__ float flip_sign(float x, uint32_t negate) {

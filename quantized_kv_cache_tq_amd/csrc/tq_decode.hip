@@ -45,16 +45,6 @@ constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kD = 128;              // head_dim handled by this kernel
 constexpr int kPartStride = kD + 4;  // o[128], m, l, pad (floats; 16-byte rows)
 
-__device__ const LevelTable<2> kLevels2;
-__device__ const LevelTable<3> kLevels3;
-__device__ const LevelTable<4> kLevels4;
-
-template <int B>
-__device__ __forceinline__ const uint32_t *level_table() {
-  if constexpr (B == 2) return kLevels2.w;
-  else if constexpr (B == 3) return kLevels3.w;
-  else return kLevels4.w;
-}
 
 // Bits [pos, pos+nbits) of a little-endian dword array (pos and nbits are
 // compile-time after unrolling; the field spans at most two dwords).
@@ -66,51 +56,21 @@ __device__ __forceinline__ uint32_t bits_at(const uint32_t *dw, int pos, int nbi
 }
 
 // Decode NEL consecutive elements held in dw (first element in bit 0) into
-// float16 pairs out[0 .. NEL/2).
+// float16 pairs out[0 .. NEL/2) through the pair table; tab points at this
+// lane's copy (dword lane of the table).
 template <int B, int NEL>
-__device__ __forceinline__ void decode_run(const uint32_t *dw, const uint32_t *lut,
-                                           uint32_t *out) {
-  using C = UnitCfg<B>;
+__device__ __forceinline__ void decode_pairs(const uint32_t *dw, const uint32_t *tab,
+                                             uint32_t *out) {
+  constexpr int PB = 2 * B;
 #pragma unroll
-  for (int u = 0; u < NEL / C::U; ++u) {
-    const uint32_t idx = bits_at(dw, u * C::IBITS, C::IBITS);
-    if constexpr (C::DW == 2) {
-      const u32x2_t e = *reinterpret_cast<const u32x2_t *>(lut + idx * 2);
-      out[2 * u] = e.x;
-      out[2 * u + 1] = e.y;
-    } else {
-      out[u] = lut[idx];
-    }
-  }
+  for (int j = 0; j < NEL / 2; ++j) out[j] = tab[bits_at(dw, PB * j, PB) * 64];
 }
 
 __device__ __forceinline__ float half_to_float(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
-template <int B, int TPW>
-struct DecodeSmem {
-  static constexpr int KPW = 16 * TPW;               // keys per wave
-  static constexpr int KPS = KPW * kDecWaves;        // keys per split
-  static constexpr int ROWW = 4 * B;                 // code dwords per key
-  static constexpr int ROWP = ROWW + 1;              // padded LDS row (dwords)
-  static constexpr int VWORDS = KPW * ROWP;          // one wave's V rows
-  static constexpr int OBUF_WORDS = kDecWaves * 8 * kD;
-  static constexpr int LUT_WORDS = UnitCfg<B>::WORDS;
-  // after the value phase the level table and V rows are dead: the output
-  // buffer reuses them
-  static constexpr int BIG = LUT_WORDS + kDecWaves * VWORDS;
-  static constexpr int ARENA = BIG > OBUF_WORDS ? BIG : OBUF_WORDS;
-};
-
 __device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
-
-// Float16 high part (hi lanes) or low part (lo lanes) of x: x - fp16(x) is
-// exact in float32, so hi + lo carries ~22 significant bits of x.
-__device__ __forceinline__ _Float16 split_half(float x, bool lo_lane) {
-  const _Float16 h = (_Float16)x;
-  return lo_lane ? (_Float16)(x - (float)h) : h;
-}
 
 // Keeps the compiler from moving LDS accesses across this point; LDS
 // operations of one wave execute in order, so other lanes' earlier writes
@@ -121,247 +81,295 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int B, int TPW, bool QBF16>
-__global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
+// Workgroup (split s, kv head g): eight waves, four key ranges of KPW = 16T
+// keys.  Waves 0-3 ("key waves") score their range and turn the scores into
+// the matrix-core operand P; waves 4-7 ("value waves") meanwhile decode the
+// V codes of the same ranges into B operands held in registers.  After one
+// barrier every value wave runs its T x 8 value products; the four partial
+// outputs are merged in shared memory and written as one split partial.
+template <int B, int T, bool QBF16>
+__global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     const uint8_t *__restrict__ kcodes, const uint16_t *__restrict__ knorms,
     const uint8_t *__restrict__ vcodes, const uint16_t *__restrict__ vnorms, int64_t n_cells,
     int64_t kv_len, const void *__restrict__ q, int n_rep, float qscale,
     float *__restrict__ ws, int n_split) {
-  using C = UnitCfg<B>;
-  using S = DecodeSmem<B, TPW>;
-  constexpr int KPW = S::KPW, KPS = S::KPS, ROWP = S::ROWP;
-  constexpr int VCH = KPW * B;                             // 16-byte V chunks per wave
-  constexpr int NV = ceil_div(VCH, 64);
-  constexpr int NLUT = ceil_div(C::WORDS / 4, kDecThreads);
+  constexpr int KPW = 16 * T;                  // keys per range
+  constexpr int KPS = 4 * KPW;                 // keys per split
+  constexpr int ROWW = 4 * B;                  // code dwords per key
+  constexpr int ROWP = ROWW + 1;               // padded LDS row
+  constexpr int RPL = ceil_div(KPW, 64);       // V rows per lane
   constexpr int NNORM = ceil_div(KPW, 64);
-  __shared__ __align__(16) uint32_t arena[S::ARENA];       // level table | V rows, later obuf
-  __shared__ __align__(16) float nk[kDecWaves][KPW];
-  __shared__ __align__(16) float nv[kDecWaves][KPW];
-  __shared__ __align__(16) uint32_t qbuf[4 * 64 * 4];      // query operand, [t][lane][8 halves]
-  __shared__ float wm[kDecWaves][8], wl[kDecWaves][8];
-  uint32_t *lut = arena;
-  uint32_t *vrows = arena + S::LUT_WORDS + (threadIdx.x >> 6) * S::VWORDS;
+  __shared__ __align__(16) uint32_t ptab[PairCfg<B>::WORDS];   // pair table, 64 copies
+  // V rows of the four ranges, plus one spare dword (a lane's two-dword
+  // read of a row may touch the dword after it)
+  __shared__ __align__(16) uint32_t vrows[4 * KPW * ROWP + 1];
+  __shared__ __align__(16) u32x2_t pbuf[4][T][64];          // P operands, per lane
+  __shared__ __align__(16) float nk[4][KPW];
+  __shared__ __align__(16) float nv[4][KPW];
+  __shared__ __align__(16) uint32_t qbuf[4 * 64 * 4];       // query operand, [t][lane][8 halves]
+  __shared__ __align__(16) float obuf[4][8 * kD];
+  __shared__ float wm[4][8], wl[4][8];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wave & 3;                     // key range of this wave
+  const bool kwave = wave < 4;
   const int col = lane & 15, quad = lane >> 4;
   const int s = blockIdx.x, g = blockIdx.y;
-  const int64_t head_base = (int64_t)g * n_cells;
-  const int64_t w0 = (int64_t)s * KPS + (int64_t)wave * KPW;     // first key of this wave
-  const int wkeys = (int)(kv_len - w0 < 0 ? 0 : (kv_len - w0 < KPW ? kv_len - w0 : KPW));
-  const int64_t wsafe = wkeys > 0 ? w0 : kv_len - 1;              // a valid row for clamping
+  // keys [w0, w0 + wkeys) of range rg; addressing is relative to row0, a
+  // valid key row, with lane offsets clamped to the range's last key
+  const int64_t w0 = (int64_t)s * KPS + (int64_t)rg * KPW;
+  const int64_t left = kv_len - w0;
+  const int wkeys = (int)(left < 0 ? 0 : (left < KPW ? left : KPW));
   const int wlast = wkeys > 0 ? wkeys - 1 : 0;
+  const int64_t row0 = (int64_t)g * n_cells + (wkeys > 0 ? w0 : kv_len - 1);
 
-  // ---- every global load, straight-line (clamped, never branched around),
-  //      in the order of first use: table, query, norms, K tiles, V rows.
-  u32x4_t lraw[NLUT];
-  const u32x4_t *lsrc = reinterpret_cast<const u32x4_t *>(level_table<B>());
+  if (kwave) {
+    // ---------------- key wave: loads first (query, norms, K codes)
+    const uint8_t *kb = kcodes + row0 * (16 * B);
+    const uint16_t *knb = knorms + row0, *vnb = vnorms + row0;
+    const int qh = 2 * rg + (lane >> 5), qj = lane & 31;
+    const int64_t qbase = ((int64_t)g * n_rep + imin(qh, n_rep - 1)) * kD + 4 * qj;
+    float qv[4];
+    if constexpr (QBF16) {
+      const u32x2_t b = *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint16_t *>(q) + qbase);
+      qv[0] = __uint_as_float(b.x << 16);
+      qv[1] = __uint_as_float(b.x & 0xffff0000u);
+      qv[2] = __uint_as_float(b.y << 16);
+      qv[3] = __uint_as_float(b.y & 0xffff0000u);
+    } else {
+      const float4 f = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(q) + qbase);
+      qv[0] = f.x; qv[1] = f.y; qv[2] = f.z; qv[3] = f.w;
+    }
+    uint16_t kn[NNORM], vn[NNORM];
 #pragma unroll
-  for (int i = 0; i < NLUT; ++i) lraw[i] = lsrc[imin(tid + kDecThreads * i, C::WORDS / 4 - 1)];
-  const int qh = 2 * (wave & 3) + (lane >> 5), qj = lane & 31;
-  const int64_t qbase = ((int64_t)g * n_rep + imin(qh, n_rep - 1)) * kD + 4 * qj;
-  float qv[4];
-  if constexpr (QBF16) {
-    const u32x2_t b = *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint16_t *>(q) + qbase);
-    qv[0] = __uint_as_float(b.x << 16);
-    qv[1] = __uint_as_float(b.x & 0xffff0000u);
-    qv[2] = __uint_as_float(b.y << 16);
-    qv[3] = __uint_as_float(b.y & 0xffff0000u);
-  } else {
-    const float4 f = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(q) + qbase);
-    qv[0] = f.x; qv[1] = f.y; qv[2] = f.z; qv[3] = f.w;
-  }
-  uint16_t kn[NNORM], vn[NNORM];
+    for (int i = 0; i < NNORM; ++i) {
+      const uint32_t kk = (uint32_t)imin(lane + 64 * i, wlast);
+      kn[i] = knb[kk];
+      vn[i] = vnb[kk];
+    }
+    // lane (col, quad) of tile t reads key 16t + col, dwords B*quad .. B*quad+B-1
+    uint32_t kd[T][B];
 #pragma unroll
-  for (int i = 0; i < NNORM; ++i) {
-    const int64_t key = wsafe + imin(lane + 64 * i, wlast);
-    kn[i] = knorms[head_base + key];
-    vn[i] = vnorms[head_base + key];
-  }
-  // K: lane (col, quad) of tile t reads key 16t + col, dwords B*quad .. B*quad+B-1
-  uint32_t kd[TPW][B];
+    for (int t = 0; t < T; ++t) {
+      const uint32_t off = (uint32_t)imin(16 * t + col, wlast) * (4u * ROWW) + 4u * B * quad;
+      const uint32_t *row = reinterpret_cast<const uint32_t *>(kb + off);
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int64_t key = wsafe + imin(16 * t + col, wlast);
-    const uint32_t *row =
-        reinterpret_cast<const uint32_t *>(kcodes + (head_base + key) * (16 * B)) + B * quad;
-#pragma unroll
-    for (int i = 0; i < B; ++i) kd[t][i] = row[i];
-  }
-  const u32x4_t *vseg = reinterpret_cast<const u32x4_t *>(vcodes + (head_base + wsafe) * (16 * B));
-  u32x4_t vraw[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) vraw[i] = vseg[imin(lane + 64 * i, wkeys * B - 1 < 0 ? 0 : wkeys * B - 1)];
+      for (int i = 0; i < B; ++i) kd[t][i] = row[i];
+    }
 
-  // ---- level table to LDS; rotate + split the queries into the operand buffer
-#pragma unroll
-  for (int i = 0; i < NLUT; ++i) {
-    const int c = tid + kDecThreads * i;
-    if (c < C::WORDS / 4) reinterpret_cast<u32x4_t *>(lut)[c] = lraw[i];
-  }
-  if (wave < 4) {
-    // thread holds elements d = 4qj .. 4qj+3 of head qh; in the MFMA B operand
-    // they are slots i = 4(qj&1) .. +3 of K-step t = (qj>>1)&3 in lane
-    // 16*(qj>>3) + qh (high half) and 16*(qj>>3) + 8 + qh (low half).
+    build_pair_table<B, kDecThreads>(ptab, tid);
+    // rotate + split heads 2rg, 2rg+1: thread holds d = 4qj .. 4qj+3 of head
+    // qh; in the MFMA B operand they are slots i = 4(qj&1) .. +3 of K-step
+    // t = (qj>>1)&3 in lane 16*(qj>>3) + qh (high half) and
+    // 16*(qj>>3) + 8 + qh (low half)
 #pragma unroll
     for (int i = 0; i < 4; ++i) qv[i] = flip_sign(qv[i], sign_bit_of(4 * qj + i));
     wht128_half(qv, qj);
-    const bool live = qh < n_rep;
-    uint32_t hw[2], lw[2];
+    {
+      const bool live = qh < n_rep;
+      uint32_t hw[2], lw[2];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const float x0 = live ? qv[2 * p] * qscale : 0.f;
-      const float x1 = live ? qv[2 * p + 1] * qscale : 0.f;
-      const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-      const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
-      hw[p] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-      lw[p] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+      for (int p = 0; p < 2; ++p) {
+        const float x0 = live ? qv[2 * p] * qscale : 0.f;
+        const float x1 = live ? qv[2 * p + 1] * qscale : 0.f;
+        const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+        const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
+        hw[p] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        lw[p] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+      }
+      const int t = (qj >> 1) & 3, qd = qj >> 3, half_off = 2 * (qj & 1);
+      *reinterpret_cast<u32x2_t *>(qbuf + (t * 64 + 16 * qd + qh) * 4 + half_off) = u32x2_t{hw[0], hw[1]};
+      *reinterpret_cast<u32x2_t *>(qbuf + (t * 64 + 16 * qd + 8 + qh) * 4 + half_off) = u32x2_t{lw[0], lw[1]};
     }
-    const int t = (qj >> 1) & 3, qd = qj >> 3, half_off = 2 * (qj & 1);
-    *reinterpret_cast<u32x2_t *>(qbuf + (t * 64 + 16 * qd + qh) * 4 + half_off) = u32x2_t{hw[0], hw[1]};
-    *reinterpret_cast<u32x2_t *>(qbuf + (t * 64 + 16 * qd + 8 + qh) * 4 + half_off) = u32x2_t{lw[0], lw[1]};
-  }
-#pragma unroll
-  for (int i = 0; i < NNORM; ++i) {
-    const int kk = lane + 64 * i;
-    if (kk < KPW) {
-      const bool ok = kk < wkeys;
-      nk[wave][kk] = ok ? half_to_float(kn[i]) : 0.f;
-      nv[wave][kk] = ok ? half_to_float(vn[i]) : 0.f;
-    }
-  }
-  __syncthreads();
+    __syncthreads();   // table and query operand complete
 
-  // Query operand: column n = lane & 15 -> head n & 7, high (n < 8) or low half;
-  // k-slot (lane >> 4, i) of K-step t <-> element d = 32*(lane>>4) + 8t + i.
-  half8_t qb[4];
+    // norms of the range (this wave's own slice)
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
-    qb[t] = __builtin_bit_cast(half8_t, reinterpret_cast<const u32x4_t *>(qbuf)[t * 64 + lane]);
+    for (int i = 0; i < NNORM; ++i) {
+      const int kk = lane + 64 * i;
+      if (kk < KPW) {
+        const bool ok = kk < wkeys;
+        nk[rg][kk] = ok ? half_to_float(kn[i]) : 0.f;
+        nv[rg][kk] = ok ? half_to_float(vn[i]) : 0.f;
+      }
+    }
+    // Query operand: column n = lane & 15 -> head n & 7, high (n < 8) or low
+    // half; k-slot (lane >> 4, i) of K-step t <-> element d = 32*(lane>>4) + 8t + i.
+    half8_t qb[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      qb[t] = __builtin_bit_cast(half8_t, reinterpret_cast<const u32x4_t *>(qbuf)[t * 64 + lane]);
+    wave_lds_fence();
 
-  // ---- scores of this wave's keys, tile by tile as their codes arrive
-  float sc[TPW][4];
-  float mx = -INFINITY;
+    // ---- scores: S^T[key][col] over the range, tile by tile
+    const uint32_t *tab = ptab + lane;
+    float sc[T][4];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    uint32_t a16[16];
-    decode_run<B, 32>(kd[t], lut, a16);
-    float4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < T; ++t) {
+      uint32_t a16[16];
+      decode_pairs<B, 32>(kd[t], tab, a16);
+      float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const u32x4_t av = {a16[4 * st], a16[4 * st + 1], a16[4 * st + 2], a16[4 * st + 3]};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[st], acc,
-                                                  0, 0, 0);
+      for (int st = 0; st < 4; ++st) {
+        const u32x4_t av = {a16[4 * st], a16[4 * st + 1], a16[4 * st + 2], a16[4 * st + 3]};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[st], acc,
+                                                    0, 0, 0);
+      }
+      const float4 n4 = *reinterpret_cast<const float4 *>(&nk[rg][16 * t + 4 * quad]);
+      const float nkv[4] = {n4.x, n4.y, n4.z, n4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[t][i] = (acc[i] + xor_lane<8>(acc[i])) * nkv[i];
     }
-    const float4 n4 = *reinterpret_cast<const float4 *>(&nk[wave][16 * t + 4 * quad]);
-    const float nkv[4] = {n4.x, n4.y, n4.z, n4.w};
+    if (wkeys < KPW) {   // wave-uniform: only a ragged last range masks
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = (acc[i] + xor_lane<8>(acc[i])) * nkv[i];
-      if (wkeys < KPW && 16 * t + 4 * quad + i >= wkeys) v = -INFINITY;
-      sc[t][i] = v;
-      mx = fmaxf(mx, v);
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (16 * t + 4 * quad + i >= wkeys) sc[t][i] = -INFINITY;
     }
-  }
-  // wave max per head (log2 domain); -inf for a wave without keys
-  mx = fmaxf(mx, xor_lane<16>(mx));
-  mx = fmaxf(mx, xor_lane<32>(mx));
-  const float msafe = mx == -INFINITY ? 0.f : mx;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[t][i]);
+    // range max per head (log2 domain); -inf for a range without keys
+    mx = fmaxf(mx, xor_lane<16>(mx));
+    mx = max_xor32(mx);
+    const float msafe = mx == -INFINITY ? 0.f : mx;
 
-  // ---- this wave's V rows to its LDS slice
+    // ---- P operand: the score layout (lane = column + 16 * key quad) is the
+    //      A-operand layout of the value product.  Rows < 8 carry the
+    //      float16 high part of p * vnorm, rows >= 8 the low part:
+    //      x - hi * lo_sel (lo_sel = 1 on low rows, 0 on high rows) is exact
+    //      in float32 and rounds once to float16.
+    const float lo_sel = col >= 8 ? 1.f : 0.f;
+    float lsum = 0.f;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int c = lane + 64 * i;
-    if (c < VCH) {
-      uint32_t *d = vrows + (c / B) * ROWP + 4 * (c % B);
-      d[0] = vraw[i].x; d[1] = vraw[i].y; d[2] = vraw[i].z; d[3] = vraw[i].w;
+    for (int t = 0; t < T; ++t) {
+      const float4 n4 = *reinterpret_cast<const float4 *>(&nv[rg][16 * t + 4 * quad]);
+      const float nvv[4] = {n4.x, n4.y, n4.z, n4.w};
+      half4_t pa;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(sc[t][i] - msafe);
+        lsum += p;
+        const float x = p * nvv[i];
+        const _Float16 h = (_Float16)x;
+        pa[i] = (_Float16)__builtin_fmaf(-(float)h, lo_sel, x);
+      }
+      pbuf[rg][t][lane] = __builtin_bit_cast(u32x2_t, pa);
     }
-  }
-  wave_lds_fence();
+    lsum += xor_lane<16>(lsum);
+    lsum = sum_xor32(lsum);
+    if (lane < 8) {
+      wm[rg][lane] = mx;
+      wl[rg][lane] = lsum;
+    }
+    __syncthreads();   // P operands complete
+    __syncthreads();   // value products done (partial outputs in obuf)
+  } else {
+    // ---------------- value wave: V rows (lane r loads rows r, r + 64, ...)
+    const uint8_t *vb = vcodes + row0 * (16 * B);
+    u32x4_t vraw[RPL][B];
+#pragma unroll
+    for (int j = 0; j < RPL; ++j)
+#pragma unroll
+      for (int i = 0; i < B; ++i)
+        vraw[j][i] = *reinterpret_cast<const u32x4_t *>(
+            vb + (uint32_t)imin(lane + 64 * j, wlast) * (16u * B) + 16u * i);
+    build_pair_table<B, kDecThreads>(ptab, tid);
+    __syncthreads();   // table and query operand complete
 
-  // ---- probabilities and values
-  float4_t o[8];
+    uint32_t *vr = vrows + rg * KPW * ROWP;
 #pragma unroll
-  for (int t = 0; t < 8; ++t) o[t] = float4_t{0.f, 0.f, 0.f, 0.f};
-  float lsum = 0.f;
-  const bool lo_lane = col >= 8;
-  constexpr int VBITS = 8 * B;
-  const int vpos = VBITS * col;  // value elements 8*col .. 8*col + 7
-  const int vw0 = vpos >> 5, vsh = vpos & 31;
+    for (int j = 0; j < RPL; ++j) {
+      const int r = lane + 64 * j;
+      if (r < KPW) {
+        uint32_t *d = vr + r * ROWP;
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const float4 n4 = *reinterpret_cast<const float4 *>(&nv[wave][16 * t + 4 * quad]);
-    const float nvv[4] = {n4.x, n4.y, n4.z, n4.w};
-    half4_t pa;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = __builtin_amdgcn_exp2f(sc[t][i] - msafe);
-      lsum += p;
-      pa[i] = split_half(p * nvv[i], lo_lane);
+        for (int i = 0; i < B; ++i) {
+          d[4 * i] = vraw[j][i].x;
+          d[4 * i + 1] = vraw[j][i].y;
+          d[4 * i + 2] = vraw[j][i].z;
+          d[4 * i + 3] = vraw[j][i].w;
+        }
+      }
     }
-    uint32_t vv[4][4];
+    wave_lds_fence();
+    // B operands: lane (n, quad) of tile t holds keys 16t + 4quad + j
+    // (j = 0..3) at d = 8n + dt of d-tile dt; it decodes the 8 elements
+    // 8n .. 8n+7 of each of its four keys and regroups them by element.
+    constexpr int VBITS = 8 * B;
+    const int vpos = VBITS * col;
+    const int vw0 = vpos >> 5, vsh = vpos & 31;
+    const uint32_t *vlane = vr + 4 * quad * ROWP + vw0;
+    const uint32_t *tab = ptab + lane;
+    u32x2_t vbop[T][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t *row = vrows + (16 * t + 4 * quad + i) * ROWP + vw0;
-      const uint32_t run[1] = {__builtin_amdgcn_alignbit(row[1], row[0], vsh)};
-      decode_run<B, 8>(run, lut, vv[i]);
-    }
+    for (int t = 0; t < T; ++t) {
+      uint32_t vv[4][4];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int w = dt >> 1;
-      const uint32_t sel = (dt & 1) ? 0x07060302u : 0x05040100u;
-      const u32x2_t bv = {__builtin_amdgcn_perm(vv[1][w], vv[0][w], sel),
-                          __builtin_amdgcn_perm(vv[3][w], vv[2][w], sel)};
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(half4_t, bv), o[dt], 0,
-                                                   0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t *row = vlane + (16 * t + i) * ROWP;
+        const uint32_t run[1] = {__builtin_amdgcn_alignbit(row[1], row[0], vsh)};
+        decode_pairs<B, 8>(run, tab, vv[i]);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const int w = dt >> 1;
+        const uint32_t sel = (dt & 1) ? 0x07060302u : 0x05040100u;
+        vbop[t][dt] = u32x2_t{__builtin_amdgcn_perm(vv[1][w], vv[0][w], sel),
+                              __builtin_amdgcn_perm(vv[3][w], vv[2][w], sel)};
+      }
     }
-  }
-  lsum += xor_lane<16>(lsum);
-  lsum += xor_lane<32>(lsum);
+    __syncthreads();   // P operands complete
 
-  // ---- combine high/low rows: after the swap, lanes 0-31 hold d-tiles 0-3
-  //      and lanes 32-63 d-tiles 4-7, each as high + low.
-  float oc[4][4];
+    float4_t o[8];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < 8; ++dt) o[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(o[dt][i]),
-                                                      __float_as_uint(o[dt + 4][i]), false, false);
-      oc[dt][i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    for (int t = 0; t < T; ++t) {
+      const half4_t pa = __builtin_bit_cast(half4_t, pbuf[rg][t][lane]);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(half4_t, vbop[t][dt]),
+                                                     o[dt], 0, 0, 0);
     }
-  if (lane < 8) {
-    wm[wave][lane] = mx;
-    wl[wave][lane] = lsum;
-  }
-  __syncthreads();  // all waves are done with the table and V rows
-  float *obuf = reinterpret_cast<float *>(arena);
-  {
+    // combine high/low rows: after the swap, lanes 0-31 hold d-tiles 0-3 and
+    // lanes 32-63 d-tiles 4-7, each as high + low; row (head) 4*((lane&31)>>4) + i
     const int qd = (lane & 31) >> 4, dhi = lane >> 5;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float4 v = make_float4(oc[0][i], oc[1][i], oc[2][i], oc[3][i]);
-      *reinterpret_cast<float4 *>(obuf + (wave * 8 + 4 * qd + i) * kD + 8 * col + 4 * dhi) = v;
+      float oc[4];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(o[dt][i]),
+                                                        __float_as_uint(o[dt + 4][i]), false, false);
+        oc[dt] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      }
+      *reinterpret_cast<float4 *>(&obuf[rg][(4 * qd + i) * kD + 8 * col + 4 * dhi]) =
+          make_float4(oc[0], oc[1], oc[2], oc[3]);
     }
+    __syncthreads();   // value products done (partial outputs in obuf)
   }
-  __syncthreads();
-  // obuf[wave][h][8c + t] holds d-tile t, column c, i.e. element d = 8c + t;
-  // each wave's sums are relative to its own max, rescaled here.
+
+  // ---- merge the four ranges: obuf[r][h][8c + t] holds element d = 8c + t
+  //      of head h, relative to the range's own max
   float *part = ws + ((int64_t)g * n_rep * n_split + s) * kPartStride;
   {
     const int h = tid >> 6, d = 2 * (tid & 63);
     if (h < n_rep) {
-      float M = wm[0][h];
-#pragma unroll
-      for (int w = 1; w < kDecWaves; ++w) M = fmaxf(M, wm[w][h]);
+      const float M = fmaxf(fmaxf(wm[0][h], wm[1][h]), fmaxf(wm[2][h], wm[3][h]));
       float a0 = 0.f, a1 = 0.f, L = 0.f;
 #pragma unroll
-      for (int w = 0; w < kDecWaves; ++w) {
-        const float mw = wm[w][h];
-        const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-        const float2 v = *reinterpret_cast<const float2 *>(obuf + (w * 8 + h) * kD + d);
+      for (int r = 0; r < 4; ++r) {
+        const float mr = wm[r][h];
+        const float f = mr == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mr - M);
+        const float2 v = *reinterpret_cast<const float2 *>(&obuf[r][h * kD + d]);
         a0 += f * v.x;
         a1 += f * v.y;
-        L += f * wl[w][h];
+        L += f * wl[r][h];
       }
       float *ph = part + (int64_t)h * n_split * kPartStride;
       *reinterpret_cast<float2 *>(ph + d) = make_float2(a0, a1);
@@ -454,15 +462,16 @@ hipError_t plan_decode(const tq_cache &k, int64_t kv_len, int32_t n_q_heads, Dec
   int n_cu = 0;
   hipError_t e = device_cu_count(&n_cu);
   if (e != hipSuccess) return e;
-  // largest tile count (<= 4) that still gives every compute unit a workgroup
+  // largest tile count (<= 4 per key range) that still gives every compute
+  // unit two workgroups; a split covers 4 ranges of 16 * tiles keys
   int tpw = 4;
   while (tpw > 1) {
-    const int64_t splits = ceil_div<int64_t>(kv_len, 16LL * kDecWaves * tpw);
-    if (splits * k.n_kv_heads >= n_cu) break;
+    const int64_t splits = ceil_div<int64_t>(kv_len, 64LL * tpw);
+    if (splits * k.n_kv_heads >= 2LL * n_cu) break;
     tpw >>= 1;
   }
   p->tiles_per_wave = tpw;
-  p->keys_per_split = 16 * kDecWaves * tpw;
+  p->keys_per_split = 64 * tpw;
   const int64_t n_split = ceil_div<int64_t>(kv_len, p->keys_per_split);
   if (n_split > 0x7fffffff) return hipErrorInvalidValue;
   p->n_split = (int)n_split;
@@ -482,7 +491,8 @@ static void launch_split(int tpw, dim3 grid, hipStream_t st, const tq_cache &k,
   switch (tpw) {
     case 1: TQ_DEC(1); break;
     case 2: TQ_DEC(2); break;
-    default: TQ_DEC(4); break;
+    case 4: TQ_DEC(4); break;
+    default: TQ_DEC(8); break;
   }
 #undef TQ_DEC
 }

@@ -16,8 +16,8 @@ hipError_t launch_set_rows(const tq_cache &c, const float *src, const int64_t *c
                            int64_t n_rows, hipStream_t stream);
 
 struct DecodePlan {
-  int tiles_per_wave;    // 16-key tiles per wave
-  int keys_per_split;    // 64 * tiles_per_wave (4 waves per workgroup)
+  int tiles_per_wave;    // 16-key tiles per key range (4 ranges per workgroup)
+  int keys_per_split;    // 64 * tiles_per_wave
   int n_split;           // workgroups per kv head
   size_t workspace_bytes;
 };
