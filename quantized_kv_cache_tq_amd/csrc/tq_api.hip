@@ -34,7 +34,9 @@ tq_status check_pair(const tq_cache *k, const tq_cache *v) {
   return TQ_OK;
 }
 
-tq_status from_hip(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_ERR_HIP; }
+tq_status from_hip(hipError_t e) {
+  return e == hipSuccess ? TQ_OK : e == hipErrorNotSupported ? TQ_ERR_UNSUPPORTED : TQ_ERR_HIP;
+}
 
 }  // namespace
 
@@ -110,7 +112,7 @@ tq_status tq_attn_decode_workspace(const tq_cache *k, int64_t kv_len, int32_t n_
   if (s != TQ_OK) return s;
   if (!bytes) return TQ_ERR_INVALID_ARG;
   DecodePlan p;
-  if (plan_decode(*k, kv_len, n_q_heads, &p) != hipSuccess) return TQ_ERR_HIP;
+  if (tq_status st = from_hip(plan_decode(*k, kv_len, n_q_heads, &p))) return st;
   *bytes = p.workspace_bytes;
   return TQ_OK;
 }
@@ -129,7 +131,7 @@ tq_status tq_attn_decode(const tq_cache *k, const tq_cache *v, int64_t kv_len, c
     return TQ_ERR_INVALID_ARG;
   if (sparse_v_tau != 0.f) return TQ_ERR_UNSUPPORTED;
   DecodePlan p;
-  if (plan_decode(*k, kv_len, n_q_heads, &p) != hipSuccess) return TQ_ERR_HIP;
+  if (tq_status st = from_hip(plan_decode(*k, kv_len, n_q_heads, &p))) return st;
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.workspace_bytes)
     return TQ_ERR_WORKSPACE;
   return from_hip(launch_decode(*k, *v, kv_len, q, q_dtype, n_q_heads, scale, out, workspace, p,

@@ -87,3 +87,43 @@ def test_decode_deterministic():
     _, a = _run(3, q, k, v, 5000, what="det-1")
     _, b_ = _run(3, q, k, v, 5000, what="det-2")
     np.testing.assert_array_equal(a, b_)
+
+
+def test_shared_workspace_across_lengths():
+    """One workspace serves calls with different split counts: each result
+    equals the result of a call with a fresh workspace, bit for bit (eager,
+    then under graph replay with eager calls in between)."""
+    import torch
+    from quantized_kv_cache_tq_amd import binding as b
+    from gpu_util import bf16_cuda
+    q, k, v = inputs.outlier_decode(seed=3, kv_len=32768)
+    kc, vc, ok, ov = _caches(3, k, v)
+    qt = bf16_cuda(q)
+    scale = 1.0 / math.sqrt(q.shape[1])
+    lens = [32768, 1000, 17, 32768, 4097]
+    fresh = {n: b.tq_attn_decode(kc, vc, n, qt, scale).cpu().numpy() for n in set(lens)}
+    nbytes = max(b.tq_attn_decode_workspace(kc, n, q.shape[0]) for n in lens)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for n in lens:
+        got = b.tq_attn_decode(kc, vc, n, qt, scale, workspace=ws).cpu().numpy()
+        np.testing.assert_array_equal(got, fresh[n], err_msg=f"kv_len={n}")
+    want = o.attn_decode(ok, ov, 1000, q.astype(np.float64), scale)
+    from gpu_util import assert_attention_close
+    assert_attention_close(fresh[1000], want, what="kv 1000")
+    # graph capture of two calls on the same workspace, replayed with eager
+    # work in between; every replay must reproduce the eager result
+    outs = [torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device="cuda") for _ in range(2)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            b.tq_attn_decode(kc, vc, 32768, qt, scale, out=outs[0], workspace=ws, stream=s)
+            b.tq_attn_decode(kc, vc, 1000, qt, scale, out=outs[1], workspace=ws, stream=s)
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(outs[0].cpu().numpy(), fresh[32768], err_msg=f"replay {rep}")
+        np.testing.assert_array_equal(outs[1].cpu().numpy(), fresh[1000], err_msg=f"replay {rep}")
+        eager = b.tq_attn_decode(kc, vc, 17, qt, scale, workspace=ws).cpu().numpy()
+        np.testing.assert_array_equal(eager, fresh[17])
