@@ -37,6 +37,34 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak
 FP32_PEAK_TFLOPS = 157.3
 
+# HBM traffic of one decode call (split + merge kernels), from two
+# `rocprofv3 --pmc` passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) over
+# `bench.py --no-cpu-baseline --only decode,copy --steps 2 --warmup 1`, each
+# scaled by what the same counter reads for the 256 MiB device copy of that
+# run (FETCH_SIZE reads 131088.6 KiB for 262144 KiB copied: x1.99975;
+# WRITE_SIZE reads 262144 KiB: x1.0).  Valid only for the decode sources it
+# was taken on (sha256 of tq_decode.hip + tq_common.h); otherwise traffic is
+# reported as null.
+DECODE_TRAFFIC = {"sources_sha256": "e94444c8af1ebea3e5ba1fac7c2baac8567cd57bf953f05e8a1ff396d4d8ae7d",
+                  "fetch_kib": {"decode_split_kernel": 6511.5, "decode_merge_kernel": 1084.5},
+                  "write_kib": {"decode_split_kernel": 2176.0, "decode_merge_kernel": 16.0},
+                  "fetch_scale": 1.99975, "write_scale": 1.0}
+
+
+def decode_traffic_bytes():
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for f in ("tq_decode.hip", "tq_common.h"):
+        with open(os.path.join(here, "quantized_kv_cache_tq_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    t = DECODE_TRAFFIC
+    if h.hexdigest() != t["sources_sha256"]:
+        return None
+    kib = (sum(t["fetch_kib"].values()) * t["fetch_scale"] +
+           sum(t["write_kib"].values()) * t["write_scale"])
+    return int(round(kib * 1024))
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -248,8 +276,10 @@ def main():
                          "GBps": round(gbps, 2), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
                          "layers_per_step": L}
         out["roofline"] = {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
-                           "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                           "kernel": "decode call (decode_split_kernel<3,4> + decode_merge_kernel)"}
+                           "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                           "traffic": decode_traffic_bytes(),
+                           "kernel": "decode call (decode_split_kernel + decode_merge_kernel), "
+                                     "algorithmic bytes = packed K+V codes and norms"}
     if ms["set_rows"] is not None:
         per_cache_us = ms["set_rows"] * 1e3
         nbytes = 2 * (KV * NKV * D * 4 + KV * NKV * 50)
