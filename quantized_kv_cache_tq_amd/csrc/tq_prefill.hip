@@ -4,23 +4,39 @@
 // [PR28] "Inline-dequant TILE prefill": the earlier path materialized the
 // whole cache as float16 temporaries on every step; the fast path decodes the
 // 3-bit K/V codes while loading each tile into shared memory.  Here each
-// 64-key tile is decoded through the LDS level table straight into two LDS
-// tiles: K as [key][d] and V transposed as [d][key], the layouts the matrix
-// cores read.  Nothing is ever written back to global memory but the output.
+// 64-key tile is decoded through the LDS pair table straight into two LDS
+// tiles, K as [key][d] and V transposed as [d][key] (the layouts the matrix
+// cores read), as float16 values level * norm / 16: the group norm is folded
+// into the tile, so the products need no per-key scaling.  Such a value is at
+// most 2.8 * 65504 / 16 in magnitude, so it never overflows float16.  Nothing
+// is written back to global memory but the output.
+//
+// Scales: the rotated coordinate of a group is level * norm / sqrt(128), and
+// the query is rotated with the unnormalized transform H (sqrt(128) times the
+// orthonormal one), so score = H(s.q) . Ktile / 8 and the output group is
+// s . H(sum_k p_k Vtile_k) / (8 sum_k p_k).
 //
 // Products (v_mfma_f32_32x32x16_f16, fp32 accumulate):
 //   S^T[key][qrow] = K[key][:] . Qrot[qrow][:]   A = K tile, B = rotated query
 //   O^T[d][qrow]  += V^T[d][key] P^T[key][qrow]  A = V^T tile, B = P
-// A "qrow" is one (query row, query head) pair; the accumulator layout of
-// S^T (one query column per lane pair) is exactly the B-operand layout P needs,
-// so softmax never leaves registers.  Per-key norms scale S^T's rows (K) and
-// fold into P (V); the rotation of Q happens at tile load and its inverse on
-// the accumulators.
+// A "qrow" is one (query row, query head) pair; the accumulator layout of S^T
+// (one query column per lane pair) is the B-operand layout P needs, so the
+// softmax never leaves registers.
 //
-// Workgroup: 64 qrows (64/n_rep query rows x n_rep heads of one kv head),
-// four waves = 2 qrow halves x 2 key halves of every tile; the two key halves
-// are merged at the end.  Causal balance: workgroup p processes query tiles p
-// and T-1-p, so every workgroup sees about the same number of key tiles.
+// Workgroup: 64 qrows (64/n_rep query rows x n_rep heads of one kv head) and
+// eight waves in two roles, one of each per SIMD:
+//   * matrix waves 0-3 (qrow half x key half of every tile): scores, softmax,
+//     P.V.  The scores of tile t+1 are issued together with the softmax of
+//     tile t, so the exponentials overlap the matrix products.
+//   * decode waves 4-7: turn the codes of later tiles into the float16 tiles
+//     in the phase that does not read them (V looked up one tile ahead into
+//     registers).
+// Two barriers per tile separate the phases; each tile buffer is single:
+//   A(t): matrix: S(t+1) from K, softmax(t)   decode: write V(t), look up V(t+1)
+//   B(t): matrix: O += V(t) P(t)              decode: decode K(t+2) into K
+// Causal balance: workgroup p processes query tiles p and T-1-p, so every
+// workgroup sees about the same number of key tiles.  After the key loop all
+// eight waves merge the two key halves and apply the inverse rotation.
 #include "tq_common.h"
 #include "tq_launch.h"
 
@@ -29,67 +45,67 @@ namespace tq {
 namespace pf {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kD = 256;             // head_dim
-constexpr int kQRows = 64;          // qrows per workgroup
-constexpr int kKT = 64;             // keys per tile
-constexpr int kKsStride = kD + 8;   // halves per K row (and per staged query row)
-constexpr int kVtStride = kKT + 8;  // halves per V^T row
-constexpr float kPTop = 15.f;       // P = p * norm stays below 2^kPTop
-constexpr float kPSet = 9.f;        // a moved reference puts the tile's top at 2^kPSet
+constexpr int kHalf = kThreads / 2;   // matrix threads; the rest decode
+constexpr int kD = 256;               // head_dim
+constexpr int kQRows = 64;            // qrows per workgroup
+constexpr int kKT = 64;               // keys per tile
+constexpr int kKsStride = kD + 8;     // halves per K row and per query row
+constexpr int kVtStride = kKT + 4;    // halves per V^T row (136 B: conflict-free both ways)
+constexpr int kKsHalves = kKT * kKsStride;
+constexpr int kVtHalves = kD * kVtStride;
+constexpr int kQsHalves = kQRows * kKsStride;
+constexpr int kTileHalves = kKsHalves + kVtHalves + kQsHalves;
+// key-half merge: per qrow half [d-tile][4 regs][64 lanes][4], d-tile
+// stride padded by 16 floats so the reads of four d-tiles hit distinct banks
+constexpr int kEDt = 16 * 64 + 16;
+constexpr int kEWave = 8 * kEDt;
+constexpr float kLazy = 8.f;          // the reference moves only past 2^8
 
-__device__ const LevelTable<2> kLevels2;
-__device__ const LevelTable<3> kLevels3;
-__device__ const LevelTable<4> kLevels4;
-template <int B>
-__device__ __forceinline__ const uint32_t *level_table() {
-  if constexpr (B == 2) return kLevels2.w;
-  else if constexpr (B == 3) return kLevels3.w;
-  else return kLevels4.w;
-}
+static_assert(2 * kEWave * 4 <= kTileHalves * 2, "merge buffer must fit in the tile buffers");
+static_assert(kKsHalves <= kVtHalves, "K tile 0 is staged in the V^T buffer");
 
-__device__ __forceinline__ uint32_t bits_at(const uint32_t *dw, int pos, int nbits) {
-  const int w = pos >> 5, sh = pos & 31;
-  uint32_t x = dw[w] >> sh;
-  if (sh + nbits > 32) x |= dw[w + 1] << (32 - sh);
-  return x & ((1u << nbits) - 1u);
-}
-
-template <int B, int NEL>
-__device__ __forceinline__ void decode_run(const uint32_t *dw, const uint32_t *lut,
-                                           uint32_t *out) {
-  using C = UnitCfg<B>;
-#pragma unroll
-  for (int u = 0; u < NEL / C::U; ++u) {
-    const uint32_t idx = bits_at(dw, u * C::IBITS, C::IBITS);
-    if constexpr (C::DW == 2) {
-      const u32x2_t e = *reinterpret_cast<const u32x2_t *>(lut + idx * 2);
-      out[2 * u] = e.x;
-      out[2 * u + 1] = e.y;
-    } else {
-      out[u] = lut[idx];
-    }
-  }
-}
-
-__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
 __device__ __forceinline__ int64_t lmin(int64_t a, int64_t b) { return a < b ? a : b; }
 
-__device__ __forceinline__ float half_to_float(uint16_t h) {
-  return (float)__builtin_bit_cast(_Float16, h);
+// nbits-bit field at bit pos of dw (pos, nbits compile-time after unrolling).
+__device__ __forceinline__ uint32_t bits_at(const uint32_t *dw, int pos, int nbits) {
+  const int w = pos >> 5, sh = pos & 31;
+  if (sh + nbits <= 32) return __builtin_amdgcn_ubfe(dw[w], sh, nbits);
+  return __builtin_amdgcn_alignbit(dw[w + 1], dw[w], sh) & ((1u << nbits) - 1u);
 }
 
-// Raw codes of one key tile, prefetched into registers.
+// Pair-table entry e of this lane's copy (tab = table + lane), scaled by the
+// float16 pair n2 (the group norm / 16 in both halves).
+__device__ __forceinline__ uint32_t pair_scaled(const uint32_t *tab, uint32_t e, uint32_t n2) {
+  const uint32_t lv = tab[e * 64];
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, lv) * __builtin_bit_cast(half2_t, n2));
+}
+
+// norm / 16 as float16, in both halves.
+__device__ __forceinline__ uint32_t norm_pair(uint16_t h) {
+  const _Float16 n = __builtin_bit_cast(_Float16, h) * (_Float16)0.0625f;
+  const uint32_t b = __builtin_bit_cast(uint16_t, n);
+  return b | (b << 16);
+}
+
+// Codes of one key tile for a decode thread.  K: key (thread & 63),
+// elements 64q .. 64q+63 with q = decode wave; V: keys 4(t&15)+i, 16
+// elements from 16(t>>4).
 template <int B>
-struct TileRaw {
-  uint32_t k[2 * B];     // K: key t>>2, elements 64*(t&3) .. +63
-  uint32_t v[4][2];      // V: keys 4*(t&15)+i, 16 elements from 16*(t>>4)
-  uint16_t nrm;          // norms: t < 128 -> K (key (t&127)>>1, group t&1); else V
+struct KRaw {
+  uint32_t c[2 * B];
+  uint16_t n;
+};
+template <int B>
+struct VRaw {
+  uint32_t c[4][2];
+  uint16_t n[4];
 };
 
 struct Args {
@@ -104,160 +120,150 @@ struct Args {
   float qscale;
 };
 
+// Per-head code and norm bases (wave-uniform); key offsets from them are
+// 32-bit (the host checks that a head's codes span less than 4 GiB).
+struct HeadPtrs {
+  const uint8_t *kc, *vc;
+  const uint16_t *kn, *vn;
+};
+
+// Global loads (keys clamped to the last valid one: tiles past the end load
+// valid rows, and their scores are masked).
 template <int B>
-__device__ __forceinline__ void load_tile(const Args &a, int64_t head_base, int kt, int tid,
-                                          TileRaw<B> &r) {
-  const int64_t last = a.kv_len - 1;
-  {
-    const int64_t key = lmin((int64_t)kt * kKT + (tid >> 2), last);
-    const u32x2_t *src = reinterpret_cast<const u32x2_t *>(a.kcodes + (head_base + key) * (32 * B) +
-                                                           8 * B * (tid & 3));
+__device__ __forceinline__ void load_k(const HeadPtrs &h, int last, int kt, int dt, KRaw<B> &r) {
+  const int q = dt >> 6;
+  const uint32_t key = (uint32_t)min(kt * kKT + (dt & 63), last);
+  const u32x2_t *src = reinterpret_cast<const u32x2_t *>(h.kc + key * (32u * B) + 8 * B * q);
 #pragma unroll
-    for (int i = 0; i < B; ++i) {
-      const u32x2_t v = src[i];
-      r.k[2 * i] = v.x;
-      r.k[2 * i + 1] = v.y;
-    }
+  for (int i = 0; i < B; ++i) {
+    const u32x2_t v = src[i];
+    r.c[2 * i] = v.x;
+    r.c[2 * i + 1] = v.y;
   }
-  {
-    const int db = tid >> 4, m = db & 7;
-    const int pos = 16 * B * m;
-    const int w0 = pos >> 5;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t key = lmin((int64_t)kt * kKT + 4 * (tid & 15) + i, last);
-      const uint32_t *row = reinterpret_cast<const uint32_t *>(
-          a.vcodes + (head_base + key) * (32 * B) + 16 * B * (db >> 3));
-      r.v[i][0] = row[w0];
-      r.v[i][1] = (B == 2) ? 0u : row[w0 + 1];
-    }
-  }
-  {
-    // two float16 norms per key (one per 128-group), [key][group]
-    const int64_t key = lmin((int64_t)kt * kKT + ((tid & 127) >> 1), last);
-    const int64_t idx = (head_base + key) * 2 + (tid & 1);
-    r.nrm = (tid < 128) ? a.knorms[idx] : a.vnorms[idx];
-  }
+  r.n = h.kn[key * 2u + (q >> 1)];
 }
 
 template <int B>
-__device__ __forceinline__ void store_tile(const Args &a, int kt, int tid, const TileRaw<B> &r,
-                                           const uint32_t *lut, _Float16 *ks, _Float16 *vt,
-                                           float *nk, float *nv, float *ve) {
-  using C = UnitCfg<B>;
-  {
-    // K: 64 elements of key t>>2 -> ks row, 8 halves (16 bytes) at a time
-    u32x4_t *dst = reinterpret_cast<u32x4_t *>(ks + (tid >> 2) * kKsStride + 64 * (tid & 3));
+__device__ __forceinline__ void load_v(const HeadPtrs &h, int last, int kt, int dt, VRaw<B> &r) {
+  const int db = dt >> 4, m = db & 7;
+  const int w0 = (16 * B * m) >> 5;
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      uint32_t h[4];
-#pragma unroll
-      for (int e = 0; e < 8 / C::U; ++e) {
-        const int u = v * (8 / C::U) + e;
-        const uint32_t idx = bits_at(r.k, u * C::IBITS, C::IBITS);
-        if constexpr (C::DW == 2) {
-          const u32x2_t w = *reinterpret_cast<const u32x2_t *>(lut + idx * 2);
-          h[2 * e] = w.x;
-          h[2 * e + 1] = w.y;
-        } else {
-          h[e] = lut[idx];
-        }
-      }
-      dst[v] = u32x4_t{h[0], h[1], h[2], h[3]};
-    }
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t key = (uint32_t)min(kt * kKT + 4 * (dt & 15) + i, last);
+    const uint32_t *row = reinterpret_cast<const uint32_t *>(h.vc + key * (32u * B) + 16 * B * (db >> 3));
+    r.c[i][0] = row[w0];
+    r.c[i][1] = (B == 2) ? 0u : row[w0 + 1];
+    r.n[i] = h.vn[key * 2u + (db >> 3)];
   }
-  {
-    // V: 4 keys x 16 elements -> V^T rows d = 16*db + j, one decode unit
-    // (U elements) of all four keys at a time
-    const int db = tid >> 4, m = db & 7;
-    const int sh = (16 * B * m) & 31;
-    uint32_t run[4][2];
+}
+
+// K part: 64 elements of one key -> its K row quarter, every pair-table read
+// first, then eight 16-byte writes.
+template <int B>
+__device__ __forceinline__ void store_k(const KRaw<B> &r, int dt, const uint32_t *tab, _Float16 *ks) {
+  const uint32_t n2 = norm_pair(r.n);
+  uint32_t h[32];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (B == 2) {
-        run[i][0] = r.v[i][0];
-        run[i][1] = 0;
-      } else {
-        run[i][0] = __builtin_amdgcn_alignbit(r.v[i][1], r.v[i][0], sh);
-        run[i][1] = sh ? (r.v[i][1] >> sh) : r.v[i][1];
-      }
-    }
-    _Float16 *base = vt + (16 * db) * kVtStride + 4 * (tid & 15);
+  for (int j = 0; j < 32; ++j) h[j] = pair_scaled(tab, bits_at(r.c, 2 * B * j, 2 * B), n2);
+  u32x4_t *dst = reinterpret_cast<u32x4_t *>(ks + (dt & 63) * kKsStride + 64 * (dt >> 6));
 #pragma unroll
-    for (int u = 0; u < 16 / C::U; ++u) {
-      uint32_t pr[4][C::DW];
+  for (int v = 0; v < 8; ++v) dst[v] = u32x4_t{h[4 * v], h[4 * v + 1], h[4 * v + 2], h[4 * v + 3]};
+}
+
+// V part, transposed: 4 keys x 16 elements -> V^T rows d = 16 db + j,
+// four keys per 8-byte write.  Looked up into w (held until the V buffer is
+// free), written by write_v.
+template <int B>
+__device__ __forceinline__ void lookup_v(const VRaw<B> &r, int dt, const uint32_t *tab, uint32_t (&w)[8][4]) {
+  const int m = (dt >> 4) & 7;
+  const int sh = (16 * B * m) & 31;
+  uint32_t run[4][2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t idx = bits_at(run[i], u * C::IBITS, C::IBITS);
-        if constexpr (C::DW == 2) {
-          const u32x2_t w = *reinterpret_cast<const u32x2_t *>(lut + idx * 2);
-          pr[i][0] = w.x;
-          pr[i][1] = w.y;
-        } else {
-          pr[i][0] = lut[idx];
-        }
-      }
-#pragma unroll
-      for (int p = 0; p < C::DW; ++p) {
-        const int d = u * C::U + 2 * p;  // elements d, d+1 of the 16
-        const u32x2_t e = {__builtin_amdgcn_perm(pr[1][p], pr[0][p], 0x05040100u),
-                           __builtin_amdgcn_perm(pr[3][p], pr[2][p], 0x05040100u)};
-        const u32x2_t o = {__builtin_amdgcn_perm(pr[1][p], pr[0][p], 0x07060302u),
-                           __builtin_amdgcn_perm(pr[3][p], pr[2][p], 0x07060302u)};
-        *reinterpret_cast<u32x2_t *>(base + d * kVtStride) = e;
-        *reinterpret_cast<u32x2_t *>(base + (d + 1) * kVtStride) = o;
-      }
-    }
-  }
-  {
-    const int64_t key = (int64_t)kt * kKT + ((tid & 127) >> 1);
-    const float n = key < a.kv_len ? half_to_float(r.nrm) : 0.f;
-    const float n2 = fmaxf(n, xor_lane<1>(n));   // larger norm of the key's two groups
-    if (tid < 2 * kKT) {
-      nk[tid] = n;                         // nk[key * 2 + group]
+  for (int i = 0; i < 4; ++i) {
+    if (B == 2) {
+      run[i][0] = r.c[i][0];
+      run[i][1] = 0;
     } else {
-      nv[tid - 2 * kKT] = n;
-      // binary exponent of the larger V norm: both norms are < 2^ve
-      if (!(tid & 1)) ve[(tid - 2 * kKT) >> 1] = (float)__builtin_amdgcn_frexp_expf(n2);
+      run[i][0] = __builtin_amdgcn_alignbit(r.c[i][1], r.c[i][0], sh);
+      run[i][1] = sh ? (r.c[i][1] >> sh) : r.c[i][1];
     }
   }
+  uint32_t n2[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) n2[i] = norm_pair(r.n[i]);
+  uint32_t prs[8][4];
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) prs[u][i] = pair_scaled(tab, bits_at(run[i], 2 * B * u, 2 * B), n2[i]);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    w[u][0] = __builtin_amdgcn_perm(prs[u][1], prs[u][0], 0x05040100u);
+    w[u][1] = __builtin_amdgcn_perm(prs[u][3], prs[u][2], 0x05040100u);
+    w[u][2] = __builtin_amdgcn_perm(prs[u][1], prs[u][0], 0x07060302u);
+    w[u][3] = __builtin_amdgcn_perm(prs[u][3], prs[u][2], 0x07060302u);
+  }
+}
+
+__device__ __forceinline__ void write_v(const uint32_t (&w)[8][4], int dt, _Float16 *vt) {
+  _Float16 *base = vt + (16 * (dt >> 4)) * kVtStride + 4 * (dt & 15);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    *reinterpret_cast<u32x2_t *>(base + (2 * u) * kVtStride) = u32x2_t{w[u][0], w[u][1]};
+    *reinterpret_cast<u32x2_t *>(base + (2 * u + 1) * kVtStride) = u32x2_t{w[u][2], w[u][3]};
+  }
+}
+
+// S^T of this wave's 32 keys x 32 qrows over all 256 dimensions.
+__device__ __forceinline__ f32x16_t scores(const _Float16 *krow, const _Float16 *qrow) {
+  f32x16_t s;
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) s[rr] = 0.f;
+#pragma unroll
+  for (int t = 0; t < 16; ++t)
+    s = __builtin_amdgcn_mfma_f32_32x32x16_f16(*reinterpret_cast<const half8_t *>(krow + 16 * t),
+                                               *reinterpret_cast<const half8_t *>(qrow + 16 * t), s, 0, 0, 0);
+  return s;
+}
+
+// One unnormalized 128-point transform step inside a thread's 2^L elements
+// (stage h: pairs (i, i + h) for i with bit h clear).
+template <int N>
+__device__ __forceinline__ void wht_in_regs(float (&x)[N]) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int h = 1; h < N; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (!(i & h)) {
+        const float u = x[i], v = x[i + h];
+        x[i] = u + v;
+        x[i + h] = u - v;
+      }
 }
 
 template <int B, bool QBF16>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
-  using C = UnitCfg<B>;
-  constexpr int NLUT = ceil_div(C::WORDS / 4, kThreads);
-  __shared__ __align__(16) uint32_t lut[C::WORDS];
-  // one arena: K tile [key][d] | V^T tile [d][key]; it also stages the query
-  // rows (first part) and, after the key loop, the key-half merge (64 KB)
-  constexpr int kArenaHalves = kKT * kKsStride + kD * kVtStride;
-  static_assert(kArenaHalves * 2 >= 2 * 8 * 16 * 64 * 4, "merge buffer must fit");
-  static_assert(kQRows * kKsStride <= kKT * kKsStride, "query staging must fit");
-  __shared__ __align__(16) _Float16 arena[kArenaHalves];
-  _Float16 *ks = arena;
-  _Float16 *vt = arena + kKT * kKsStride;
-  __shared__ __align__(16) float nk[2 * kKT];   // [key][group]
-  __shared__ __align__(16) float nv[2 * kKT];
-  __shared__ __align__(16) float ve[kKT];       // V-norm exponent per key
-  __shared__ float mstat[2][32], lstat[2][32];
+  // aligned to its size, so a lookup address is (entry << 8) | (lane << 2)
+  // on top of the table base with no carries
+  __shared__ __align__(PairCfg<B>::WORDS * 4) uint32_t ptab[PairCfg<B>::WORDS];
+  // the K tile, the V^T tile, the rotated query rows; after the key loop the
+  // same bytes hold the key-half merge
+  __shared__ __align__(16) _Float16 tiles[kTileHalves];
+  __shared__ float mst[2][kQRows], lst[2][kQRows];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int qhalf = wave & 1, khalf = wave >> 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = blockIdx.y;
   const int64_t head_base = (int64_t)g * a.n_cells;
-  const int ql = lane & 31, hl = lane >> 5;       // column (qrow within the wave), lane half
-  const int qrow = 32 * qhalf + ql;               // qrow within the workgroup
-  const int head_local = qrow / a.bq, row_local = qrow % a.bq;
-  const int head = g * a.n_rep + head_local;
+  _Float16 *kbuf = tiles;
+  _Float16 *vbuf = tiles + kKsHalves;
+  _Float16 *qbuf = vbuf + kVtHalves;
+  float *ebuf = reinterpret_cast<float *>(tiles);
+  const uint32_t *tab = ptab + lane;   // this lane's pair-table copy
 
-  {
-    const u32x4_t *lsrc = reinterpret_cast<const u32x4_t *>(level_table<B>());
-#pragma unroll
-    for (int i = 0; i < NLUT; ++i) {
-      const int c = tid + kThreads * i;
-      if (c < C::WORDS / 4) reinterpret_cast<u32x4_t *>(lut)[c] = lsrc[c];
-    }
-  }
+  build_pair_table<B, kThreads>(ptab, tid);
+  __syncthreads();
 
   for (int pass = 0; pass < 2; ++pass) {
     const int qt = pass == 0 ? (int)blockIdx.x : a.n_qtiles - 1 - (int)blockIdx.x;
@@ -266,240 +272,303 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
     const int64_t last_row = lmin(row0 + a.bq, a.n_rows) - 1;
     const int64_t kend = lmin(a.kv_len, a.q_pos0 + last_row + 1);
     const int n_kt = (int)ceil_div<int64_t>(kend, kKT);
-    const int64_t r = row0 + row_local;
-    const int64_t pos = lmin(a.q_pos0 + r, a.kv_len - 1);   // mask bound of this column
+    // tiles past this key need the causal mask (the first row sees keys <= pos_min)
+    const int64_t pos_min = lmin(a.q_pos0 + row0, a.kv_len - 1);
 
-    // ---- stage the rotated query rows (float16) in ks; (qrow, group) pairs
-    //      are rotated by half-waves, 4 elements per lane
-    __syncthreads();  // previous pass is done with ks
-    for (int batch = 0; batch < 4; ++batch) {
-      float qv[8][4];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int idx = 16 * batch + 2 * k + (lane >> 5);   // 0..63 within the wave
-        const int c = 32 * qhalf + (idx >> 1);  // qrow
-        const int grp = idx & 1;
+    if (wave < 4) {
+      // ================================================= matrix waves
+      const int qhalf = wave & 1, khalf = wave >> 1;
+      const int ql = lane & 31, hl = lane >> 5;
+      {
+        // ---- rotated query rows: thread (c, group, h) owns elements
+        //      64h .. 64h+63 of one group of qrow c
+        const int h = tid & 1, c = (tid >> 1) & 63, grp = tid >> 7;
         const int hq = c / a.bq, rq = c % a.bq;
         const int64_t rr = lmin(row0 + rq, a.n_rows - 1);
-        const int64_t off = (rr * a.n_q + g * a.n_rep + hq) * kD + 128 * grp + 4 * (lane & 31);
+        const int64_t off = (rr * a.n_q + g * a.n_rep + hq) * kD + 128 * grp + 64 * h;
+        float x[64];
         if constexpr (QBF16) {
-          const u32x2_t b = *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint16_t *>(a.q) + off);
-          qv[k][0] = __uint_as_float(b.x << 16);
-          qv[k][1] = __uint_as_float(b.x & 0xffff0000u);
-          qv[k][2] = __uint_as_float(b.y << 16);
-          qv[k][3] = __uint_as_float(b.y & 0xffff0000u);
-        } else {
-          const float4 f = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.q) + off);
-          qv[k][0] = f.x; qv[k][1] = f.y; qv[k][2] = f.z; qv[k][3] = f.w;
-        }
-      }
-      if (khalf == 0) {
+          const u32x4_t *src = reinterpret_cast<const u32x4_t *>(reinterpret_cast<const uint16_t *>(a.q) + off);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int idx = 16 * batch + 2 * k + (lane >> 5);
-          const int c = 32 * qhalf + (idx >> 1);
-          const int grp = idx & 1;
-          const int j = lane & 31;
+          for (int v = 0; v < 8; ++v) {
+            const u32x4_t b = src[v];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) qv[k][i] = flip_sign(qv[k][i], sign_bit_of(4 * j + i));
-          wht128_half(qv[k], j);
-          const _Float16 h0 = (_Float16)(qv[k][0] * a.qscale), h1 = (_Float16)(qv[k][1] * a.qscale);
-          const _Float16 h2 = (_Float16)(qv[k][2] * a.qscale), h3 = (_Float16)(qv[k][3] * a.qscale);
-          const u32x2_t w = {(uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16),
-                             (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16)};
-          *reinterpret_cast<u32x2_t *>(ks + c * kKsStride + 128 * grp + 4 * j) = w;
-        }
-      }
-    }
-    __syncthreads();
-    // query operand: lane (ql, hl) holds qrow ql of this wave, d = 16t + 8hl + i
-    half8_t qb[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t)
-      qb[t] = *reinterpret_cast<const half8_t *>(ks + (32 * qhalf + ql) * kKsStride + 16 * t + 8 * hl);
-    __syncthreads();  // ks is about to hold K tiles
-
-    f32x16_t o[8];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) o[dt][rr] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
-
-    TileRaw<B> raw;
-    load_tile<B>(a, head_base, 0, tid, raw);
-    for (int kt = 0; kt < n_kt; ++kt) {
-      store_tile<B>(a, kt, tid, raw, lut, ks, vt, nk, nv, ve);
-      if (kt + 1 < n_kt) load_tile<B>(a, head_base, kt + 1, tid, raw);
-      __syncthreads();
-
-      // ---- scores S^T for this wave's 32 keys x 32 qrows
-      // one accumulator per 128-group: each group has its own norm
-      f32x16_t s, s1;
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) { s[rr] = 0.f; s1[rr] = 0.f; }
-      const _Float16 *krow = ks + (32 * khalf + ql) * kKsStride + 8 * hl;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const half8_t av = *reinterpret_cast<const half8_t *>(krow + 16 * t);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qb[t], s, 0, 0, 0);
-      }
-#pragma unroll
-      for (int t = 8; t < 16; ++t) {
-        const half8_t av = *reinterpret_cast<const half8_t *>(krow + 16 * t);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qb[t], s1, 0, 0, 0);
-      }
-      // register rr <-> key 8(rr/4) + 4hl + rr%4 of this wave's half; keys
-      // past lim = pos - (first key of the half) are masked
-      const int64_t lim64 = pos - ((int64_t)kt * kKT + 32 * khalf);
-      const int lim = lim64 > 64 ? 64 : (int)lim64;
-      // m_run is a reference, not the running maximum: p = exp2(s - m_run)
-      // and P = p * (V norm) goes to float16.  With e the binary exponent of
-      // a key's larger V norm, P < 2^(s + e - m_run); the reference moves
-      // only when some key would reach 2^kPTop, and then to put the tile's
-      // top at 2^kPSet.  So P never overflows, stays clear of float16
-      // subnormals, and the accumulators are rescaled rarely.  Softmax does
-      // not depend on the reference.
-      float tref = -INFINITY;
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int kk = 8 * (rr >> 2) + 4 * hl + (rr & 3);
-        const float2 nn = *reinterpret_cast<const float2 *>(nk + 2 * (32 * khalf + kk));
-        float v = s[rr] * nn.x + s1[rr] * nn.y;
-        if (kk > lim) v = -INFINITY;
-        s[rr] = v;
-        tref = fmaxf(tref, v + ve[32 * khalf + kk]);
-      }
-      tref = fmaxf(tref, xor_lane<32>(tref));
-      const float m_new = tref > m_run + kPTop ? tref - kPSet : m_run;
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
-      half8_t pb[2], pb1[2];   // P of group 0 / group 1
-      float psum = 0.f;
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int kk = 8 * (rr >> 2) + 4 * hl + (rr & 3);
-        const float p = __builtin_amdgcn_exp2f(s[rr] - m_use);
-        psum += p;
-        const float2 nn = *reinterpret_cast<const float2 *>(nv + 2 * (32 * khalf + kk));
-        pb[rr >> 3][rr & 7] = (_Float16)(p * nn.x);
-        pb1[rr >> 3][rr & 7] = (_Float16)(p * nn.y);
-      }
-      l_run = l_run * alpha + psum;
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) o[dt][rr] *= alpha;
-      }
-
-      // ---- O^T += V^T P^T; k-slot (hl, i) of group ga <-> key 16ga + 8(i>>2) + 4hl + (i&3)
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const _Float16 *vrow = vt + (32 * dt + ql) * kVtStride + 32 * khalf + 4 * hl;
-#pragma unroll
-        for (int ga = 0; ga < 2; ++ga) {
-          const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vrow + 16 * ga);
-          const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vrow + 16 * ga + 8);
-          const u32x4_t av = {lo.x, lo.y, hi.x, hi.y};
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, av),
-                                                        dt < 4 ? pb[ga] : pb1[ga], o[dt], 0, 0, 0);
-        }
-      }
-      __syncthreads();  // the next store_tile overwrites ks / vt
-    }
-
-    // ---- merge the two key halves (waves khalf=1 hand their state to khalf=0)
-    l_run += xor_lane<32>(l_run);
-    float *mbuf = reinterpret_cast<float *>(arena);  // 2 waves x 128 regs x 64 lanes = 64 KB
-    if (khalf == 1) {
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) mbuf[((qhalf * 8 + dt) * 16 + rr) * 64 + lane] = o[dt][rr];
-      if (hl == 0) {
-        mstat[qhalf][ql] = m_run;
-        lstat[qhalf][ql] = l_run;
-      }
-    }
-    __syncthreads();
-    if (khalf == 0) {
-      const float m2 = mstat[qhalf][ql], l2 = lstat[qhalf][ql];
-      const float M = fmaxf(m_run, m2);
-      const float f1 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
-      const float f2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
-      const float L = l_run * f1 + l2 * f2;
-      const float rinv = 1.0f / (128.0f * L);
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr)
-          o[dt][rr] = (o[dt][rr] * f1 + mbuf[((qhalf * 8 + dt) * 16 + rr) * 64 + lane] * f2) * rinv;
-      // inverse transform per 128-group: d = 32dt + 8(rr/4) + 4hl + rr%4.
-      // Stages over d bits 0,1 (rr%4), 2 (hl: lanes 32 apart), 3,4 (rr/4),
-      // 5,6 (dt&3); d bit 7 (dt>>2) selects the group.
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-#pragma unroll
-        for (int hbit = 1; hbit <= 8; hbit <<= 1) {
-          if (hbit == 4) continue;
-          // in-register stage over register index bit: hbit 1,2 -> rr bits 0,1; 8 -> rr bit 2 (d bit 3)
-          const int rb = hbit == 8 ? 4 : hbit;
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr)
-            if (!(rr & rb)) {
-              const float x = o[dt][rr], y = o[dt][rr + rb];
-              o[dt][rr] = x + y;
-              o[dt][rr + rb] = x - y;
+            for (int k = 0; k < 4; ++k) {
+              x[8 * v + 2 * k] = __uint_as_float(b[k] << 16);
+              x[8 * v + 2 * k + 1] = __uint_as_float(b[k] & 0xffff0000u);
             }
-        }
-        // d bit 4 <-> rr bit 3
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr)
-          if (!(rr & 8)) {
-            const float x = o[dt][rr], y = o[dt][rr + 8];
-            o[dt][rr] = x + y;
-            o[dt][rr + 8] = x - y;
           }
-        // d bit 2 <-> lane bit 5 (partner 32 lanes away): upper half takes partner - self
+        } else {
+          const float4 *src = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.q) + off);
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const float p = xor_lane<32>(o[dt][rr]);
-          o[dt][rr] = hl ? (p - o[dt][rr]) : (o[dt][rr] + p);
+          for (int v = 0; v < 16; ++v) {
+            const float4 f = src[v];
+            x[4 * v] = f.x; x[4 * v + 1] = f.y; x[4 * v + 2] = f.z; x[4 * v + 3] = f.w;
+          }
+        }
+        uint32_t sw[2] = {(uint32_t)(h ? kSignWord1 : kSignWord0), (uint32_t)((h ? kSignWord1 : kSignWord0) >> 32)};
+        // opaque, so the 64 sign masks are formed here and not hoisted out
+        // of the pass loop (where they would be spilled)
+        asm volatile("" : "+v"(sw[0]), "+v"(sw[1]));
+#pragma unroll
+        for (int e = 0; e < 64; ++e) x[e] = flip_sign(x[e], (sw[e >> 5] >> (e & 31)) & 1u);
+        wht_in_regs<64>(x);
+#pragma unroll
+        for (int e = 0; e < 64; ++e) x[e] = bfly_lane<1>(x[e], h != 0);
+        u32x4_t *dst = reinterpret_cast<u32x4_t *>(qbuf + c * kKsStride + 128 * grp + 64 * h);
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          uint32_t w[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const _Float16 lo = (_Float16)(x[8 * v + 2 * k] * a.qscale);
+            const _Float16 hi = (_Float16)(x[8 * v + 2 * k + 1] * a.qscale);
+            w[k] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+          }
+          dst[v] = u32x4_t{w[0], w[1], w[2], w[3]};
         }
       }
-      // d bits 5, 6 <-> dt bits 0, 1 within each group (dt>>2)
+      const int qrow = 32 * qhalf + ql;
+      const int64_t r = row0 + qrow % a.bq;
+      const int64_t pos = lmin(a.q_pos0 + r, a.kv_len - 1);   // last key this column sees
+      const _Float16 *qrow_p = qbuf + qrow * kKsStride + 8 * hl;
+      const int koff = (32 * khalf + ql) * kKsStride + 8 * hl;
+      __syncthreads();   // query rows, K tiles 0 (in the V^T buffer) and 1 ready
+      f32x16_t sa = scores(vbuf + koff, qrow_p), sb;
+      __syncthreads();   // K tile 0 read: the V^T buffer may take V tile 0
+
+      f32x16_t o[8];
 #pragma unroll
-      for (int gq = 0; gq < 2; ++gq)
+      for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-        for (int b = 1; b <= 2; b <<= 1)
+        for (int rr = 0; rr < 16; ++rr) o[dt][rr] = 0.f;
+      float m_run = -INFINITY, l_run = 0.f;
+
+      auto step = [&](int kt, const f32x16_t &cur, f32x16_t &nxt) {
+        half8_t pb[2];
+        float alpha = 1.f;
+        // phase A: scores of tile kt+1 (past the end: unused) with the
+        // softmax of tile kt
+        auto phase_a = [&](auto mask_tag) {
+          constexpr bool kMask = decltype(mask_tag)::value;
+          // distinct markers keep the two variants from sharing (and hoisting
+          // above the branch) their operand reads
+          if constexpr (kMask)
+            asm volatile("; masked tile" ::: "memory");
+          else
+            asm volatile("; full tile" ::: "memory");
+          // scores of tile kt+1: operands three products ahead in a 4-slot
+          // ring, two accumulators (even/odd d-steps) so consecutive products
+          // do not wait on each other; the softmax of tile kt runs in 16
+          // slices between the products
+          const _Float16 *kb = kbuf + koff;
+          half8_t ka[4], qa[4];
 #pragma unroll
-          for (int dl = 0; dl < 4; ++dl)
-            if (!(dl & b)) {
+          for (int i = 0; i < 3; ++i) {
+            ka[i] = *reinterpret_cast<const half8_t *>(kb + 16 * i);
+            qa[i] = *reinterpret_cast<const half8_t *>(qrow_p + 16 * i);
+          }
+          f32x16_t s0, s1;
 #pragma unroll
-              for (int rr = 0; rr < 16; ++rr) {
-                const float x = o[4 * gq + dl][rr], y = o[4 * gq + dl + b][rr];
-                o[4 * gq + dl][rr] = x + y;
-                o[4 * gq + dl + b][rr] = x - y;
-              }
+          for (int rr = 0; rr < 16; ++rr) { s0[rr] = 0.f; s1[rr] = 0.f; }
+          // register rr <-> key 8(rr/4) + 4hl + rr%4 of this wave's half
+          const int64_t lim64 = pos - ((int64_t)kt * kKT + 32 * khalf);
+          const int lim = lim64 > 64 ? 64 : (int)lim64;
+          float v[16], tmax = -INFINITY, m_use = 0.f, psum = 0.f;
+#pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            if (t + 3 < 16) {
+              ka[(t + 3) & 3] = *reinterpret_cast<const half8_t *>(kb + 16 * (t + 3));
+              qa[(t + 3) & 3] = *reinterpret_cast<const half8_t *>(qrow_p + 16 * (t + 3));
             }
-      if (r < a.n_rows) {
-        float *orow = a.out + (r * a.n_q + head) * kD;
+            if (t & 1)
+              s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[t & 3], qa[t & 3], s1, 0, 0, 0);
+            else
+              s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[t & 3], qa[t & 3], s0, 0, 0, 0);
+            if (t < 8) {
+#pragma unroll
+              for (int e = 2 * t; e < 2 * t + 2; ++e) {
+                v[e] = cur[e];
+                if (kMask && 8 * (e >> 2) + 4 * hl + (e & 3) > lim) v[e] = -INFINITY;
+              }
+              tmax = fmaxf(tmax, fmaxf(v[2 * t], v[2 * t + 1]));
+            }
+            if (t == 7) {
+              tmax = max_xor32(tmax);
+              // lazy reference: it moves only when a score passes it by
+              // 2^kLazy, so P <= 2^kLazy and rescales are rare
+              const float m_new = tmax > m_run + kLazy ? tmax : m_run;
+              m_use = m_new == -INFINITY ? 0.f : m_new;
+              alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+              m_run = m_new;
+            }
+            if (t >= 8) {
+              const int e = 2 * (t - 8);
+              const float p0 = __builtin_amdgcn_exp2f(v[e] - m_use);
+              const float p1 = __builtin_amdgcn_exp2f(v[e + 1] - m_use);
+              psum += p0 + p1;
+              pb[e >> 3][e & 7] = (_Float16)p0;
+              pb[e >> 3][(e & 7) + 1] = (_Float16)p1;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          l_run = l_run * alpha + psum;
+          nxt = s0 + s1;
+        };
+        if ((int64_t)kt * kKT + kKT - 1 > pos_min)
+          phase_a(std::true_type{});
+        else
+          phase_a(std::false_type{});
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) o[dt][rr] *= alpha;
+        }
+        __syncthreads();   // V tile kt written; K tile kt+1 read
+        // phase B: O^T += V^T P^T; k-slot (hl, i) of step ga <-> key
+        // 16ga + 8(i>>2) + 4hl + (i&3).  Products in the order (ga, dt), so
+        // no two consecutive ones share an accumulator; V^T operands three
+        // products ahead.
+        const _Float16 *vt = vbuf + ql * kVtStride + 32 * khalf + 4 * hl;
+        auto vop = [&](int idx) {
+          const _Float16 *vr = vt + 32 * (idx & 7) * kVtStride + 16 * (idx >> 3);
+          const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vr);
+          const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vr + 8);
+          return __builtin_bit_cast(half8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+        };
+        half8_t va[4];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) va[i] = vop(i);
+#pragma unroll
+        for (int idx = 0; idx < 16; ++idx) {
+          if (idx + 3 < 16) va[(idx + 3) & 3] = vop(idx + 3);
+          o[idx & 7] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[idx & 3], pb[idx >> 3], o[idx & 7], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();   // V tile kt consumed; K tile kt+2 written
+      };
+      for (int kt = 0; kt < n_kt; kt += 2) {
+        step(kt, sa, sb);
+        if (kt + 1 < n_kt) step(kt + 1, sb, sa);
+      }
+
+      // ---- merge the key halves: khalf 1 hands its partial output to
+      //      khalf 0, which writes the normalized sum back in place
+      l_run += xor_lane<32>(l_run);
+      float *ew = ebuf + qhalf * kEWave + lane * 4;
+      if (hl == 0) {
+        mst[khalf][qrow] = m_run;
+        lst[khalf][qrow] = l_run;
+      }
+      if (khalf == 1) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq)
+            *reinterpret_cast<float4 *>(ew + dt * kEDt + rq * 256) =
+                float4{o[dt][4 * rq], o[dt][4 * rq + 1], o[dt][4 * rq + 2], o[dt][4 * rq + 3]};
+      }
+      __syncthreads();   // partial outputs and statistics in shared memory
+      if (khalf == 0) {
+        const float m2 = mst[1][qrow], l2 = lst[1][qrow];
+        const float M = fmaxf(m_run, m2);
+        const float f1 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+        const float f2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
+        const float rinv = 1.0f / (8.0f * (l_run * f1 + l2 * f2));
+        const float g1 = f1 * rinv, g2 = f2 * rinv;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
           for (int rq = 0; rq < 4; ++rq) {
-            const int d0 = 32 * dt + 8 * rq + 4 * hl;
-            float4 v;
-            v.x = flip_sign(o[dt][4 * rq + 0], sign_bit_of((d0 + 0) & 127));
-            v.y = flip_sign(o[dt][4 * rq + 1], sign_bit_of((d0 + 1) & 127));
-            v.z = flip_sign(o[dt][4 * rq + 2], sign_bit_of((d0 + 2) & 127));
-            v.w = flip_sign(o[dt][4 * rq + 3], sign_bit_of((d0 + 3) & 127));
-            *reinterpret_cast<float4 *>(orow + d0) = v;
+            float4 *ptr = reinterpret_cast<float4 *>(ew + dt * kEDt + rq * 256);
+            const float4 u = *ptr;
+            *ptr = float4{o[dt][4 * rq] * g1 + u.x * g2, o[dt][4 * rq + 1] * g1 + u.y * g2,
+                          o[dt][4 * rq + 2] * g1 + u.z * g2, o[dt][4 * rq + 3] * g1 + u.w * g2};
           }
       }
+    } else {
+      // ================================================= decode waves
+      const int dt = tid - kHalf;
+      int last = (int)(a.kv_len - 1);
+      asm volatile("" : "+s"(last));   // keeps tile addresses in the pass (not hoisted, spilled)
+      HeadPtrs hp;
+      hp.kc = a.kcodes + head_base * (32 * B);
+      hp.vc = a.vcodes + head_base * (32 * B);
+      hp.kn = a.knorms + head_base * 2;
+      hp.vn = a.vnorms + head_base * 2;
+      KRaw<B> kr0, kr1;
+      VRaw<B> vr;
+      uint32_t vw[8][4];
+      load_k<B>(hp, last, 0, dt, kr0);
+      load_k<B>(hp, last, 1, dt, kr1);
+      load_v<B>(hp, last, 0, dt, vr);
+      store_k<B>(kr0, dt, tab, vbuf);   // K tile 0 goes where V tile 0 will
+      store_k<B>(kr1, dt, tab, kbuf);
+      lookup_v<B>(vr, dt, tab, vw);
+      // loads are unconditional (tile index clamped): a conditional load
+      // would merge into the loop-carried registers through copies that wait
+      // for the data
+      load_k<B>(hp, last, min(2, n_kt - 1), dt, kr0);
+      load_v<B>(hp, last, min(1, n_kt - 1), dt, vr);
+      __syncthreads();   // query rows, K tiles 0 (in the V^T buffer) and 1 ready
+      __syncthreads();   // K tile 0 read: the V^T buffer may take V tile 0
+      for (int kt = 0; kt < n_kt; ++kt) {
+        // phase A: V tile kt into the buffer, look up V tile kt+1
+        write_v(vw, dt, vbuf);
+        lookup_v<B>(vr, dt, tab, vw);   // past the end: never written
+        load_v<B>(hp, last, min(kt + 2, n_kt - 1), dt, vr);
+        __syncthreads();   // V tile kt written; K tile kt+1 read
+        // phase B: K tile kt+2 into the (now free) K buffer
+        if (kt + 2 < n_kt) store_k<B>(kr0, dt, tab, kbuf);
+        load_k<B>(hp, last, min(kt + 3, n_kt - 1), dt, kr0);
+        __syncthreads();   // V tile kt consumed; K tile kt+2 written
+      }
+      __syncthreads();   // partial outputs and statistics in shared memory
     }
+    __syncthreads();   // merged output in shared memory
+
+    // ---- merge, normalize, inverse transform: thread (j, c, group) owns
+    //      elements 32j .. 32j+31 of one group of qrow c
+    {
+      const int j = tid & 3, c = (tid >> 2) & 63, grp = tid >> 8;
+      const int qh = c >> 5, ql = c & 31;
+      const float *e0 = ebuf + qh * kEWave + (4 * grp + j) * kEDt;
+      float x[32];
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          // element e = 8rq + 4hh + i <-> register 4rq + i of lane ql + 32hh
+          const float4 u = *reinterpret_cast<const float4 *>(e0 + rq * 256 + (ql + 32 * hh) * 4);
+          x[8 * rq + 4 * hh + 0] = u.x;
+          x[8 * rq + 4 * hh + 1] = u.y;
+          x[8 * rq + 4 * hh + 2] = u.z;
+          x[8 * rq + 4 * hh + 3] = u.w;
+        }
+      wht_in_regs<32>(x);
+#pragma unroll
+      for (int e = 0; e < 32; ++e) x[e] = bfly_lane<1>(x[e], (j & 1) != 0);
+#pragma unroll
+      for (int e = 0; e < 32; ++e) x[e] = bfly_lane<2>(x[e], (j & 2) != 0);
+      const int hq = c / a.bq;
+      const int64_t r = row0 + c % a.bq;
+      if (r < a.n_rows) {
+        uint32_t sw = (uint32_t)((j < 2 ? kSignWord0 : kSignWord1) >> (32 * (j & 1)));
+        asm volatile("" : "+v"(sw));   // formed here, not hoisted and spilled
+        float *orow = a.out + (r * a.n_q + g * a.n_rep + hq) * kD + 128 * grp + 32 * j;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          float4 f;
+          f.x = flip_sign(x[4 * v + 0], (sw >> (4 * v + 0)) & 1u);
+          f.y = flip_sign(x[4 * v + 1], (sw >> (4 * v + 1)) & 1u);
+          f.z = flip_sign(x[4 * v + 2], (sw >> (4 * v + 2)) & 1u);
+          f.w = flip_sign(x[4 * v + 3], (sw >> (4 * v + 3)) & 1u);
+          reinterpret_cast<float4 *>(orow)[v] = f;
+        }
+      }
+    }
+    __syncthreads();   // merge buffer read: the tiles may be overwritten
   }
 }
 
@@ -510,6 +579,8 @@ hipError_t plan_prefill(const tq_cache &k, int64_t n_rows, int32_t n_q_heads, in
   (void)kv_len;
   const int n_rep = n_q_heads / k.n_kv_heads;
   if (n_rep < 1 || pf::kQRows % n_rep != 0) return hipErrorNotSupported;
+  // key offsets inside one head are 32-bit
+  if (k.n_cells > (int64_t)(0xffffffffu / (32u * 4))) return hipErrorNotSupported;
   p->rows_per_tile = pf::kQRows / n_rep;
   const int64_t tiles = ceil_div<int64_t>(n_rows, p->rows_per_tile);
   if (tiles > 0x3fffffff) return hipErrorInvalidValue;
@@ -540,8 +611,8 @@ hipError_t launch_prefill(const tq_cache &k, const tq_cache &v, int64_t kv_len, 
   a.n_rep = n_q_heads / k.n_kv_heads;
   a.bq = p.rows_per_tile;
   a.n_qtiles = p.n_row_tiles;
-  // log2 domain; 1/128 for the 1/sqrt(128) of the rotated query and level
-  a.qscale = scale * 1.4426950408889634f / 128.0f;
+  // log2 domain; 1/8 for the transform and tile scales (score = H(s.q) . K / 8)
+  a.qscale = scale * 1.4426950408889634f / 8.0f;
   dim3 grid((unsigned)ceil_div(p.n_row_tiles, 2), (unsigned)k.n_kv_heads);
   dim3 block(pf::kThreads);
   if (k.type == TQ_TURBO3) {
