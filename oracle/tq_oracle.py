@@ -392,6 +392,60 @@ def attn_prefill(kc: dict, vc: dict, kv_len: int, q: np.ndarray, q_pos0: int,
 
 
 # --------------------------------------------------------------------------
+# O4. Sparse-V decode (float64): value skip and its error bound
+# --------------------------------------------------------------------------
+#
+# [PR36] (d), the VEC flash-attention optimisations, item 3: the sparse-V
+# threshold is raised to 5e-3 for turbo3/turbo4 and 1e-2 for turbo2.
+# Reading (the page does not define the weight it compares): the weight of key
+# j is p_j = e^(S_j - m) with m a running reference no larger than the true
+# maximum m*; a key whose p_j < tau is left out of the value sum only, and the
+# normalizer keeps every key.  A kernel's reference depends on its key order,
+# so the GPU result is checked against the bound below rather than one exact
+# skipped set.
+
+def decode_scores(kc: dict, kv_len: int, q: np.ndarray, scale: float) -> np.ndarray:
+    """Natural-log scores S[h, j] = scale <q_h, k_{g(h), j}> over the dequantized cache."""
+    k = dequant_cache(kc, kv_len)
+    q = np.asarray(q, dtype=np.float64)
+    g_of = kv_head_of(q.shape[0], k.shape[0])
+    return scale * np.einsum("hd,hjd->hj", q, k[g_of])
+
+
+def attn_decode_sparse_v(kc: dict, vc: dict, kv_len: int, q: np.ndarray, scale: float,
+                         tau: float) -> np.ndarray:
+    """Decode with the value skip taken against the true maximum m* (the
+    largest reference any kernel can use, so the largest skipped set):
+    out_h = sum_{j: p_j >= tau} p_j v_j / sum_j p_j, p_j = e^(S_hj - m*_h)."""
+    s = decode_scores(kc, kv_len, q, scale)
+    v = dequant_cache(vc, kv_len)
+    g_of = kv_head_of(s.shape[0], v.shape[0])
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    keep = np.where(p >= tau, p, 0.0)
+    return np.einsum("hj,hjd->hd", keep, v[g_of]) / p.sum(axis=1)[:, None]
+
+
+def sparse_v_bound(kc: dict, vc: dict, kv_len: int, q: np.ndarray, scale: float, tau: float):
+    """The error bound of any value skip whose reference is <= m*.
+
+    T_h = {j : e^(S_hj - m*_h) < tau} holds every key such a kernel can skip
+    (its weight against a smaller reference is even larger, so it is skipped
+    only if its weight against m* is below tau).  Leaving a set S of keys out
+    of the value sum changes the output by - sum_{j in S} (p_j / L) v_j, whose
+    largest element is at most its 2-norm, at most
+    B_h = sum_{j in T_h} (p_j / L_h) ||v_j||_2.
+    Returns (B [n_q], |T_h| [n_q])."""
+    s = decode_scores(kc, kv_len, q, scale)
+    v = dequant_cache(vc, kv_len)
+    g_of = kv_head_of(s.shape[0], v.shape[0])
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    w = p / p.sum(axis=1, keepdims=True)
+    small = p < tau
+    vnorm = np.linalg.norm(v, axis=2)[g_of]          # [n_q, kv_len]
+    return (w * vnorm * small).sum(axis=1), small.sum(axis=1)
+
+
+# --------------------------------------------------------------------------
 # O5. int8 paged prompt attention (float64)
 # --------------------------------------------------------------------------
 

@@ -394,20 +394,35 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
   const float *part = ws + (int64_t)h * n_split * kPartStride;
   float mg = -INFINITY, L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-  for (int s = grp; s < n_split; s += kMergeGroups) {
-    const float *p = part + (int64_t)s * kPartStride;
-    const float2 ml = *reinterpret_cast<const float2 *>(p + kD);
-    const float4 v = reinterpret_cast<const float4 *>(p)[j];
-    const float mn = fmaxf(mg, ml.x);
-    const float a = __builtin_amdgcn_exp2f(mg - mn);
-    const float w = __builtin_amdgcn_exp2f(ml.x - mn);
-    L = L * a + w * ml.y;
-    acc.x = acc.x * a + w * v.x;
-    acc.y = acc.y * a + w * v.y;
-    acc.z = acc.z * a + w * v.z;
-    acc.w = acc.w * a + w * v.w;
-    mg = mn;
+  // batches of 8 splits per group, every load of a batch issued before the
+  // first use: the partials come from other compute units' writes, so each
+  // dependent round costs a full memory latency
+  constexpr int kBatch = 8;
+  for (int s0 = grp; s0 < n_split; s0 += kBatch * kMergeGroups) {
+    float2 ml[kBatch];
+    float4 v[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int s = s0 + i * kMergeGroups;
+      if (s < n_split) {
+        const float *p = part + (int64_t)s * kPartStride;
+        ml[i] = *reinterpret_cast<const float2 *>(p + kD);
+        v[i] = reinterpret_cast<const float4 *>(p)[j];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (s0 + i * kMergeGroups >= n_split) break;
+      const float mn = fmaxf(mg, ml[i].x);
+      const float a = __builtin_amdgcn_exp2f(mg - mn);
+      const float w = __builtin_amdgcn_exp2f(ml[i].x - mn);
+      L = L * a + w * ml[i].y;
+      acc.x = acc.x * a + w * v[i].x;
+      acc.y = acc.y * a + w * v[i].y;
+      acc.z = acc.z * a + w * v[i].z;
+      acc.w = acc.w * a + w * v[i].w;
+      mg = mn;
+    }
   }
   obuf[grp][j] = acc;
   if (j == 0) {

@@ -393,3 +393,73 @@ def test_int8_brute_force_and_page_invariance():
             w = [np.exp(s - m) for s in sc]
             ref = [sum(w[j] * vl[j, 0, t] for j in range(len(w))) / sum(w) for t in range(8)]
             np.testing.assert_allclose(got[i, h], ref, atol=1e-12)
+
+
+# ---------------------------------------------------------------- sparse V
+
+def _sparse_fixture(seed=11, n=40, n_q=4, n_kv=2, sharp=3.0):
+    rng = np.random.default_rng(seed)
+    kc = o.new_cache(3, 128, n_kv, n); vc = o.new_cache(3, 128, n_kv, n)
+    o.set_rows(kc, rng.standard_normal((n, n_kv, 128)).astype(F32), np.arange(n))
+    o.set_rows(vc, rng.standard_normal((n, n_kv, 128)).astype(F32), np.arange(n))
+    q = sharp * rng.standard_normal((n_q, 128))
+    return kc, vc, q
+
+
+def test_sparse_v_brute_force():
+    """attn_decode_sparse_v and sparse_v_bound against per-key Python loops."""
+    kc, vc, q = _sparse_fixture()
+    kv, scale, tau = 33, 0.09, 0.05
+    k = o.dequant_cache(kc, kv); v = o.dequant_cache(vc, kv)
+    got = o.attn_decode_sparse_v(kc, vc, kv, q, scale, tau)
+    bnd, n_t = o.sparse_v_bound(kc, vc, kv, q, scale, tau)
+    for h in range(4):
+        g = h // 2
+        s = [scale * float(np.dot(q[h], k[g, j])) for j in range(kv)]
+        m = max(s)
+        p = [np.exp(x - m) for x in s]
+        L = sum(p)
+        want = sum((p[j] if p[j] >= tau else 0.0) * v[g, j] for j in range(kv)) / L
+        np.testing.assert_allclose(got[h], want, atol=1e-12)
+        b = sum(p[j] / L * np.sqrt(np.sum(v[g, j] ** 2)) for j in range(kv) if p[j] < tau)
+        assert abs(bnd[h] - b) < 1e-12 and n_t[h] == sum(1 for x in p if x < tau)
+    assert n_t.sum() > 0   # the fixture does skip keys
+
+
+def test_sparse_v_limits():
+    """tau = 0 is dense decode with B = 0; tau > 1 skips every key (output 0,
+    and B is then an upper bound on the dense output itself); B grows with tau."""
+    kc, vc, q = _sparse_fixture(seed=12)
+    dense = o.attn_decode(kc, vc, 40, q, 0.09)
+    np.testing.assert_allclose(o.attn_decode_sparse_v(kc, vc, 40, q, 0.09, 0.0), dense, atol=1e-12)
+    b0, t0 = o.sparse_v_bound(kc, vc, 40, q, 0.09, 0.0)
+    assert np.all(b0 == 0) and np.all(t0 == 0)
+    assert np.all(o.attn_decode_sparse_v(kc, vc, 40, q, 0.09, 2.0) == 0)
+    b2, t2 = o.sparse_v_bound(kc, vc, 40, q, 0.09, 2.0)
+    assert np.all(t2 == 40) and np.all(b2 >= np.abs(dense).max(axis=1) - 1e-12)
+    prev = np.zeros(4)
+    for tau in [1e-4, 1e-3, 5e-3, 1e-2, 0.1, 0.5]:
+        b, _ = o.sparse_v_bound(kc, vc, 40, q, 0.09, tau)
+        assert np.all(b >= prev - 1e-15)
+        prev = b
+
+
+def test_sparse_v_bound_covers_smaller_references():
+    """Any skip taken against a reference <= m* (here the maximum of each
+    chunk of keys seen so far, or of the chunk alone) stays within B of the
+    dense output."""
+    kc, vc, q = _sparse_fixture(seed=13, n=64, sharp=4.0)
+    kv, scale = 64, 0.09
+    s = o.decode_scores(kc, kv, q, scale)
+    v = o.dequant_cache(vc, kv)[o.kv_head_of(4, 2)]
+    dense = o.attn_decode(kc, vc, kv, q, scale)
+    m_star = s.max(axis=1, keepdims=True)
+    L = np.exp(s - m_star).sum(axis=1)
+    for tau in [5e-3, 1e-2, 0.1]:
+        bnd, _ = o.sparse_v_bound(kc, vc, kv, q, scale, tau)
+        for chunk in [4, 16, 64]:
+            ref = np.concatenate([np.repeat(s[:, c:c + chunk].max(axis=1, keepdims=True),
+                                            min(chunk, kv - c), axis=1) for c in range(0, kv, chunk)], axis=1)
+            keep = np.exp(s - ref) >= tau
+            out = np.einsum("hj,hjd->hd", np.exp(s - m_star) * keep, v) / L[:, None]
+            assert np.all(np.abs(out - dense).max(axis=1) <= bnd + 1e-12)
