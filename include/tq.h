@@ -139,8 +139,13 @@ tq_status tq_set_rows(const tq_cache *dst, const float *src, const int64_t *cell
  * Requires k and v of the same type, head_dim and n_kv_heads,
  * 1 <= kv_len <= n_cells, n_q_heads a multiple of n_kv_heads with at most 8
  * q heads per kv head, and head_dim == 128 in this build.
- * sparse_v_tau must be 0 in this build (skipping value rows with small
- * weights, [PR36] (d) item 3, returns TQ_ERR_UNSUPPORTED).
+ * sparse_v_tau >= 0 ([PR36] (d) item 3; 0 = off): a key whose weight
+ * e^(s - m) is below tau is left out of the value sum and kept in the
+ * normalizer, with m the maximum over the block of 16, 32 or 64 keys that
+ * one wave scores (chosen by the plan; at most the true maximum).  The output then differs from the dense one by at most
+ * sum over {j : e^(s_j - m*) < tau} of (e^(s_j - m*) / sum_i e^(s_i - m*)) |v_j|_2
+ * (m* the true maximum).  The products are not skipped, so the call costs
+ * the same as a dense one.  A NaN or negative tau is TQ_ERR_INVALID_ARG.
  * The workspace holds per-split partial results; its size comes from
  * tq_attn_decode_workspace for the same arguments on the same device.
  */

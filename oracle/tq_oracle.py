@@ -413,16 +413,26 @@ def decode_scores(kc: dict, kv_len: int, q: np.ndarray, scale: float) -> np.ndar
 
 
 def attn_decode_sparse_v(kc: dict, vc: dict, kv_len: int, q: np.ndarray, scale: float,
-                         tau: float) -> np.ndarray:
-    """Decode with the value skip taken against the true maximum m* (the
-    largest reference any kernel can use, so the largest skipped set):
-    out_h = sum_{j: p_j >= tau} p_j v_j / sum_j p_j, p_j = e^(S_hj - m*_h)."""
+                         tau: float, ref_block: int | None = None) -> np.ndarray:
+    """Decode with the value skip:
+    out_h = sum_{j: e^(S_hj - r_hj) >= tau} w_hj v_j / sum_j w_hj, w_hj = e^(S_hj - m*_h),
+    where the reference r_hj is the true maximum m*_h (ref_block None: the
+    largest reference, so the largest skipped set) or the maximum over the
+    aligned block of ref_block keys holding j (a kernel that scores the keys
+    in blocks and takes each block's own maximum)."""
     s = decode_scores(kc, kv_len, q, scale)
     v = dequant_cache(vc, kv_len)
     g_of = kv_head_of(s.shape[0], v.shape[0])
-    p = np.exp(s - s.max(axis=1, keepdims=True))
-    keep = np.where(p >= tau, p, 0.0)
-    return np.einsum("hj,hjd->hd", keep, v[g_of]) / p.sum(axis=1)[:, None]
+    m = s.max(axis=1, keepdims=True)
+    if ref_block is None:
+        ref = np.broadcast_to(m, s.shape)
+    else:
+        ref = np.empty_like(s)
+        for j0 in range(0, kv_len, ref_block):
+            ref[:, j0:j0 + ref_block] = s[:, j0:j0 + ref_block].max(axis=1, keepdims=True)
+    w = np.exp(s - m)
+    keep = np.where(np.exp(s - ref) >= tau, w, 0.0)
+    return np.einsum("hj,hjd->hd", keep, v[g_of]) / w.sum(axis=1)[:, None]
 
 
 def sparse_v_bound(kc: dict, vc: dict, kv_len: int, q: np.ndarray, scale: float, tau: float):

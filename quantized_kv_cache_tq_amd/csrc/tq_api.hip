@@ -129,12 +129,11 @@ tq_status tq_attn_decode(const tq_cache *k, const tq_cache *v, int64_t kv_len, c
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
   if (!(scale == scale) || !(sparse_v_tau == sparse_v_tau) || sparse_v_tau < 0.f)
     return TQ_ERR_INVALID_ARG;
-  if (sparse_v_tau != 0.f) return TQ_ERR_UNSUPPORTED;
   DecodePlan p;
   if (tq_status st = from_hip(plan_decode(*k, kv_len, n_q_heads, &p))) return st;
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.workspace_bytes)
     return TQ_ERR_WORKSPACE;
-  return from_hip(launch_decode(*k, *v, kv_len, q, q_dtype, n_q_heads, scale, out, workspace, p,
+  return from_hip(launch_decode(*k, *v, kv_len, q, q_dtype, n_q_heads, scale, sparse_v_tau, out, workspace, p,
                                 (hipStream_t)stream));
 }
 

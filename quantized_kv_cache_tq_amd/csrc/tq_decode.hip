@@ -91,7 +91,7 @@ template <int B, int T, bool QBF16>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     const uint8_t *__restrict__ kcodes, const uint16_t *__restrict__ knorms,
     const uint8_t *__restrict__ vcodes, const uint16_t *__restrict__ vnorms, int64_t n_cells,
-    int64_t kv_len, const void *__restrict__ q, int n_rep, float qscale,
+    int64_t kv_len, const void *__restrict__ q, int n_rep, float qscale, float tau,
     float *__restrict__ ws, int n_split) {
   constexpr int KPW = 16 * T;                  // keys per range
   constexpr int KPS = 4 * KPW;                 // keys per split
@@ -242,7 +242,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     //      A-operand layout of the value product.  Rows < 8 carry the
     //      float16 high part of p * vnorm, rows >= 8 the low part:
     //      x - hi * lo_sel (lo_sel = 1 on low rows, 0 on high rows) is exact
-    //      in float32 and rounds once to float16.
+    //      in float32 and rounds once to float16.  Sparse V ([PR36] (d) item
+    //      3): a key whose weight against the range maximum (<= the true
+    //      maximum) is below tau leaves the value sum but stays in lsum.
     const float lo_sel = col >= 8 ? 1.f : 0.f;
     float lsum = 0.f;
 #pragma unroll
@@ -254,7 +256,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
       for (int i = 0; i < 4; ++i) {
         const float p = __builtin_amdgcn_exp2f(sc[t][i] - msafe);
         lsum += p;
-        const float x = p * nvv[i];
+        const float x = p < tau ? 0.f : p * nvv[i];
         const _Float16 h = (_Float16)x;
         pa[i] = (_Float16)__builtin_fmaf(-(float)h, lo_sel, x);
       }
@@ -498,11 +500,11 @@ hipError_t plan_decode(const tq_cache &k, int64_t kv_len, int32_t n_q_heads, Dec
 template <int B, bool QBF>
 static void launch_split(int tpw, dim3 grid, hipStream_t st, const tq_cache &k,
                          const tq_cache &v, int64_t kv_len, const void *q, int n_rep, float qs,
-                         float *ws, int n_split) {
+                         float tau, float *ws, int n_split) {
   dim3 block(kDecThreads);
 #define TQ_DEC(T)                                                                             \
   hipLaunchKernelGGL((decode_split_kernel<B, T, QBF>), grid, block, 0, st, k.codes, k.norms, \
-                     v.codes, v.norms, k.n_cells, kv_len, q, n_rep, qs, ws, n_split)
+                     v.codes, v.norms, k.n_cells, kv_len, q, n_rep, qs, tau, ws, n_split)
   switch (tpw) {
     case 1: TQ_DEC(1); break;
     case 2: TQ_DEC(2); break;
@@ -515,14 +517,14 @@ static void launch_split(int tpw, dim3 grid, hipStream_t st, const tq_cache &k,
 template <int B>
 static void launch_split_q(int qbf, int tpw, dim3 grid, hipStream_t st, const tq_cache &k,
                            const tq_cache &v, int64_t kv_len, const void *q, int n_rep, float qs,
-                           float *ws, int n_split) {
-  if (qbf) launch_split<B, true>(tpw, grid, st, k, v, kv_len, q, n_rep, qs, ws, n_split);
-  else launch_split<B, false>(tpw, grid, st, k, v, kv_len, q, n_rep, qs, ws, n_split);
+                           float tau, float *ws, int n_split) {
+  if (qbf) launch_split<B, true>(tpw, grid, st, k, v, kv_len, q, n_rep, qs, tau, ws, n_split);
+  else launch_split<B, false>(tpw, grid, st, k, v, kv_len, q, n_rep, qs, tau, ws, n_split);
 }
 
 hipError_t launch_decode(const tq_cache &k, const tq_cache &v, int64_t kv_len, const void *q,
-                         int q_dtype, int32_t n_q_heads, float scale, float *out, void *workspace,
-                         const DecodePlan &p, hipStream_t stream) {
+                         int q_dtype, int32_t n_q_heads, float scale, float sparse_v_tau,
+                         float *out, void *workspace, const DecodePlan &p, hipStream_t stream) {
   const int n_rep = n_q_heads / k.n_kv_heads;
   // scores in the log2 domain: scale * log2(e), and 1/128 for the two
   // 1/sqrt(128) factors of the rotated query and the rotated levels
@@ -531,9 +533,9 @@ hipError_t launch_decode(const tq_cache &k, const tq_cache &v, int64_t kv_len, c
   dim3 grid(p.n_split, k.n_kv_heads);
   const int qbf = q_dtype == TQ_BF16 ? 1 : 0;
   switch (k.type) {
-    case TQ_TURBO2: launch_split_q<2>(qbf, p.tiles_per_wave, grid, stream, k, v, kv_len, q, n_rep, qs, ws, p.n_split); break;
-    case TQ_TURBO3: launch_split_q<3>(qbf, p.tiles_per_wave, grid, stream, k, v, kv_len, q, n_rep, qs, ws, p.n_split); break;
-    default: launch_split_q<4>(qbf, p.tiles_per_wave, grid, stream, k, v, kv_len, q, n_rep, qs, ws, p.n_split); break;
+    case TQ_TURBO2: launch_split_q<2>(qbf, p.tiles_per_wave, grid, stream, k, v, kv_len, q, n_rep, qs, sparse_v_tau, ws, p.n_split); break;
+    case TQ_TURBO3: launch_split_q<3>(qbf, p.tiles_per_wave, grid, stream, k, v, kv_len, q, n_rep, qs, sparse_v_tau, ws, p.n_split); break;
+    default: launch_split_q<4>(qbf, p.tiles_per_wave, grid, stream, k, v, kv_len, q, n_rep, qs, sparse_v_tau, ws, p.n_split); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -127,3 +127,51 @@ def test_shared_workspace_across_lengths():
         np.testing.assert_array_equal(outs[1].cpu().numpy(), fresh[1000], err_msg=f"replay {rep}")
         eager = b.tq_attn_decode(kc, vc, 17, qt, scale, workspace=ws).cpu().numpy()
         np.testing.assert_array_equal(eager, fresh[17])
+
+
+@pytest.mark.parametrize("bits,tau", [(2, 1e-2), (3, 5e-3), (4, 5e-3), (3, 0.05)])
+def test_sparse_v_within_bound(bits, tau):
+    """Sparse V ([PR36] (d) item 3): |out - dense| <= B + 2e-3 per head, with B
+    the oracle's bound over every key the kernel may skip."""
+    import torch
+    from quantized_kv_cache_tq_amd import binding as b
+    from gpu_util import bf16_cuda
+    kv = 8192
+    q, k, v = inputs.outlier_decode(seed=5, kv_len=kv)
+    kc, vc, ok, ov = _caches(bits, k, v)
+    scale = 1.0 / math.sqrt(q.shape[1])
+    print(f"[decode] sparse-V bits={bits} tau={tau} kv={kv}", flush=True)
+    got = b.tq_attn_decode(kc, vc, kv, bf16_cuda(q), scale, sparse_v_tau=tau).cpu().numpy()
+    dense = o.attn_decode(ok, ov, kv, q.astype(np.float64), scale)
+    bound, n_t = o.sparse_v_bound(ok, ov, kv, q.astype(np.float64), scale, tau)
+    err = np.abs(got - dense).max(axis=1)
+    print(f"    keys with weight < tau: {n_t.mean() / kv:.1%}; max err {err.max():.3g}; "
+          f"bound {bound.max():.3g}")
+    assert n_t.sum() > 0
+    assert np.all(err <= bound + 2e-3), (err - bound).max()
+    # tight check: the kernel's own rule, a skip against the maximum of each
+    # block of keys one wave scores (16 * tiles-per-wave keys, from the plan)
+    import torch
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    tpw = 4
+    while tpw > 1 and -(-kv // (64 * tpw)) * k.shape[1] < 2 * n_cu:
+        tpw //= 2
+    want = o.attn_decode_sparse_v(ok, ov, kv, q.astype(np.float64), scale, tau, ref_block=16 * tpw)
+    from gpu_util import assert_attention_close
+    assert_attention_close(got, want, what=f"sparse-V block rule, block {16 * tpw}")
+
+
+def test_sparse_v_limits_on_gpu():
+    """tau = 0 is the dense call bit for bit; tau = 2 leaves every key out of
+    the value sum (each weight against its range maximum is at most 1)."""
+    from quantized_kv_cache_tq_amd import binding as b
+    from gpu_util import bf16_cuda
+    q, k, v = inputs.outlier_decode(seed=6, kv_len=3000)
+    kc, vc, ok, ov = _caches(3, k, v)
+    qt = bf16_cuda(q)
+    scale = 1.0 / math.sqrt(q.shape[1])
+    dense = b.tq_attn_decode(kc, vc, 3000, qt, scale).cpu().numpy()
+    zero_tau = b.tq_attn_decode(kc, vc, 3000, qt, scale, sparse_v_tau=0.0).cpu().numpy()
+    np.testing.assert_array_equal(zero_tau, dense)
+    allskip = b.tq_attn_decode(kc, vc, 3000, qt, scale, sparse_v_tau=2.0).cpu().numpy()
+    assert np.all(allskip == 0)

@@ -463,3 +463,29 @@ def test_sparse_v_bound_covers_smaller_references():
             keep = np.exp(s - ref) >= tau
             out = np.einsum("hj,hjd->hd", np.exp(s - m_star) * keep, v) / L[:, None]
             assert np.all(np.abs(out - dense).max(axis=1) <= bnd + 1e-12)
+
+
+def test_sparse_v_block_reference():
+    """ref_block = kv_len is the true-maximum rule; ref_block = 1 keeps every
+    key (each key is its own maximum, weight 1 >= tau < 1); a block rule
+    matches a per-block Python loop."""
+    kc, vc, q = _sparse_fixture(seed=14, n=48, sharp=4.0)
+    kv, scale, tau = 45, 0.09, 0.02
+    full = o.attn_decode_sparse_v(kc, vc, kv, q, scale, tau)
+    np.testing.assert_allclose(o.attn_decode_sparse_v(kc, vc, kv, q, scale, tau, ref_block=kv), full, atol=1e-12)
+    np.testing.assert_allclose(o.attn_decode_sparse_v(kc, vc, kv, q, scale, tau, ref_block=1),
+                               o.attn_decode(kc, vc, kv, q, scale), atol=1e-12)
+    k = o.dequant_cache(kc, kv); v = o.dequant_cache(vc, kv)
+    got = o.attn_decode_sparse_v(kc, vc, kv, q, scale, tau, ref_block=16)
+    for h in range(4):
+        g = h // 2
+        s = [scale * float(np.dot(q[h], k[g, j])) for j in range(kv)]
+        m = max(s)
+        num = np.zeros(128); den = 0.0
+        for j in range(kv):
+            blk = s[16 * (j // 16): 16 * (j // 16) + 16]
+            w = np.exp(s[j] - m)
+            den += w
+            if np.exp(s[j] - max(blk)) >= tau:
+                num += w * v[g, j]
+        np.testing.assert_allclose(got[h], num / den, atol=1e-12)
