@@ -191,6 +191,14 @@ def main():
             torch.cuda.synchronize()
             flops = 4.0 * PD * PNQ * (R * (R + 1) / 2)
             prefill = dict(fn=fn, rows=R, flops=flops)
+            # the other two cache types through the same prefill kernel
+            # (timed after the steps, not part of a step)
+            for bits in (2, 4):
+                xk, xv = b.new_cache(bits, PD, PNKV, R), b.new_cache(bits, PD, PNKV, R)
+                b.tq_set_rows(xk, torch.from_numpy(pk).to(dev), pidx)
+                b.tq_set_rows(xv, torch.from_numpy(pv).to(dev), pidx)
+                prefill[f"turbo{bits}"] = (lambda xk=xk, xv=xv: b.tq_attn_prefill(
+                    xk, xv, R, pqt, 0, pscale, out=pout, workspace=pws))
         except b.TQError as e:
             log(f"[bench] prefill leg skipped: {e}")
 
@@ -254,6 +262,31 @@ def main():
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / max(1, args.steps)
     log("[bench] timed region done")
+
+    # ---------------- extras, timed after the steps (not part of a step)
+    def time_eager(fn, reps=10):
+        leg = Leg("extra")
+        for _ in range(2):
+            leg.run(fn, False)
+        for _ in range(reps):
+            leg.run(fn, True)
+        torch.cuda.synchronize()
+        return leg.mean_ms()
+    extras = {}
+    if prefill is not None:
+        for bits in (2, 4):
+            t_ms = time_eager(prefill[f"turbo{bits}"])
+            tf = prefill["flops"] / (t_ms * 1e-3) / 1e12
+            extras[f"prefill_turbo{bits}"] = {"us": round(t_ms * 1e3, 2), "TFLOPs": round(tf, 2),
+                                              "frac_mfma_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+    if graph is not None:
+        # sparse V at the pages' turbo3 threshold against the dense call, one
+        # 32K cache, eager (launch overhead included in both)
+        for tau in (0.0, 5e-3):
+            t_ms = time_eager(lambda tau=tau: b.tq_attn_decode(kcs[0], vcs[0], KV, q_dec, scale_dec, out=outs[0],
+                                                                workspace=ws, sparse_v_tau=tau), reps=50)
+            extras[f"decode_eager_tau_{tau:g}"] = {"us_per_call": round(t_ms * 1e3, 3)}
+    log("[bench] extras done")
 
     res = {}
     ms = {n: legs[n].mean_ms() for n in legs}
@@ -328,6 +361,8 @@ def main():
                                          f"(numpy: unpack, dequantize, float64 attention); "
                                          f"{dt:.2f} s per call"}
         out["parity_check"] = {"decode_max_abs_vs_oracle": float(np.abs(got - ref).max())}
+    if extras:
+        out["extras"] = extras
     out["wall_s_total"] = round(time.time() - t_wall0, 1)
     print(json.dumps(out), flush=True)
 

@@ -80,10 +80,36 @@ __device__ __forceinline__ uint32_t bits_at(const uint32_t *dw, int pos, int nbi
   return __builtin_amdgcn_alignbit(dw[w + 1], dw[w], sh) & ((1u << nbits) - 1u);
 }
 
-// Pair-table entry e of this lane's copy (tab = table + lane), scaled by the
+// Pair table: entry e (two B-bit codes, the first in the low bits) holds
+// their two float16 levels, in C = 32 copies with copy c of entry e at dword
+// 32e + c.  Lane l reads copy l % 32; an LDS 32-bit read serves 32 lanes at
+// a time, so the lanes served together read distinct copies and hit distinct
+// banks whatever their indices (measured as fast as 64 copies).  2 / 8 /
+// 32 KB for 2 / 3 / 4-bit codes.
+template <int B>
+struct PfTable {
+  static constexpr int C = 32;
+  static constexpr int N = 1 << (2 * B);
+  static constexpr int WORDS = N * C;
+};
+
+template <int B, int NT>
+__device__ __forceinline__ void build_pf_table(uint32_t *tab, int tid) {
+  using T = PfTable<B>;
+  constexpr uint32_t CM = (1u << B) - 1u;
+  static_assert(T::WORDS % NT == 0, "pair table fill");
+#pragma unroll
+  for (int j = 0; j < T::WORDS / NT; ++j) {
+    const uint32_t e = (uint32_t)(tid + NT * j) / T::C;
+    tab[tid + NT * j] = level_pair<B>(e & CM, e >> B);
+  }
+}
+
+// Pair-table entry e of this lane's copy (tab = table + copy), scaled by the
 // float16 pair n2 (the group norm / 16 in both halves).
+template <int B>
 __device__ __forceinline__ uint32_t pair_scaled(const uint32_t *tab, uint32_t e, uint32_t n2) {
-  const uint32_t lv = tab[e * 64];
+  const uint32_t lv = tab[e * PfTable<B>::C];
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, lv) * __builtin_bit_cast(half2_t, n2));
 }
 
@@ -164,7 +190,7 @@ __device__ __forceinline__ void store_k(const KRaw<B> &r, int dt, const uint32_t
   const uint32_t n2 = norm_pair(r.n);
   uint32_t h[32];
 #pragma unroll
-  for (int j = 0; j < 32; ++j) h[j] = pair_scaled(tab, bits_at(r.c, 2 * B * j, 2 * B), n2);
+  for (int j = 0; j < 32; ++j) h[j] = pair_scaled<B>(tab, bits_at(r.c, 2 * B * j, 2 * B), n2);
   u32x4_t *dst = reinterpret_cast<u32x4_t *>(ks + (dt & 63) * kKsStride + 64 * (dt >> 6));
 #pragma unroll
   for (int v = 0; v < 8; ++v) dst[v] = u32x4_t{h[4 * v], h[4 * v + 1], h[4 * v + 2], h[4 * v + 3]};
@@ -195,7 +221,7 @@ __device__ __forceinline__ void lookup_v(const VRaw<B> &r, int dt, const uint32_
 #pragma unroll
   for (int u = 0; u < 8; ++u)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) prs[u][i] = pair_scaled(tab, bits_at(run[i], 2 * B * u, 2 * B), n2[i]);
+    for (int i = 0; i < 4; ++i) prs[u][i] = pair_scaled<B>(tab, bits_at(run[i], 2 * B * u, 2 * B), n2[i]);
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     w[u][0] = __builtin_amdgcn_perm(prs[u][1], prs[u][0], 0x05040100u);
@@ -246,7 +272,7 @@ template <int B, bool QBF16>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
   // aligned to its size, so a lookup address is (entry << 8) | (lane << 2)
   // on top of the table base with no carries
-  __shared__ __align__(PairCfg<B>::WORDS * 4) uint32_t ptab[PairCfg<B>::WORDS];
+  __shared__ __align__(PfTable<B>::WORDS * 4) uint32_t ptab[PfTable<B>::WORDS];
   // the K tile, the V^T tile, the rotated query rows; after the key loop the
   // same bytes hold the key-half merge
   __shared__ __align__(16) _Float16 tiles[kTileHalves];
@@ -260,9 +286,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
   _Float16 *vbuf = tiles + kKsHalves;
   _Float16 *qbuf = vbuf + kVtHalves;
   float *ebuf = reinterpret_cast<float *>(tiles);
-  const uint32_t *tab = ptab + lane;   // this lane's pair-table copy
+  const uint32_t *tab = ptab + lane % PfTable<B>::C;   // this lane's pair-table copy
 
-  build_pair_table<B, kThreads>(ptab, tid);
+  build_pf_table<B, kThreads>(ptab, tid);
   __syncthreads();
 
   for (int pass = 0; pass < 2; ++pass) {
@@ -615,14 +641,20 @@ hipError_t launch_prefill(const tq_cache &k, const tq_cache &v, int64_t kv_len, 
   a.qscale = scale * 1.4426950408889634f / 8.0f;
   dim3 grid((unsigned)ceil_div(p.n_row_tiles, 2), (unsigned)k.n_kv_heads);
   dim3 block(pf::kThreads);
-  if (k.type == TQ_TURBO3) {
-    if (q_dtype == TQ_BF16)
-      hipLaunchKernelGGL((pf::prefill_kernel<3, true>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((pf::prefill_kernel<3, false>), grid, block, 0, stream, a);
-  } else {
-    return hipErrorNotSupported;
+#define TQ_PF(B)                                                                  \
+  do {                                                                            \
+    if (q_dtype == TQ_BF16)                                                       \
+      hipLaunchKernelGGL((pf::prefill_kernel<B, true>), grid, block, 0, stream, a); \
+    else                                                                          \
+      hipLaunchKernelGGL((pf::prefill_kernel<B, false>), grid, block, 0, stream, a); \
+  } while (0)
+  switch (k.type) {
+    case TQ_TURBO2: TQ_PF(2); break;
+    case TQ_TURBO3: TQ_PF(3); break;
+    case TQ_TURBO4: TQ_PF(4); break;
+    default: return hipErrorNotSupported;
   }
+#undef TQ_PF
   return hipGetLastError();
 }
 

@@ -137,8 +137,6 @@ def test_prefill_rejects_bad_arguments():
     assert call(nrows=-1) == -1
     assert call(kv=2048) == -1
     assert call(nq=12) == -1
-    t2 = _cache(b, type_=2, head_dim=256, n_kv=8, n_cells=1024)
-    assert call(k=t2, v=t2) == -2                 # turbo2 prefill: no kernel in this build
     d128 = _cache(b, head_dim=128, n_kv=8, n_cells=1024)
     assert call(k=d128, v=d128) == -2
     assert call(nrows=0, q0=0) == 0               # empty: no-op

@@ -1,4 +1,4 @@
-"""GPU parity of tq_attn_prefill (turbo3, head_dim 256) against the float64
+"""GPU parity of tq_attn_prefill (turbo3, and turbo2/turbo4 on a subset; head_dim 256) against the float64
 oracle; bar: max-abs <= 2e-3 and relative L2 <= 1e-3.
 
 The grid mirrors the correctness check of the "HIP/turbo3: graph-safe decode
@@ -19,21 +19,21 @@ from quantized_kv_cache_tq_amd import inputs
 pytestmark = pytest.mark.gpu
 
 
-def _run(q, k, v, kv_len, q_pos0, q_bf16=True, what="", out_scale=1.0):
+def _run(q, k, v, kv_len, q_pos0, q_bf16=True, what="", out_scale=1.0, bits=3):
     import torch
     from quantized_kv_cache_tq_amd import binding as b
     from gpu_util import assert_attention_close, bf16_cuda, cuda
     n_rows, n_q, d = q.shape
     n_cells, n_kv, _ = k.shape
     idx = np.arange(n_cells)
-    kc, vc = b.new_cache(3, d, n_kv, n_cells), b.new_cache(3, d, n_kv, n_cells)
+    kc, vc = b.new_cache(bits, d, n_kv, n_cells), b.new_cache(bits, d, n_kv, n_cells)
     b.tq_set_rows(kc, cuda(k), cuda(idx))
     b.tq_set_rows(vc, cuda(v), cuda(idx))
-    ok, ov = o.new_cache(3, d, n_kv, n_cells), o.new_cache(3, d, n_kv, n_cells)
+    ok, ov = o.new_cache(bits, d, n_kv, n_cells), o.new_cache(bits, d, n_kv, n_cells)
     o.set_rows(ok, k, idx)
     o.set_rows(ov, v, idx)
     scale = 1.0 / math.sqrt(d)
-    print(f"[prefill] {what} rows={n_rows} heads={n_q}/{n_kv} kv={kv_len} q0={q_pos0}", flush=True)
+    print(f"[prefill] {what} bits={bits} rows={n_rows} heads={n_q}/{n_kv} kv={kv_len} q0={q_pos0}", flush=True)
     qt = bf16_cuda(q) if q_bf16 else cuda(q)
     got = b.tq_attn_prefill(kc, vc, kv_len, qt, q_pos0, scale)
     torch.cuda.synchronize()
@@ -116,3 +116,13 @@ def test_large_value_norms():
     exact-maximum path; outputs are compared at unit V scale."""
     q, k, v = inputs.prefill(seed=10, rows=300, kv_len=300)
     _run(q, k, v * np.float32(4000), 300, 0, what="large norms", out_scale=4000.0)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("rows,kv,q0", [(3, 1024, 1021), (64, 512, 448), (512, 512, 0), (65, 200, 100), (1, 1, 0)])
+def test_turbo2_turbo4(bits, rows, kv, q0):
+    """The other two cache types of [PR36] (d) through the same kernel (its
+    pair table holds 2 or 4-bit code pairs)."""
+    q, k, v = inputs.prefill(seed=rows + kv + bits, rows=rows, kv_len=kv)
+    (ma, rl), _ = _run(q, k, v, kv, q0, what="turbo2/4", bits=bits)
+    print(f"    max_abs={ma:.3g} rel_l2={rl:.3g}")
