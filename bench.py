@@ -199,6 +199,15 @@ def main():
                 b.tq_set_rows(xv, torch.from_numpy(pv).to(dev), pidx)
                 prefill[f"turbo{bits}"] = (lambda xk=xk, xv=xv: b.tq_attn_prefill(
                     xk, xv, R, pqt, 0, pscale, out=pout, workspace=pws))
+            # 128-wide heads, twice the q heads: the same products per call
+            hq_, hk_, hv_ = inputs.prefill(seed=1, rows=R, n_q=2 * PNQ, n_kv=PNKV, d=PD // 2)
+            hkc, hvc = b.new_cache(3, PD // 2, PNKV, R), b.new_cache(3, PD // 2, PNKV, R)
+            b.tq_set_rows(hkc, torch.from_numpy(hk_).to(dev), pidx)
+            b.tq_set_rows(hvc, torch.from_numpy(hv_).to(dev), pidx)
+            hqt = torch.from_numpy(hq_).to(torch.bfloat16).to(dev)
+            hout = torch.empty((R, 2 * PNQ, PD // 2), dtype=torch.float32, device=dev)
+            prefill["d128"] = (lambda: b.tq_attn_prefill(hkc, hvc, R, hqt, 0, 1.0 / math.sqrt(PD // 2),
+                                                         out=hout, workspace=pws))
         except b.TQError as e:
             log(f"[bench] prefill leg skipped: {e}")
 
@@ -279,6 +288,10 @@ def main():
             tf = prefill["flops"] / (t_ms * 1e-3) / 1e12
             extras[f"prefill_turbo{bits}"] = {"us": round(t_ms * 1e3, 2), "TFLOPs": round(tf, 2),
                                               "frac_mfma_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+        t_ms = time_eager(prefill["d128"])
+        tf = prefill["flops"] / (t_ms * 1e-3) / 1e12
+        extras["prefill_turbo3_d128_32q8kv"] = {"us": round(t_ms * 1e3, 2), "TFLOPs": round(tf, 2),
+                                                "frac_mfma_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
     if graph is not None:
         # sparse V at the pages' turbo3 threshold against the dense call, one
         # 32K cache, eager (launch overhead included in both)

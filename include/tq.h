@@ -165,10 +165,11 @@ tq_status tq_attn_decode(const tq_cache *k, const tq_cache *v, int64_t kv_len, c
  * (causal, aligned so that the last row sees q_pos0 + n_rows - 1 keys + 1).
  * Same formula and head mapping as decode.  Requires
  * 0 <= q_pos0, q_pos0 + n_rows <= kv_len <= n_cells; n_rows == 0 is a no-op.
- * This build supports turbo2, turbo3 and turbo4 with head_dim 256 and at
- * most 8 q heads per kv head (others: TQ_ERR_UNSUPPORTED; [PR28] "Scope /
- * honesty" validates its fast path for turbo3 only, the other two types use
- * the same kernel with a wider or narrower pair table).
+ * This build supports turbo2, turbo3 and turbo4 with head_dim 128 or 256
+ * and at most 8 q heads per kv head (others: TQ_ERR_UNSUPPORTED; [PR28]
+ * "Scope / honesty" validates its fast path for turbo3 at head_dim 256 only;
+ * the other types use the same kernel with a wider or narrower pair table,
+ * head_dim 128 the same kernel with half the products per tile).
  */
 tq_status tq_attn_prefill_workspace(const tq_cache *k, int64_t n_rows, int32_t n_q_heads,
                                     int64_t kv_len, size_t *bytes /*[host]*/);

@@ -145,7 +145,8 @@ static tq_status prefill_check(const tq_cache *k, int64_t n_rows, int32_t n_q_he
   if (s != TQ_OK) return s;
   if (n_rows < 0 || kv_len < 1 || kv_len > k->n_cells) return TQ_ERR_INVALID_ARG;
   if (n_q_heads < 1 || n_q_heads % k->n_kv_heads) return TQ_ERR_INVALID_ARG;
-  if (k->head_dim != 256 || n_q_heads / k->n_kv_heads > 8) return TQ_ERR_UNSUPPORTED;
+  if ((k->head_dim != 128 && k->head_dim != 256) || n_q_heads / k->n_kv_heads > 8)
+    return TQ_ERR_UNSUPPORTED;
   return TQ_OK;
 }
 

@@ -53,23 +53,39 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kHalf = kThreads / 2;   // matrix threads; the rest decode
-constexpr int kD = 256;               // head_dim
 constexpr int kQRows = 64;            // qrows per workgroup
 constexpr int kKT = 64;               // keys per tile
-constexpr int kKsStride = kD + 8;     // halves per K row and per query row
 constexpr int kVtStride = kKT + 4;    // halves per V^T row (136 B: conflict-free both ways)
-constexpr int kKsHalves = kKT * kKsStride;
-constexpr int kVtHalves = kD * kVtStride;
-constexpr int kQsHalves = kQRows * kKsStride;
-constexpr int kTileHalves = kKsHalves + kVtHalves + kQsHalves;
 // key-half merge: per qrow half [d-tile][4 regs][64 lanes][4], d-tile
 // stride padded by 16 floats so the reads of four d-tiles hit distinct banks
 constexpr int kEDt = 16 * 64 + 16;
-constexpr int kEWave = 8 * kEDt;
 constexpr float kLazy = 8.f;          // the reference moves only past 2^8
 
-static_assert(2 * kEWave * 4 <= kTileHalves * 2, "merge buffer must fit in the tile buffers");
-static_assert(kKsHalves <= kVtHalves, "K tile 0 is staged in the V^T buffer");
+// Sizes that follow the head dimension KD (256 or 128: one or two groups).
+template <int KD>
+struct Dims {
+  static_assert(KD == 128 || KD == 256, "head_dim 128 or 256");
+  static constexpr int NG = KD / 128;              // groups per key
+  static constexpr int KsStride = KD + 8;          // halves per K row and per query row
+  static constexpr int KsHalves = kKT * KsStride;
+  static constexpr int VtHalves = KD * kVtStride;
+  static constexpr int QsHalves = kQRows * KsStride;
+  static constexpr int TileHalves = KsHalves + VtHalves + QsHalves;
+  static constexpr int NS = KD / 16;               // products per score tile
+  static constexpr int ND = KD / 32;               // 32-row d-tiles of the output
+  static constexpr int EK = KD / 4;                // K elements per decode thread (one key)
+  static constexpr int EV = KD / 16;               // V elements per key per decode thread
+  static constexpr int EQ = KD / 4;                // query elements per matrix thread
+  static constexpr int EE = KD / 8;                // output elements per thread
+  static constexpr int EWave = ND * kEDt;          // merge floats per qrow half
+  static_assert(2 * EWave * 4 <= TileHalves * 2, "merge buffer must fit in the tile buffers");
+  static_assert(KsHalves <= VtHalves, "K tile 0 is staged in the V^T buffer");
+};
+
+// 32 sign bits of a group starting at element 32w (w = 0..3).
+__device__ __forceinline__ uint32_t sign_word32(int w) {
+  return (uint32_t)(((w >> 1) ? kSignWord1 : kSignWord0) >> (32 * (w & 1)));
+}
 
 __device__ __forceinline__ int64_t lmin(int64_t a, int64_t b) { return a < b ? a : b; }
 
@@ -120,12 +136,12 @@ __device__ __forceinline__ uint32_t norm_pair(uint16_t h) {
   return b | (b << 16);
 }
 
-// Codes of one key tile for a decode thread.  K: key (thread & 63),
-// elements 64q .. 64q+63 with q = decode wave; V: keys 4(t&15)+i, 16
-// elements from 16(t>>4).
-template <int B>
+// Codes of one key tile for a decode thread dt (0..255).  K: key dt & 63,
+// elements EK q .. EK q + EK - 1 with q = dt >> 6 (its decode wave); V: keys
+// 4(dt & 15) + i, elements EV(dt >> 4) .. EV(dt >> 4) + EV - 1.
+template <int B, int KD>
 struct KRaw {
-  uint32_t c[2 * B];
+  uint32_t c[KD * B / 128];
   uint16_t n;
 };
 template <int B>
@@ -154,61 +170,78 @@ struct HeadPtrs {
 };
 
 // Global loads (keys clamped to the last valid one: tiles past the end load
-// valid rows, and their scores are masked).
-template <int B>
-__device__ __forceinline__ void load_k(const HeadPtrs &h, int last, int kt, int dt, KRaw<B> &r) {
+// valid rows, and their scores are masked).  A key's codes are its groups'
+// codes back to back, so element e of the key starts at bit e * B.
+template <int B, int KD>
+__device__ __forceinline__ void load_k(const HeadPtrs &h, int last, int kt, int dt, KRaw<B, KD> &r) {
+  using D = Dims<KD>;
   const int q = dt >> 6;
   const uint32_t key = (uint32_t)min(kt * kKT + (dt & 63), last);
-  const u32x2_t *src = reinterpret_cast<const u32x2_t *>(h.kc + key * (32u * B) + 8 * B * q);
+  const uint8_t *src = h.kc + key * (16u * B * D::NG) + (D::EK * B / 8) * q;
+  if constexpr (KD == 256) {
 #pragma unroll
-  for (int i = 0; i < B; ++i) {
-    const u32x2_t v = src[i];
-    r.c[2 * i] = v.x;
-    r.c[2 * i + 1] = v.y;
+    for (int i = 0; i < B; ++i) {
+      const u32x2_t v = reinterpret_cast<const u32x2_t *>(src)[i];
+      r.c[2 * i] = v.x;
+      r.c[2 * i + 1] = v.y;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < B; ++i) r.c[i] = reinterpret_cast<const uint32_t *>(src)[i];
   }
-  r.n = h.kn[key * 2u + (q >> 1)];
+  r.n = h.kn[key * (uint32_t)D::NG + (D::EK * q) / 128];
 }
 
-template <int B>
+template <int B, int KD>
 __device__ __forceinline__ void load_v(const HeadPtrs &h, int last, int kt, int dt, VRaw<B> &r) {
-  const int db = dt >> 4, m = db & 7;
-  const int w0 = (16 * B * m) >> 5;
+  using D = Dims<KD>;
+  constexpr int kParts = 128 / D::EV;                 // thread parts per group
+  // a part spans two code words unless its bits always fit in one
+  constexpr bool kTwo = (B == 3) || (D::EV * B > 32);
+  const int db = dt >> 4, grp = db / kParts, m = db % kParts;
+  const int w0 = (D::EV * B * m) >> 5;
+  const int w1 = min(w0 + 1, 4 * B - 1);             // stays inside the group
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t key = (uint32_t)min(kt * kKT + 4 * (dt & 15) + i, last);
-    const uint32_t *row = reinterpret_cast<const uint32_t *>(h.vc + key * (32u * B) + 16 * B * (db >> 3));
+    const uint32_t *row = reinterpret_cast<const uint32_t *>(h.vc + key * (16u * B * D::NG) + 16 * B * grp);
     r.c[i][0] = row[w0];
-    r.c[i][1] = (B == 2) ? 0u : row[w0 + 1];
-    r.n[i] = h.vn[key * 2u + (db >> 3)];
+    r.c[i][1] = kTwo ? row[w1] : 0u;
+    r.n[i] = h.vn[key * (uint32_t)D::NG + grp];
   }
 }
 
-// K part: 64 elements of one key -> its K row quarter, every pair-table read
-// first, then eight 16-byte writes.
-template <int B>
-__device__ __forceinline__ void store_k(const KRaw<B> &r, int dt, const uint32_t *tab, _Float16 *ks) {
+// K part: EK elements of one key -> its K row part, every pair-table read
+// first, then 16-byte writes.
+template <int B, int KD>
+__device__ __forceinline__ void store_k(const KRaw<B, KD> &r, int dt, const uint32_t *tab, _Float16 *ks) {
+  using D = Dims<KD>;
   const uint32_t n2 = norm_pair(r.n);
-  uint32_t h[32];
+  uint32_t h[D::EK / 2];
 #pragma unroll
-  for (int j = 0; j < 32; ++j) h[j] = pair_scaled<B>(tab, bits_at(r.c, 2 * B * j, 2 * B), n2);
-  u32x4_t *dst = reinterpret_cast<u32x4_t *>(ks + (dt & 63) * kKsStride + 64 * (dt >> 6));
+  for (int j = 0; j < D::EK / 2; ++j) h[j] = pair_scaled<B>(tab, bits_at(r.c, 2 * B * j, 2 * B), n2);
+  u32x4_t *dst = reinterpret_cast<u32x4_t *>(ks + (dt & 63) * D::KsStride + D::EK * (dt >> 6));
 #pragma unroll
-  for (int v = 0; v < 8; ++v) dst[v] = u32x4_t{h[4 * v], h[4 * v + 1], h[4 * v + 2], h[4 * v + 3]};
+  for (int v = 0; v < D::EK / 8; ++v) dst[v] = u32x4_t{h[4 * v], h[4 * v + 1], h[4 * v + 2], h[4 * v + 3]};
 }
 
-// V part, transposed: 4 keys x 16 elements -> V^T rows d = 16 db + j,
-// four keys per 8-byte write.  Looked up into w (held until the V buffer is
+// V part, transposed: 4 keys x EV elements -> V^T rows d = EV db + j, four
+// keys per 8-byte write.  Looked up into w (held until the V buffer is
 // free), written by write_v.
-template <int B>
-__device__ __forceinline__ void lookup_v(const VRaw<B> &r, int dt, const uint32_t *tab, uint32_t (&w)[8][4]) {
-  const int m = (dt >> 4) & 7;
-  const int sh = (16 * B * m) & 31;
+template <int B, int KD>
+__device__ __forceinline__ void lookup_v(const VRaw<B> &r, int dt, const uint32_t *tab,
+                                         uint32_t (&w)[KD / 32][4]) {
+  using D = Dims<KD>;
+  const int m = (dt >> 4) % (128 / D::EV);
+  const int sh = (D::EV * B * m) & 31;
+  // parts of a whole number of words start on a word boundary
+  constexpr bool kAligned = (D::EV * B) % 32 == 0;
   uint32_t run[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (B == 2) {
+    if (kAligned) {
       run[i][0] = r.c[i][0];
-      run[i][1] = 0;
+      run[i][1] = r.c[i][1];
     } else {
       run[i][0] = __builtin_amdgcn_alignbit(r.c[i][1], r.c[i][0], sh);
       run[i][1] = sh ? (r.c[i][1] >> sh) : r.c[i][1];
@@ -217,13 +250,13 @@ __device__ __forceinline__ void lookup_v(const VRaw<B> &r, int dt, const uint32_
   uint32_t n2[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) n2[i] = norm_pair(r.n[i]);
-  uint32_t prs[8][4];
+  uint32_t prs[D::EV / 2][4];
 #pragma unroll
-  for (int u = 0; u < 8; ++u)
+  for (int u = 0; u < D::EV / 2; ++u)
 #pragma unroll
     for (int i = 0; i < 4; ++i) prs[u][i] = pair_scaled<B>(tab, bits_at(run[i], 2 * B * u, 2 * B), n2[i]);
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < D::EV / 2; ++u) {
     w[u][0] = __builtin_amdgcn_perm(prs[u][1], prs[u][0], 0x05040100u);
     w[u][1] = __builtin_amdgcn_perm(prs[u][3], prs[u][2], 0x05040100u);
     w[u][2] = __builtin_amdgcn_perm(prs[u][1], prs[u][0], 0x07060302u);
@@ -231,22 +264,25 @@ __device__ __forceinline__ void lookup_v(const VRaw<B> &r, int dt, const uint32_
   }
 }
 
-__device__ __forceinline__ void write_v(const uint32_t (&w)[8][4], int dt, _Float16 *vt) {
-  _Float16 *base = vt + (16 * (dt >> 4)) * kVtStride + 4 * (dt & 15);
+template <int KD>
+__device__ __forceinline__ void write_v(const uint32_t (&w)[KD / 32][4], int dt, _Float16 *vt) {
+  constexpr int EV = Dims<KD>::EV;
+  _Float16 *base = vt + (EV * (dt >> 4)) * kVtStride + 4 * (dt & 15);
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < EV / 2; ++u) {
     *reinterpret_cast<u32x2_t *>(base + (2 * u) * kVtStride) = u32x2_t{w[u][0], w[u][1]};
     *reinterpret_cast<u32x2_t *>(base + (2 * u + 1) * kVtStride) = u32x2_t{w[u][2], w[u][3]};
   }
 }
 
-// S^T of this wave's 32 keys x 32 qrows over all 256 dimensions.
+// S^T of this wave's 32 keys x 32 qrows over all KD dimensions.
+template <int KD>
 __device__ __forceinline__ f32x16_t scores(const _Float16 *krow, const _Float16 *qrow) {
   f32x16_t s;
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr) s[rr] = 0.f;
 #pragma unroll
-  for (int t = 0; t < 16; ++t)
+  for (int t = 0; t < KD / 16; ++t)
     s = __builtin_amdgcn_mfma_f32_32x32x16_f16(*reinterpret_cast<const half8_t *>(krow + 16 * t),
                                                *reinterpret_cast<const half8_t *>(qrow + 16 * t), s, 0, 0, 0);
   return s;
@@ -268,14 +304,15 @@ __device__ __forceinline__ void wht_in_regs(float (&x)[N]) {
       }
 }
 
-template <int B, bool QBF16>
+template <int B, int KD, bool QBF16>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
+  using D = Dims<KD>;
   // aligned to its size, so a lookup address is (entry << 8) | (lane << 2)
   // on top of the table base with no carries
   __shared__ __align__(PfTable<B>::WORDS * 4) uint32_t ptab[PfTable<B>::WORDS];
   // the K tile, the V^T tile, the rotated query rows; after the key loop the
   // same bytes hold the key-half merge
-  __shared__ __align__(16) _Float16 tiles[kTileHalves];
+  __shared__ __align__(16) _Float16 tiles[D::TileHalves];
   __shared__ float mst[2][kQRows], lst[2][kQRows];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -283,8 +320,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
   const int g = blockIdx.y;
   const int64_t head_base = (int64_t)g * a.n_cells;
   _Float16 *kbuf = tiles;
-  _Float16 *vbuf = tiles + kKsHalves;
-  _Float16 *qbuf = vbuf + kVtHalves;
+  _Float16 *vbuf = tiles + D::KsHalves;
+  _Float16 *qbuf = vbuf + D::VtHalves;
   float *ebuf = reinterpret_cast<float *>(tiles);
   const uint32_t *tab = ptab + lane % PfTable<B>::C;   // this lane's pair-table copy
 
@@ -306,17 +343,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
       const int qhalf = wave & 1, khalf = wave >> 1;
       const int ql = lane & 31, hl = lane >> 5;
       {
-        // ---- rotated query rows: thread (c, group, h) owns elements
-        //      64h .. 64h+63 of one group of qrow c
-        const int h = tid & 1, c = (tid >> 1) & 63, grp = tid >> 7;
+        // ---- rotated query rows: thread (pi, c, grp) owns elements
+        //      EQ pi .. EQ pi + EQ - 1 of group grp of qrow c
+        constexpr int EQ = D::EQ, PP = 128 / EQ;
+        const int pi = tid % PP, c = (tid / PP) & 63, grp = tid / (PP * 64);
         const int hq = c / a.bq, rq = c % a.bq;
         const int64_t rr = lmin(row0 + rq, a.n_rows - 1);
-        const int64_t off = (rr * a.n_q + g * a.n_rep + hq) * kD + 128 * grp + 64 * h;
-        float x[64];
+        const int64_t off = (rr * a.n_q + g * a.n_rep + hq) * KD + 128 * grp + EQ * pi;
+        float x[EQ];
         if constexpr (QBF16) {
           const u32x4_t *src = reinterpret_cast<const u32x4_t *>(reinterpret_cast<const uint16_t *>(a.q) + off);
 #pragma unroll
-          for (int v = 0; v < 8; ++v) {
+          for (int v = 0; v < EQ / 8; ++v) {
             const u32x4_t b = src[v];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -327,23 +365,30 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
         } else {
           const float4 *src = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.q) + off);
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
+          for (int v = 0; v < EQ / 4; ++v) {
             const float4 f = src[v];
             x[4 * v] = f.x; x[4 * v + 1] = f.y; x[4 * v + 2] = f.z; x[4 * v + 3] = f.w;
           }
         }
-        uint32_t sw[2] = {(uint32_t)(h ? kSignWord1 : kSignWord0), (uint32_t)((h ? kSignWord1 : kSignWord0) >> 32)};
-        // opaque, so the 64 sign masks are formed here and not hoisted out
-        // of the pass loop (where they would be spilled)
-        asm volatile("" : "+v"(sw[0]), "+v"(sw[1]));
+        uint32_t sw[EQ / 32];
 #pragma unroll
-        for (int e = 0; e < 64; ++e) x[e] = flip_sign(x[e], (sw[e >> 5] >> (e & 31)) & 1u);
-        wht_in_regs<64>(x);
+        for (int w = 0; w < EQ / 32; ++w) sw[w] = sign_word32((EQ / 32) * pi + w);
+        // opaque, so the sign masks are formed here and not hoisted out of
+        // the pass loop (where they would be spilled)
 #pragma unroll
-        for (int e = 0; e < 64; ++e) x[e] = bfly_lane<1>(x[e], h != 0);
-        u32x4_t *dst = reinterpret_cast<u32x4_t *>(qbuf + c * kKsStride + 128 * grp + 64 * h);
+        for (int w = 0; w < EQ / 32; ++w) asm volatile("" : "+v"(sw[w]));
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
+        for (int e = 0; e < EQ; ++e) x[e] = flip_sign(x[e], (sw[e >> 5] >> (e & 31)) & 1u);
+        wht_in_regs<EQ>(x);
+#pragma unroll
+        for (int e = 0; e < EQ; ++e) x[e] = bfly_lane<1>(x[e], (pi & 1) != 0);
+        if constexpr (PP > 2) {
+#pragma unroll
+          for (int e = 0; e < EQ; ++e) x[e] = bfly_lane<2>(x[e], (pi & 2) != 0);
+        }
+        u32x4_t *dst = reinterpret_cast<u32x4_t *>(qbuf + c * D::KsStride + 128 * grp + EQ * pi);
+#pragma unroll
+        for (int v = 0; v < EQ / 8; ++v) {
           uint32_t w[4];
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
@@ -357,15 +402,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
       const int qrow = 32 * qhalf + ql;
       const int64_t r = row0 + qrow % a.bq;
       const int64_t pos = lmin(a.q_pos0 + r, a.kv_len - 1);   // last key this column sees
-      const _Float16 *qrow_p = qbuf + qrow * kKsStride + 8 * hl;
-      const int koff = (32 * khalf + ql) * kKsStride + 8 * hl;
+      const _Float16 *qrow_p = qbuf + qrow * D::KsStride + 8 * hl;
+      const int koff = (32 * khalf + ql) * D::KsStride + 8 * hl;
       __syncthreads();   // query rows, K tiles 0 (in the V^T buffer) and 1 ready
-      f32x16_t sa = scores(vbuf + koff, qrow_p), sb;
+      f32x16_t sa = scores<KD>(vbuf + koff, qrow_p), sb;
       __syncthreads();   // K tile 0 read: the V^T buffer may take V tile 0
 
-      f32x16_t o[8];
+      constexpr int ND = D::ND, NS = D::NS;
+      f32x16_t o[ND];
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
+      for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) o[dt][rr] = 0.f;
       float m_run = -INFINITY, l_run = 0.f;
@@ -385,8 +431,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
             asm volatile("; full tile" ::: "memory");
           // scores of tile kt+1: operands three products ahead in a 4-slot
           // ring, two accumulators (even/odd d-steps) so consecutive products
-          // do not wait on each other; the softmax of tile kt runs in 16
-          // slices between the products
+          // do not wait on each other; the softmax of tile kt runs in NS
+          // slices between the products (maxima, then exponentials)
+          constexpr int HS = NS / 2, PER = 16 / HS;
           const _Float16 *kb = kbuf + koff;
           half8_t ka[4], qa[4];
 #pragma unroll
@@ -402,8 +449,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
           const int lim = lim64 > 64 ? 64 : (int)lim64;
           float v[16], tmax = -INFINITY, m_use = 0.f, psum = 0.f;
 #pragma unroll
-          for (int t = 0; t < 16; ++t) {
-            if (t + 3 < 16) {
+          for (int t = 0; t < NS; ++t) {
+            if (t + 3 < NS) {
               ka[(t + 3) & 3] = *reinterpret_cast<const half8_t *>(kb + 16 * (t + 3));
               qa[(t + 3) & 3] = *reinterpret_cast<const half8_t *>(qrow_p + 16 * (t + 3));
             }
@@ -411,15 +458,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
               s1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[t & 3], qa[t & 3], s1, 0, 0, 0);
             else
               s0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[t & 3], qa[t & 3], s0, 0, 0, 0);
-            if (t < 8) {
+            if (t < HS) {
 #pragma unroll
-              for (int e = 2 * t; e < 2 * t + 2; ++e) {
+              for (int e = PER * t; e < PER * t + PER; ++e) {
                 v[e] = cur[e];
                 if (kMask && 8 * (e >> 2) + 4 * hl + (e & 3) > lim) v[e] = -INFINITY;
               }
-              tmax = fmaxf(tmax, fmaxf(v[2 * t], v[2 * t + 1]));
+#pragma unroll
+              for (int e = PER * t; e < PER * t + PER; e += 2) tmax = fmaxf(tmax, fmaxf(v[e], v[e + 1]));
             }
-            if (t == 7) {
+            if (t == HS - 1) {
               tmax = max_xor32(tmax);
               // lazy reference: it moves only when a score passes it by
               // 2^kLazy, so P <= 2^kLazy and rescales are rare
@@ -428,13 +476,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
               alpha = __builtin_amdgcn_exp2f(m_run - m_use);
               m_run = m_new;
             }
-            if (t >= 8) {
-              const int e = 2 * (t - 8);
-              const float p0 = __builtin_amdgcn_exp2f(v[e] - m_use);
-              const float p1 = __builtin_amdgcn_exp2f(v[e + 1] - m_use);
-              psum += p0 + p1;
-              pb[e >> 3][e & 7] = (_Float16)p0;
-              pb[e >> 3][(e & 7) + 1] = (_Float16)p1;
+            if (t >= HS) {
+#pragma unroll
+              for (int e = PER * (t - HS); e < PER * (t - HS) + PER; e += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(v[e] - m_use);
+                const float p1 = __builtin_amdgcn_exp2f(v[e + 1] - m_use);
+                psum += p0 + p1;
+                pb[e >> 3][e & 7] = (_Float16)p0;
+                pb[e >> 3][(e & 7) + 1] = (_Float16)p1;
+              }
             }
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -447,7 +497,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
           phase_a(std::false_type{});
         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt)
+          for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) o[dt][rr] *= alpha;
         }
@@ -458,7 +508,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
         // products ahead.
         const _Float16 *vt = vbuf + ql * kVtStride + 32 * khalf + 4 * hl;
         auto vop = [&](int idx) {
-          const _Float16 *vr = vt + 32 * (idx & 7) * kVtStride + 16 * (idx >> 3);
+          const _Float16 *vr = vt + 32 * (idx % ND) * kVtStride + 16 * (idx / ND);
           const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vr);
           const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vr + 8);
           return __builtin_bit_cast(half8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
@@ -467,9 +517,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
 #pragma unroll
         for (int i = 0; i < 3; ++i) va[i] = vop(i);
 #pragma unroll
-        for (int idx = 0; idx < 16; ++idx) {
-          if (idx + 3 < 16) va[(idx + 3) & 3] = vop(idx + 3);
-          o[idx & 7] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[idx & 3], pb[idx >> 3], o[idx & 7], 0, 0, 0);
+        for (int idx = 0; idx < 2 * ND; ++idx) {
+          if (idx + 3 < 2 * ND) va[(idx + 3) & 3] = vop(idx + 3);
+          o[idx % ND] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[idx & 3], pb[idx / ND], o[idx % ND], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();   // V tile kt consumed; K tile kt+2 written
@@ -482,14 +532,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
       // ---- merge the key halves: khalf 1 hands its partial output to
       //      khalf 0, which writes the normalized sum back in place
       l_run += xor_lane<32>(l_run);
-      float *ew = ebuf + qhalf * kEWave + lane * 4;
+      float *ew = ebuf + qhalf * D::EWave + lane * 4;
       if (hl == 0) {
         mst[khalf][qrow] = m_run;
         lst[khalf][qrow] = l_run;
       }
       if (khalf == 1) {
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
+        for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
           for (int rq = 0; rq < 4; ++rq)
             *reinterpret_cast<float4 *>(ew + dt * kEDt + rq * 256) =
@@ -504,7 +554,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
         const float rinv = 1.0f / (8.0f * (l_run * f1 + l2 * f2));
         const float g1 = f1 * rinv, g2 = f2 * rinv;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
+        for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
           for (int rq = 0; rq < 4; ++rq) {
             float4 *ptr = reinterpret_cast<float4 *>(ew + dt * kEDt + rq * 256);
@@ -519,72 +569,79 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
       int last = (int)(a.kv_len - 1);
       asm volatile("" : "+s"(last));   // keeps tile addresses in the pass (not hoisted, spilled)
       HeadPtrs hp;
-      hp.kc = a.kcodes + head_base * (32 * B);
-      hp.vc = a.vcodes + head_base * (32 * B);
-      hp.kn = a.knorms + head_base * 2;
-      hp.vn = a.vnorms + head_base * 2;
-      KRaw<B> kr0, kr1;
+      hp.kc = a.kcodes + head_base * (16 * B * D::NG);
+      hp.vc = a.vcodes + head_base * (16 * B * D::NG);
+      hp.kn = a.knorms + head_base * D::NG;
+      hp.vn = a.vnorms + head_base * D::NG;
+      KRaw<B, KD> kr0, kr1;
       VRaw<B> vr;
-      uint32_t vw[8][4];
-      load_k<B>(hp, last, 0, dt, kr0);
-      load_k<B>(hp, last, 1, dt, kr1);
-      load_v<B>(hp, last, 0, dt, vr);
-      store_k<B>(kr0, dt, tab, vbuf);   // K tile 0 goes where V tile 0 will
-      store_k<B>(kr1, dt, tab, kbuf);
-      lookup_v<B>(vr, dt, tab, vw);
+      uint32_t vw[KD / 32][4];
+      load_k<B, KD>(hp, last, 0, dt, kr0);
+      load_k<B, KD>(hp, last, 1, dt, kr1);
+      load_v<B, KD>(hp, last, 0, dt, vr);
+      store_k<B, KD>(kr0, dt, tab, vbuf);   // K tile 0 goes where V tile 0 will
+      store_k<B, KD>(kr1, dt, tab, kbuf);
+      lookup_v<B, KD>(vr, dt, tab, vw);
       // loads are unconditional (tile index clamped): a conditional load
       // would merge into the loop-carried registers through copies that wait
       // for the data
-      load_k<B>(hp, last, min(2, n_kt - 1), dt, kr0);
-      load_v<B>(hp, last, min(1, n_kt - 1), dt, vr);
+      load_k<B, KD>(hp, last, min(2, n_kt - 1), dt, kr0);
+      load_v<B, KD>(hp, last, min(1, n_kt - 1), dt, vr);
       __syncthreads();   // query rows, K tiles 0 (in the V^T buffer) and 1 ready
       __syncthreads();   // K tile 0 read: the V^T buffer may take V tile 0
       for (int kt = 0; kt < n_kt; ++kt) {
         // phase A: V tile kt into the buffer, look up V tile kt+1
-        write_v(vw, dt, vbuf);
-        lookup_v<B>(vr, dt, tab, vw);   // past the end: never written
-        load_v<B>(hp, last, min(kt + 2, n_kt - 1), dt, vr);
+        write_v<KD>(vw, dt, vbuf);
+        lookup_v<B, KD>(vr, dt, tab, vw);   // past the end: never written
+        load_v<B, KD>(hp, last, min(kt + 2, n_kt - 1), dt, vr);
         __syncthreads();   // V tile kt written; K tile kt+1 read
         // phase B: K tile kt+2 into the (now free) K buffer
-        if (kt + 2 < n_kt) store_k<B>(kr0, dt, tab, kbuf);
-        load_k<B>(hp, last, min(kt + 3, n_kt - 1), dt, kr0);
+        if (kt + 2 < n_kt) store_k<B, KD>(kr0, dt, tab, kbuf);
+        load_k<B, KD>(hp, last, min(kt + 3, n_kt - 1), dt, kr0);
         __syncthreads();   // V tile kt consumed; K tile kt+2 written
       }
       __syncthreads();   // partial outputs and statistics in shared memory
     }
     __syncthreads();   // merged output in shared memory
 
-    // ---- merge, normalize, inverse transform: thread (j, c, group) owns
-    //      elements 32j .. 32j+31 of one group of qrow c
+    // ---- merge, normalize, inverse transform: thread (j, c, grp) owns
+    //      elements EE j .. EE j + EE - 1 of group grp of qrow c
     {
-      const int j = tid & 3, c = (tid >> 2) & 63, grp = tid >> 8;
+      constexpr int EE = D::EE, PE = 128 / EE;
+      const int j = tid % PE, c = (tid / PE) & 63, grp = tid / (PE * 64);
       const int qh = c >> 5, ql = c & 31;
-      const float *e0 = ebuf + qh * kEWave + (4 * grp + j) * kEDt;
-      float x[32];
+      const int d0 = 128 * grp + EE * j;   // first element (its d-tile: d0 / 32)
+      const float *e0 = ebuf + qh * D::EWave + (d0 >> 5) * kEDt + ((d0 & 31) >> 3) * 256;
+      float x[EE];
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq)
+      for (int rq = 0; rq < EE / 8; ++rq)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          // element e = 8rq + 4hh + i <-> register 4rq + i of lane ql + 32hh
+          // element 8rq + 4hh + i of the d-tile <-> register 4rq + i of lane
+          // ql + 32hh
           const float4 u = *reinterpret_cast<const float4 *>(e0 + rq * 256 + (ql + 32 * hh) * 4);
           x[8 * rq + 4 * hh + 0] = u.x;
           x[8 * rq + 4 * hh + 1] = u.y;
           x[8 * rq + 4 * hh + 2] = u.z;
           x[8 * rq + 4 * hh + 3] = u.w;
         }
-      wht_in_regs<32>(x);
+      wht_in_regs<EE>(x);
 #pragma unroll
-      for (int e = 0; e < 32; ++e) x[e] = bfly_lane<1>(x[e], (j & 1) != 0);
+      for (int e = 0; e < EE; ++e) x[e] = bfly_lane<1>(x[e], (j & 1) != 0);
 #pragma unroll
-      for (int e = 0; e < 32; ++e) x[e] = bfly_lane<2>(x[e], (j & 2) != 0);
+      for (int e = 0; e < EE; ++e) x[e] = bfly_lane<2>(x[e], (j & 2) != 0);
+      if constexpr (PE > 4) {
+#pragma unroll
+        for (int e = 0; e < EE; ++e) x[e] = bfly_lane<4>(x[e], (j & 4) != 0);
+      }
       const int hq = c / a.bq;
       const int64_t r = row0 + c % a.bq;
       if (r < a.n_rows) {
-        uint32_t sw = (uint32_t)((j < 2 ? kSignWord0 : kSignWord1) >> (32 * (j & 1)));
+        uint32_t sw = sign_word32((EE * j) >> 5) >> ((EE * j) & 31);
         asm volatile("" : "+v"(sw));   // formed here, not hoisted and spilled
-        float *orow = a.out + (r * a.n_q + g * a.n_rep + hq) * kD + 128 * grp + 32 * j;
+        float *orow = a.out + (r * a.n_q + g * a.n_rep + hq) * KD + d0;
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
+        for (int v = 0; v < EE / 4; ++v) {
           float4 f;
           f.x = flip_sign(x[4 * v + 0], (sw >> (4 * v + 0)) & 1u);
           f.y = flip_sign(x[4 * v + 1], (sw >> (4 * v + 1)) & 1u);
@@ -641,19 +698,27 @@ hipError_t launch_prefill(const tq_cache &k, const tq_cache &v, int64_t kv_len, 
   a.qscale = scale * 1.4426950408889634f / 8.0f;
   dim3 grid((unsigned)ceil_div(p.n_row_tiles, 2), (unsigned)k.n_kv_heads);
   dim3 block(pf::kThreads);
-#define TQ_PF(B)                                                                  \
-  do {                                                                            \
-    if (q_dtype == TQ_BF16)                                                       \
-      hipLaunchKernelGGL((pf::prefill_kernel<B, true>), grid, block, 0, stream, a); \
-    else                                                                          \
-      hipLaunchKernelGGL((pf::prefill_kernel<B, false>), grid, block, 0, stream, a); \
+#define TQ_PF(B, KD)                                                                  \
+  do {                                                                                \
+    if (q_dtype == TQ_BF16)                                                           \
+      hipLaunchKernelGGL((pf::prefill_kernel<B, KD, true>), grid, block, 0, stream, a); \
+    else                                                                              \
+      hipLaunchKernelGGL((pf::prefill_kernel<B, KD, false>), grid, block, 0, stream, a); \
   } while (0)
-  switch (k.type) {
-    case TQ_TURBO2: TQ_PF(2); break;
-    case TQ_TURBO3: TQ_PF(3); break;
-    case TQ_TURBO4: TQ_PF(4); break;
-    default: return hipErrorNotSupported;
+#define TQ_PF_TYPES(KD)                  \
+  switch (k.type) {                      \
+    case TQ_TURBO2: TQ_PF(2, KD); break; \
+    case TQ_TURBO3: TQ_PF(3, KD); break; \
+    case TQ_TURBO4: TQ_PF(4, KD); break; \
+    default: return hipErrorNotSupported; \
   }
+  if (k.head_dim == 256)
+    TQ_PF_TYPES(256)
+  else if (k.head_dim == 128)
+    TQ_PF_TYPES(128)
+  else
+    return hipErrorNotSupported;
+#undef TQ_PF_TYPES
 #undef TQ_PF
   return hipGetLastError();
 }

@@ -137,8 +137,11 @@ def test_prefill_rejects_bad_arguments():
     assert call(nrows=-1) == -1
     assert call(kv=2048) == -1
     assert call(nq=12) == -1
+    d384 = _cache(b, head_dim=384, n_kv=8, n_cells=1024)
+    assert call(k=d384, v=d384) == -2             # head_dim 384: no kernel
     d128 = _cache(b, head_dim=128, n_kv=8, n_cells=1024)
-    assert call(k=d128, v=d128) == -2
+    assert call(k=d128, v=_cache(b, head_dim=256, n_kv=8, n_cells=1024)) == -1
+    assert call(k=d128, v=d128, nrows=0, q0=0) == 0
     assert call(nrows=0, q0=0) == 0               # empty: no-op
 
 

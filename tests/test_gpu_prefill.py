@@ -1,5 +1,6 @@
-"""GPU parity of tq_attn_prefill (turbo3, and turbo2/turbo4 on a subset; head_dim 256) against the float64
-oracle; bar: max-abs <= 2e-3 and relative L2 <= 1e-3.
+"""GPU parity of tq_attn_prefill (turbo3, and turbo2/turbo4 on a subset;
+head_dim 256, and 128 on a subset) against the float64 oracle; bar: max-abs
+<= 2e-3 and relative L2 <= 1e-3.
 
 The grid mirrors the correctness check of the "HIP/turbo3: graph-safe decode
 + inline-dequant TILE prefill" page (section Correctness: turbo3, 256-wide
@@ -125,4 +126,23 @@ def test_turbo2_turbo4(bits, rows, kv, q0):
     pair table holds 2 or 4-bit code pairs)."""
     q, k, v = inputs.prefill(seed=rows + kv + bits, rows=rows, kv_len=kv)
     (ma, rl), _ = _run(q, k, v, kv, q0, what="turbo2/4", bits=bits)
+    print(f"    max_abs={ma:.3g} rel_l2={rl:.3g}")
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("rows,kv,q0,n_q,n_kv", [(3, 1024, 1021, 16, 8), (64, 512, 448, 32, 4),
+                                                 (256, 256, 0, 8, 8), (65, 200, 100, 16, 2),
+                                                 (1, 1, 0, 8, 1), (130, 700, 570, 32, 8)])
+def test_head_dim_128(bits, rows, kv, q0, n_q, n_kv):
+    """128-wide heads (one group per key, the head width of the decode
+    workload): the same kernel with half the products and half the codes per
+    tile."""
+    q, k, v = inputs.prefill(seed=rows + kv + 11 * bits, rows=rows, kv_len=kv, n_q=n_q, n_kv=n_kv, d=128)
+    (ma, rl), _ = _run(q, k, v, kv, q0, q_bf16=(rows % 2 == 0), what="d128", bits=bits)
+    print(f"    max_abs={ma:.3g} rel_l2={rl:.3g}")
+
+
+def test_head_dim_128_causal_1024():
+    q, k, v = inputs.prefill(seed=12, rows=1024, n_q=32, n_kv=8, d=128)
+    (ma, rl), _ = _run(q, k, v, 1024, 0, what="d128 causal")
     print(f"    max_abs={ma:.3g} rel_l2={rl:.3g}")
