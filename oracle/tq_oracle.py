@@ -345,17 +345,21 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
               q_pos0: int, block: int = 512) -> np.ndarray:
     """Causal softmax attention, float64.
 
-    q: [n_rows, n_q_heads, D]; k, v: [n_kv_heads, L, D].  Query row r sits at
-    absolute position q_pos0 + r and sees keys j <= q_pos0 + r (reading: the
-    query block is aligned to the end of the keys it was appended after, the
-    prefill/spec-verify case of [PR28] "Inline-dequant TILE prefill").
-    out[r, h] = sum_j softmax_j(scale * <q[r,h], k[g(h), j]>) v[g(h), j].
+    q: [n_rows, n_q_heads, D_K]; k: [n_kv_heads, L, D_K]; v: [n_kv_heads, L,
+    D_V].  Query row r sits at absolute position q_pos0 + r and sees keys
+    j <= q_pos0 + r (reading: the query block is aligned to the end of the keys
+    it was appended after, the prefill/spec-verify case of [PR28]
+    "Inline-dequant TILE prefill").
+    out[r, h] = sum_j softmax_j(scale * <q[r,h], k[g(h), j]>) v[g(h), j], of
+    V's width: the key and value widths may differ ([PR36] (b): 192-wide keys,
+    padded to 256, beside 128-wide values).
     """
     q = np.asarray(q, dtype=np.float64)
     n_rows, n_q, d = q.shape
     n_kv, L, _ = k.shape
+    assert k.shape[2] == d and v.shape[:2] == k.shape[:2]
     g_of = kv_head_of(n_q, n_kv)
-    out = np.zeros((n_rows, n_q, d))
+    out = np.zeros((n_rows, n_q, v.shape[2]))
     for h in range(n_q):
         kh = k[g_of[h]]
         vh = v[g_of[h]]
@@ -371,7 +375,7 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
 
 
 def attn_decode(kc: dict, vc: dict, kv_len: int, q: np.ndarray, scale: float) -> np.ndarray:
-    """One query row over the whole cache: q [n_q_heads, D] -> [n_q_heads, D] float64.
+    """One query row over the whole cache: q [n_q_heads, D_K] -> [n_q_heads, D_V] float64.
 
     The decode case of [PR36] (c)/(d) and [PR28] "Graph-safe decode".
     """

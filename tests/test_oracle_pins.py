@@ -369,6 +369,44 @@ def test_decode_prefill_use_dequantized_cache():
     assert err < 0.05
 
 
+@pytest.mark.parametrize("dk,dv", [(48, 16), (16, 40)])
+def test_attention_asymmetric_widths_match_sdpa(dk, dv):
+    """Keys and values of different widths ([PR36] (b): 192-wide keys padded
+    to 256 beside 128-wide values): the output takes V's width; torch's
+    scaled_dot_product_attention accepts such V natively."""
+    rng = np.random.default_rng(13)
+    q = rng.standard_normal((4, 6, dk))
+    k = rng.standard_normal((3, 30, dk))
+    v = rng.standard_normal((3, 30, dv))
+    got = o.attention(q, k, v, 0.2, 26, block=3)
+    assert got.shape == (4, 6, dv)
+    np.testing.assert_allclose(got, _sdpa_fp64(q, k, v, 0.2, 26), atol=1e-12)
+
+
+def test_asymmetric_cache_decode():
+    """A 256-wide K cache (a 192-wide head zero-padded) with a 128-wide V
+    cache: the decode is attention over the two dequantized caches, the
+    padding of the query and the keys adds nothing to any score, and padding
+    V with zeros to 256 only appends zero columns to the output."""
+    rng = np.random.default_rng(14)
+    n = 23
+    k192 = rng.standard_normal((n, 2, 192)).astype(F32)
+    kk = np.concatenate([k192, np.zeros((n, 2, 64), F32)], axis=2)
+    vv = rng.standard_normal((n, 2, 128)).astype(F32)
+    kc = o.new_cache(3, 256, 2, n); vc = o.new_cache(3, 128, 2, n)
+    o.set_rows(kc, kk, np.arange(n)); o.set_rows(vc, vv, np.arange(n))
+    q = np.concatenate([rng.standard_normal((4, 192)), np.zeros((4, 64))], axis=1)
+    got = o.attn_decode(kc, vc, n, q, 0.1)
+    assert got.shape == (4, 128)
+    k = o.dequant_cache(kc, n); v = o.dequant_cache(vc, n)
+    np.testing.assert_allclose(got, _sdpa_fp64(q[None], k, v, 0.1, n - 1)[0], atol=1e-12)
+    vc2 = o.new_cache(3, 256, 2, n)
+    o.set_rows(vc2, np.concatenate([vv, np.zeros((n, 2, 128), F32)], axis=2), np.arange(n))
+    wide = o.attn_decode(kc, vc2, n, q, 0.1)
+    np.testing.assert_allclose(wide[:, :128], got, atol=1e-12)
+    np.testing.assert_array_equal(wide[:, 128:], 0.0)
+
+
 # ---------------------------------------------------------------- int8
 
 def test_int8_brute_force_and_page_invariance():
