@@ -146,7 +146,7 @@ def main():
         vcs[i].codes.copy_(vcs[0].codes); vcs[i].norms.copy_(vcs[0].norms)
     torch.cuda.synchronize()
     scale_dec = 1.0 / math.sqrt(D)
-    ws_bytes = b.tq_attn_decode_workspace(kcs[0], KV, NQ)
+    ws_bytes = b.tq_attn_decode_workspace(kcs[0], vcs[0], KV, NQ)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     outs = [torch.empty((NQ, D), dtype=torch.float32, device=dev) for _ in range(L)]
     kv_bytes_per_call = 2 * NKV * KV * (48 + 2)      # packed codes + fp16 norm, K and V
@@ -299,6 +299,58 @@ def main():
             t_ms = time_eager(lambda tau=tau: b.tq_attn_decode(kcs[0], vcs[0], KV, q_dec, scale_dec, out=outs[0],
                                                                 workspace=ws, sparse_v_tau=tau), reps=50)
             extras[f"decode_eager_tau_{tau:g}"] = {"us_per_call": round(t_ms * 1e3, 3)}
+
+        def time_graph(calls, reps=5):
+            """ms per call of `calls` captured into one graph (warmed first)."""
+            for c in calls:
+                c()
+            torch.cuda.synchronize()
+            st = torch.cuda.Stream()
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                for c in calls:
+                    c()
+            torch.cuda.current_stream().wait_stream(st)
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for c in calls:
+                    c()
+            gr.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                gr.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps / len(calls)
+
+        # 256-wide heads (16 q / 2 kv heads: the bytes of the headline call),
+        # and a 256-wide K beside a 128-wide V, over L distinct 32K caches
+        # (leg "decode_wide": left out of `--only decode`, whose kernel
+        # profiles then hold the headline shape alone)
+        for dk, dv in ((256, 256), (256, 128)) if want("decode_wide") else ():
+            wq, wk, wv = inputs.outlier_decode(seed=7, kv_len=KV, n_q=16, n_kv=2, d=dk, dv=dv)
+            wkc = [b.new_cache(3, dk, 2, KV) for _ in range(L)]
+            wvc = [b.new_cache(3, dv, 2, KV) for _ in range(L)]
+            b.tq_set_rows(wkc[0], torch.from_numpy(wk).to(dev), idx)
+            b.tq_set_rows(wvc[0], torch.from_numpy(wv).to(dev), idx)
+            for i in range(1, L):
+                wkc[i].codes.copy_(wkc[0].codes); wkc[i].norms.copy_(wkc[0].norms)
+                wvc[i].codes.copy_(wvc[0].codes); wvc[i].norms.copy_(wvc[0].norms)
+            wqt = torch.from_numpy(wq).to(torch.bfloat16).to(dev)
+            wws = torch.empty(b.tq_attn_decode_workspace(wkc[0], wvc[0], KV, 16), dtype=torch.uint8, device=dev)
+            wout = [torch.empty((16, dv), dtype=torch.float32, device=dev) for _ in range(L)]
+            calls = [lambda i=i: b.tq_attn_decode(wkc[i], wvc[i], KV, wqt, 1.0 / math.sqrt(dk), out=wout[i],
+                                                  workspace=wws) for i in range(L)]
+            t_ms = time_graph(calls)
+            nbytes = KV * 2 * (dk // 128 + dv // 128) * (48 + 2)
+            gbps = nbytes / (t_ms * 1e-3) / 1e9
+            extras[f"decode_turbo3_32k_k{dk}_v{dv}_16q2kv"] = {
+                "us_per_call": round(t_ms * 1e3, 3), "bytes_per_call": nbytes, "GBps": round(gbps, 1),
+                "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+            del wkc, wvc, wout, wws
     log("[bench] extras done")
 
     res = {}

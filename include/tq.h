@@ -128,29 +128,36 @@ tq_status tq_set_rows(const tq_cache *dst, const float *src, const int64_t *cell
  * Decode attention: one query row over cells [0, kv_len) ([PR36] (c),(d):
  * decode over a turbo cache, the single-column flash-attention case;
  * [PR28] "Graph-safe decode").
- *   q    [n_q_heads][head_dim], float32 or bfloat16 (q_dtype), 16-byte aligned
- *   out  float32 [n_q_heads][head_dim], 16-byte aligned
+ *   q    [n_q_heads][k->head_dim], float32 or bfloat16 (q_dtype), 16-byte aligned
+ *   out  float32 [n_q_heads][v->head_dim], 16-byte aligned
  * Computes, for q head h and kv head g = h / (n_q_heads / n_kv_heads):
  *   out[h] = sum_j softmax_j(scale * <q[h], k_hat_j>) v_hat_j,
  * with k_hat, v_hat the dequantized rows: x_hat = s (.) H w / sqrt(128) per
  * group, w_d = code_values[code_d] * norm / sqrt(128), H the 128-point
  * Sylvester-Hadamard matrix.  (The kernels work in the rotated domain,
  * rotating q in and the output back out.)
- * Requires k and v of the same type, head_dim and n_kv_heads,
- * 1 <= kv_len <= n_cells, n_q_heads a multiple of n_kv_heads with at most 8
- * q heads per kv head, and head_dim == 128 in this build.
+ * Requires k and v of the same type, n_kv_heads and n_cells,
+ * 1 <= kv_len <= n_cells, n_q_heads a multiple of n_kv_heads (else
+ * TQ_ERR_INVALID_ARG); this build takes head widths of 128 or 256 for each
+ * of k and v, which may differ ([PR36] (b): a 192-wide K head padded to 256
+ * beside 128-wide V heads, decoded natively), and at most 8 q heads per kv
+ * head (else TQ_ERR_UNSUPPORTED).
  * sparse_v_tau >= 0 ([PR36] (d) item 3; 0 = off): a key whose weight
  * e^(s - m) is below tau is left out of the value sum and kept in the
- * normalizer, with m the maximum over the block of 16, 32 or 64 keys that
- * one wave scores (chosen by the plan; at most the true maximum).  The output then differs from the dense one by at most
+ * normalizer, with m the maximum over the aligned block of 16 T keys that
+ * one wave scores (at most the true maximum).  T is the plan's: the largest
+ * of 8, 4, 2, 1 with T (k->head_dim + v->head_dim) / 128 <= 16 and
+ * ceil(kv_len / 64T) * n_kv_heads >= the device's compute units, else 1.
+ * The output then differs from the dense one by at most
  * sum over {j : e^(s_j - m*) < tau} of (e^(s_j - m*) / sum_i e^(s_i - m*)) |v_j|_2
  * (m* the true maximum).  The products are not skipped, so the call costs
  * the same as a dense one.  A NaN or negative tau is TQ_ERR_INVALID_ARG.
  * The workspace holds per-split partial results; its size comes from
- * tq_attn_decode_workspace for the same arguments on the same device.
+ * tq_attn_decode_workspace for the same caches and arguments on the same
+ * device (it grows with v->head_dim).
  */
-tq_status tq_attn_decode_workspace(const tq_cache *k, int64_t kv_len, int32_t n_q_heads,
-                                   size_t *bytes /*[host]*/);
+tq_status tq_attn_decode_workspace(const tq_cache *k, const tq_cache *v, int64_t kv_len,
+                                   int32_t n_q_heads, size_t *bytes /*[host]*/);
 tq_status tq_attn_decode(const tq_cache *k, const tq_cache *v, int64_t kv_len, const void *q,
                          int q_dtype, int32_t n_q_heads, float scale, float sparse_v_tau,
                          float *out, void *workspace, size_t workspace_bytes, tq_stream_t stream);
@@ -163,7 +170,8 @@ tq_status tq_attn_decode(const tq_cache *k, const tq_cache *v, int64_t kv_len, c
  *   out  float32 [n_rows][n_q_heads][head_dim], 16-byte aligned
  * Query row r sits at position q_pos0 + r and sees cells j <= q_pos0 + r
  * (causal, aligned so that the last row sees q_pos0 + n_rows - 1 keys + 1).
- * Same formula and head mapping as decode.  Requires
+ * Same formula and head mapping as decode.  Requires k and v of the same
+ * type, head_dim, n_kv_heads and n_cells, and
  * 0 <= q_pos0, q_pos0 + n_rows <= kv_len <= n_cells; n_rows == 0 is a no-op.
  * This build supports turbo2, turbo3 and turbo4 with head_dim 128 or 256
  * and at most 8 q heads per kv head (others: TQ_ERR_UNSUPPORTED; [PR28]

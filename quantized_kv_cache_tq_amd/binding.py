@@ -42,7 +42,8 @@ _SIGS = {
     "tq_cache_plane_bytes": (c_int, [c_int, c_int32, c_int32, c_int64, POINTER(c_size_t), POINTER(c_size_t)]),
     "tq_codebook": (c_int, [c_int, POINTER(c_float), POINTER(c_float), POINTER(c_uint64)]),
     "tq_set_rows": (c_int, [POINTER(TQCache), c_void_p, c_void_p, c_int64, c_void_p]),
-    "tq_attn_decode_workspace": (c_int, [POINTER(TQCache), c_int64, c_int32, POINTER(c_size_t)]),
+    "tq_attn_decode_workspace": (c_int, [POINTER(TQCache), POINTER(TQCache), c_int64, c_int32,
+                                         POINTER(c_size_t)]),
     "tq_attn_decode": (c_int, [POINTER(TQCache), POINTER(TQCache), c_int64, c_void_p, c_int, c_int32,
                                c_float, c_float, c_void_p, c_void_p, c_size_t, c_void_p]),
     "tq_attn_prefill_workspace": (c_int, [POINTER(TQCache), c_int64, c_int32, c_int64, POINTER(c_size_t)]),
@@ -174,10 +175,10 @@ def _workspace(nbytes: int, device, workspace):
     return workspace
 
 
-def tq_attn_decode_workspace(k: TQCacheTensors, kv_len: int, n_q_heads: int) -> int:
+def tq_attn_decode_workspace(k: TQCacheTensors, v: TQCacheTensors, kv_len: int, n_q_heads: int) -> int:
     b = c_size_t()
-    _check(load_library().tq_attn_decode_workspace(ctypes.byref(k.struct), kv_len, n_q_heads,
-                                                   ctypes.byref(b)), "tq_attn_decode_workspace")
+    _check(load_library().tq_attn_decode_workspace(ctypes.byref(k.struct), ctypes.byref(v.struct), kv_len,
+                                                   n_q_heads, ctypes.byref(b)), "tq_attn_decode_workspace")
     return b.value
 
 
@@ -187,12 +188,14 @@ def tq_attn_decode(k: TQCacheTensors, v: TQCacheTensors, kv_len: int, q: torch.T
     qd = _q_dtype(q)
     _dev_tensor(q, q.dtype, "q")
     if q.dim() != 2 or q.shape[1] != k.head_dim:
-        raise ValueError("q must be [n_q_heads, head_dim]")
+        raise ValueError("q must be [n_q_heads, k.head_dim]")
     n_q = q.shape[0]
     if out is None:
-        out = torch.empty((n_q, k.head_dim), dtype=torch.float32, device=q.device)
+        out = torch.empty((n_q, v.head_dim), dtype=torch.float32, device=q.device)
     _dev_tensor(out, torch.float32, "out")
-    ws = _workspace(tq_attn_decode_workspace(k, kv_len, n_q), q.device, workspace)
+    if tuple(out.shape) != (n_q, v.head_dim):
+        raise ValueError("out must be [n_q_heads, v.head_dim]")
+    ws = _workspace(tq_attn_decode_workspace(k, v, kv_len, n_q), q.device, workspace)
     _check(load_library().tq_attn_decode(ctypes.byref(k.struct), ctypes.byref(v.struct), kv_len,
                                          q.data_ptr(), qd, n_q, scale, sparse_v_tau, out.data_ptr(),
                                          ws.data_ptr(), ws.numel(), _stream(stream)), "tq_attn_decode")

@@ -24,13 +24,17 @@ tq_status check_cache(const tq_cache *c) {
   return TQ_OK;
 }
 
-tq_status check_pair(const tq_cache *k, const tq_cache *v) {
+// K and V of one attention call: the same type, kv heads and cells (the
+// kernels address both with one cell count); the head widths must match
+// unless the call allows them to differ.
+tq_status check_pair(const tq_cache *k, const tq_cache *v, bool same_width = true) {
   tq_status s = check_cache(k);
   if (s != TQ_OK) return s;
   s = check_cache(v);
   if (s != TQ_OK) return s;
-  if (k->type != v->type || k->head_dim != v->head_dim || k->n_kv_heads != v->n_kv_heads)
+  if (k->type != v->type || k->n_kv_heads != v->n_kv_heads || k->n_cells != v->n_cells)
     return TQ_ERR_INVALID_ARG;
+  if (same_width && k->head_dim != v->head_dim) return TQ_ERR_INVALID_ARG;
   return TQ_OK;
 }
 
@@ -97,22 +101,25 @@ tq_status tq_set_rows(const tq_cache *dst, const float *src, const int64_t *cell
 
 // ---------------------------------------------------------------- decode
 
-static tq_status decode_check(const tq_cache *k, int64_t kv_len, int32_t n_q_heads) {
-  tq_status s = check_cache(k);
+static tq_status decode_check(const tq_cache *k, const tq_cache *v, int64_t kv_len,
+                              int32_t n_q_heads) {
+  tq_status s = check_pair(k, v, /*same_width=*/false);
   if (s != TQ_OK) return s;
   if (kv_len < 1 || kv_len > k->n_cells) return TQ_ERR_INVALID_ARG;
   if (n_q_heads < 1 || n_q_heads % k->n_kv_heads) return TQ_ERR_INVALID_ARG;
-  if (k->head_dim != 128 || n_q_heads / k->n_kv_heads > 8) return TQ_ERR_UNSUPPORTED;
+  if ((k->head_dim != 128 && k->head_dim != 256) || (v->head_dim != 128 && v->head_dim != 256) ||
+      n_q_heads / k->n_kv_heads > 8)
+    return TQ_ERR_UNSUPPORTED;
   return TQ_OK;
 }
 
-tq_status tq_attn_decode_workspace(const tq_cache *k, int64_t kv_len, int32_t n_q_heads,
-                                   size_t *bytes) {
-  tq_status s = decode_check(k, kv_len, n_q_heads);
+tq_status tq_attn_decode_workspace(const tq_cache *k, const tq_cache *v, int64_t kv_len,
+                                   int32_t n_q_heads, size_t *bytes) {
+  tq_status s = decode_check(k, v, kv_len, n_q_heads);
   if (s != TQ_OK) return s;
   if (!bytes) return TQ_ERR_INVALID_ARG;
   DecodePlan p;
-  if (tq_status st = from_hip(plan_decode(*k, kv_len, n_q_heads, &p))) return st;
+  if (tq_status st = from_hip(plan_decode(*k, *v, kv_len, n_q_heads, &p))) return st;
   *bytes = p.workspace_bytes;
   return TQ_OK;
 }
@@ -121,16 +128,14 @@ tq_status tq_attn_decode(const tq_cache *k, const tq_cache *v, int64_t kv_len, c
                          int q_dtype, int32_t n_q_heads, float scale, float sparse_v_tau,
                          float *out, void *workspace, size_t workspace_bytes,
                          tq_stream_t stream) {
-  tq_status s = check_pair(k, v);
-  if (s != TQ_OK) return s;
-  s = decode_check(k, kv_len, n_q_heads);
+  tq_status s = decode_check(k, v, kv_len, n_q_heads);
   if (s != TQ_OK) return s;
   if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return TQ_ERR_INVALID_ARG;
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
   if (!(scale == scale) || !(sparse_v_tau == sparse_v_tau) || sparse_v_tau < 0.f)
     return TQ_ERR_INVALID_ARG;
   DecodePlan p;
-  if (tq_status st = from_hip(plan_decode(*k, kv_len, n_q_heads, &p))) return st;
+  if (tq_status st = from_hip(plan_decode(*k, *v, kv_len, n_q_heads, &p))) return st;
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.workspace_bytes)
     return TQ_ERR_WORKSPACE;
   return from_hip(launch_decode(*k, *v, kv_len, q, q_dtype, n_q_heads, scale, sparse_v_tau, out, workspace, p,

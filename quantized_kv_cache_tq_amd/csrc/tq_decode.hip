@@ -42,8 +42,9 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = 64 * kDecWaves;
-constexpr int kD = 128;              // head_dim handled by this kernel
-constexpr int kPartStride = kD + 4;  // o[128], m, l, pad (floats; 16-byte rows)
+// A split partial is o[head width], m, l, pad: head width + 4 floats
+// (16-byte rows).
+__host__ __device__ constexpr int part_stride(int dv) { return dv + 4; }
 
 
 // Bits [pos, pos+nbits) of a little-endian dword array (pos and nbits are
@@ -87,28 +88,46 @@ __device__ __forceinline__ void wave_lds_fence() {
 // V codes of the same ranges into B operands held in registers.  After one
 // barrier every value wave runs its T x 8 value products; the four partial
 // outputs are merged in shared memory and written as one split partial.
-template <int B, int T, bool QBF16>
+// K rows hold GK and V rows GV 128-element groups (head widths 128 GK and
+// 128 GV, which may differ): a score sums its K groups' products, each
+// scaled by that group's norm, and P has one operand per V group (p times
+// that group's norm), the V groups taking their products one after another.
+template <int B, int T, int GK, int GV, bool QBF16>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     const uint8_t *__restrict__ kcodes, const uint16_t *__restrict__ knorms,
     const uint8_t *__restrict__ vcodes, const uint16_t *__restrict__ vnorms, int64_t n_cells,
     int64_t kv_len, const void *__restrict__ q, int n_rep, float qscale, float tau,
     float *__restrict__ ws, int n_split) {
+  constexpr int DV = kGroup * GV;              // output width
   constexpr int KPW = 16 * T;                  // keys per range
   constexpr int KPS = 4 * KPW;                 // keys per split
-  constexpr int ROWW = 4 * B;                  // code dwords per key
-  constexpr int ROWP = ROWW + 1;               // padded LDS row
+  constexpr int GW = 4 * B;                    // code dwords per group
+  constexpr int ROWP = GV * GW + 1;            // padded LDS V row
   constexpr int RPL = ceil_div(KPW, 64);       // V rows per lane
   constexpr int NNORM = ceil_div(KPW, 64);
-  __shared__ __align__(16) uint32_t ptab[PairCfg<B>::WORDS];   // pair table, 64 copies
-  // V rows of the four ranges, plus one spare dword (a lane's two-dword
-  // read of a row may touch the dword after it)
-  __shared__ __align__(16) uint32_t vrows[4 * KPW * ROWP + 1];
-  __shared__ __align__(16) u32x2_t pbuf[4][T][64];          // P operands, per lane
-  __shared__ __align__(16) float nk[4][KPW];
-  __shared__ __align__(16) float nv[4][KPW];
-  __shared__ __align__(16) uint32_t qbuf[4 * 64 * 4];       // query operand, [t][lane][8 halves]
-  __shared__ __align__(16) float obuf[4][8 * kD];
+  constexpr int PSTRIDE = DV + 4;              // floats per split partial
+  // One block of shared memory for the V rows of the four ranges (plus one
+  // spare dword: a lane's two-dword read of a row may touch the dword after
+  // it), the P operands [GV][4][T][64] and the range outputs [4][8][DV].
+  // With two V groups the outputs reuse the bytes of the rows and operands,
+  // dead by then, so that two workgroups still fit one compute unit.
+  constexpr int kRowWords = (4 * KPW * ROWP + 1 + 3) & ~3;
+  constexpr int kPWords = GV * 4 * T * 64 * 2;
+  constexpr int kOutWords = 4 * 8 * DV;
+  constexpr bool kReuse = GV > 1;
+  constexpr int kOutOff = kReuse ? 0 : kRowWords + kPWords;
+  constexpr int kBlockWords = kReuse ? (kRowWords + kPWords > kOutWords ? kRowWords + kPWords : kOutWords)
+                                     : kRowWords + kPWords + kOutWords;
+  // 256-byte aligned: a lookup address is the entry offset OR the lane offset
+  __shared__ __align__(256) uint32_t ptab[PairCfg<B>::WORDS];   // pair table, 64 copies
+  __shared__ __align__(16) uint32_t block[kBlockWords];
+  __shared__ __align__(16) float nk[GK][4][KPW];
+  __shared__ __align__(16) float nv[GV][4][KPW];
+  __shared__ __align__(16) uint32_t qbuf[GK][4 * 64 * 4];   // query operand, [t][lane][8 halves]
   __shared__ float wm[4][8], wl[4][8];
+  uint32_t *vrows = block;
+  u32x2_t *pbuf = reinterpret_cast<u32x2_t *>(block + kRowWords);
+  float *obuf = reinterpret_cast<float *>(block + kOutOff);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -126,61 +145,71 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
 
   if (kwave) {
     // ---------------- key wave: loads first (query, norms, K codes)
-    const uint8_t *kb = kcodes + row0 * (16 * B);
-    const uint16_t *knb = knorms + row0, *vnb = vnorms + row0;
+    const uint8_t *kb = kcodes + row0 * (16 * B * GK);
+    const uint16_t *knb = knorms + row0 * GK, *vnb = vnorms + row0 * GV;
     const int qh = 2 * rg + (lane >> 5), qj = lane & 31;
-    const int64_t qbase = ((int64_t)g * n_rep + imin(qh, n_rep - 1)) * kD + 4 * qj;
-    float qv[4];
-    if constexpr (QBF16) {
-      const u32x2_t b = *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint16_t *>(q) + qbase);
-      qv[0] = __uint_as_float(b.x << 16);
-      qv[1] = __uint_as_float(b.x & 0xffff0000u);
-      qv[2] = __uint_as_float(b.y << 16);
-      qv[3] = __uint_as_float(b.y & 0xffff0000u);
-    } else {
-      const float4 f = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(q) + qbase);
-      qv[0] = f.x; qv[1] = f.y; qv[2] = f.z; qv[3] = f.w;
+    const int64_t qbase = ((int64_t)g * n_rep + imin(qh, n_rep - 1)) * (kGroup * GK) + 4 * qj;
+    float qv[GK][4];
+#pragma unroll
+    for (int gk = 0; gk < GK; ++gk) {
+      if constexpr (QBF16) {
+        const u32x2_t b = *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint16_t *>(q) + qbase +
+                                                             kGroup * gk);
+        qv[gk][0] = __uint_as_float(b.x << 16);
+        qv[gk][1] = __uint_as_float(b.x & 0xffff0000u);
+        qv[gk][2] = __uint_as_float(b.y << 16);
+        qv[gk][3] = __uint_as_float(b.y & 0xffff0000u);
+      } else {
+        const float4 f = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(q) + qbase + kGroup * gk);
+        qv[gk][0] = f.x; qv[gk][1] = f.y; qv[gk][2] = f.z; qv[gk][3] = f.w;
+      }
     }
-    uint16_t kn[NNORM], vn[NNORM];
+    uint16_t kn[NNORM][GK], vn[NNORM][GV];
 #pragma unroll
     for (int i = 0; i < NNORM; ++i) {
       const uint32_t kk = (uint32_t)imin(lane + 64 * i, wlast);
-      kn[i] = knb[kk];
-      vn[i] = vnb[kk];
-    }
-    // lane (col, quad) of tile t reads key 16t + col, dwords B*quad .. B*quad+B-1
-    uint32_t kd[T][B];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const uint32_t off = (uint32_t)imin(16 * t + col, wlast) * (4u * ROWW) + 4u * B * quad;
-      const uint32_t *row = reinterpret_cast<const uint32_t *>(kb + off);
+      for (int gk = 0; gk < GK; ++gk) kn[i][gk] = knb[kk * GK + gk];
 #pragma unroll
-      for (int i = 0; i < B; ++i) kd[t][i] = row[i];
+      for (int gv = 0; gv < GV; ++gv) vn[i][gv] = vnb[kk * GV + gv];
     }
+    // lane (col, quad) of tile t reads key 16t + col, dwords B*quad ..
+    // B*quad+B-1 of each group
+    uint32_t kd[T][GK][B];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int gk = 0; gk < GK; ++gk) {
+        const uint32_t off = (uint32_t)imin(16 * t + col, wlast) * (16u * B * GK) + 16u * B * gk + 4u * B * quad;
+        const uint32_t *row = reinterpret_cast<const uint32_t *>(kb + off);
+#pragma unroll
+        for (int i = 0; i < B; ++i) kd[t][gk][i] = row[i];
+      }
 
     build_pair_table<B, kDecThreads>(ptab, tid);
-    // rotate + split heads 2rg, 2rg+1: thread holds d = 4qj .. 4qj+3 of head
-    // qh; in the MFMA B operand they are slots i = 4(qj&1) .. +3 of K-step
-    // t = (qj>>1)&3 in lane 16*(qj>>3) + qh (high half) and
+    // rotate + split heads 2rg, 2rg+1, group by group: thread holds d = 4qj ..
+    // 4qj+3 of head qh; in the MFMA B operand they are slots i = 4(qj&1) ..
+    // +3 of K-step t = (qj>>1)&3 in lane 16*(qj>>3) + qh (high half) and
     // 16*(qj>>3) + 8 + qh (low half)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) qv[i] = flip_sign(qv[i], sign_bit_of(4 * qj + i));
-    wht128_half(qv, qj);
-    {
+    for (int gk = 0; gk < GK; ++gk) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qv[gk][i] = flip_sign(qv[gk][i], sign_bit_of(4 * qj + i));
+      wht128_half(qv[gk], qj);
       const bool live = qh < n_rep;
       uint32_t hw[2], lw[2];
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        const float x0 = live ? qv[2 * p] * qscale : 0.f;
-        const float x1 = live ? qv[2 * p + 1] * qscale : 0.f;
+        const float x0 = live ? qv[gk][2 * p] * qscale : 0.f;
+        const float x1 = live ? qv[gk][2 * p + 1] * qscale : 0.f;
         const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
         const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
         hw[p] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
         lw[p] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
       }
       const int t = (qj >> 1) & 3, qd = qj >> 3, half_off = 2 * (qj & 1);
-      *reinterpret_cast<u32x2_t *>(qbuf + (t * 64 + 16 * qd + qh) * 4 + half_off) = u32x2_t{hw[0], hw[1]};
-      *reinterpret_cast<u32x2_t *>(qbuf + (t * 64 + 16 * qd + 8 + qh) * 4 + half_off) = u32x2_t{lw[0], lw[1]};
+      *reinterpret_cast<u32x2_t *>(qbuf[gk] + (t * 64 + 16 * qd + qh) * 4 + half_off) = u32x2_t{hw[0], hw[1]};
+      *reinterpret_cast<u32x2_t *>(qbuf[gk] + (t * 64 + 16 * qd + 8 + qh) * 4 + half_off) = u32x2_t{lw[0], lw[1]};
     }
     __syncthreads();   // table and query operand complete
 
@@ -190,16 +219,20 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
       const int kk = lane + 64 * i;
       if (kk < KPW) {
         const bool ok = kk < wkeys;
-        nk[rg][kk] = ok ? half_to_float(kn[i]) : 0.f;
-        nv[rg][kk] = ok ? half_to_float(vn[i]) : 0.f;
+#pragma unroll
+        for (int gk = 0; gk < GK; ++gk) nk[gk][rg][kk] = ok ? half_to_float(kn[i][gk]) : 0.f;
+#pragma unroll
+        for (int gv = 0; gv < GV; ++gv) nv[gv][rg][kk] = ok ? half_to_float(vn[i][gv]) : 0.f;
       }
     }
     // Query operand: column n = lane & 15 -> head n & 7, high (n < 8) or low
     // half; k-slot (lane >> 4, i) of K-step t <-> element d = 32*(lane>>4) + 8t + i.
-    half8_t qb[4];
+    half8_t qb[GK][4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      qb[t] = __builtin_bit_cast(half8_t, reinterpret_cast<const u32x4_t *>(qbuf)[t * 64 + lane]);
+    for (int gk = 0; gk < GK; ++gk)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        qb[gk][t] = __builtin_bit_cast(half8_t, reinterpret_cast<const u32x4_t *>(qbuf[gk])[t * 64 + lane]);
     wave_lds_fence();
 
     // ---- scores: S^T[key][col] over the range, tile by tile
@@ -207,19 +240,25 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     float sc[T][4];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      uint32_t a16[16];
-      decode_pairs<B, 32>(kd[t], tab, a16);
-      float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const u32x4_t av = {a16[4 * st], a16[4 * st + 1], a16[4 * st + 2], a16[4 * st + 3]};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[st], acc,
-                                                    0, 0, 0);
+      for (int gk = 0; gk < GK; ++gk) {
+        uint32_t a16[16];
+        decode_pairs<B, 32>(kd[t][gk], tab, a16);
+        float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const u32x4_t av = {a16[4 * st], a16[4 * st + 1], a16[4 * st + 2], a16[4 * st + 3]};
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[gk][st], acc,
+                                                      0, 0, 0);
+        }
+        const float4 n4 = *reinterpret_cast<const float4 *>(&nk[gk][rg][16 * t + 4 * quad]);
+        const float nkv[4] = {n4.x, n4.y, n4.z, n4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = (acc[i] + xor_lane<8>(acc[i])) * nkv[i];
+          sc[t][i] = gk == 0 ? x : sc[t][i] + x;
+        }
       }
-      const float4 n4 = *reinterpret_cast<const float4 *>(&nk[rg][16 * t + 4 * quad]);
-      const float nkv[4] = {n4.x, n4.y, n4.z, n4.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sc[t][i] = (acc[i] + xor_lane<8>(acc[i])) * nkv[i];
     }
     if (wkeys < KPW) {   // wave-uniform: only a ragged last range masks
 #pragma unroll
@@ -238,8 +277,8 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     mx = max_xor32(mx);
     const float msafe = mx == -INFINITY ? 0.f : mx;
 
-    // ---- P operand: the score layout (lane = column + 16 * key quad) is the
-    //      A-operand layout of the value product.  Rows < 8 carry the
+    // ---- P operands: the score layout (lane = column + 16 * key quad) is
+    //      the A-operand layout of the value product.  Rows < 8 carry the
     //      float16 high part of p * vnorm, rows >= 8 the low part:
     //      x - hi * lo_sel (lo_sel = 1 on low rows, 0 on high rows) is exact
     //      in float32 and rounds once to float16.  Sparse V ([PR36] (d) item
@@ -249,18 +288,25 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     float lsum = 0.f;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      const float4 n4 = *reinterpret_cast<const float4 *>(&nv[rg][16 * t + 4 * quad]);
-      const float nvv[4] = {n4.x, n4.y, n4.z, n4.w};
-      half4_t pa;
+      float p[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(sc[t][i] - msafe);
-        lsum += p;
-        const float x = p < tau ? 0.f : p * nvv[i];
-        const _Float16 h = (_Float16)x;
-        pa[i] = (_Float16)__builtin_fmaf(-(float)h, lo_sel, x);
+        p[i] = __builtin_amdgcn_exp2f(sc[t][i] - msafe);
+        lsum += p[i];
       }
-      pbuf[rg][t][lane] = __builtin_bit_cast(u32x2_t, pa);
+#pragma unroll
+      for (int gv = 0; gv < GV; ++gv) {
+        const float4 n4 = *reinterpret_cast<const float4 *>(&nv[gv][rg][16 * t + 4 * quad]);
+        const float nvv[4] = {n4.x, n4.y, n4.z, n4.w};
+        half4_t pa;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = p[i] < tau ? 0.f : p[i] * nvv[i];
+          const _Float16 h = (_Float16)x;
+          pa[i] = (_Float16)__builtin_fmaf(-(float)h, lo_sel, x);
+        }
+        pbuf[((gv * 4 + rg) * T + t) * 64 + lane] = __builtin_bit_cast(u32x2_t, pa);
+      }
     }
     lsum += xor_lane<16>(lsum);
     lsum = sum_xor32(lsum);
@@ -269,17 +315,18 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
       wl[rg][lane] = lsum;
     }
     __syncthreads();   // P operands complete
+    if constexpr (kReuse) __syncthreads();   // V rows and P operands consumed
     __syncthreads();   // value products done (partial outputs in obuf)
   } else {
     // ---------------- value wave: V rows (lane r loads rows r, r + 64, ...)
-    const uint8_t *vb = vcodes + row0 * (16 * B);
-    u32x4_t vraw[RPL][B];
+    const uint8_t *vb = vcodes + row0 * (16 * B * GV);
+    u32x4_t vraw[RPL][GV * B];
 #pragma unroll
     for (int j = 0; j < RPL; ++j)
 #pragma unroll
-      for (int i = 0; i < B; ++i)
+      for (int i = 0; i < GV * B; ++i)
         vraw[j][i] = *reinterpret_cast<const u32x4_t *>(
-            vb + (uint32_t)imin(lane + 64 * j, wlast) * (16u * B) + 16u * i);
+            vb + (uint32_t)imin(lane + 64 * j, wlast) * (16u * B * GV) + 16u * i);
     build_pair_table<B, kDecThreads>(ptab, tid);
     __syncthreads();   // table and query operand complete
 
@@ -290,7 +337,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
       if (r < KPW) {
         uint32_t *d = vr + r * ROWP;
 #pragma unroll
-        for (int i = 0; i < B; ++i) {
+        for (int i = 0; i < GV * B; ++i) {
           d[4 * i] = vraw[j][i].x;
           d[4 * i + 1] = vraw[j][i].y;
           d[4 * i + 2] = vraw[j][i].z;
@@ -305,95 +352,114 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     constexpr int VBITS = 8 * B;
     const int vpos = VBITS * col;
     const int vw0 = vpos >> 5, vsh = vpos & 31;
-    const uint32_t *vlane = vr + 4 * quad * ROWP + vw0;
     const uint32_t *tab = ptab + lane;
-    u32x2_t vbop[T][8];
+    // after the swap, lanes 0-31 hold d-tiles 0-3 and lanes 32-63 d-tiles
+    // 4-7, each as high + low; row (head) 4*((lane&31)>>4) + i
+    const int qd = (lane & 31) >> 4, dhi = lane >> 5;
+    float4 res[GV][4];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      uint32_t vv[4][4];
+    for (int gv = 0; gv < GV; ++gv) {
+      const uint32_t *vlane = vr + 4 * quad * ROWP + GW * gv + vw0;
+      u32x2_t vbop[T][8];
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        uint32_t vv[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t *row = vlane + (16 * t + i) * ROWP;
+          const uint32_t run[1] = {__builtin_amdgcn_alignbit(row[1], row[0], vsh)};
+          decode_pairs<B, 8>(run, tab, vv[i]);
+        }
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const int w = dt >> 1;
+          const uint32_t sel = (dt & 1) ? 0x07060302u : 0x05040100u;
+          vbop[t][dt] = u32x2_t{__builtin_amdgcn_perm(vv[1][w], vv[0][w], sel),
+                                __builtin_amdgcn_perm(vv[3][w], vv[2][w], sel)};
+        }
+      }
+      if (gv == 0) __syncthreads();   // P operands complete
+
+      float4_t o[8];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const half4_t pa = __builtin_bit_cast(half4_t, pbuf[((gv * 4 + rg) * T + t) * 64 + lane]);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(half4_t, vbop[t][dt]),
+                                                       o[dt], 0, 0, 0);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t *row = vlane + (16 * t + i) * ROWP;
-        const uint32_t run[1] = {__builtin_amdgcn_alignbit(row[1], row[0], vsh)};
-        decode_pairs<B, 8>(run, tab, vv[i]);
-      }
+        float oc[4];
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const int w = dt >> 1;
-        const uint32_t sel = (dt & 1) ? 0x07060302u : 0x05040100u;
-        vbop[t][dt] = u32x2_t{__builtin_amdgcn_perm(vv[1][w], vv[0][w], sel),
-                              __builtin_amdgcn_perm(vv[3][w], vv[2][w], sel)};
+        for (int dt = 0; dt < 4; ++dt) {
+          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(o[dt][i]),
+                                                          __float_as_uint(o[dt + 4][i]), false, false);
+          oc[dt] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+        res[gv][i] = make_float4(oc[0], oc[1], oc[2], oc[3]);
       }
     }
-    __syncthreads();   // P operands complete
-
-    float4_t o[8];
+    if constexpr (kReuse) __syncthreads();   // V rows and P operands consumed
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int gv = 0; gv < GV; ++gv)
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const half4_t pa = __builtin_bit_cast(half4_t, pbuf[rg][t][lane]);
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(half4_t, vbop[t][dt]),
-                                                     o[dt], 0, 0, 0);
-    }
-    // combine high/low rows: after the swap, lanes 0-31 hold d-tiles 0-3 and
-    // lanes 32-63 d-tiles 4-7, each as high + low; row (head) 4*((lane&31)>>4) + i
-    const int qd = (lane & 31) >> 4, dhi = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float oc[4];
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(o[dt][i]),
-                                                        __float_as_uint(o[dt + 4][i]), false, false);
-        oc[dt] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-      }
-      *reinterpret_cast<float4 *>(&obuf[rg][(4 * qd + i) * kD + 8 * col + 4 * dhi]) =
-          make_float4(oc[0], oc[1], oc[2], oc[3]);
-    }
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<float4 *>(&obuf[(rg * 8 + 4 * qd + i) * DV + kGroup * gv + 8 * col + 4 * dhi]) =
+            res[gv][i];
     __syncthreads();   // value products done (partial outputs in obuf)
   }
 
-  // ---- merge the four ranges: obuf[r][h][8c + t] holds element d = 8c + t
-  //      of head h, relative to the range's own max
-  float *part = ws + ((int64_t)g * n_rep * n_split + s) * kPartStride;
+  // ---- merge the four ranges: obuf[r][h][128gv + 8c + t] holds element
+  //      8c + t of group gv of head h, relative to the range's own max
+  float *part = ws + ((int64_t)g * n_rep * n_split + s) * PSTRIDE;
   {
     const int h = tid >> 6, d = 2 * (tid & 63);
     if (h < n_rep) {
       const float M = fmaxf(fmaxf(wm[0][h], wm[1][h]), fmaxf(wm[2][h], wm[3][h]));
-      float a0 = 0.f, a1 = 0.f, L = 0.f;
+      float f[4], L = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float mr = wm[r][h];
-        const float f = mr == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mr - M);
-        const float2 v = *reinterpret_cast<const float2 *>(&obuf[r][h * kD + d]);
-        a0 += f * v.x;
-        a1 += f * v.y;
-        L += f * wl[r][h];
+        f[r] = mr == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mr - M);
+        L += f[r] * wl[r][h];
       }
-      float *ph = part + (int64_t)h * n_split * kPartStride;
-      *reinterpret_cast<float2 *>(ph + d) = make_float2(a0, a1);
-      if (d == 0) *reinterpret_cast<float2 *>(ph + kD) = make_float2(M, L);
+      float *ph = part + (int64_t)h * n_split * PSTRIDE;
+#pragma unroll
+      for (int gv = 0; gv < GV; ++gv) {
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float2 v = *reinterpret_cast<const float2 *>(&obuf[(r * 8 + h) * DV + kGroup * gv + d]);
+          a0 += f[r] * v.x;
+          a1 += f[r] * v.y;
+        }
+        *reinterpret_cast<float2 *>(ph + kGroup * gv + d) = make_float2(a0, a1);
+      }
+      if (d == 0) *reinterpret_cast<float2 *>(ph + DV) = make_float2(M, L);
     }
   }
 }
 
-// Merge the split partials of one query head, undo the rotation and write the
+// Merge the split partials of one 128-element group (blockIdx.y) of one
+// query head (blockIdx.x), undo the rotation and write that part of the
 // float32 output row: out = s (.) H O / (128 L).  Sixteen 32-lane groups
 // share the splits (s = group mod 16), each with its own running max; lane j
-// owns elements 4j..4j+3.
+// owns elements 4j..4j+3.  dv is the output width (128 x gridDim.y).
 constexpr int kMergeThreads = 512;
 constexpr int kMergeGroups = kMergeThreads / 32;
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float *__restrict__ ws,
-                                                                     int n_split,
+                                                                     int n_split, int dv,
                                                                      float *__restrict__ out) {
   __shared__ float4 obuf[kMergeGroups][32];
   __shared__ float lbuf[kMergeGroups], mbuf[kMergeGroups];
-  const int h = blockIdx.x, tid = threadIdx.x;
+  const int h = blockIdx.x, og = blockIdx.y, tid = threadIdx.x;
   const int grp = tid >> 5, j = tid & 31;
-  const float *part = ws + (int64_t)h * n_split * kPartStride;
+  const int pstride = part_stride(dv);
+  const float *part = ws + (int64_t)h * n_split * pstride;
   float mg = -INFINITY, L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   // batches of 8 splits per group, every load of a batch issued before the
@@ -407,9 +473,9 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
     for (int i = 0; i < kBatch; ++i) {
       const int s = s0 + i * kMergeGroups;
       if (s < n_split) {
-        const float *p = part + (int64_t)s * kPartStride;
-        ml[i] = *reinterpret_cast<const float2 *>(p + kD);
-        v[i] = reinterpret_cast<const float4 *>(p)[j];
+        const float *p = part + (int64_t)s * pstride;
+        ml[i] = *reinterpret_cast<const float2 *>(p + dv);
+        v[i] = reinterpret_cast<const float4 *>(p + kGroup * og)[j];
       }
     }
 #pragma unroll
@@ -452,7 +518,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
   res.y = flip_sign(u[1] * r, sign_bit_of(4 * j + 1));
   res.z = flip_sign(u[2] * r, sign_bit_of(4 * j + 2));
   res.w = flip_sign(u[3] * r, sign_bit_of(4 * j + 3));
-  reinterpret_cast<float4 *>(out + (int64_t)h * kD)[j] = res;
+  reinterpret_cast<float4 *>(out + (int64_t)h * dv + kGroup * og)[j] = res;
 }
 
 // ---------------------------------------------------------------- host side
@@ -475,16 +541,21 @@ hipError_t device_cu_count(int *n_cu) {
   return hipSuccess;
 }
 
-hipError_t plan_decode(const tq_cache &k, int64_t kv_len, int32_t n_q_heads, DecodePlan *p) {
+hipError_t plan_decode(const tq_cache &k, const tq_cache &v, int64_t kv_len, int32_t n_q_heads,
+                       DecodePlan *p) {
   int n_cu = 0;
   hipError_t e = device_cu_count(&n_cu);
   if (e != hipSuccess) return e;
-  // largest tile count (<= 4 per key range) that still gives every compute
-  // unit two workgroups; a split covers 4 ranges of 16 * tiles keys
-  int tpw = 4;
+  // a split covers 4 ranges of 16 * tiles keys.  Tiles per range: the most
+  // (1, 2, 4 or 8) with at most 16 group-tiles per range (tiles x (K groups
+  // + V groups)) that still give every compute unit a workgroup.  Measured:
+  // fewer, larger workgroups cost less setup and fewer split partials, up to
+  // the point where a range's registers and shared memory run short.
+  const int groups = k.head_dim / kGroup + v.head_dim / kGroup;
+  int tpw = 8;
   while (tpw > 1) {
     const int64_t splits = ceil_div<int64_t>(kv_len, 64LL * tpw);
-    if (splits * k.n_kv_heads >= 2LL * n_cu) break;
+    if (tpw * groups <= 16 && splits * k.n_kv_heads >= n_cu) break;
     tpw >>= 1;
   }
   p->tiles_per_wave = tpw;
@@ -492,55 +563,94 @@ hipError_t plan_decode(const tq_cache &k, int64_t kv_len, int32_t n_q_heads, Dec
   const int64_t n_split = ceil_div<int64_t>(kv_len, p->keys_per_split);
   if (n_split > 0x7fffffff) return hipErrorInvalidValue;
   p->n_split = (int)n_split;
-  const size_t bytes = (size_t)n_q_heads * (size_t)n_split * kPartStride * sizeof(float);
+  const size_t bytes = (size_t)n_q_heads * (size_t)n_split * part_stride(v.head_dim) * sizeof(float);
   p->workspace_bytes = (bytes + 255) & ~(size_t)255;
   return hipSuccess;
 }
 
-template <int B, bool QBF>
-static void launch_split(int tpw, dim3 grid, hipStream_t st, const tq_cache &k,
-                         const tq_cache &v, int64_t kv_len, const void *q, int n_rep, float qs,
-                         float tau, float *ws, int n_split) {
+namespace {
+
+struct SplitArgs {
+  const tq_cache *k, *v;
+  int64_t kv_len;
+  const void *q;
+  int n_rep;
+  float qs, tau;
+  float *ws;
+  int n_split;
+};
+
+// Tile counts the plan can choose for GK + GV groups (8 only for one group
+// each: the ranges of wider heads would not fit the registers and LDS).
+template <int B, int GK, int GV, bool QBF>
+hipError_t launch_split(int tpw, dim3 grid, hipStream_t st, const SplitArgs &a) {
   dim3 block(kDecThreads);
-#define TQ_DEC(T)                                                                             \
-  hipLaunchKernelGGL((decode_split_kernel<B, T, QBF>), grid, block, 0, st, k.codes, k.norms, \
-                     v.codes, v.norms, k.n_cells, kv_len, q, n_rep, qs, tau, ws, n_split)
+#define TQ_DEC(T)                                                                                  \
+  hipLaunchKernelGGL((decode_split_kernel<B, T, GK, GV, QBF>), grid, block, 0, st, a.k->codes,    \
+                     a.k->norms, a.v->codes, a.v->norms, a.k->n_cells, a.kv_len, a.q, a.n_rep,    \
+                     a.qs, a.tau, a.ws, a.n_split)
   switch (tpw) {
     case 1: TQ_DEC(1); break;
     case 2: TQ_DEC(2); break;
     case 4: TQ_DEC(4); break;
-    default: TQ_DEC(8); break;
+    case 8:
+      if constexpr (GK + GV == 2) {
+        TQ_DEC(8);
+        break;
+      } else {
+        return hipErrorNotSupported;
+      }
+    default: return hipErrorNotSupported;
   }
 #undef TQ_DEC
+  return hipSuccess;
+}
+
+template <int B, int GK, int GV>
+hipError_t launch_split_q(int qbf, int tpw, dim3 grid, hipStream_t st, const SplitArgs &a) {
+  return qbf ? launch_split<B, GK, GV, true>(tpw, grid, st, a) : launch_split<B, GK, GV, false>(tpw, grid, st, a);
 }
 
 template <int B>
-static void launch_split_q(int qbf, int tpw, dim3 grid, hipStream_t st, const tq_cache &k,
-                           const tq_cache &v, int64_t kv_len, const void *q, int n_rep, float qs,
-                           float tau, float *ws, int n_split) {
-  if (qbf) launch_split<B, true>(tpw, grid, st, k, v, kv_len, q, n_rep, qs, tau, ws, n_split);
-  else launch_split<B, false>(tpw, grid, st, k, v, kv_len, q, n_rep, qs, tau, ws, n_split);
+hipError_t launch_split_dims(int gk, int gv, int qbf, int tpw, dim3 grid, hipStream_t st, const SplitArgs &a) {
+  if (gk == 1 && gv == 1) return launch_split_q<B, 1, 1>(qbf, tpw, grid, st, a);
+  if (gk == 2 && gv == 2) return launch_split_q<B, 2, 2>(qbf, tpw, grid, st, a);
+  if (gk == 2) return launch_split_q<B, 2, 1>(qbf, tpw, grid, st, a);
+  return launch_split_q<B, 1, 2>(qbf, tpw, grid, st, a);
 }
+
+}  // namespace
 
 hipError_t launch_decode(const tq_cache &k, const tq_cache &v, int64_t kv_len, const void *q,
                          int q_dtype, int32_t n_q_heads, float scale, float sparse_v_tau,
                          float *out, void *workspace, const DecodePlan &p, hipStream_t stream) {
-  const int n_rep = n_q_heads / k.n_kv_heads;
+  const int gk = k.head_dim / kGroup, gv = v.head_dim / kGroup;
+  if (gk < 1 || gk > 2 || gv < 1 || gv > 2 || k.type != v.type) return hipErrorNotSupported;
+  SplitArgs a;
+  a.k = &k;
+  a.v = &v;
+  a.kv_len = kv_len;
+  a.q = q;
+  a.n_rep = n_q_heads / k.n_kv_heads;
   // scores in the log2 domain: scale * log2(e), and 1/128 for the two
   // 1/sqrt(128) factors of the rotated query and the rotated levels
-  const float qs = scale * 1.4426950408889634f / 128.0f;
-  float *ws = reinterpret_cast<float *>(workspace);
+  a.qs = scale * 1.4426950408889634f / 128.0f;
+  a.tau = sparse_v_tau;
+  a.ws = reinterpret_cast<float *>(workspace);
+  a.n_split = p.n_split;
   dim3 grid(p.n_split, k.n_kv_heads);
   const int qbf = q_dtype == TQ_BF16 ? 1 : 0;
+  hipError_t e;
   switch (k.type) {
-    case TQ_TURBO2: launch_split_q<2>(qbf, p.tiles_per_wave, grid, stream, k, v, kv_len, q, n_rep, qs, sparse_v_tau, ws, p.n_split); break;
-    case TQ_TURBO3: launch_split_q<3>(qbf, p.tiles_per_wave, grid, stream, k, v, kv_len, q, n_rep, qs, sparse_v_tau, ws, p.n_split); break;
-    default: launch_split_q<4>(qbf, p.tiles_per_wave, grid, stream, k, v, kv_len, q, n_rep, qs, sparse_v_tau, ws, p.n_split); break;
+    case TQ_TURBO2: e = launch_split_dims<2>(gk, gv, qbf, p.tiles_per_wave, grid, stream, a); break;
+    case TQ_TURBO3: e = launch_split_dims<3>(gk, gv, qbf, p.tiles_per_wave, grid, stream, a); break;
+    default: e = launch_split_dims<4>(gk, gv, qbf, p.tiles_per_wave, grid, stream, a); break;
   }
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(n_q_heads), dim3(kMergeThreads), 0, stream, ws,
-                     p.n_split, out);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(n_q_heads, gv), dim3(kMergeThreads), 0, stream, a.ws,
+                     p.n_split, v.head_dim, out);
   return hipGetLastError();
 }
 

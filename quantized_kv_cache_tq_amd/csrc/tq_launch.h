@@ -21,7 +21,8 @@ struct DecodePlan {
   int n_split;           // workgroups per kv head
   size_t workspace_bytes;
 };
-hipError_t plan_decode(const tq_cache &k, int64_t kv_len, int32_t n_q_heads, DecodePlan *p);
+hipError_t plan_decode(const tq_cache &k, const tq_cache &v, int64_t kv_len, int32_t n_q_heads,
+                       DecodePlan *p);
 hipError_t launch_decode(const tq_cache &k, const tq_cache &v, int64_t kv_len, const void *q,
                          int q_dtype, int32_t n_q_heads, float scale, float sparse_v_tau,
                          float *out, void *workspace, const DecodePlan &p, hipStream_t stream);

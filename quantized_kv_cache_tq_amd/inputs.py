@@ -29,26 +29,32 @@ def normal(rng: np.random.Generator, shape) -> np.ndarray:
     return rng.standard_normal(shape, dtype=np.float64).astype(np.float32)
 
 
-def small_decode(seed: int = 0, kv_len: int = 256, n_q: int = 1, n_kv: int = 1, d: int = 128):
-    """turbo quantize+decode smoke shape: Q [n_q, d], K and V [kv_len, n_kv, d], iid N(0,1)."""
+def small_decode(seed: int = 0, kv_len: int = 256, n_q: int = 1, n_kv: int = 1, d: int = 128,
+                 dv: int | None = None):
+    """turbo quantize+decode smoke shape: Q [n_q, d], K [kv_len, n_kv, d] and
+    V [kv_len, n_kv, dv] (dv = d unless given), iid N(0,1)."""
+    dv = d if dv is None else dv
     rng = np.random.default_rng(seed)
     q = normal(rng, (n_q, d))
     k = normal(rng, (kv_len, n_kv, d))
-    v = normal(rng, (kv_len, n_kv, d))
+    v = normal(rng, (kv_len, n_kv, dv))
     return q, k, v
 
 
-def outlier_decode(seed: int = 0, kv_len: int = 32768, n_q: int = 32, n_kv: int = 4, d: int = 128):
+def outlier_decode(seed: int = 0, kv_len: int = 32768, n_q: int = 32, n_kv: int = 4, d: int = 128,
+                   dv: int | None = None):
     """GQA decode with outlier channels.
 
-    sigma_K, sigma_V = exp(N(0,1)) per (kv head, channel); K = N(0,1) * sigma_K,
-    V = N(0,1) * sigma_V, shape [kv_len, n_kv, d]; Q = bf16(N(0,1)) [n_q, d].
+    sigma_K = exp(N(0,1)) per (kv head, channel) [n_kv, d], sigma_V likewise
+    [n_kv, dv]; K = N(0,1) * sigma_K [kv_len, n_kv, d], V = N(0,1) * sigma_V
+    [kv_len, n_kv, dv] (dv = d unless given); Q = bf16(N(0,1)) [n_q, d].
     """
+    dv = d if dv is None else dv
     rng = np.random.default_rng(seed)
     sk = np.exp(rng.standard_normal((n_kv, d))).astype(np.float32)
-    sv = np.exp(rng.standard_normal((n_kv, d))).astype(np.float32)
+    sv = np.exp(rng.standard_normal((n_kv, dv))).astype(np.float32)
     k = (normal(rng, (kv_len, n_kv, d)) * sk[None]).astype(np.float32)
-    v = (normal(rng, (kv_len, n_kv, d)) * sv[None]).astype(np.float32)
+    v = (normal(rng, (kv_len, n_kv, dv)) * sv[None]).astype(np.float32)
     q = bf16_round(normal(rng, (n_q, d)))
     return q, k, v
 

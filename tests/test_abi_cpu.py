@@ -115,7 +115,10 @@ def test_decode_rejects_bad_arguments():
     assert call(nq=36 * 4) == -2                  # 36 q heads per kv head: no kernel
     assert call(v=_cache(b, type_=2)) == -1       # K and V types differ
     assert call(v=_cache(b, n_kv=2)) == -1
-    assert call(k=_cache(b, head_dim=256), v=_cache(b, head_dim=256)) == -2
+    assert call(k=_cache(b, head_dim=384), v=_cache(b, head_dim=384)) == -2   # 3 groups: no kernel
+    assert call(v=_cache(b, head_dim=384)) == -2
+    assert call(v=_cache(b, n_cells=101)) == -1   # K and V address cells alike
+    assert call(v=_cache(b, head_dim=256, type_=4)) == -1
     assert call(q=None) == -1
     assert call(q=FAKE + 2) == -1
     assert call(out=FAKE + 8) == -1
@@ -123,6 +126,21 @@ def test_decode_rejects_bad_arguments():
     assert call(sc=float("nan")) == -1
     assert call(tau=-1.0) == -1
     assert call(tau=float('nan')) == -1
+
+
+@needs_lib
+def test_decode_workspace_rejects_bad_arguments():
+    from quantized_kv_cache_tq_amd import binding as b
+    lib = b.load_library()
+    k, v = _cache(b), _cache(b, head_dim=256)
+    n = ctypes.c_size_t()
+    ws = lambda k=k, v=v, kv=50, nq=32, out=ctypes.byref(n): lib.tq_attn_decode_workspace(
+        ctypes.byref(k) if k is not None else None, ctypes.byref(v) if v is not None else None, kv, nq, out)
+    assert ws(v=None) == -1
+    assert ws(out=None) == -1
+    assert ws(kv=0) == -1
+    assert ws(v=_cache(b, n_kv=2)) == -1
+    assert ws(v=_cache(b, head_dim=512)) == -2
 
 
 @needs_lib
@@ -137,6 +155,8 @@ def test_prefill_rejects_bad_arguments():
     assert call(nrows=-1) == -1
     assert call(kv=2048) == -1
     assert call(nq=12) == -1
+    assert call(v=_cache(b, head_dim=256, n_kv=8, n_cells=2048)) == -1   # n_cells differ
+    assert call(v=_cache(b, head_dim=128, n_kv=8, n_cells=1024)) == -1   # widths differ
     d384 = _cache(b, head_dim=384, n_kv=8, n_cells=1024)
     assert call(k=d384, v=d384) == -2             # head_dim 384: no kernel
     d128 = _cache(b, head_dim=128, n_kv=8, n_cells=1024)

@@ -21,17 +21,31 @@ def _caches(bits, k, v, kv_len=None):
     from quantized_kv_cache_tq_amd import binding as b
     from gpu_util import cuda
     n_rows, n_kv, d = k.shape
+    dv = v.shape[2]
     idx = np.arange(n_rows)
-    kc, vc = b.new_cache(bits, d, n_kv, n_rows), b.new_cache(bits, d, n_kv, n_rows)
+    kc, vc = b.new_cache(bits, d, n_kv, n_rows), b.new_cache(bits, dv, n_kv, n_rows)
     b.tq_set_rows(kc, cuda(k), cuda(idx))
     b.tq_set_rows(vc, cuda(v), cuda(idx))
-    ok, ov = o.new_cache(bits, d, n_kv, n_rows), o.new_cache(bits, d, n_kv, n_rows)
+    ok, ov = o.new_cache(bits, d, n_kv, n_rows), o.new_cache(bits, dv, n_kv, n_rows)
     o.set_rows(ok, k, idx)
     o.set_rows(ov, v, idx)
     torch.cuda.synchronize()
     assert np.array_equal(kc.codes.cpu().numpy(), ok["codes"])
     assert np.array_equal(vc.codes.cpu().numpy(), ov["codes"])
     return kc, vc, ok, ov
+
+
+def _plan_block(kv, n_kv, dk, dv):
+    """Keys one wave scores (16 T), T as tq.h states the plan picks it: the
+    largest of 8, 4, 2, 1 with T (dk + dv) / 128 <= 16 and at least one
+    workgroup per compute unit."""
+    import torch
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    groups = (dk + dv) // 128
+    tpw = 8
+    while tpw > 1 and not (tpw * groups <= 16 and -(-kv // (64 * tpw)) * n_kv >= n_cu):
+        tpw //= 2
+    return 16 * tpw
 
 
 def _run(bits, q, k, v, kv_len, q_bf16=False, what=""):
@@ -41,7 +55,8 @@ def _run(bits, q, k, v, kv_len, q_bf16=False, what=""):
     d = q.shape[1]
     scale = 1.0 / math.sqrt(d)
     kc, vc, ok, ov = _caches(bits, k, v)
-    print(f"[decode] {what} bits={bits} n_q={q.shape[0]} n_kv={k.shape[1]} kv={kv_len}", flush=True)
+    print(f"[decode] {what} bits={bits} n_q={q.shape[0]} n_kv={k.shape[1]} kv={kv_len} "
+          f"dk={k.shape[2]} dv={v.shape[2]}", flush=True)
     qt = bf16_cuda(q) if q_bf16 else cuda(q)
     got = b.tq_attn_decode(kc, vc, kv_len, qt, scale)
     torch.cuda.synchronize()
@@ -102,7 +117,7 @@ def test_shared_workspace_across_lengths():
     scale = 1.0 / math.sqrt(q.shape[1])
     lens = [32768, 1000, 17, 32768, 4097]
     fresh = {n: b.tq_attn_decode(kc, vc, n, qt, scale).cpu().numpy() for n in set(lens)}
-    nbytes = max(b.tq_attn_decode_workspace(kc, n, q.shape[0]) for n in lens)
+    nbytes = max(b.tq_attn_decode_workspace(kc, vc, n, q.shape[0]) for n in lens)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     for n in lens:
         got = b.tq_attn_decode(kc, vc, n, qt, scale, workspace=ws).cpu().numpy()
@@ -151,14 +166,10 @@ def test_sparse_v_within_bound(bits, tau):
     assert np.all(err <= bound + 2e-3), (err - bound).max()
     # tight check: the kernel's own rule, a skip against the maximum of each
     # block of keys one wave scores (16 * tiles-per-wave keys, from the plan)
-    import torch
-    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
-    tpw = 4
-    while tpw > 1 and -(-kv // (64 * tpw)) * k.shape[1] < 2 * n_cu:
-        tpw //= 2
-    want = o.attn_decode_sparse_v(ok, ov, kv, q.astype(np.float64), scale, tau, ref_block=16 * tpw)
+    block = _plan_block(kv, k.shape[1], k.shape[2], v.shape[2])
+    want = o.attn_decode_sparse_v(ok, ov, kv, q.astype(np.float64), scale, tau, ref_block=block)
     from gpu_util import assert_attention_close
-    assert_attention_close(got, want, what=f"sparse-V block rule, block {16 * tpw}")
+    assert_attention_close(got, want, what=f"sparse-V block rule, block {block}")
 
 
 def test_sparse_v_limits_on_gpu():
@@ -175,3 +186,59 @@ def test_sparse_v_limits_on_gpu():
     np.testing.assert_array_equal(zero_tau, dense)
     allskip = b.tq_attn_decode(kc, vc, 3000, qt, scale, sparse_v_tau=2.0).cpu().numpy()
     assert np.all(allskip == 0)
+
+
+# ---------------------------------------------------------------- head widths
+
+@pytest.mark.parametrize("dk,dv", [(256, 256), (256, 128), (128, 256)])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_head_widths(bits, dk, dv):
+    """K and V heads of 128 or 256 elements, equal or not ([PR36] (b): the
+    decode kernel takes a 256-wide K beside a 128-wide V natively), GQA 8
+    over 5000 keys (several splits and a ragged last range)."""
+    q, k, v = inputs.outlier_decode(seed=20 + bits, kv_len=5000, n_q=16, n_kv=2, d=dk, dv=dv)
+    (ma, rl), got = _run(bits, q, k, v, 4999, q_bf16=True, what=f"widths {dk}/{dv}")
+    assert got.shape == (16, dv)
+    print(f"    max_abs={ma:.3g} rel_l2={rl:.3g}")
+
+
+@pytest.mark.parametrize("dk,dv", [(256, 256), (256, 128)])
+@pytest.mark.parametrize("kv_len,n_q,n_kv", [(1, 1, 1), (17, 4, 2), (65, 8, 8), (1000, 12, 3), (4097, 8, 1)])
+def test_head_widths_ragged(dk, dv, kv_len, n_q, n_kv):
+    q, k, v = inputs.small_decode(seed=kv_len + n_q, kv_len=4100, n_q=n_q, n_kv=n_kv, d=dk, dv=dv)
+    _run(3, q, k, v, kv_len, what=f"widths {dk}/{dv} ragged")
+
+
+def test_padded_192_key_heads():
+    """The case of [PR36] (b): 192-wide K heads zero-padded to 256 (query
+    padded the same way) beside 128-wide V heads, turbo3, 32K keys."""
+    q, k, v = inputs.outlier_decode(seed=30, kv_len=32768, n_q=16, n_kv=2, d=256, dv=128)
+    k[:, :, 192:] = 0.0
+    q[:, 192:] = 0.0
+    (ma, rl), _ = _run(3, q, k, v, 32768, q_bf16=True, what="K 192->256 / V 128")
+    print(f"    max_abs={ma:.3g} rel_l2={rl:.3g}")
+
+
+
+
+@pytest.mark.parametrize("dk,dv,tau", [(256, 256, 5e-3), (256, 128, 5e-3), (256, 256, 0.05)])
+def test_sparse_v_wide_heads(dk, dv, tau):
+    """Sparse V with two-group heads: within the oracle's bound of the dense
+    output, and at the normal bar against the block-reference emulation."""
+    from quantized_kv_cache_tq_amd import binding as b
+    from gpu_util import assert_attention_close, bf16_cuda
+    kv = 8192
+    q, k, v = inputs.outlier_decode(seed=31, kv_len=kv, n_q=16, n_kv=2, d=dk, dv=dv)
+    kc, vc, ok, ov = _caches(3, k, v)
+    scale = 1.0 / math.sqrt(dk)
+    print(f"[decode] sparse-V widths {dk}/{dv} tau={tau} kv={kv}", flush=True)
+    got = b.tq_attn_decode(kc, vc, kv, bf16_cuda(q), scale, sparse_v_tau=tau).cpu().numpy()
+    qd = q.astype(np.float64)
+    dense = o.attn_decode(ok, ov, kv, qd, scale)
+    bound, n_t = o.sparse_v_bound(ok, ov, kv, qd, scale, tau)
+    err = np.abs(got - dense).max(axis=1)
+    assert n_t.sum() > 0
+    assert np.all(err <= bound + 2e-3), (err - bound).max()
+    block = _plan_block(kv, k.shape[1], dk, dv)
+    want = o.attn_decode_sparse_v(ok, ov, kv, qd, scale, tau, ref_block=block)
+    assert_attention_close(got, want, what=f"sparse-V {dk}/{dv} block rule, block {block}")
