@@ -41,14 +41,14 @@ FP32_PEAK_TFLOPS = 157.3
 # `rocprofv3 --pmc` passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) over
 # `bench.py --no-cpu-baseline --only decode,copy --steps 2 --warmup 1`, each
 # scaled by what the same counter reads for the 256 MiB device copy of that
-# run (FETCH_SIZE reads 131093.2 KiB for 262144 KiB copied: x1.99969;
+# run (FETCH_SIZE reads 131088.5 KiB for 262144 KiB copied: x1.99975;
 # WRITE_SIZE reads 262144 KiB: x1.0).  Valid only for the decode sources it
 # was taken on (sha256 of tq_decode.hip + tq_common.h); otherwise traffic is
 # reported as null.
-DECODE_TRAFFIC = {"sources_sha256": "870edd6a010f3d58e6127284c8b6b8239c3bf8455f466605ee13e9bb7c0fe1fe",
-                  "fetch_kib": {"decode_split_kernel": 6512.2, "decode_merge_kernel": 1094.5},
-                  "write_kib": {"decode_split_kernel": 2176.0, "decode_merge_kernel": 16.0},
-                  "fetch_scale": 1.99969, "write_scale": 1.0}
+DECODE_TRAFFIC = {"sources_sha256": "c525c36f9a4b83dba3d6f8ca20ed53030efaab10a79995fba310385157785688",
+                  "fetch_kib": {"decode_split_kernel": 6558.71, "decode_merge_kernel": 570.51},
+                  "write_kib": {"decode_split_kernel": 1088.0, "decode_merge_kernel": 16.0},
+                  "fetch_scale": 1.99975, "write_scale": 1.0}
 
 
 def decode_traffic_bytes():
