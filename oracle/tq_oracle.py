@@ -384,6 +384,34 @@ def attn_decode(kc: dict, vc: dict, kv_len: int, q: np.ndarray, scale: float) ->
     return attention(np.asarray(q)[None], k, v, scale, kv_len - 1)[0]
 
 
+def attn_decode_batch(kc: dict, vc: dict, seq_start, seq_len, q: np.ndarray,
+                      scale: float) -> np.ndarray:
+    """Several sequences and one or two query rows each, in one call: the
+    decode case of [PR28] "Graph-safe decode" (query batches of at most two
+    rows take the single-row kernel) for a batch of sequences.
+
+    Reading: sequence i owns cells [seq_start[i], seq_start[i] + seq_len[i])
+    of every kv head; its n_rows query rows are the last n_rows positions, so
+    row r sees its sequence's cells j <= seq_len[i] - n_rows + r (causal, as
+    in attention()).  q [n_seq, n_rows, n_q_heads, D_K] -> [n_seq, n_rows,
+    n_q_heads, D_V] float64; a row that sees no cell is zero.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    n_seq, n_rows = q.shape[:2]
+    out = np.zeros((n_seq, n_rows, q.shape[2], vc["head_dim"]))
+    for i in range(n_seq):
+        a, n = int(seq_start[i]), int(seq_len[i])
+        if n < 1:
+            continue
+        k = dequant_cache(kc, a + n)[:, a:]
+        v = dequant_cache(vc, a + n)[:, a:]
+        first = n - n_rows                        # position of row 0
+        lo = max(0, -first)                       # rows that see no cell stay zero
+        if lo < n_rows:
+            out[i, lo:] = attention(q[i, lo:], k, v, scale, first + lo)
+    return out
+
+
 def attn_prefill(kc: dict, vc: dict, kv_len: int, q: np.ndarray, q_pos0: int,
                  scale: float) -> np.ndarray:
     """Multi-row causal attention ([PR28] "Inline-dequant TILE prefill").

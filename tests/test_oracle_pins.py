@@ -5,6 +5,7 @@ routine, brute force, or a value derived by hand in the test's docstring).
 CPU only; no GPU and no HIP library involved.
 """
 
+import math
 import os
 
 import numpy as np
@@ -405,6 +406,49 @@ def test_asymmetric_cache_decode():
     wide = o.attn_decode(kc, vc2, n, q, 0.1)
     np.testing.assert_allclose(wide[:, :128], got, atol=1e-12)
     np.testing.assert_array_equal(wide[:, 128:], 0.0)
+
+
+def test_decode_batch_reduces_to_single_decodes():
+    """Each (sequence, row) of the batched decode is the single-row decode of
+    that sequence's cells copied into a cache of their own, over the first
+    len - n_rows + r + 1 of them; rows that see no cell are zero."""
+    rng = np.random.default_rng(15)
+    n_cells, n_kv, d = 60, 2, 128
+    kk = rng.standard_normal((n_cells, n_kv, d)).astype(F32)
+    vv = rng.standard_normal((n_cells, n_kv, d)).astype(F32)
+    kc = o.new_cache(2, d, n_kv, n_cells); vc = o.new_cache(2, d, n_kv, n_cells)
+    o.set_rows(kc, kk, np.arange(n_cells)); o.set_rows(vc, vv, np.arange(n_cells))
+    starts, lens = [0, 7, 30, 59, 10], [7, 23, 30, 1, 0]
+    q = rng.standard_normal((5, 2, 4, d))
+    got = o.attn_decode_batch(kc, vc, starts, lens, q, 0.09)
+    assert got.shape == (5, 2, 4, d)
+    for i, (a, n) in enumerate(zip(starts, lens)):
+        for r in range(2):
+            vis = n - 2 + r + 1                    # cells this row sees
+            if vis < 1:
+                np.testing.assert_array_equal(got[i, r], 0.0)
+                continue
+            k1 = o.new_cache(2, d, n_kv, vis); v1 = o.new_cache(2, d, n_kv, vis)
+            o.set_rows(k1, kk[a:a + vis], np.arange(vis)); o.set_rows(v1, vv[a:a + vis], np.arange(vis))
+            np.testing.assert_allclose(got[i, r], o.attn_decode(k1, v1, vis, q[i, r], 0.09), atol=1e-12)
+
+
+def test_decode_batch_brute_force_tiny():
+    """Three cells, two rows, by hand: row 0 sees cells 0-1 of its sequence,
+    row 1 all three (softmax written out over the dequantized rows)."""
+    rng = np.random.default_rng(16)
+    kk = rng.standard_normal((5, 1, 128)).astype(F32)
+    vv = rng.standard_normal((5, 1, 128)).astype(F32)
+    kc = o.new_cache(3, 128, 1, 5); vc = o.new_cache(3, 128, 1, 5)
+    o.set_rows(kc, kk, np.arange(5)); o.set_rows(vc, vv, np.arange(5))
+    k = o.dequant_cache(kc, 5)[0]; v = o.dequant_cache(vc, 5)[0]
+    q = rng.standard_normal((1, 2, 1, 128))
+    got = o.attn_decode_batch(kc, vc, [2], [3], q, 0.2)
+    for r, cells in ((0, [2, 3]), (1, [2, 3, 4])):
+        s = [0.2 * float(q[0, r, 0] @ k[c]) for c in cells]
+        w = [math.exp(x - max(s)) for x in s]
+        want = sum(wi * v[c] for wi, c in zip(w, cells)) / sum(w)
+        np.testing.assert_allclose(got[0, r, 0], want, atol=1e-12)
 
 
 # ---------------------------------------------------------------- int8
