@@ -140,14 +140,18 @@ tq_status tq_set_rows(const tq_cache *dst, const float *src, const int64_t *cell
  * 1 <= kv_len <= n_cells, n_q_heads a multiple of n_kv_heads (else
  * TQ_ERR_INVALID_ARG); this build takes head widths of 128 or 256 for each
  * of k and v, which may differ ([PR36] (b): a 192-wide K head padded to 256
- * beside 128-wide V heads, decoded natively), and at most 8 q heads per kv
- * head (else TQ_ERR_UNSUPPORTED).
+ * beside 128-wide V heads, decoded natively; else TQ_ERR_UNSUPPORTED).  A
+ * workgroup serves eight q heads of one kv head; more q heads per kv head
+ * take more workgroups over the same cells.
  * sparse_v_tau >= 0 ([PR36] (d) item 3; 0 = off): a key whose weight
  * e^(s - m) is below tau is left out of the value sum and kept in the
  * normalizer, with m the maximum over the aligned block of 16 T keys that
  * one wave scores (at most the true maximum).  T is the plan's: the largest
  * of 8, 4, 2, 1 with T (k->head_dim + v->head_dim) / 128 <= 16 and
- * ceil(kv_len / 64T) * n_kv_heads >= the device's compute units, else 1.
+ * ceil(kv_len / 64T) * n_kv_heads * ceil(n_rep / 8) >= the device's compute
+ * units, else 1 (n_rep = n_q_heads / n_kv_heads; for the batched call below,
+ * kv_len is max_kv_len and the count is multiplied by n_seq, and n_rep by
+ * n_rows).
  * The output then differs from the dense one by at most
  * sum over {j : e^(s_j - m*) < tau} of (e^(s_j - m*) / sum_i e^(s_i - m*)) |v_j|_2
  * (m* the true maximum).  The products are not skipped, so the call costs
@@ -161,6 +165,40 @@ tq_status tq_attn_decode_workspace(const tq_cache *k, const tq_cache *v, int64_t
 tq_status tq_attn_decode(const tq_cache *k, const tq_cache *v, int64_t kv_len, const void *q,
                          int q_dtype, int32_t n_q_heads, float scale, float sparse_v_tau,
                          float *out, void *workspace, size_t workspace_bytes, tq_stream_t stream);
+
+/*
+ * Batched decode: n_seq sequences with n_rows (1..16) query rows each, in
+ * one call ([PR28] "Graph-safe decode": query batches of at most two rows
+ * take the single-row decode kernel, not the tile kernel; here any number
+ * of sequences share one launch).
+ *   seq_start int64 [n_seq], seq_len int32 [n_seq]: DEVICE arrays, 8- and
+ *             4-byte aligned, read by the kernels, so a captured graph
+ *             replays with whatever they hold at replay time.  Sequence i
+ *             owns cells [seq_start[i], seq_start[i] + seq_len[i]) of every
+ *             kv head (sequences may share cells).
+ *   q    [n_seq][n_rows][n_q_heads][k->head_dim], float32 or bfloat16, 16-byte aligned
+ *   out  float32 [n_seq][n_rows][n_q_heads][v->head_dim], 16-byte aligned
+ * Row r of sequence i is the query at position seq_len[i] - n_rows + r of
+ * that sequence and sees its cells j <= seq_len[i] - n_rows + r (causal;
+ * the same formula as tq_attn_decode over those cells).  max_kv_len (host,
+ * 1 <= max_kv_len <= n_cells) sizes the grid and the workspace: every
+ * seq_len[i] must be at most max_kv_len.  The kernels clamp the arrays'
+ * entries so that no access leaves the cache (seq_start into [0, n_cells],
+ * seq_len into [0, min(max_kv_len, n_cells - seq_start)]); a row that sees
+ * no cell (seq_len[i] < n_rows - r) is written as zeros.  n_seq == 0 is a
+ * no-op.  Same requirements on k, v, n_q_heads and sparse_v_tau as
+ * tq_attn_decode; the workspace size comes from
+ * tq_attn_decode_batch_workspace for the same caches and arguments.  Calls
+ * that share a workspace must not run concurrently.
+ */
+tq_status tq_attn_decode_batch_workspace(const tq_cache *k, const tq_cache *v, int32_t n_seq,
+                                         int32_t n_rows, int64_t max_kv_len, int32_t n_q_heads,
+                                         size_t *bytes /*[host]*/);
+tq_status tq_attn_decode_batch(const tq_cache *k, const tq_cache *v, int32_t n_seq, int32_t n_rows,
+                               const int64_t *seq_start, const int32_t *seq_len, int64_t max_kv_len,
+                               const void *q, int q_dtype, int32_t n_q_heads, float scale,
+                               float sparse_v_tau, float *out, void *workspace,
+                               size_t workspace_bytes, tq_stream_t stream);
 
 /*
  * Prefill / speculative-verify attention: n_rows query rows

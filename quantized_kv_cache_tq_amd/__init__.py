@@ -7,7 +7,8 @@ call into the binding does, and raises if the library was not built.
 """
 
 _BINDING_NAMES = (
-    "tq_set_rows", "tq_attn_decode", "tq_attn_decode_workspace", "tq_attn_prefill",
+    "tq_set_rows", "tq_attn_decode", "tq_attn_decode_workspace", "tq_attn_decode_batch",
+    "tq_attn_decode_batch_workspace", "tq_attn_prefill",
     "tq_attn_prefill_workspace", "tq_attn_int8_prompt", "tq_attn_int8_prompt_workspace",
     "tq_codebook", "tq_cache_plane_bytes", "tq_version", "TQCache", "TQError", "new_cache",
     "load_library",

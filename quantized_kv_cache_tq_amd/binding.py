@@ -46,6 +46,11 @@ _SIGS = {
                                          POINTER(c_size_t)]),
     "tq_attn_decode": (c_int, [POINTER(TQCache), POINTER(TQCache), c_int64, c_void_p, c_int, c_int32,
                                c_float, c_float, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "tq_attn_decode_batch_workspace": (c_int, [POINTER(TQCache), POINTER(TQCache), c_int32, c_int32, c_int64,
+                                               c_int32, POINTER(c_size_t)]),
+    "tq_attn_decode_batch": (c_int, [POINTER(TQCache), POINTER(TQCache), c_int32, c_int32, c_void_p, c_void_p,
+                                     c_int64, c_void_p, c_int, c_int32, c_float, c_float, c_void_p, c_void_p,
+                                     c_size_t, c_void_p]),
     "tq_attn_prefill_workspace": (c_int, [POINTER(TQCache), c_int64, c_int32, c_int64, POINTER(c_size_t)]),
     "tq_attn_prefill": (c_int, [POINTER(TQCache), POINTER(TQCache), c_int64, c_void_p, c_int, c_int64,
                                 c_int32, c_int64, c_float, c_void_p, c_void_p, c_size_t, c_void_p]),
@@ -199,6 +204,44 @@ def tq_attn_decode(k: TQCacheTensors, v: TQCacheTensors, kv_len: int, q: torch.T
     _check(load_library().tq_attn_decode(ctypes.byref(k.struct), ctypes.byref(v.struct), kv_len,
                                          q.data_ptr(), qd, n_q, scale, sparse_v_tau, out.data_ptr(),
                                          ws.data_ptr(), ws.numel(), _stream(stream)), "tq_attn_decode")
+    return out
+
+
+def tq_attn_decode_batch_workspace(k: TQCacheTensors, v: TQCacheTensors, n_seq: int, n_rows: int,
+                                   max_kv_len: int, n_q_heads: int) -> int:
+    b = c_size_t()
+    _check(load_library().tq_attn_decode_batch_workspace(ctypes.byref(k.struct), ctypes.byref(v.struct), n_seq,
+                                                         n_rows, max_kv_len, n_q_heads, ctypes.byref(b)),
+           "tq_attn_decode_batch_workspace")
+    return b.value
+
+
+def tq_attn_decode_batch(k: TQCacheTensors, v: TQCacheTensors, seq_start: torch.Tensor, seq_len: torch.Tensor,
+                         max_kv_len: int, q: torch.Tensor, scale: float, out: torch.Tensor | None = None,
+                         workspace: torch.Tensor | None = None, sparse_v_tau: float = 0.0,
+                         stream=None) -> torch.Tensor:
+    """q [n_seq, n_rows, n_q_heads, k.head_dim]; seq_start int64 / seq_len int32
+    device tensors [n_seq] -> out [n_seq, n_rows, n_q_heads, v.head_dim]."""
+    qd = _q_dtype(q)
+    _dev_tensor(q, q.dtype, "q")
+    _dev_tensor(seq_start, torch.int64, "seq_start")
+    _dev_tensor(seq_len, torch.int32, "seq_len")
+    if q.dim() != 4 or q.shape[3] != k.head_dim:
+        raise ValueError("q must be [n_seq, n_rows, n_q_heads, k.head_dim]")
+    n_seq, n_rows, n_q = q.shape[:3]
+    if seq_start.shape != (n_seq,) or seq_len.shape != (n_seq,):
+        raise ValueError("seq_start and seq_len must be [n_seq]")
+    if out is None:
+        out = torch.empty((n_seq, n_rows, n_q, v.head_dim), dtype=torch.float32, device=q.device)
+    _dev_tensor(out, torch.float32, "out")
+    if tuple(out.shape) != (n_seq, n_rows, n_q, v.head_dim):
+        raise ValueError("out must be [n_seq, n_rows, n_q_heads, v.head_dim]")
+    ws = _workspace(tq_attn_decode_batch_workspace(k, v, n_seq, n_rows, max_kv_len, n_q), q.device, workspace)
+    _check(load_library().tq_attn_decode_batch(ctypes.byref(k.struct), ctypes.byref(v.struct), n_seq, n_rows,
+                                               seq_start.data_ptr(), seq_len.data_ptr(), max_kv_len,
+                                               q.data_ptr(), qd, n_q, scale, sparse_v_tau, out.data_ptr(),
+                                               ws.data_ptr(), ws.numel(), _stream(stream)),
+           "tq_attn_decode_batch")
     return out
 
 

@@ -107,10 +107,31 @@ static tq_status decode_check(const tq_cache *k, const tq_cache *v, int64_t kv_l
   if (s != TQ_OK) return s;
   if (kv_len < 1 || kv_len > k->n_cells) return TQ_ERR_INVALID_ARG;
   if (n_q_heads < 1 || n_q_heads % k->n_kv_heads) return TQ_ERR_INVALID_ARG;
-  if ((k->head_dim != 128 && k->head_dim != 256) || (v->head_dim != 128 && v->head_dim != 256) ||
-      n_q_heads / k->n_kv_heads > 8)
+  if ((k->head_dim != 128 && k->head_dim != 256) || (v->head_dim != 128 && v->head_dim != 256))
     return TQ_ERR_UNSUPPORTED;
   return TQ_OK;
+}
+
+static tq_status batch_check(int32_t n_seq, int32_t n_rows) {
+  if (n_seq < 0 || n_seq > 65535 || n_rows < 1 || n_rows > 16) return TQ_ERR_INVALID_ARG;
+  return TQ_OK;
+}
+
+static tq_status decode_call(const tq_cache *k, const tq_cache *v, int32_t n_seq, int32_t n_rows,
+                             const int64_t *seq_start, const int32_t *seq_len, int64_t kv_len,
+                             const void *q, int q_dtype, int32_t n_q_heads, float scale,
+                             float sparse_v_tau, float *out, void *workspace,
+                             size_t workspace_bytes, tq_stream_t stream) {
+  if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return TQ_ERR_INVALID_ARG;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
+  if (!(scale == scale) || !(sparse_v_tau == sparse_v_tau) || sparse_v_tau < 0.f)
+    return TQ_ERR_INVALID_ARG;
+  DecodePlan p;
+  if (tq_status st = from_hip(plan_decode(*k, *v, kv_len, n_q_heads, n_rows, n_seq, &p))) return st;
+  if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.workspace_bytes)
+    return TQ_ERR_WORKSPACE;
+  return from_hip(launch_decode(*k, *v, seq_start, seq_len, kv_len, q, q_dtype, n_q_heads, scale,
+                                sparse_v_tau, out, workspace, p, (hipStream_t)stream));
 }
 
 tq_status tq_attn_decode_workspace(const tq_cache *k, const tq_cache *v, int64_t kv_len,
@@ -119,7 +140,7 @@ tq_status tq_attn_decode_workspace(const tq_cache *k, const tq_cache *v, int64_t
   if (s != TQ_OK) return s;
   if (!bytes) return TQ_ERR_INVALID_ARG;
   DecodePlan p;
-  if (tq_status st = from_hip(plan_decode(*k, *v, kv_len, n_q_heads, &p))) return st;
+  if (tq_status st = from_hip(plan_decode(*k, *v, kv_len, n_q_heads, 1, 1, &p))) return st;
   *bytes = p.workspace_bytes;
   return TQ_OK;
 }
@@ -130,16 +151,39 @@ tq_status tq_attn_decode(const tq_cache *k, const tq_cache *v, int64_t kv_len, c
                          tq_stream_t stream) {
   tq_status s = decode_check(k, v, kv_len, n_q_heads);
   if (s != TQ_OK) return s;
-  if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return TQ_ERR_INVALID_ARG;
-  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
-  if (!(scale == scale) || !(sparse_v_tau == sparse_v_tau) || sparse_v_tau < 0.f)
-    return TQ_ERR_INVALID_ARG;
+  return decode_call(k, v, 1, 1, nullptr, nullptr, kv_len, q, q_dtype, n_q_heads, scale, sparse_v_tau,
+                     out, workspace, workspace_bytes, stream);
+}
+
+tq_status tq_attn_decode_batch_workspace(const tq_cache *k, const tq_cache *v, int32_t n_seq,
+                                         int32_t n_rows, int64_t max_kv_len, int32_t n_q_heads,
+                                         size_t *bytes) {
+  tq_status s = decode_check(k, v, max_kv_len, n_q_heads);
+  if (s != TQ_OK) return s;
+  if ((s = batch_check(n_seq, n_rows)) != TQ_OK) return s;
+  if (!bytes) return TQ_ERR_INVALID_ARG;
+  if (n_seq == 0) {
+    *bytes = 0;
+    return TQ_OK;
+  }
   DecodePlan p;
-  if (tq_status st = from_hip(plan_decode(*k, *v, kv_len, n_q_heads, &p))) return st;
-  if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.workspace_bytes)
-    return TQ_ERR_WORKSPACE;
-  return from_hip(launch_decode(*k, *v, kv_len, q, q_dtype, n_q_heads, scale, sparse_v_tau, out, workspace, p,
-                                (hipStream_t)stream));
+  if (tq_status st = from_hip(plan_decode(*k, *v, max_kv_len, n_q_heads, n_rows, n_seq, &p))) return st;
+  *bytes = p.workspace_bytes;
+  return TQ_OK;
+}
+
+tq_status tq_attn_decode_batch(const tq_cache *k, const tq_cache *v, int32_t n_seq, int32_t n_rows,
+                               const int64_t *seq_start, const int32_t *seq_len, int64_t max_kv_len,
+                               const void *q, int q_dtype, int32_t n_q_heads, float scale,
+                               float sparse_v_tau, float *out, void *workspace,
+                               size_t workspace_bytes, tq_stream_t stream) {
+  tq_status s = decode_check(k, v, max_kv_len, n_q_heads);
+  if (s != TQ_OK) return s;
+  if ((s = batch_check(n_seq, n_rows)) != TQ_OK) return s;
+  if (!seq_start || !seq_len || !aligned(seq_start, 8) || !aligned(seq_len, 4)) return TQ_ERR_INVALID_ARG;
+  if (n_seq == 0) return TQ_OK;
+  return decode_call(k, v, n_seq, n_rows, seq_start, seq_len, max_kv_len, q, q_dtype, n_q_heads, scale,
+                     sparse_v_tau, out, workspace, workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------- prefill

@@ -82,6 +82,23 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// The cells of sequence z: [start, start + len) of every kv head.  Without
+// arrays, one sequence of kv_len cells from cell 0; with them, the entries
+// are clamped so that no access leaves the cache (start into [0, n_cells],
+// len into [0, min(max_len, n_cells - start)]).
+struct SeqExtent {
+  int64_t start, len;
+};
+__device__ __forceinline__ SeqExtent seq_extent(const int64_t *seq_start, const int32_t *seq_len, int z,
+                                                int64_t kv_len, int64_t n_cells) {
+  if (!seq_len) return SeqExtent{0, kv_len};
+  int64_t a = seq_start[z], n = seq_len[z];
+  a = a < 0 ? 0 : (a > n_cells ? n_cells : a);
+  const int64_t cap = kv_len < n_cells - a ? kv_len : n_cells - a;
+  n = n < 0 ? 0 : (n > cap ? cap : n);
+  return SeqExtent{a, n};
+}
+
 // Workgroup (split s, kv head g): eight waves, four key ranges of KPW = 16T
 // keys.  Waves 0-3 ("key waves") score their range and turn the scores into
 // the matrix-core operand P; waves 4-7 ("value waves") meanwhile decode the
@@ -92,11 +109,17 @@ __device__ __forceinline__ void wave_lds_fence() {
 // 128 GV, which may differ): a score sums its K groups' products, each
 // scaled by that group's norm, and P has one operand per V group (p times
 // that group's norm), the V groups taking their products one after another.
+// The eight heads of a workgroup are (query row, q head) pairs: sequence z =
+// blockIdx.z has n_rows query rows, row r seeing the sequence's cells j <=
+// len - n_rows + r, and a kv head's n_rows * n_rep pairs are cut into
+// head groups of eight (blockIdx.y = kv head * n_hg + head group).  Splits
+// past the sequence's length exit at once and write nothing.
 template <int B, int T, int GK, int GV, bool QBF16>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     const uint8_t *__restrict__ kcodes, const uint16_t *__restrict__ knorms,
     const uint8_t *__restrict__ vcodes, const uint16_t *__restrict__ vnorms, int64_t n_cells,
-    int64_t kv_len, const void *__restrict__ q, int n_rep, float qscale, float tau,
+    const int64_t *__restrict__ seq_start, const int32_t *__restrict__ seq_len, int64_t kv_len,
+    const void *__restrict__ q, int n_q, int n_rep, int n_rows, int n_hg, float qscale, float tau,
     float *__restrict__ ws, int n_split) {
   constexpr int DV = kGroup * GV;              // output width
   constexpr int KPW = 16 * T;                  // keys per range
@@ -134,21 +157,32 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
   const int rg = wave & 3;                     // key range of this wave
   const bool kwave = wave < 4;
   const int col = lane & 15, quad = lane >> 4;
-  const int s = blockIdx.x, g = blockIdx.y;
-  // keys [w0, w0 + wkeys) of range rg; addressing is relative to row0, a
-  // valid key row, with lane offsets clamped to the range's last key
+  const int s = blockIdx.x, z = blockIdx.z;
+  // (divisions only where there are several head groups or rows: they sit
+  // in front of the first loads)
+  const int g = n_hg == 1 ? (int)blockIdx.y : (int)blockIdx.y / n_hg;
+  const int hg = (int)blockIdx.y - g * n_hg;
+  const SeqExtent ext = seq_extent(seq_start, seq_len, z, kv_len, n_cells);
+  if ((int64_t)s * KPS >= ext.len) return;     // uniform: the whole workgroup
+  const int n_vh = n_rows * n_rep;             // (row, head) pairs of a kv head
+  // keys [w0, w0 + wkeys) of range rg (relative to the sequence start);
+  // addressing is relative to row0, a valid key row, with lane offsets
+  // clamped to the range's last key
   const int64_t w0 = (int64_t)s * KPS + (int64_t)rg * KPW;
-  const int64_t left = kv_len - w0;
+  const int64_t left = ext.len - w0;
   const int wkeys = (int)(left < 0 ? 0 : (left < KPW ? left : KPW));
   const int wlast = wkeys > 0 ? wkeys - 1 : 0;
-  const int64_t row0 = (int64_t)g * n_cells + (wkeys > 0 ? w0 : kv_len - 1);
+  const int64_t row0 = (int64_t)g * n_cells + ext.start + (wkeys > 0 ? w0 : ext.len - 1);
 
   if (kwave) {
     // ---------------- key wave: loads first (query, norms, K codes)
     const uint8_t *kb = kcodes + row0 * (16 * B * GK);
     const uint16_t *knb = knorms + row0 * GK, *vnb = vnorms + row0 * GV;
     const int qh = 2 * rg + (lane >> 5), qj = lane & 31;
-    const int64_t qbase = ((int64_t)g * n_rep + imin(qh, n_rep - 1)) * (kGroup * GK) + 4 * qj;
+    const int vq = imin(8 * hg + qh, n_vh - 1);   // (row, head) pair of this lane's head
+    const int vr = n_rows == 1 ? 0 : vq / n_rep;
+    const int64_t qbase = (((int64_t)z * n_rows + vr) * n_q + (int64_t)g * n_rep + (vq - vr * n_rep)) *
+                              (kGroup * GK) + 4 * qj;
     float qv[GK][4];
 #pragma unroll
     for (int gk = 0; gk < GK; ++gk) {
@@ -196,7 +230,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) qv[gk][i] = flip_sign(qv[gk][i], sign_bit_of(4 * qj + i));
       wht128_half(qv[gk], qj);
-      const bool live = qh < n_rep;
+      const bool live = 8 * hg + qh < n_vh;
       uint32_t hw[2], lw[2];
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
@@ -260,12 +294,18 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
         }
       }
     }
-    if (wkeys < KPW) {   // wave-uniform: only a ragged last range masks
+    // causal limit of this lane's column (head 8hg + (col & 7)): the key
+    // (relative to the range) of its row's last visible cell; only ranges
+    // reaching past the first row's limit mask (wave-uniform)
+    if (w0 + KPW - 1 > ext.len - n_rows) {
+      const int vc = 8 * hg + (col & 7);
+      const int64_t lim64 = ext.len - n_rows + (vc < n_vh && n_rows > 1 ? vc / n_rep : 0) - w0;
+      const int lim = lim64 < -1 ? -1 : (lim64 > KPW ? KPW : (int)lim64);
 #pragma unroll
       for (int t = 0; t < T; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (16 * t + 4 * quad + i >= wkeys) sc[t][i] = -INFINITY;
+          if (16 * t + 4 * quad + i > lim) sc[t][i] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -415,10 +455,10 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
 
   // ---- merge the four ranges: obuf[r][h][128gv + 8c + t] holds element
   //      8c + t of group gv of head h, relative to the range's own max
-  float *part = ws + ((int64_t)g * n_rep * n_split + s) * PSTRIDE;
   {
     const int h = tid >> 6, d = 2 * (tid & 63);
-    if (h < n_rep) {
+    const int vh = 8 * hg + h;
+    if (vh < n_vh) {
       const float M = fmaxf(fmaxf(wm[0][h], wm[1][h]), fmaxf(wm[2][h], wm[3][h]));
       float f[4], L = 0.f;
 #pragma unroll
@@ -427,7 +467,10 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
         f[r] = mr == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mr - M);
         L += f[r] * wl[r][h];
       }
-      float *ph = part + (int64_t)h * n_split * PSTRIDE;
+      // partial of (sequence z, row, q head), split s
+      const int vr = n_rows == 1 ? 0 : vh / n_rep;
+      const int64_t qrow = ((int64_t)z * n_rows + vr) * n_q + (int64_t)g * n_rep + (vh - vr * n_rep);
+      float *ph = ws + (qrow * n_split + s) * PSTRIDE;
 #pragma unroll
       for (int gv = 0; gv < GV; ++gv) {
         float a0 = 0.f, a1 = 0.f;
@@ -445,20 +488,30 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
 }
 
 // Merge the split partials of one 128-element group (blockIdx.y) of one
-// query head (blockIdx.x), undo the rotation and write that part of the
-// float32 output row: out = s (.) H O / (128 L).  Sixteen 32-lane groups
-// share the splits (s = group mod 16), each with its own running max; lane j
-// owns elements 4j..4j+3.  dv is the output width (128 x gridDim.y).
+// output row (blockIdx.x: (sequence, query row, q head)), undo the rotation
+// and write that part of the float32 row: out = s (.) H O / (128 L).  Only
+// the splits that hold the sequence's cells are read.  Sixteen 32-lane
+// groups share the splits (s = group mod 16), each with its own running max;
+// lane j owns elements 4j..4j+3.  dv is the output width (128 x gridDim.y);
+// a split holds 2^split_log2 cells.
+// A row that sees no cell (all its splits' maxima -inf) is written as zeros.
+// kRowsMasked: several query rows per sequence, so a split may hold no cell
+// that a row sees (maximum -inf); one-row calls never have such splits and
+// keep the unguarded chain of running maxima.
 constexpr int kMergeThreads = 512;
 constexpr int kMergeGroups = kMergeThreads / 32;
-__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float *__restrict__ ws,
-                                                                     int n_split, int dv,
-                                                                     float *__restrict__ out) {
+template <bool kRowsMasked>
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
+    const float *__restrict__ ws, int n_split, int split_log2, int dv, const int64_t *__restrict__ seq_start,
+    const int32_t *__restrict__ seq_len, int64_t kv_len, int64_t n_cells, int rows_per_seq,
+    float *__restrict__ out) {
   __shared__ float4 obuf[kMergeGroups][32];
   __shared__ float lbuf[kMergeGroups], mbuf[kMergeGroups];
   const int h = blockIdx.x, og = blockIdx.y, tid = threadIdx.x;
   const int grp = tid >> 5, j = tid & 31;
   const int pstride = part_stride(dv);
+  const SeqExtent ext = seq_extent(seq_start, seq_len, h / rows_per_seq, kv_len, n_cells);
+  const int n_valid = (int)((ext.len + (1 << split_log2) - 1) >> split_log2);   // splits holding its cells
   const float *part = ws + (int64_t)h * n_split * pstride;
   float mg = -INFINITY, L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -466,13 +519,13 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
   // first use: the partials come from other compute units' writes, so each
   // dependent round costs a full memory latency
   constexpr int kBatch = 8;
-  for (int s0 = grp; s0 < n_split; s0 += kBatch * kMergeGroups) {
+  for (int s0 = grp; s0 < n_valid; s0 += kBatch * kMergeGroups) {
     float2 ml[kBatch];
     float4 v[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int s = s0 + i * kMergeGroups;
-      if (s < n_split) {
+      if (s < n_valid) {
         const float *p = part + (int64_t)s * pstride;
         ml[i] = *reinterpret_cast<const float2 *>(p + dv);
         v[i] = reinterpret_cast<const float4 *>(p + kGroup * og)[j];
@@ -480,10 +533,15 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
     }
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      if (s0 + i * kMergeGroups >= n_split) break;
+      if (s0 + i * kMergeGroups >= n_valid) break;
       const float mn = fmaxf(mg, ml[i].x);
-      const float a = __builtin_amdgcn_exp2f(mg - mn);
-      const float w = __builtin_amdgcn_exp2f(ml[i].x - mn);
+      float a = __builtin_amdgcn_exp2f(mg - mn);
+      float w = __builtin_amdgcn_exp2f(ml[i].x - mn);
+      if constexpr (kRowsMasked) {
+        // both maxima -inf: nothing seen yet, and -inf - -inf is NaN
+        a = mg == -INFINITY ? 0.f : a;
+        w = ml[i].x == -INFINITY ? 0.f : w;
+      }
       L = L * a + w * ml[i].y;
       acc.x = acc.x * a + w * v[i].x;
       acc.y = acc.y * a + w * v[i].y;
@@ -512,7 +570,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
     Lt += w * lbuf[gq];
   }
   wht128_half(u, j);
-  const float r = 1.0f / (128.0f * Lt);
+  const float r = Lt > 0.f ? 1.0f / (128.0f * Lt) : 0.f;
   float4 res;
   res.x = flip_sign(u[0] * r, sign_bit_of(4 * j + 0));
   res.y = flip_sign(u[1] * r, sign_bit_of(4 * j + 1));
@@ -541,29 +599,36 @@ hipError_t device_cu_count(int *n_cu) {
   return hipSuccess;
 }
 
-hipError_t plan_decode(const tq_cache &k, const tq_cache &v, int64_t kv_len, int32_t n_q_heads,
-                       DecodePlan *p) {
+hipError_t plan_decode(const tq_cache &k, const tq_cache &v, int64_t max_len, int32_t n_q_heads,
+                       int n_rows, int n_seq, DecodePlan *p) {
   int n_cu = 0;
   hipError_t e = device_cu_count(&n_cu);
   if (e != hipSuccess) return e;
+  const int n_rep = n_q_heads / k.n_kv_heads;
+  p->n_rows = n_rows;
+  p->n_seq = n_seq;
+  p->head_groups = ceil_div(n_rows * n_rep, 8);
   // a split covers 4 ranges of 16 * tiles keys.  Tiles per range: the most
   // (1, 2, 4 or 8) with at most 16 group-tiles per range (tiles x (K groups
   // + V groups)) that still give every compute unit a workgroup.  Measured:
   // fewer, larger workgroups cost less setup and fewer split partials, up to
   // the point where a range's registers and shared memory run short.
   const int groups = k.head_dim / kGroup + v.head_dim / kGroup;
+  const int64_t wg_per_split = (int64_t)k.n_kv_heads * p->head_groups * n_seq;
   int tpw = 8;
   while (tpw > 1) {
-    const int64_t splits = ceil_div<int64_t>(kv_len, 64LL * tpw);
-    if (tpw * groups <= 16 && splits * k.n_kv_heads >= n_cu) break;
+    const int64_t splits = ceil_div<int64_t>(max_len, 64LL * tpw);
+    if (tpw * groups <= 16 && splits * wg_per_split >= n_cu) break;
     tpw >>= 1;
   }
   p->tiles_per_wave = tpw;
   p->keys_per_split = 64 * tpw;
-  const int64_t n_split = ceil_div<int64_t>(kv_len, p->keys_per_split);
-  if (n_split > 0x7fffffff) return hipErrorInvalidValue;
+  const int64_t n_split = ceil_div<int64_t>(max_len, p->keys_per_split);
+  if (n_split > 0x7fffffff || (int64_t)k.n_kv_heads * p->head_groups > 65535 || n_seq > 65535)
+    return hipErrorInvalidValue;
   p->n_split = (int)n_split;
-  const size_t bytes = (size_t)n_q_heads * (size_t)n_split * part_stride(v.head_dim) * sizeof(float);
+  const size_t bytes = (size_t)n_seq * (size_t)n_rows * (size_t)n_q_heads * (size_t)n_split *
+                       part_stride(v.head_dim) * sizeof(float);
   p->workspace_bytes = (bytes + 255) & ~(size_t)255;
   return hipSuccess;
 }
@@ -572,9 +637,11 @@ namespace {
 
 struct SplitArgs {
   const tq_cache *k, *v;
+  const int64_t *seq_start;
+  const int32_t *seq_len;
   int64_t kv_len;
   const void *q;
-  int n_rep;
+  int n_q, n_rep, n_rows, n_hg;
   float qs, tau;
   float *ws;
   int n_split;
@@ -585,10 +652,10 @@ struct SplitArgs {
 template <int B, int GK, int GV, bool QBF>
 hipError_t launch_split(int tpw, dim3 grid, hipStream_t st, const SplitArgs &a) {
   dim3 block(kDecThreads);
-#define TQ_DEC(T)                                                                                  \
-  hipLaunchKernelGGL((decode_split_kernel<B, T, GK, GV, QBF>), grid, block, 0, st, a.k->codes,    \
-                     a.k->norms, a.v->codes, a.v->norms, a.k->n_cells, a.kv_len, a.q, a.n_rep,    \
-                     a.qs, a.tau, a.ws, a.n_split)
+#define TQ_DEC(T)                                                                                   \
+  hipLaunchKernelGGL((decode_split_kernel<B, T, GK, GV, QBF>), grid, block, 0, st, a.k->codes,     \
+                     a.k->norms, a.v->codes, a.v->norms, a.k->n_cells, a.seq_start, a.seq_len,     \
+                     a.kv_len, a.q, a.n_q, a.n_rep, a.n_rows, a.n_hg, a.qs, a.tau, a.ws, a.n_split)
   switch (tpw) {
     case 1: TQ_DEC(1); break;
     case 2: TQ_DEC(2); break;
@@ -621,24 +688,30 @@ hipError_t launch_split_dims(int gk, int gv, int qbf, int tpw, dim3 grid, hipStr
 
 }  // namespace
 
-hipError_t launch_decode(const tq_cache &k, const tq_cache &v, int64_t kv_len, const void *q,
-                         int q_dtype, int32_t n_q_heads, float scale, float sparse_v_tau,
-                         float *out, void *workspace, const DecodePlan &p, hipStream_t stream) {
+hipError_t launch_decode(const tq_cache &k, const tq_cache &v, const int64_t *seq_start,
+                         const int32_t *seq_len, int64_t kv_len, const void *q, int q_dtype,
+                         int32_t n_q_heads, float scale, float sparse_v_tau, float *out,
+                         void *workspace, const DecodePlan &p, hipStream_t stream) {
   const int gk = k.head_dim / kGroup, gv = v.head_dim / kGroup;
   if (gk < 1 || gk > 2 || gv < 1 || gv > 2 || k.type != v.type) return hipErrorNotSupported;
   SplitArgs a;
   a.k = &k;
   a.v = &v;
+  a.seq_start = seq_start;
+  a.seq_len = seq_len;
   a.kv_len = kv_len;
   a.q = q;
+  a.n_q = n_q_heads;
   a.n_rep = n_q_heads / k.n_kv_heads;
+  a.n_rows = p.n_rows;
+  a.n_hg = p.head_groups;
   // scores in the log2 domain: scale * log2(e), and 1/128 for the two
   // 1/sqrt(128) factors of the rotated query and the rotated levels
   a.qs = scale * 1.4426950408889634f / 128.0f;
   a.tau = sparse_v_tau;
   a.ws = reinterpret_cast<float *>(workspace);
   a.n_split = p.n_split;
-  dim3 grid(p.n_split, k.n_kv_heads);
+  dim3 grid(p.n_split, k.n_kv_heads * p.head_groups, p.n_seq);
   const int qbf = q_dtype == TQ_BF16 ? 1 : 0;
   hipError_t e;
   switch (k.type) {
@@ -649,8 +722,15 @@ hipError_t launch_decode(const tq_cache &k, const tq_cache &v, int64_t kv_len, c
   if (e != hipSuccess) return e;
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(n_q_heads, gv), dim3(kMergeThreads), 0, stream, a.ws,
-                     p.n_split, v.head_dim, out);
+  const int64_t rows_out = (int64_t)p.n_seq * p.n_rows * n_q_heads;
+  const dim3 mgrid((unsigned)rows_out, gv);
+  const int split_log2 = __builtin_ctz((unsigned)p.keys_per_split);
+  if (p.n_rows > 1)
+    hipLaunchKernelGGL(decode_merge_kernel<true>, mgrid, dim3(kMergeThreads), 0, stream, a.ws, p.n_split,
+                       split_log2, v.head_dim, seq_start, seq_len, kv_len, k.n_cells, p.n_rows * n_q_heads, out);
+  else
+    hipLaunchKernelGGL(decode_merge_kernel<false>, mgrid, dim3(kMergeThreads), 0, stream, a.ws, p.n_split,
+                       split_log2, v.head_dim, seq_start, seq_len, kv_len, k.n_cells, p.n_rows * n_q_heads, out);
   return hipGetLastError();
 }
 

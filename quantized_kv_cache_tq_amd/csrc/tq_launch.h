@@ -18,14 +18,21 @@ hipError_t launch_set_rows(const tq_cache &c, const float *src, const int64_t *c
 struct DecodePlan {
   int tiles_per_wave;    // 16-key tiles per key range (4 ranges per workgroup)
   int keys_per_split;    // 64 * tiles_per_wave
-  int n_split;           // workgroups per kv head
+  int n_split;           // splits of the longest sequence
+  int n_rows;            // query rows per sequence
+  int n_seq;             // sequences per call
+  int head_groups;       // workgroups per (split, kv head): eight (row, q head) pairs each
   size_t workspace_bytes;
 };
-hipError_t plan_decode(const tq_cache &k, const tq_cache &v, int64_t kv_len, int32_t n_q_heads,
-                       DecodePlan *p);
-hipError_t launch_decode(const tq_cache &k, const tq_cache &v, int64_t kv_len, const void *q,
-                         int q_dtype, int32_t n_q_heads, float scale, float sparse_v_tau,
-                         float *out, void *workspace, const DecodePlan &p, hipStream_t stream);
+// max_len: the longest sequence the call may see (sizes the grid).
+hipError_t plan_decode(const tq_cache &k, const tq_cache &v, int64_t max_len, int32_t n_q_heads,
+                       int n_rows, int n_seq, DecodePlan *p);
+// seq_start / seq_len: device arrays [n_seq] (null: one sequence of kv_len
+// cells from cell 0); kv_len is otherwise the largest length allowed.
+hipError_t launch_decode(const tq_cache &k, const tq_cache &v, const int64_t *seq_start,
+                         const int32_t *seq_len, int64_t kv_len, const void *q, int q_dtype,
+                         int32_t n_q_heads, float scale, float sparse_v_tau, float *out,
+                         void *workspace, const DecodePlan &p, hipStream_t stream);
 
 struct PrefillPlan {
   int rows_per_tile;     // query rows per workgroup

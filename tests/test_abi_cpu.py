@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ["tq_set_rows", "tq_attn_decode", "tq_attn_prefill", "tq_attn_int8_prompt",
+    for n in ["tq_set_rows", "tq_attn_decode", "tq_attn_decode_batch", "tq_attn_prefill", "tq_attn_int8_prompt",
               "tq_codebook", "tq_cache_plane_bytes", "tq_version", "tq_status_str"]:
         assert n in names
 
@@ -112,7 +112,6 @@ def test_decode_rejects_bad_arguments():
     assert call(kv=0) == -1
     assert call(kv=101) == -1                     # beyond n_cells
     assert call(nq=30) == -1                      # not a multiple of n_kv_heads
-    assert call(nq=36 * 4) == -2                  # 36 q heads per kv head: no kernel
     assert call(v=_cache(b, type_=2)) == -1       # K and V types differ
     assert call(v=_cache(b, n_kv=2)) == -1
     assert call(k=_cache(b, head_dim=384), v=_cache(b, head_dim=384)) == -2   # 3 groups: no kernel
@@ -126,6 +125,36 @@ def test_decode_rejects_bad_arguments():
     assert call(sc=float("nan")) == -1
     assert call(tau=-1.0) == -1
     assert call(tau=float('nan')) == -1
+
+
+@needs_lib
+def test_decode_batch_rejects_bad_arguments():
+    from quantized_kv_cache_tq_amd import binding as b
+    lib = b.load_library()
+    k, v = _cache(b), _cache(b)
+    call = lambda k=k, v=v, ns=3, nr=2, st=FAKE, ln=FAKE, mx=50, q=FAKE, nq=32, tau=0.0, out=FAKE: \
+        lib.tq_attn_decode_batch(ctypes.byref(k), ctypes.byref(v), ns, nr, st, ln, mx, q, 1, nq, 0.1, tau, out,
+                                 FAKE, 1 << 20, None)
+    assert call(ns=-1) == -1
+    assert call(ns=65536) == -1
+    assert call(nr=0) == -1
+    assert call(nr=17) == -1
+    assert call(st=None) == -1
+    assert call(ln=None) == -1
+    assert call(st=FAKE + 4) == -1                # int64 array, 8-byte aligned
+    assert call(ln=FAKE + 2) == -1
+    assert call(mx=0) == -1
+    assert call(mx=101) == -1                     # beyond n_cells
+    assert call(nq=30) == -1
+    assert call(v=_cache(b, n_cells=99)) == -1
+    assert call(k=_cache(b, head_dim=384), v=_cache(b, head_dim=384)) == -2
+    assert call(tau=-1.0) == -1
+    assert call(q=FAKE + 8) == -1
+    assert call(ns=0) == 0                        # no sequences: no-op
+    n = ctypes.c_size_t(7)
+    assert lib.tq_attn_decode_batch_workspace(ctypes.byref(k), ctypes.byref(v), 0, 1, 50, 32, ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert lib.tq_attn_decode_batch_workspace(ctypes.byref(k), ctypes.byref(v), 2, 0, 50, 32, ctypes.byref(n)) == -1
 
 
 @needs_lib
