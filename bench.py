@@ -351,6 +351,59 @@ def main():
                 "us_per_call": round(t_ms * 1e3, 3), "bytes_per_call": nbytes, "GBps": round(gbps, 1),
                 "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
             del wkc, wvc, wout, wws
+
+        # batched decode (leg "decode_batch"): 8 sequences of mixed lengths
+        # (131,072 cells in all), 2 query rows each, 32 q / 4 kv heads, one
+        # call per layer over L layer caches in one graph; beside it the same
+        # sequences as 8 single-row calls per layer (one row each)
+        if want("decode_batch"):
+            lens = [32768, 16384, 8192, 4096, 30000, 2000, 12000, 25632]
+            starts = np.cumsum([0] + lens[:-1]).tolist()
+            NC = int(sum(lens))
+            bq_np, bk_np, bv_np = inputs.outlier_decode(seed=8, kv_len=NC)
+            bkc = [b.new_cache(3, D, NKV, NC) for _ in range(L)]
+            bvc = [b.new_cache(3, D, NKV, NC) for _ in range(L)]
+            bidx = torch.arange(NC, dtype=torch.int64, device=dev)
+            b.tq_set_rows(bkc[0], torch.from_numpy(bk_np).to(dev), bidx)
+            b.tq_set_rows(bvc[0], torch.from_numpy(bv_np).to(dev), bidx)
+            for i in range(1, L):
+                bkc[i].codes.copy_(bkc[0].codes); bkc[i].norms.copy_(bkc[0].norms)
+                bvc[i].codes.copy_(bvc[0].codes); bvc[i].norms.copy_(bvc[0].norms)
+            rng = np.random.default_rng(9)
+            bq = torch.from_numpy(inputs.bf16_round(rng.standard_normal((8, 2, NQ, D)).astype(np.float32)))
+            bq = bq.to(torch.bfloat16).to(dev)
+            st = torch.tensor(starts, dtype=torch.int64, device=dev)
+            ln = torch.tensor(lens, dtype=torch.int32, device=dev)
+            MAXL = max(lens)
+            bws = torch.empty(b.tq_attn_decode_batch_workspace(bkc[0], bvc[0], 8, 2, MAXL, NQ), dtype=torch.uint8,
+                              device=dev)
+            bout = [torch.empty((8, 2, NQ, D), dtype=torch.float32, device=dev) for _ in range(L)]
+            calls = [lambda i=i: b.tq_attn_decode_batch(bkc[i], bvc[i], st, ln, MAXL, bq, scale_dec, out=bout[i],
+                                                        workspace=bws) for i in range(L)]
+            t_ms = time_graph(calls)
+            nbytes = NC * NKV * 2 * (48 + 2)
+            gbps = nbytes / (t_ms * 1e-3) / 1e9
+            extras["decode_batch_8seq_2rows_131k_cells"] = {
+                "us_per_call": round(t_ms * 1e3, 3), "bytes_per_call": nbytes, "GBps": round(gbps, 1),
+                "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+            # the same cells through single-sequence calls (one row each)
+            def seq_cache(c, a, n):
+                x = b.new_cache(3, D, NKV, n)
+                x.codes.copy_(c.codes[:, a:a + n])
+                x.norms.copy_(c.norms[:, a:a + n])
+                return x
+            sk = [[seq_cache(c, a, n) for a, n in zip(starts, lens)] for c in bkc]
+            sv = [[seq_cache(c, a, n) for a, n in zip(starts, lens)] for c in bvc]
+            sws = torch.empty(max(b.tq_attn_decode_workspace(sk[0][j], sv[0][j], lens[j], NQ) for j in range(8)),
+                              dtype=torch.uint8, device=dev)
+            sq = bq[:, 1].contiguous()
+            sout = torch.empty((NQ, D), dtype=torch.float32, device=dev)
+            scalls = [lambda i=i, j=j: b.tq_attn_decode(sk[i][j], sv[i][j], lens[j], sq[j], scale_dec, out=sout,
+                                                        workspace=sws) for i in range(L) for j in range(8)]
+            t_ms = time_graph(scalls) * 8
+            extras["decode_8_single_calls_1row_131k_cells"] = {
+                "us_per_layer": round(t_ms * 1e3, 3), "GBps": round(nbytes / (t_ms * 1e-3) / 1e9, 1)}
+            del bkc, bvc, bout, sk, sv
     log("[bench] extras done")
 
     res = {}

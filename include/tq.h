@@ -148,10 +148,10 @@ tq_status tq_set_rows(const tq_cache *dst, const float *src, const int64_t *cell
  * normalizer, with m the maximum over the aligned block of 16 T keys that
  * one wave scores (at most the true maximum).  T is the plan's: the largest
  * of 8, 4, 2, 1 with T (k->head_dim + v->head_dim) / 128 <= 16 and
- * ceil(kv_len / 64T) * n_kv_heads * ceil(n_rep / 8) >= the device's compute
- * units, else 1 (n_rep = n_q_heads / n_kv_heads; for the batched call below,
- * kv_len is max_kv_len and the count is multiplied by n_seq, and n_rep by
- * n_rows).
+ * W(T) = ceil(kv_len / 64T) * n_kv_heads * ceil(n_rep / 8) >= the device's
+ * compute units C, else 1; and 4 in place of 8 when W(8) > C
+ * (n_rep = n_q_heads / n_kv_heads; for the batched call below, kv_len is
+ * max_kv_len, W is multiplied by n_seq and n_rep by n_rows).
  * The output then differs from the dense one by at most
  * sum over {j : e^(s_j - m*) < tau} of (e^(s_j - m*) / sum_i e^(s_i - m*)) |v_j|_2
  * (m* the true maximum).  The products are not skipped, so the call costs

@@ -610,15 +610,21 @@ hipError_t plan_decode(const tq_cache &k, const tq_cache &v, int64_t max_len, in
   p->head_groups = ceil_div(n_rows * n_rep, 8);
   // a split covers 4 ranges of 16 * tiles keys.  Tiles per range: the most
   // (1, 2, 4 or 8) with at most 16 group-tiles per range (tiles x (K groups
-  // + V groups)) that still give every compute unit a workgroup.  Measured:
-  // fewer, larger workgroups cost less setup and fewer split partials, up to
-  // the point where a range's registers and shared memory run short.
+  // + V groups)) that still give every compute unit a workgroup; 8 only
+  // while its grid is a single round (8-tile workgroups hold one compute
+  // unit each).  Measured: fewer, larger workgroups cost less setup and
+  // fewer split partials in one round; over several rounds two 4-tile
+  // workgroups per compute unit hide each other's memory latency (20% faster
+  // for 8 sequences of 2 rows).
   const int groups = k.head_dim / kGroup + v.head_dim / kGroup;
   const int64_t wg_per_split = (int64_t)k.n_kv_heads * p->head_groups * n_seq;
   int tpw = 8;
   while (tpw > 1) {
     const int64_t splits = ceil_div<int64_t>(max_len, 64LL * tpw);
-    if (tpw * groups <= 16 && splits * wg_per_split >= n_cu) break;
+    if (tpw * groups <= 16 && splits * wg_per_split >= n_cu) {
+      if (tpw == 8 && splits * wg_per_split > n_cu) tpw = 4;
+      break;
+    }
     tpw >>= 1;
   }
   p->tiles_per_wave = tpw;

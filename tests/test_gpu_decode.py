@@ -38,13 +38,15 @@ def _caches(bits, k, v, kv_len=None):
 def _plan_block(kv, n_kv, dk, dv):
     """Keys one wave scores (16 T), T as tq.h states the plan picks it: the
     largest of 8, 4, 2, 1 with T (dk + dv) / 128 <= 16 and at least one
-    workgroup per compute unit."""
+    workgroup per compute unit, 4 in place of 8 past one round."""
     import torch
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     groups = (dk + dv) // 128
     tpw = 8
     while tpw > 1 and not (tpw * groups <= 16 and -(-kv // (64 * tpw)) * n_kv >= n_cu):
         tpw //= 2
+    if tpw == 8 and -(-kv // 512) * n_kv > n_cu:
+        tpw = 4
     return 16 * tpw
 
 
