@@ -41,14 +41,14 @@ FP32_PEAK_TFLOPS = 157.3
 # `rocprofv3 --pmc` passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) over
 # `bench.py --no-cpu-baseline --only decode,copy --steps 2 --warmup 1`, each
 # scaled by what the same counter reads for the 256 MiB device copy of that
-# run (FETCH_SIZE reads 131088.5 KiB for 262144 KiB copied: x1.99975;
+# run (FETCH_SIZE reads 131089.8 KiB for 262144 KiB copied: x1.99973;
 # WRITE_SIZE reads 262144 KiB: x1.0).  Valid only for the decode sources it
 # was taken on (sha256 of tq_decode.hip + tq_common.h); otherwise traffic is
 # reported as null.
-DECODE_TRAFFIC = {"sources_sha256": "c525c36f9a4b83dba3d6f8ca20ed53030efaab10a79995fba310385157785688",
-                  "fetch_kib": {"decode_split_kernel": 6558.71, "decode_merge_kernel": 570.51},
+DECODE_TRAFFIC = {"sources_sha256": "f7f573a4eac8f84271fafb52fc2baf9a63429f464ddccd1a2ffd3f6b8c7a7cf5",
+                  "fetch_kib": {"decode_split_kernel": 6568.19, "decode_merge_kernel": 574.04},
                   "write_kib": {"decode_split_kernel": 1088.0, "decode_merge_kernel": 16.0},
-                  "fetch_scale": 1.99975, "write_scale": 1.0}
+                  "fetch_scale": 1.99973, "write_scale": 1.0}
 
 
 def decode_traffic_bytes():
