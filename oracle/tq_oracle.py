@@ -283,6 +283,40 @@ def dequant(codes: np.ndarray, norm16: np.ndarray, bits: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# O2b. The 8-bit block format for an asymmetric K cache
+# --------------------------------------------------------------------------
+#
+# [PR36] (b): the fork can keep K in q8_0 (8-bit blocks) beside a turbo V,
+# "auto-asymmetric".  The page names the format only; reading: a row is cut
+# into blocks of 32 elements, each stored as 32 signed 8-bit codes and one
+# float16 scale d = fp16(max|x| / 127); code = clamp(rint(x / d), -127, 127)
+# with the division in float32 and ties to even; a block whose scale is 0 or
+# not finite stores zero codes.  The element is code * d.  This K is not
+# rotated.
+
+Q8_BLOCK = 32
+Q8_BITS = 8                      # the "bits" tag of a cache in this format
+
+
+def quantize_q8(x: np.ndarray):
+    """float32 [..., 32] -> (codes int8 [..., 32], scales float16 [...])."""
+    x = np.asarray(x, dtype=np.float32)
+    assert x.shape[-1] == Q8_BLOCK
+    amax = np.abs(x).max(axis=-1)
+    d16 = (amax / np.float32(127)).astype(np.float32).astype(np.float16)
+    d32 = d16.astype(np.float32)
+    ok = np.isfinite(d32) & (d32 > 0)
+    safe = np.where(ok, d32, np.float32(1))
+    q = np.clip(np.rint(x / safe[..., None]), -127, 127)
+    return np.where(ok[..., None], q, 0).astype(np.int8), d16
+
+
+def dequant_q8(codes: np.ndarray, d16: np.ndarray) -> np.ndarray:
+    """codes int8 [..., 32], scales float16 [...] -> float64 [..., 32]."""
+    return codes.astype(np.float64) * d16.astype(np.float64)[..., None]
+
+
+# --------------------------------------------------------------------------
 # The compressed cache (two planes per K or V cache)
 # --------------------------------------------------------------------------
 
@@ -296,6 +330,13 @@ def new_cache(bits: int, head_dim: int, n_kv_heads: int, n_cells: int) -> dict:
     """
     assert head_dim % GROUP == 0
     g = head_dim // GROUP
+    if bits == Q8_BITS:
+        # the 8-bit block format: codes int8 [n_kv_heads, n_cells, head_dim/32,
+        # 32], scales float16 [n_kv_heads, n_cells, head_dim/32]
+        nb = head_dim // Q8_BLOCK
+        return {"bits": bits, "head_dim": head_dim,
+                "codes": np.zeros((n_kv_heads, n_cells, nb, Q8_BLOCK), np.int8),
+                "norms": np.zeros((n_kv_heads, n_cells, nb), np.float16)}
     return {
         "bits": bits,
         "head_dim": head_dim,
@@ -313,10 +354,15 @@ def set_rows(cache: dict, src: np.ndarray, cell_idx: np.ndarray) -> None:
     bits = cache["bits"]
     src = np.asarray(src, dtype=np.float32)
     n_rows, n_kv, d = src.shape
+    idx = np.asarray(cell_idx, dtype=np.int64)
+    if bits == Q8_BITS:
+        q, d16 = quantize_q8(src.reshape(n_rows, n_kv, d // Q8_BLOCK, Q8_BLOCK))
+        cache["codes"][:, idx] = q.transpose(1, 0, 2, 3)
+        cache["norms"][:, idx] = d16.transpose(1, 0, 2)
+        return
     g = d // GROUP
     codes, norm16 = quantize_groups(src.reshape(n_rows, n_kv, g, GROUP), bits)
     packed = pack_codes(codes, bits)
-    idx = np.asarray(cell_idx, dtype=np.int64)
     cache["codes"][:, idx] = packed.transpose(1, 0, 2, 3)
     cache["norms"][:, idx] = norm16.transpose(1, 0, 2)
 
@@ -324,6 +370,9 @@ def set_rows(cache: dict, src: np.ndarray, cell_idx: np.ndarray) -> None:
 def dequant_cache(cache: dict, kv_len: int) -> np.ndarray:
     """Original-domain float64 rows [n_kv_heads, kv_len, head_dim]."""
     bits = cache["bits"]
+    if bits == Q8_BITS:
+        x = dequant_q8(cache["codes"][:, :kv_len], cache["norms"][:, :kv_len])
+        return x.reshape(x.shape[0], x.shape[1], -1)
     packed = cache["codes"][:, :kv_len]
     codes = unpack_codes(packed, bits)
     x = dequant(codes, cache["norms"][:, :kv_len], bits)

@@ -451,6 +451,68 @@ def test_decode_batch_brute_force_tiny():
         np.testing.assert_allclose(got[0, r, 0], want, atol=1e-12)
 
 
+# ---------------------------------------------------------------- 8-bit block K
+
+def test_q8_nearest_code_brute_force():
+    """Each code is the integer in [-127, 127] nearest to x / d (d the stored
+    float16 scale; ties to even), found by trying all 255 codes."""
+    rng = np.random.default_rng(17)
+    x = (rng.standard_normal((40, 32)) * np.exp(rng.standard_normal((40, 1)) * 3)).astype(F32)
+    q, d16 = o.quantize_q8(x)
+    d = d16.astype(F32)
+    cand = np.arange(-127, 128, dtype=np.float64)
+    for b in range(40):
+        y = (x[b] / d[b]).astype(np.float64)                 # float32 quotient, as stored
+        err = np.abs(y[:, None] - cand[None, :])
+        best = cand[np.argmin(err, axis=1)]
+        tie = np.isclose(np.sort(err, axis=1)[:, 0], np.sort(err, axis=1)[:, 1])
+        np.testing.assert_array_equal(q[b][~tie], best[~tie])
+        assert np.all(np.abs(q[b][tie] % 2) == 0)            # halves go to the even code
+    assert np.all(d16 == (np.abs(x).max(axis=1) / F32(127)).astype(F32).astype(np.float16))
+
+
+def test_q8_special_cases():
+    z, dz = o.quantize_q8(np.zeros((1, 32), F32))
+    assert np.all(z == 0) and dz[0] == 0
+    one = np.zeros((1, 32), F32); one[0, 5] = -3.5
+    q, d = o.quantize_q8(one)
+    assert q[0, 5] == -127 and np.count_nonzero(q) == 1
+    assert d[0] == np.float16(F32(3.5) / F32(127))
+    # a power-of-two scaling of the block scales d and keeps the codes
+    rng = np.random.default_rng(18)
+    x = rng.standard_normal((8, 32)).astype(F32)
+    q1, d1 = o.quantize_q8(x)
+    q2, d2 = o.quantize_q8(x * F32(16))
+    np.testing.assert_array_equal(q1, q2)
+    np.testing.assert_array_equal(d2.astype(F32), d1.astype(F32) * 16)
+    # error bound: |x - q d| <= d / 2 except where the fp16 scale rounded
+    # down and the largest element clamps at 127 (at most 127 d 2^-11 more)
+    err = np.abs(x - o.dequant_q8(q1, d1))
+    dd = d1.astype(np.float64)[:, None]
+    assert np.all(err <= 0.5 * dd + 127 * dd * 2.0 ** -11 + 1e-12)
+
+
+def test_q8_cache_round_trip_and_decode():
+    """A cache of the 8-bit block format stores what quantize_q8 gives in the
+    [head, cell, block, 32] layout, and the decode over it (K in this format,
+    V turbo3) is attention over the dequantized rows."""
+    rng = np.random.default_rng(19)
+    n, n_kv = 21, 2
+    kk = rng.standard_normal((n, n_kv, 256)).astype(F32)
+    vv = rng.standard_normal((n, n_kv, 128)).astype(F32)
+    kc = o.new_cache(8, 256, n_kv, n); vc = o.new_cache(3, 128, n_kv, n)
+    o.set_rows(kc, kk, np.arange(n)[::-1]); o.set_rows(vc, vv, np.arange(n))
+    q, d = o.quantize_q8(kk[::-1].reshape(n, n_kv, 8, 32))
+    np.testing.assert_array_equal(kc["codes"], q.transpose(1, 0, 2, 3))
+    np.testing.assert_array_equal(kc["norms"], d.transpose(1, 0, 2))
+    k = o.dequant_cache(kc, n)
+    assert k.shape == (n_kv, n, 256)
+    np.testing.assert_allclose(k, kk[::-1].transpose(1, 0, 2), atol=np.abs(kk).max() / 127)
+    qq = rng.standard_normal((4, 256))
+    got = o.attn_decode(kc, vc, n, qq, 0.07)
+    np.testing.assert_allclose(got, _sdpa_fp64(qq[None], k, o.dequant_cache(vc, n), 0.07, n - 1)[0], atol=1e-12)
+
+
 # ---------------------------------------------------------------- int8
 
 def test_int8_brute_force_and_page_invariance():
