@@ -352,6 +352,24 @@ def main():
                 "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
             del wkc, wvc, wout, wws
 
+        # asymmetric cache of the headline shape (leg "decode_wide"): K in
+        # the 8-bit block format beside the turbo3 V, 32 q / 4 kv heads, 32K
+        if want("decode_wide"):
+            akc = [b.new_cache(8, D, NKV, KV) for _ in range(L)]
+            b.tq_set_rows(akc[0], k_src, idx)
+            for i in range(1, L):
+                akc[i].codes.copy_(akc[0].codes); akc[i].norms.copy_(akc[0].norms)
+            aws = torch.empty(b.tq_attn_decode_workspace(akc[0], vcs[0], KV, NQ), dtype=torch.uint8, device=dev)
+            calls = [lambda i=i: b.tq_attn_decode(akc[i], vcs[i], KV, q_dec, scale_dec, out=outs[i], workspace=aws)
+                     for i in range(L)]
+            t_ms = time_graph(calls)
+            nbytes = KV * NKV * ((D + 2 * D // 32) + (48 + 2) * D // 128)
+            gbps = nbytes / (t_ms * 1e-3) / 1e9
+            extras["decode_q8k_turbo3v_32k_gqa8"] = {
+                "us_per_call": round(t_ms * 1e3, 3), "bytes_per_call": nbytes, "GBps": round(gbps, 1),
+                "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+            del akc, aws
+
         # batched decode (leg "decode_batch"): 8 sequences of mixed lengths
         # (131,072 cells in all), 2 query rows each, 32 q / 4 kv heads, one
         # call per layer over L layer caches in one graph; beside it the same

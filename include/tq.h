@@ -51,8 +51,11 @@ typedef enum {
 } tq_status;
 
 /* Cache element types ([PR36] (c)/(d) results table: turbo2, turbo3, turbo4):
- * b = 2, 3, 4 bits per element, 2^b reconstruction levels. */
-typedef enum { TQ_TURBO2 = 2, TQ_TURBO3 = 3, TQ_TURBO4 = 4 } tq_type;
+ * b = 2, 3, 4 bits per element, 2^b reconstruction levels.  TQ_Q8 is the
+ * 8-bit block format of an asymmetric cache's K ([PR36] (b): K kept in
+ * 8-bit blocks beside a turbo V); it serves as the K cache of
+ * tq_attn_decode / tq_attn_decode_batch only. */
+typedef enum { TQ_TURBO2 = 2, TQ_TURBO3 = 3, TQ_TURBO4 = 4, TQ_Q8 = 8 } tq_type;
 
 /* Element type of a query tensor. */
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
@@ -73,6 +76,10 @@ typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
  * Planes (head-major, so one kv head's cells are contiguous):
  *   codes : uint8  [n_kv_heads][n_cells][G][16*b]   16-byte aligned
  *   norms : uint16 [n_kv_heads][n_cells][G]         float16 bits, 4-byte aligned
+ * A TQ_Q8 cache cuts every row into blocks of 32 elements, each stored as
+ * 32 int8 codes and one float16 scale d (element = code * d; not rotated):
+ *   codes : int8   [n_kv_heads][n_cells][head_dim/32][32]   16-byte aligned
+ *   norms : uint16 [n_kv_heads][n_cells][head_dim/32]       float16 scales, 4-byte aligned
  */
 typedef struct {
   int32_t type;       /* tq_type */
@@ -118,6 +125,10 @@ tq_status tq_codebook(int type, float *code_values /*[host]*/, float *mag_thresh
  *   h = 1, 2, .., 64 in that order, the lower element of each pair taking
  *   a + b and the upper a - b ([PR36] (a)); y = u * (1/norm) (0 if norm is
  *   not > 0); sign bit = (y < 0); qs = #{k : |y| > mag_thresholds[k]}.
+ * For a TQ_Q8 cache, per 32-element block x: d = float16(max|x_i| / 127)
+ * (float32 division, nearest-even to float16); code_i = clamp(rint(x_i / d),
+ * -127, 127) with x_i / d the correctly rounded float32 quotient by the
+ * stored d and ties to even; all codes 0 when d is 0 or not finite.
  * The written bytes and norms are a pure function of the source values.
  * n_rows == 0 is a no-op.
  */
@@ -136,7 +147,10 @@ tq_status tq_set_rows(const tq_cache *dst, const float *src, const int64_t *cell
  * group, w_d = code_values[code_d] * norm / sqrt(128), H the 128-point
  * Sylvester-Hadamard matrix.  (The kernels work in the rotated domain,
  * rotating q in and the output back out.)
- * Requires k and v of the same type, n_kv_heads and n_cells,
+ * k may also be a TQ_Q8 cache beside a turbo v ([PR36] (b): the
+ * asymmetric cache): its rows are used as stored (code * scale, no
+ * rotation) and only v's rotation is undone on the output.
+ * Requires k and v of the same turbo type (or k TQ_Q8), n_kv_heads and n_cells,
  * 1 <= kv_len <= n_cells, n_q_heads a multiple of n_kv_heads (else
  * TQ_ERR_INVALID_ARG); this build takes head widths of 128 or 256 for each
  * of k and v, which may differ ([PR36] (b): a 192-wide K head padded to 256
@@ -149,7 +163,7 @@ tq_status tq_set_rows(const tq_cache *dst, const float *src, const int64_t *cell
  * one wave scores (at most the true maximum).  T is the plan's: the largest
  * of 8, 4, 2, 1 with T (k->head_dim + v->head_dim) / 128 <= 16 and
  * W(T) = ceil(kv_len / 64T) * n_kv_heads * ceil(n_rep / 8) >= the device's
- * compute units C, else 1; and 4 in place of 8 when W(8) > C
+ * compute units C, else 1; and 4 in place of 8 when W(8) > C or k is TQ_Q8
  * (n_rep = n_q_heads / n_kv_heads; for the batched call below, kv_len is
  * max_kv_len, W is multiplied by n_seq and n_rep by n_rows).
  * The output then differs from the dense one by at most

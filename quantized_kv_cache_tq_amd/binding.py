@@ -17,9 +17,9 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "lib", "libtq.so")
 
-TQ_TURBO2, TQ_TURBO3, TQ_TURBO4 = 2, 3, 4
+TQ_TURBO2, TQ_TURBO3, TQ_TURBO4, TQ_Q8 = 2, 3, 4, 8
 TQ_F32, TQ_BF16 = 0, 1
-TYPE_BY_NAME = {"turbo2": 2, "turbo3": 3, "turbo4": 4}
+TYPE_BY_NAME = {"turbo2": 2, "turbo3": 3, "turbo4": 4, "q8": 8}
 
 
 class TQError(RuntimeError):
@@ -140,10 +140,15 @@ class TQCacheTensors:
             type_ = TYPE_BY_NAME[type_]
         g = head_dim // 128
         self.type, self.head_dim, self.n_kv_heads, self.n_cells = type_, head_dim, n_kv_heads, n_cells
+        # turbo: [head][cell][group][16 b] code bytes and a norm per group; the
+        # 8-bit block format: [head][cell][block][32] int8 bytes and a scale per block
+        code_shape = (n_kv_heads, n_cells, head_dim // 32, 32) if type_ == TQ_Q8 else \
+            (n_kv_heads, n_cells, g, 16 * type_)
+        norm_shape = (n_kv_heads, n_cells, head_dim // 32) if type_ == TQ_Q8 else (n_kv_heads, n_cells, g)
         if codes is None:
-            codes = torch.zeros((n_kv_heads, n_cells, g, 16 * type_), dtype=torch.uint8, device=device)
+            codes = torch.zeros(code_shape, dtype=torch.uint8, device=device)
         if norms is None:
-            norms = torch.zeros((n_kv_heads, n_cells, g), dtype=torch.float16, device=device)
+            norms = torch.zeros(norm_shape, dtype=torch.float16, device=device)
         self.codes = _dev_tensor(codes, torch.uint8, "codes")
         self.norms = _dev_tensor(norms, torch.float16, "norms")
         self.struct = TQCache(type_, head_dim, n_kv_heads, 0, n_cells,

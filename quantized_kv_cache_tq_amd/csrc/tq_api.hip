@@ -13,10 +13,12 @@ namespace {
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 bool valid_type(int t) { return t == TQ_TURBO2 || t == TQ_TURBO3 || t == TQ_TURBO4; }
+// a cache may also hold the 8-bit block format (an asymmetric cache's K)
+bool valid_cache_type(int t) { return valid_type(t) || t == TQ_Q8; }
 
 tq_status check_cache(const tq_cache *c) {
   if (!c) return TQ_ERR_INVALID_ARG;
-  if (!valid_type(c->type) || c->head_dim < kGroup || c->head_dim % kGroup != 0 ||
+  if (!valid_cache_type(c->type) || c->head_dim < kGroup || c->head_dim % kGroup != 0 ||
       c->n_kv_heads < 1 || c->n_cells < 1 || c->reserved != 0)
     return TQ_ERR_INVALID_ARG;
   if (!c->codes || !c->norms || !aligned(c->codes, 16) || !aligned(c->norms, 4))
@@ -24,16 +26,19 @@ tq_status check_cache(const tq_cache *c) {
   return TQ_OK;
 }
 
-// K and V of one attention call: the same type, kv heads and cells (the
-// kernels address both with one cell count); the head widths must match
-// unless the call allows them to differ.
-tq_status check_pair(const tq_cache *k, const tq_cache *v, bool same_width = true) {
+// K and V of one attention call: the same kv heads and cells (the kernels
+// address both with one cell count) and the same turbo type, unless the call
+// takes an 8-bit block K beside a turbo V; the head widths must match unless
+// the call allows them to differ.
+tq_status check_pair(const tq_cache *k, const tq_cache *v, bool same_width = true,
+                     bool q8_k = false) {
   tq_status s = check_cache(k);
   if (s != TQ_OK) return s;
   s = check_cache(v);
   if (s != TQ_OK) return s;
-  if (k->type != v->type || k->n_kv_heads != v->n_kv_heads || k->n_cells != v->n_cells)
-    return TQ_ERR_INVALID_ARG;
+  if (k->n_kv_heads != v->n_kv_heads || k->n_cells != v->n_cells) return TQ_ERR_INVALID_ARG;
+  if (v->type == TQ_Q8 || (k->type == TQ_Q8 && !q8_k)) return TQ_ERR_UNSUPPORTED;
+  if (k->type != TQ_Q8 && k->type != v->type) return TQ_ERR_INVALID_ARG;
   if (same_width && k->head_dim != v->head_dim) return TQ_ERR_INVALID_ARG;
   return TQ_OK;
 }
@@ -61,10 +66,16 @@ const char *tq_status_str(int status) {
 
 tq_status tq_cache_plane_bytes(int type, int32_t head_dim, int32_t n_kv_heads, int64_t n_cells,
                                size_t *codes_bytes, size_t *norms_bytes) {
-  if (!valid_type(type) || head_dim < kGroup || head_dim % kGroup || n_kv_heads < 1 ||
+  if (!valid_cache_type(type) || head_dim < kGroup || head_dim % kGroup || n_kv_heads < 1 ||
       n_cells < 1)
     return TQ_ERR_INVALID_ARG;
-  const size_t groups = (size_t)n_kv_heads * (size_t)n_cells * (size_t)(head_dim / kGroup);
+  const size_t rows = (size_t)n_kv_heads * (size_t)n_cells;
+  if (type == TQ_Q8) {   // one byte per element, a float16 scale per 32
+    if (codes_bytes) *codes_bytes = rows * (size_t)head_dim;
+    if (norms_bytes) *norms_bytes = rows * (size_t)(head_dim / 32) * 2u;
+    return TQ_OK;
+  }
+  const size_t groups = rows * (size_t)(head_dim / kGroup);
   if (codes_bytes) *codes_bytes = groups * 16u * (size_t)type;
   if (norms_bytes) *norms_bytes = groups * 2u;
   return TQ_OK;
@@ -103,7 +114,7 @@ tq_status tq_set_rows(const tq_cache *dst, const float *src, const int64_t *cell
 
 static tq_status decode_check(const tq_cache *k, const tq_cache *v, int64_t kv_len,
                               int32_t n_q_heads) {
-  tq_status s = check_pair(k, v, /*same_width=*/false);
+  tq_status s = check_pair(k, v, /*same_width=*/false, /*q8_k=*/true);
   if (s != TQ_OK) return s;
   if (kv_len < 1 || kv_len > k->n_cells) return TQ_ERR_INVALID_ARG;
   if (n_q_heads < 1 || n_q_heads % k->n_kv_heads) return TQ_ERR_INVALID_ARG;

@@ -82,6 +82,19 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Four int8 codes (one dword, first in the low byte) -> four exact float16
+// values as two half2 dwords: byte ^ 0x80 is code + 128 in [0, 255]; placed
+// under the exponent bits of 1024 it reads 1024 + code + 128, and
+// subtracting 1152 leaves the code.
+__device__ __forceinline__ u32x2_t i8x4_to_half4(uint32_t w) {
+  typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+  const uint32_t x = w ^ 0x80808080u;
+  const h2_t bias = {(_Float16)1152.f, (_Float16)1152.f};
+  const h2_t lo = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u)) - bias;
+  const h2_t hi = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u)) - bias;
+  return u32x2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
 // The cells of sequence z: [start, start + len) of every kv head.  Without
 // arrays, one sequence of kv_len cells from cell 0; with them, the entries
 // are clamped so that no access leaves the cache (start into [0, n_cells],
@@ -114,7 +127,12 @@ __device__ __forceinline__ SeqExtent seq_extent(const int64_t *seq_start, const 
 // len - n_rows + r, and a kv head's n_rows * n_rep pairs are cut into
 // head groups of eight (blockIdx.y = kv head * n_hg + head group).  Splits
 // past the sequence's length exit at once and write nothing.
-template <int B, int T, int GK, int GV, bool QBF16>
+// KQ8: K in the 8-bit block format ([PR36] (b): an asymmetric cache's K in
+// 8-bit blocks beside the turbo V of type B).  Such K is not rotated, so the
+// query is not either; a key row's 32-element blocks map onto the 32 k-slots
+// of one product each (k-slot (lane >> 4, i) of K-step st <-> element 32 st +
+// 8 (lane >> 4) + i), and each product is scaled by its block's scale.
+template <int B, int T, int GK, int GV, bool QBF16, bool KQ8>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     const uint8_t *__restrict__ kcodes, const uint16_t *__restrict__ knorms,
     const uint8_t *__restrict__ vcodes, const uint16_t *__restrict__ vnorms, int64_t n_cells,
@@ -144,7 +162,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
   // 256-byte aligned: a lookup address is the entry offset OR the lane offset
   __shared__ __align__(256) uint32_t ptab[PairCfg<B>::WORDS];   // pair table, 64 copies
   __shared__ __align__(16) uint32_t block[kBlockWords];
-  __shared__ __align__(16) float nk[GK][4][KPW];
+  __shared__ __align__(16) float nk[GK][4][KPW * (KQ8 ? 4 : 1)];   // K norms, or 4 block scales per key
   __shared__ __align__(16) float nv[GV][4][KPW];
   __shared__ __align__(16) uint32_t qbuf[GK][4 * 64 * 4];   // query operand, [t][lane][8 halves]
   __shared__ float wm[4][8], wl[4][8];
@@ -176,8 +194,11 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
 
   if (kwave) {
     // ---------------- key wave: loads first (query, norms, K codes)
-    const uint8_t *kb = kcodes + row0 * (16 * B * GK);
-    const uint16_t *knb = knorms + row0 * GK, *vnb = vnorms + row0 * GV;
+    constexpr int KRB = KQ8 ? kGroup * GK : 16 * B * GK;   // K bytes per key row
+    constexpr int KNS = KQ8 ? 4 : 1;                          // K scales per group
+    constexpr int KDW = KQ8 ? 8 : B;                          // K dwords per lane, tile and group
+    const uint8_t *kb = kcodes + row0 * KRB;
+    const uint16_t *knb = knorms + row0 * (KNS * GK), *vnb = vnorms + row0 * GV;
     const int qh = 2 * rg + (lane >> 5), qj = lane & 31;
     const int vq = imin(8 * hg + qh, n_vh - 1);   // (row, head) pair of this lane's head
     const int vr = n_rows == 1 ? 0 : vq / n_rep;
@@ -198,38 +219,60 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
         qv[gk][0] = f.x; qv[gk][1] = f.y; qv[gk][2] = f.z; qv[gk][3] = f.w;
       }
     }
-    uint16_t kn[NNORM][GK], vn[NNORM][GV];
+    uint16_t kn[NNORM][GK][KNS], vn[NNORM][GV];
 #pragma unroll
     for (int i = 0; i < NNORM; ++i) {
       const uint32_t kk = (uint32_t)imin(lane + 64 * i, wlast);
 #pragma unroll
-      for (int gk = 0; gk < GK; ++gk) kn[i][gk] = knb[kk * GK + gk];
+      for (int gk = 0; gk < GK; ++gk) {
+        if constexpr (KQ8) {
+          const u32x2_t w = *reinterpret_cast<const u32x2_t *>(knb + (kk * GK + gk) * 4);
+          kn[i][gk][0] = (uint16_t)w.x; kn[i][gk][1] = (uint16_t)(w.x >> 16);
+          kn[i][gk][2] = (uint16_t)w.y; kn[i][gk][3] = (uint16_t)(w.y >> 16);
+        } else {
+          kn[i][gk][0] = knb[kk * GK + gk];
+        }
+      }
 #pragma unroll
       for (int gv = 0; gv < GV; ++gv) vn[i][gv] = vnb[kk * GV + gv];
     }
-    // lane (col, quad) of tile t reads key 16t + col, dwords B*quad ..
-    // B*quad+B-1 of each group
-    uint32_t kd[T][GK][B];
+    // lane (col, quad) of tile t reads key 16t + col: turbo, dwords B*quad ..
+    // B*quad+B-1 of each group; 8-bit blocks, bytes 8quad .. 8quad+7 of each
+    // of the group's four blocks
+    uint32_t kd[T][GK][KDW];
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
       for (int gk = 0; gk < GK; ++gk) {
-        const uint32_t off = (uint32_t)imin(16 * t + col, wlast) * (16u * B * GK) + 16u * B * gk + 4u * B * quad;
-        const uint32_t *row = reinterpret_cast<const uint32_t *>(kb + off);
+        const uint32_t key = (uint32_t)imin(16 * t + col, wlast);
+        if constexpr (KQ8) {
+          const uint8_t *row = kb + key * (uint32_t)KRB + kGroup * gk + 8 * quad;
 #pragma unroll
-        for (int i = 0; i < B; ++i) kd[t][gk][i] = row[i];
+          for (int st = 0; st < 4; ++st) {
+            const u32x2_t w = *reinterpret_cast<const u32x2_t *>(row + 32 * st);
+            kd[t][gk][2 * st] = w.x;
+            kd[t][gk][2 * st + 1] = w.y;
+          }
+        } else {
+          const uint32_t *row = reinterpret_cast<const uint32_t *>(kb + key * (uint32_t)KRB + 16u * B * gk + 4u * B * quad);
+#pragma unroll
+          for (int i = 0; i < B; ++i) kd[t][gk][i] = row[i];
+        }
       }
 
     build_pair_table<B, kDecThreads>(ptab, tid);
-    // rotate + split heads 2rg, 2rg+1, group by group: thread holds d = 4qj ..
-    // 4qj+3 of head qh; in the MFMA B operand they are slots i = 4(qj&1) ..
-    // +3 of K-step t = (qj>>1)&3 in lane 16*(qj>>3) + qh (high half) and
-    // 16*(qj>>3) + 8 + qh (low half)
+    // rotate (turbo K) + split heads 2rg, 2rg+1, group by group: thread holds
+    // d = 4qj .. 4qj+3 of head qh; in the MFMA B operand they are slots
+    // i = 4(qj&1) .. +3 of K-step t = (qj>>1)&3 in lane 16*(qj>>3) + qh (high
+    // half) and 16*(qj>>3) + 8 + qh (low half); for 8-bit block K, of K-step
+    // qj>>3 in lanes 16*((qj>>1)&3) + qh and + 8
 #pragma unroll
     for (int gk = 0; gk < GK; ++gk) {
+      if constexpr (!KQ8) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qv[gk][i] = flip_sign(qv[gk][i], sign_bit_of(4 * qj + i));
-      wht128_half(qv[gk], qj);
+        for (int i = 0; i < 4; ++i) qv[gk][i] = flip_sign(qv[gk][i], sign_bit_of(4 * qj + i));
+        wht128_half(qv[gk], qj);
+      }
       const bool live = 8 * hg + qh < n_vh;
       uint32_t hw[2], lw[2];
 #pragma unroll
@@ -241,7 +284,8 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
         hw[p] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
         lw[p] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
       }
-      const int t = (qj >> 1) & 3, qd = qj >> 3, half_off = 2 * (qj & 1);
+      const int t = KQ8 ? qj >> 3 : (qj >> 1) & 3, qd = KQ8 ? (qj >> 1) & 3 : qj >> 3;
+      const int half_off = 2 * (qj & 1);
       *reinterpret_cast<u32x2_t *>(qbuf[gk] + (t * 64 + 16 * qd + qh) * 4 + half_off) = u32x2_t{hw[0], hw[1]};
       *reinterpret_cast<u32x2_t *>(qbuf[gk] + (t * 64 + 16 * qd + 8 + qh) * 4 + half_off) = u32x2_t{lw[0], lw[1]};
     }
@@ -254,7 +298,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
       if (kk < KPW) {
         const bool ok = kk < wkeys;
 #pragma unroll
-        for (int gk = 0; gk < GK; ++gk) nk[gk][rg][kk] = ok ? half_to_float(kn[i][gk]) : 0.f;
+        for (int gk = 0; gk < GK; ++gk)
+#pragma unroll
+          for (int b = 0; b < KNS; ++b) nk[gk][rg][KNS * kk + b] = ok ? half_to_float(kn[i][gk][b]) : 0.f;
 #pragma unroll
         for (int gv = 0; gv < GV; ++gv) nv[gv][rg][kk] = ok ? half_to_float(vn[i][gv]) : 0.f;
       }
@@ -276,21 +322,41 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     for (int t = 0; t < T; ++t) {
 #pragma unroll
       for (int gk = 0; gk < GK; ++gk) {
-        uint32_t a16[16];
-        decode_pairs<B, 32>(kd[t][gk], tab, a16);
-        float4_t acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (KQ8) {
+          // one product per 32-element block, each times its block's scale
+          float4_t acc[4];
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const u32x4_t av = {a16[4 * st], a16[4 * st + 1], a16[4 * st + 2], a16[4 * st + 3]};
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[gk][st], acc,
-                                                      0, 0, 0);
-        }
-        const float4 n4 = *reinterpret_cast<const float4 *>(&nk[gk][rg][16 * t + 4 * quad]);
-        const float nkv[4] = {n4.x, n4.y, n4.z, n4.w};
+          for (int st = 0; st < 4; ++st) {
+            const u32x2_t a0 = i8x4_to_half4(kd[t][gk][2 * st]);
+            const u32x2_t a1 = i8x4_to_half4(kd[t][gk][2 * st + 1]);
+            const u32x4_t av = {a0.x, a0.y, a1.x, a1.y};
+            acc[st] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[gk][st],
+                                                            float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = (acc[i] + xor_lane<8>(acc[i])) * nkv[i];
-          sc[t][i] = gk == 0 ? x : sc[t][i] + x;
+          for (int i = 0; i < 4; ++i) {
+            const float4 d4 = *reinterpret_cast<const float4 *>(&nk[gk][rg][4 * (16 * t + 4 * quad + i)]);
+            const float y = acc[0][i] * d4.x + acc[1][i] * d4.y + acc[2][i] * d4.z + acc[3][i] * d4.w;
+            const float x = y + xor_lane<8>(y);
+            sc[t][i] = gk == 0 ? x : sc[t][i] + x;
+          }
+        } else {
+          uint32_t a16[16];
+          decode_pairs<B, 32>(kd[t][gk], tab, a16);
+          float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int st = 0; st < 4; ++st) {
+            const u32x4_t av = {a16[4 * st], a16[4 * st + 1], a16[4 * st + 2], a16[4 * st + 3]};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[gk][st], acc,
+                                                        0, 0, 0);
+          }
+          const float4 n4 = *reinterpret_cast<const float4 *>(&nk[gk][rg][16 * t + 4 * quad]);
+          const float nkv[4] = {n4.x, n4.y, n4.z, n4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = (acc[i] + xor_lane<8>(acc[i])) * nkv[i];
+            sc[t][i] = gk == 0 ? x : sc[t][i] + x;
+          }
         }
       }
     }
@@ -618,7 +684,7 @@ hipError_t plan_decode(const tq_cache &k, const tq_cache &v, int64_t max_len, in
   // for 8 sequences of 2 rows).
   const int groups = k.head_dim / kGroup + v.head_dim / kGroup;
   const int64_t wg_per_split = (int64_t)k.n_kv_heads * p->head_groups * n_seq;
-  int tpw = 8;
+  int tpw = k.type == TQ_Q8 ? 4 : 8;   // 8-bit block K: no 8-tile kernel (its rows are 2.7x wider)
   while (tpw > 1) {
     const int64_t splits = ceil_div<int64_t>(max_len, 64LL * tpw);
     if (tpw * groups <= 16 && splits * wg_per_split >= n_cu) {
@@ -653,13 +719,13 @@ struct SplitArgs {
   int n_split;
 };
 
-// Tile counts the plan can choose for GK + GV groups (8 only for one group
-// each: the ranges of wider heads would not fit the registers and LDS).
-template <int B, int GK, int GV, bool QBF>
+// Tile counts the plan can choose for GK + GV groups (8 only for one turbo
+// group each: the ranges of wider heads would not fit the registers and LDS).
+template <int B, int GK, int GV, bool QBF, bool KQ8>
 hipError_t launch_split(int tpw, dim3 grid, hipStream_t st, const SplitArgs &a) {
   dim3 block(kDecThreads);
 #define TQ_DEC(T)                                                                                   \
-  hipLaunchKernelGGL((decode_split_kernel<B, T, GK, GV, QBF>), grid, block, 0, st, a.k->codes,     \
+  hipLaunchKernelGGL((decode_split_kernel<B, T, GK, GV, QBF, KQ8>), grid, block, 0, st, a.k->codes, \
                      a.k->norms, a.v->codes, a.v->norms, a.k->n_cells, a.seq_start, a.seq_len,     \
                      a.kv_len, a.q, a.n_q, a.n_rep, a.n_rows, a.n_hg, a.qs, a.tau, a.ws, a.n_split)
   switch (tpw) {
@@ -667,7 +733,7 @@ hipError_t launch_split(int tpw, dim3 grid, hipStream_t st, const SplitArgs &a) 
     case 2: TQ_DEC(2); break;
     case 4: TQ_DEC(4); break;
     case 8:
-      if constexpr (GK + GV == 2) {
+      if constexpr (GK + GV == 2 && !KQ8) {
         TQ_DEC(8);
         break;
       } else {
@@ -680,16 +746,21 @@ hipError_t launch_split(int tpw, dim3 grid, hipStream_t st, const SplitArgs &a) 
 }
 
 template <int B, int GK, int GV>
-hipError_t launch_split_q(int qbf, int tpw, dim3 grid, hipStream_t st, const SplitArgs &a) {
-  return qbf ? launch_split<B, GK, GV, true>(tpw, grid, st, a) : launch_split<B, GK, GV, false>(tpw, grid, st, a);
+hipError_t launch_split_q(int qbf, int kq8, int tpw, dim3 grid, hipStream_t st, const SplitArgs &a) {
+  if (kq8)
+    return qbf ? launch_split<B, GK, GV, true, true>(tpw, grid, st, a)
+               : launch_split<B, GK, GV, false, true>(tpw, grid, st, a);
+  return qbf ? launch_split<B, GK, GV, true, false>(tpw, grid, st, a)
+             : launch_split<B, GK, GV, false, false>(tpw, grid, st, a);
 }
 
 template <int B>
-hipError_t launch_split_dims(int gk, int gv, int qbf, int tpw, dim3 grid, hipStream_t st, const SplitArgs &a) {
-  if (gk == 1 && gv == 1) return launch_split_q<B, 1, 1>(qbf, tpw, grid, st, a);
-  if (gk == 2 && gv == 2) return launch_split_q<B, 2, 2>(qbf, tpw, grid, st, a);
-  if (gk == 2) return launch_split_q<B, 2, 1>(qbf, tpw, grid, st, a);
-  return launch_split_q<B, 1, 2>(qbf, tpw, grid, st, a);
+hipError_t launch_split_dims(int gk, int gv, int qbf, int kq8, int tpw, dim3 grid, hipStream_t st,
+                             const SplitArgs &a) {
+  if (gk == 1 && gv == 1) return launch_split_q<B, 1, 1>(qbf, kq8, tpw, grid, st, a);
+  if (gk == 2 && gv == 2) return launch_split_q<B, 2, 2>(qbf, kq8, tpw, grid, st, a);
+  if (gk == 2) return launch_split_q<B, 2, 1>(qbf, kq8, tpw, grid, st, a);
+  return launch_split_q<B, 1, 2>(qbf, kq8, tpw, grid, st, a);
 }
 
 }  // namespace
@@ -699,7 +770,9 @@ hipError_t launch_decode(const tq_cache &k, const tq_cache &v, const int64_t *se
                          int32_t n_q_heads, float scale, float sparse_v_tau, float *out,
                          void *workspace, const DecodePlan &p, hipStream_t stream) {
   const int gk = k.head_dim / kGroup, gv = v.head_dim / kGroup;
-  if (gk < 1 || gk > 2 || gv < 1 || gv > 2 || k.type != v.type) return hipErrorNotSupported;
+  const int kq8 = k.type == TQ_Q8 ? 1 : 0;
+  if (gk < 1 || gk > 2 || gv < 1 || gv > 2 || (!kq8 && k.type != v.type) || v.type == TQ_Q8)
+    return hipErrorNotSupported;
   SplitArgs a;
   a.k = &k;
   a.v = &v;
@@ -711,19 +784,19 @@ hipError_t launch_decode(const tq_cache &k, const tq_cache &v, const int64_t *se
   a.n_rep = n_q_heads / k.n_kv_heads;
   a.n_rows = p.n_rows;
   a.n_hg = p.head_groups;
-  // scores in the log2 domain: scale * log2(e), and 1/128 for the two
-  // 1/sqrt(128) factors of the rotated query and the rotated levels
-  a.qs = scale * 1.4426950408889634f / 128.0f;
+  // scores in the log2 domain: scale * log2(e), and for turbo K 1/128 for
+  // the two 1/sqrt(128) factors of the rotated query and the rotated levels
+  a.qs = scale * 1.4426950408889634f / (kq8 ? 1.0f : 128.0f);
   a.tau = sparse_v_tau;
   a.ws = reinterpret_cast<float *>(workspace);
   a.n_split = p.n_split;
   dim3 grid(p.n_split, k.n_kv_heads * p.head_groups, p.n_seq);
   const int qbf = q_dtype == TQ_BF16 ? 1 : 0;
   hipError_t e;
-  switch (k.type) {
-    case TQ_TURBO2: e = launch_split_dims<2>(gk, gv, qbf, p.tiles_per_wave, grid, stream, a); break;
-    case TQ_TURBO3: e = launch_split_dims<3>(gk, gv, qbf, p.tiles_per_wave, grid, stream, a); break;
-    default: e = launch_split_dims<4>(gk, gv, qbf, p.tiles_per_wave, grid, stream, a); break;
+  switch (v.type) {
+    case TQ_TURBO2: e = launch_split_dims<2>(gk, gv, qbf, kq8, p.tiles_per_wave, grid, stream, a); break;
+    case TQ_TURBO3: e = launch_split_dims<3>(gk, gv, qbf, kq8, p.tiles_per_wave, grid, stream, a); break;
+    default: e = launch_split_dims<4>(gk, gv, qbf, kq8, p.tiles_per_wave, grid, stream, a); break;
   }
   if (e != hipSuccess) return e;
   e = hipGetLastError();

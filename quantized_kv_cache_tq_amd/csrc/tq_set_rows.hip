@@ -104,8 +104,63 @@ __global__ __launch_bounds__(64 * kSrWaves) void set_rows_kernel(
   }
 }
 
+// The 8-bit block format (an asymmetric cache's K, [PR36] (b)): eight lanes
+// per 32-element block, each with one 16-byte load of four elements; the
+// block maximum is an exchange over the eight lanes, and each lane writes its
+// four codes as one dword.  Rows are [n_rows][n_kv][head_dim], blocks in
+// order, so consecutive lanes read and write consecutive bytes.
+constexpr int kQ8Threads = 256;
+constexpr int kQ8Block = 32;
+
+__global__ __launch_bounds__(kQ8Threads) void set_rows_q8_kernel(
+    int8_t *__restrict__ codes, uint16_t *__restrict__ scales, const float *__restrict__ src,
+    const int64_t *__restrict__ cell_idx, int64_t n_rows, int32_t n_kv, int32_t head_dim,
+    int64_t n_cells) {
+#pragma clang fp contract(off)
+  const int64_t quad = (int64_t)blockIdx.x * kQ8Threads + threadIdx.x;   // 4 elements
+  const int64_t row_elems = (int64_t)n_kv * head_dim;
+  const int64_t total = n_rows * row_elems / 4;
+  const bool live = quad < total;
+  const float4 x = live ? reinterpret_cast<const float4 *>(src)[quad] : make_float4(0.f, 0.f, 0.f, 0.f);
+  float amax = fmaxf(fmaxf(__builtin_fabsf(x.x), __builtin_fabsf(x.y)),
+                     fmaxf(__builtin_fabsf(x.z), __builtin_fabsf(x.w)));
+  amax = fmaxf(amax, xor_lane<1>(amax));
+  amax = fmaxf(amax, xor_lane<2>(amax));
+  amax = fmaxf(amax, xor_lane<4>(amax));
+  const _Float16 d16 = (_Float16)(amax / 127.0f);      // correctly rounded, then nearest-even
+  const float d = (float)d16;
+  const bool ok = d > 0.f && d <= 65504.f;
+  const float e[4] = {x.x, x.y, x.z, x.w};
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float q = ok ? __builtin_rintf(e[i] / d) : 0.f;    // correctly rounded quotient, ties to even
+    q = fminf(fmaxf(q, -127.f), 127.f);
+    word |= ((uint32_t)(int32_t)q & 0xffu) << (8 * i);
+  }
+  if (!live) return;
+  const int64_t r = (4 * quad) / row_elems;
+  const int64_t rem = 4 * quad - r * row_elems;
+  const int head = (int)(rem / head_dim);
+  const int elem = (int)(rem - (int64_t)head * head_dim);
+  const int64_t c = cell_idx[r];
+  if (c < 0 || c >= n_cells) return;
+  const int64_t row = (int64_t)head * n_cells + c;
+  reinterpret_cast<uint32_t *>(codes + row * head_dim)[elem >> 2] = word;
+  if ((elem & (kQ8Block - 1)) == 0) scales[row * (head_dim / kQ8Block) + elem / kQ8Block] = __builtin_bit_cast(uint16_t, d16);
+}
+
 hipError_t launch_set_rows(const tq_cache &c, const float *src, const int64_t *cell_idx,
                            int64_t n_rows, hipStream_t stream) {
+  if (c.type == TQ_Q8) {
+    const int64_t quads = n_rows * (int64_t)c.n_kv_heads * c.head_dim / 4;
+    const int64_t blocks = ceil_div<int64_t>(quads, kQ8Threads);
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(set_rows_q8_kernel, dim3((unsigned)blocks), dim3(kQ8Threads), 0, stream,
+                       reinterpret_cast<int8_t *>(c.codes), c.norms, src, cell_idx, n_rows, c.n_kv_heads,
+                       c.head_dim, c.n_cells);
+    return hipGetLastError();
+  }
   const int32_t gph = c.head_dim / kGroup;
   const int64_t total = n_rows * (int64_t)c.n_kv_heads * gph;
   const int64_t blocks = ceil_div<int64_t>(total, kSrGroupsPerBlock);

@@ -76,6 +76,27 @@ def test_plane_bytes(bits, per_group):
         b.tq_cache_plane_bytes(5, 128, 8, 1000)         # no such type
 
 
+@needs_lib
+def test_q8_plane_bytes_and_rules():
+    """The 8-bit block K format: one byte per element and a float16 scale
+    per 32; it is a K cache for decode only."""
+    from quantized_kv_cache_tq_amd import binding as b
+    assert b.tq_cache_plane_bytes(8, 256, 4, 100) == (4 * 100 * 256, 4 * 100 * 8 * 2)
+    with pytest.raises(b.TQError):
+        b.tq_codebook(8)
+    lib = b.load_library()
+    q8, t3 = _cache(b, type_=8), _cache(b, type_=3)
+    dec = lambda k, v: lib.tq_attn_decode(ctypes.byref(k), ctypes.byref(v), 50, FAKE + 8, 1, 32, 0.1, 0.0,
+                                          FAKE, FAKE, 1 << 20, None)
+    assert dec(t3, q8) == -2                      # V in the 8-bit format: no kernel
+    assert dec(q8, q8) == -2
+    assert dec(q8, t3) == -1                      # accepted pair; the misaligned q is what fails
+    pre = lambda k, v: lib.tq_attn_prefill(ctypes.byref(k), ctypes.byref(v), 50, FAKE, 1, 3, 32, 47, 0.1,
+                                           FAKE, FAKE, 1 << 20, None)
+    assert pre(q8, t3) == -2
+    assert lib.tq_set_rows(ctypes.byref(q8), FAKE, FAKE, 0, None) == 0
+
+
 # ------------------------------------------------------------ host validation
 
 FAKE = 0x10000000  # aligned, never dereferenced: every call below fails on the host
