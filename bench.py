@@ -45,8 +45,8 @@ FP32_PEAK_TFLOPS = 157.3
 # WRITE_SIZE reads 262144 KiB: x1.0).  Valid only for the decode sources it
 # was taken on (sha256 of tq_decode.hip + tq_common.h); otherwise traffic is
 # reported as null.
-DECODE_TRAFFIC = {"sources_sha256": "f7f573a4eac8f84271fafb52fc2baf9a63429f464ddccd1a2ffd3f6b8c7a7cf5",
-                  "fetch_kib": {"decode_split_kernel": 6568.19, "decode_merge_kernel": 574.04},
+DECODE_TRAFFIC = {"sources_sha256": "e54cc4b5b391baf4badd2357432aa4b71f233bf1651917fffc6be5ddede48fbd",
+                  "fetch_kib": {"decode_split_kernel": 6567.69, "decode_merge_kernel": 574.03},
                   "write_kib": {"decode_split_kernel": 1088.0, "decode_merge_kernel": 16.0},
                   "fetch_scale": 1.99973, "write_scale": 1.0}
 

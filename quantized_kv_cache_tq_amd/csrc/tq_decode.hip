@@ -392,6 +392,12 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     //      maximum) is below tau leaves the value sum but stays in lsum.
     const float lo_sel = col >= 8 ? 1.f : 0.f;
     float lsum = 0.f;
+    // every tile's V norms read up front, so the reads' latencies overlap
+    float4 nvq[T][GV];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int gv = 0; gv < GV; ++gv) nvq[t][gv] = *reinterpret_cast<const float4 *>(&nv[gv][rg][16 * t + 4 * quad]);
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       float p[4];
@@ -402,7 +408,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
       }
 #pragma unroll
       for (int gv = 0; gv < GV; ++gv) {
-        const float4 n4 = *reinterpret_cast<const float4 *>(&nv[gv][rg][16 * t + 4 * quad]);
+        const float4 n4 = nvq[t][gv];
         const float nvv[4] = {n4.x, n4.y, n4.z, n4.w};
         half4_t pa;
 #pragma unroll
@@ -424,31 +430,34 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     if constexpr (kReuse) __syncthreads();   // V rows and P operands consumed
     __syncthreads();   // value products done (partial outputs in obuf)
   } else {
-    // ---------------- value wave: V rows (lane r loads rows r, r + 64, ...)
+    // ---------------- value wave: the range's V rows are contiguous; lane
+    //                  l loads 16-byte chunks l, l + 64, ... of them, so each
+    //                  load instruction covers 1 KB of consecutive bytes
+    constexpr int CH = GV * B;                 // 16-byte chunks per row
+    constexpr int NCH = KPW * CH;
+    constexpr int CPL = ceil_div(NCH, 64);     // chunks per lane
     const uint8_t *vb = vcodes + row0 * (16 * B * GV);
-    u32x4_t vraw[RPL][GV * B];
+    u32x4_t vraw[CPL];
 #pragma unroll
-    for (int j = 0; j < RPL; ++j)
-#pragma unroll
-      for (int i = 0; i < GV * B; ++i)
-        vraw[j][i] = *reinterpret_cast<const u32x4_t *>(
-            vb + (uint32_t)imin(lane + 64 * j, wlast) * (16u * B * GV) + 16u * i);
+    for (int j = 0; j < CPL; ++j) {
+      const int c = imin(lane + 64 * j, NCH - 1);
+      const int r = c / CH, part = c - r * CH;
+      vraw[j] = *reinterpret_cast<const u32x4_t *>(vb + (uint32_t)imin(r, wlast) * (16u * B * GV) + 16u * part);
+    }
     build_pair_table<B, kDecThreads>(ptab, tid);
     __syncthreads();   // table and query operand complete
 
     uint32_t *vr = vrows + rg * KPW * ROWP;
 #pragma unroll
-    for (int j = 0; j < RPL; ++j) {
-      const int r = lane + 64 * j;
-      if (r < KPW) {
-        uint32_t *d = vr + r * ROWP;
-#pragma unroll
-        for (int i = 0; i < GV * B; ++i) {
-          d[4 * i] = vraw[j][i].x;
-          d[4 * i + 1] = vraw[j][i].y;
-          d[4 * i + 2] = vraw[j][i].z;
-          d[4 * i + 3] = vraw[j][i].w;
-        }
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j;
+      if (NCH % 64 == 0 || c < NCH) {
+        const int r = c / CH, part = c - r * CH;
+        uint32_t *d = vr + r * ROWP + 4 * part;
+        d[0] = vraw[j].x;
+        d[1] = vraw[j].y;
+        d[2] = vraw[j].z;
+        d[3] = vraw[j].w;
       }
     }
     wave_lds_fence();
