@@ -79,20 +79,54 @@ struct TileRaw {
   bool page_ok;       // this thread's V/K keys' pages exist
 };
 
-// Physical row of logical key j (j < ctx_len); ok = page entry in range.
-__device__ __forceinline__ int64_t phys_row(const Args &a, int64_t j, bool &ok) {
-  const int64_t pg = a.pt[j >> 5];
-  ok = pg >= 0 && pg < a.n_phys_pages;
-  return (ok ? pg : 0) * kPage + (j & (kPage - 1));
+// The two pages of key tile kt (wave-uniform, so the page-table entries are
+// scalar loads): tile key kk (0..63, clamped to the last key) sits on page
+// p[(kk' >> 5)] at row p * 32 + (kk' & 31); ok = that entry is in range.
+struct TilePages {
+  int64_t base[2];   // first physical row of each page (0 for an entry out of range)
+  bool ok[2];
+  int last_rel;      // last valid key of the tile, relative to its first key
+};
+
+__device__ __forceinline__ TilePages tile_pages(const Args &a, int64_t kt) {
+  const int64_t last = a.ctx_len - 1, lastpg = last >> 5;
+  TilePages t;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int32_t pg = a.pt[lmin(2 * kt + h, lastpg)];
+    t.ok[h] = pg >= 0 && pg < a.n_phys_pages;
+    t.base[h] = (int64_t)(t.ok[h] ? pg : 0) * kPage;
+  }
+  const int64_t rel = last - kt * kKT;
+  t.last_rel = rel < kKT - 1 ? (int)rel : kKT - 1;
+  return t;
 }
 
+// Row index (cell * n_kv + g) of tile key kk for kv head g, and its byte
+// offset in the K / V planes (32-bit arithmetic when the whole cache is below
+// 2^32 bytes, which the host checks).
+template <bool kOff32>
+__device__ __forceinline__ int64_t key_row(const Args &a, const TilePages &t, int g, int kk, bool &ok) {
+  const int j = kk < t.last_rel ? kk : t.last_rel;
+  const int h = j >> 5;
+  ok = h ? t.ok[1] : t.ok[0];
+  const int64_t cell = (h ? t.base[1] : t.base[0]) + (j & (kPage - 1));
+  if constexpr (kOff32) return (int64_t)((uint32_t)cell * (uint32_t)a.n_kv + (uint32_t)g);
+  return cell * a.n_kv + g;
+}
+template <bool kOff32>
+__device__ __forceinline__ int64_t row_bytes(int64_t row) {
+  if constexpr (kOff32) return (int64_t)((uint32_t)row * (uint32_t)kD);
+  return row * kD;
+}
+
+template <bool kOff32>
 __device__ __forceinline__ void load_tile(const Args &a, int g, int64_t kt, int tid, TileRaw &r) {
-  const int64_t last = a.ctx_len - 1;
+  const TilePages t = tile_pages(a, kt);
   bool ok;
   {
-    const int64_t j = lmin(kt * kKT + (tid >> 2), last);
-    const int64_t row = phys_row(a, j, ok);
-    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(a.k + (row * a.n_kv + g) * kD + 32 * (tid & 3));
+    const int64_t e = key_row<kOff32>(a, t, g, tid >> 2, ok);
+    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(a.k + row_bytes<kOff32>(e) + 32 * (tid & 3));
     r.k[0] = src[0];
     r.k[1] = src[1];
   }
@@ -100,18 +134,16 @@ __device__ __forceinline__ void load_tile(const Args &a, int g, int64_t kt, int 
     const int db = tid >> 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t j = lmin(kt * kKT + 4 * (tid & 15) + i, last);
-      const int64_t row = phys_row(a, j, ok);
-      const u32x2_t w = *reinterpret_cast<const u32x2_t *>(a.v + (row * a.n_kv + g) * kD + 8 * db);
+      const int64_t e = key_row<kOff32>(a, t, g, 4 * (tid & 15) + i, ok);
+      const u32x2_t w = *reinterpret_cast<const u32x2_t *>(a.v + row_bytes<kOff32>(e) + 8 * db);
       r.v[i][0] = w.x;
       r.v[i][1] = w.y;
     }
   }
   {
-    const int64_t j = lmin(kt * kKT + (tid & 63), last);
-    const int64_t row = phys_row(a, j, ok);
+    const int64_t e = key_row<kOff32>(a, t, g, tid & 63, ok);
     r.page_ok = ok;
-    r.scl = (tid < 64) ? a.ks[row * a.n_kv + g] : a.vs[row * a.n_kv + g];
+    r.scl = (tid < 64) ? a.ks[e] : a.vs[e];
   }
 }
 
@@ -165,6 +197,7 @@ __device__ __forceinline__ void split_hl(float x, _Float16 &hi, _Float16 &lo) {
   lo = (_Float16)(x - (float)hi);
 }
 
+template <bool kOff32>
 __global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
   constexpr int kArenaHalves = kKT * kKsStride + kD * kVtStride;
   static_assert(kArenaHalves * 2 >= 2 * 4 * 16 * 64 * 4, "merge buffer must fit");
@@ -235,10 +268,10 @@ __global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
   float m_run = -INFINITY, l_run = 0.f;
 
   TileRaw raw;
-  if (kt0 < kt1) load_tile(a, g, kt0, tid, raw);
+  if (kt0 < kt1) load_tile<kOff32>(a, g, kt0, tid, raw);
   for (int64_t kt = kt0; kt < kt1; ++kt) {
     store_tile(a, kt, tid, raw, ksm, vt, sk, sv, ve, kval);
-    if (kt + 1 < kt1) load_tile(a, g, kt + 1, tid, raw);
+    if (kt + 1 < kt1) load_tile<kOff32>(a, g, kt + 1, tid, raw);
     __syncthreads();
 
     f32x16_t s;
@@ -260,15 +293,34 @@ __global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
     // the tile's top at 2^kPSet.  So P never overflows, its parts stay clear
     // of float16 subnormals, and the accumulators are rescaled rarely.
     // Softmax does not depend on the reference.
+    // a tile whose 64 keys all exist (in context, pages in range) and whose
+    // key half no column's causal limit cuts needs no per-key test; the test
+    // is taken wave-uniformly, so the fast path reads no existence flags
+    const TilePages tp = tile_pages(a, kt);
+    const bool whole = tp.last_rel == kKT - 1 && tp.ok[0] && tp.ok[1] && __all(lim >= 31);
     float tref = -INFINITY;
+    auto scale_scores = [&](auto mask_tag) {
+      constexpr bool kMask = decltype(mask_tag)::value;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int kk = 8 * (rr >> 2) + 4 * hl + (rr & 3);
-      float v = __builtin_amdgcn_ldexpf(s[rr], -qexp) * sk[32 * khalf + kk];
-      if (kk > lim || !kval[32 * khalf + kk]) v = -INFINITY;  // causal / no such key
-      s[rr] = v;
-      tref = fmaxf(tref, v + ve[32 * khalf + kk]);
-    }
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int k0 = 8 * g4 + 4 * hl;   // keys k0 .. k0+3 of the half <-> registers 4 g4 .. 4 g4 + 3
+        const float4 sk4 = *reinterpret_cast<const float4 *>(&sk[32 * khalf + k0]);
+        const float4 ve4 = *reinterpret_cast<const float4 *>(&ve[32 * khalf + k0]);
+        const float skv[4] = {sk4.x, sk4.y, sk4.z, sk4.w}, vev[4] = {ve4.x, ve4.y, ve4.z, ve4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = 4 * g4 + i, kk = k0 + i;
+          float v = __builtin_amdgcn_ldexpf(s[rr], -qexp) * skv[i];
+          if (kMask && (kk > lim || !kval[32 * khalf + kk])) v = -INFINITY;  // causal / no such key
+          s[rr] = v;
+          tref = fmaxf(tref, v + vev[i]);
+        }
+      }
+    };
+    if (whole)
+      scale_scores(std::false_type{});
+    else
+      scale_scores(std::true_type{});
     tref = fmaxf(tref, xor_lane<32>(tref));
     const float m_new = tref > m_run + kPTop ? tref - kPSet : m_run;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
@@ -277,14 +329,19 @@ __global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
     half8_t phi[2], plo[2];
     float psum = 0.f;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int kk = 8 * (rr >> 2) + 4 * hl + (rr & 3);
-      const float p = __builtin_amdgcn_exp2f(s[rr] - m_use);
-      psum += p;
-      _Float16 h, l;
-      split_hl(p * sv[32 * khalf + kk], h, l);
-      phi[rr >> 3][rr & 7] = h;
-      plo[rr >> 3][rr & 7] = l;
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const float4 sv4 = *reinterpret_cast<const float4 *>(&sv[32 * khalf + 8 * g4 + 4 * hl]);
+      const float svv[4] = {sv4.x, sv4.y, sv4.z, sv4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = 4 * g4 + i;
+        const float p = __builtin_amdgcn_exp2f(s[rr] - m_use);
+        psum += p;
+        _Float16 h, l;
+        split_hl(p * svv[i], h, l);
+        phi[rr >> 3][rr & 7] = h;
+        plo[rr >> 3][rr & 7] = l;
+      }
     }
     l_run = l_run * alpha + psum;
     if (__any(alpha != 1.0f)) {
@@ -441,7 +498,12 @@ hipError_t launch_int8(const float *q, int64_t n_q, int32_t n_q_heads, const int
   a.qscale = scale * 1.4426950408889634f;  // log2 domain
   if (n_kv_heads > 65535) return hipErrorInvalidValue;
   dim3 grid((unsigned)p.n_q_tiles, (unsigned)p.n_split, (unsigned)n_kv_heads);
-  hipLaunchKernelGGL(i8::int8_prompt_kernel, grid, dim3(i8::kThreads), 0, stream, a);
+  // element offsets of rows fit 32 bits when the whole paged cache does
+  const bool off32 = (uint64_t)n_phys_pages * i8::kPage * (uint64_t)n_kv_heads * i8::kD < (1ull << 32);
+  if (off32)
+    hipLaunchKernelGGL(i8::int8_prompt_kernel<true>, grid, dim3(i8::kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(i8::int8_prompt_kernel<false>, grid, dim3(i8::kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 1) return e;
   const int64_t rows = n_q * n_q_heads;
