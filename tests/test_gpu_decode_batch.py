@@ -1,5 +1,5 @@
-"""GPU parity of tq_attn_decode_batch (several sequences, one or two query
-rows each, lengths read from device arrays) against the float64 oracle's
+"""GPU parity of tq_attn_decode_batch (several sequences, 1-16 query rows
+each, lengths read from device arrays) against the float64 oracle's
 attn_decode_batch; bar: max-abs <= 2e-3 and relative L2 <= 1e-3 per row.
 
 The decode case of the "Graph-safe decode" section of the PR28 page: query
@@ -193,3 +193,15 @@ def test_batch_graph_replay_with_new_lengths():
         np.testing.assert_array_equal(replayed, out.cpu().numpy(), err_msg=f"step {step}")
         want = o.attn_decode_batch(ok, ov, starts, lens, q.astype(np.float64), scale)
         _check(replayed, want, f"replay step {step}")
+
+
+@pytest.mark.parametrize("n_rows,n_q,n_kv", [(3, 8, 2), (5, 4, 1), (16, 2, 1), (1, 32, 2), (4, 48, 3)])
+def test_batch_many_rows_and_wide_gqa(n_rows, n_q, n_kv):
+    """Speculative-verify batches of 3-16 rows and 16 q heads per kv head:
+    (row, head) pairs beyond eight take more head groups over the same cells,
+    each column masked at its own row's causal limit."""
+    starts, lens = [0, 900, 1500], [900, 600, n_rows - 1]
+    got, q, *_, ok, ov, scale = _run(3, 2000, n_kv, n_q, 128, 128, starts, lens, n_rows, 900,
+                                     seed=60 + n_rows + n_q)
+    want = o.attn_decode_batch(ok, ov, starts, lens, q.astype(np.float64), scale)
+    _check(got, want, f"rows={n_rows} heads={n_q}/{n_kv}")
