@@ -20,7 +20,9 @@ constexpr int kSrWaves = 4;
 constexpr int kSrRounds = 4;                              // groups per half-wave
 constexpr int kSrGroupsPerBlock = kSrWaves * 2 * kSrRounds;
 
-template <int B>
+// kSmall: fewer than 2^31 groups in the call, so the one division that
+// places a lane's first group is 32-bit.
+template <int B, bool kSmall>
 __global__ __launch_bounds__(64 * kSrWaves) void set_rows_kernel(
     uint8_t *__restrict__ codes, uint16_t *__restrict__ norms, const float *__restrict__ src,
     const int64_t *__restrict__ cell_idx, int64_t n_rows, int32_t n_kv, int32_t n_groups_per_head,
@@ -32,6 +34,40 @@ __global__ __launch_bounds__(64 * kSrWaves) void set_rows_kernel(
   const int64_t total = n_rows * groups_per_row;
   const int64_t gbase = ((int64_t)blockIdx.x * kSrWaves + wave) * (2 * kSrRounds) + half;
 
+  // the lane's groups gbase, gbase + 2, ...: row, kv head and group of the
+  // first by one division, the later ones stepped from it (the group index
+  // grows by 2, so each carry loop runs at most twice)
+  int64_t row;
+  int head, grp;
+  if constexpr (kSmall) {
+    const uint32_t g32 = (uint32_t)gbase, gpr = (uint32_t)groups_per_row;
+    const uint32_t r32 = g32 / gpr, rem = g32 - r32 * gpr;
+    row = r32;
+    head = (int)(rem / (uint32_t)n_groups_per_head);
+    grp = (int)(rem - (uint32_t)head * (uint32_t)n_groups_per_head);
+  } else {
+    row = gbase / groups_per_row;
+    const int64_t rem = gbase - row * groups_per_row;
+    head = (int)(rem / n_groups_per_head);
+    grp = (int)(rem - (int64_t)head * n_groups_per_head);
+  }
+  int64_t rrow[kSrRounds];
+  int rhead[kSrRounds], rgrp[kSrRounds];
+#pragma unroll
+  for (int r = 0; r < kSrRounds; ++r) {
+    rrow[r] = row;
+    rhead[r] = head;
+    rgrp[r] = grp;
+    grp += 2;
+    while (grp >= n_groups_per_head) {
+      grp -= n_groups_per_head;
+      ++head;
+    }
+    while (head >= n_kv) {
+      head -= n_kv;
+      ++row;
+    }
+  }
   // issue every load first
   float4 x[kSrRounds];
   int64_t cell[kSrRounds];
@@ -40,7 +76,7 @@ __global__ __launch_bounds__(64 * kSrWaves) void set_rows_kernel(
     const int64_t gi = gbase + 2 * r;
     if (gi < total) {
       x[r] = reinterpret_cast<const float4 *>(src + gi * kGroup)[j];
-      cell[r] = cell_idx[gi / groups_per_row];
+      cell[r] = cell_idx[rrow[r]];
     } else {
       x[r] = make_float4(0.f, 0.f, 0.f, 0.f);
       cell[r] = -1;
@@ -91,10 +127,7 @@ __global__ __launch_bounds__(64 * kSrWaves) void set_rows_kernel(
     }
     const int64_t c = cell[r];
     if (gi < total && c >= 0 && c < n_cells) {
-      const int64_t rem = gi % groups_per_row;
-      const int head = (int)(rem / n_groups_per_head);
-      const int grp = (int)(rem - (int64_t)head * n_groups_per_head);
-      const int64_t slot = ((int64_t)head * n_cells + c) * n_groups_per_head + grp;
+      const int64_t slot = ((int64_t)rhead[r] * n_cells + c) * n_groups_per_head + rgrp[r];
       if (w < FB) reinterpret_cast<uint32_t *>(codes + slot * (16 * B))[w] = word;
       if (j == 0) {
         const _Float16 h16 = (_Float16)norm;
@@ -166,20 +199,23 @@ hipError_t launch_set_rows(const tq_cache &c, const float *src, const int64_t *c
   const int64_t blocks = ceil_div<int64_t>(total, kSrGroupsPerBlock);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   dim3 grid((unsigned)blocks), block(64 * kSrWaves);
+  // a lane's first group index stays below total + the groups of one block
+  const bool small = total + kSrGroupsPerBlock < 0x7fffffffLL;
+#define TQ_SR(B)                                                                                   \
+  do {                                                                                             \
+    if (small)                                                                                     \
+      hipLaunchKernelGGL((set_rows_kernel<B, true>), grid, block, 0, stream, c.codes, c.norms, src, \
+                         cell_idx, n_rows, c.n_kv_heads, gph, c.n_cells);                          \
+    else                                                                                           \
+      hipLaunchKernelGGL((set_rows_kernel<B, false>), grid, block, 0, stream, c.codes, c.norms,    \
+                         src, cell_idx, n_rows, c.n_kv_heads, gph, c.n_cells);                     \
+  } while (0)
   switch (c.type) {
-    case TQ_TURBO2:
-      hipLaunchKernelGGL(set_rows_kernel<2>, grid, block, 0, stream, c.codes, c.norms, src,
-                         cell_idx, n_rows, c.n_kv_heads, gph, c.n_cells);
-      break;
-    case TQ_TURBO3:
-      hipLaunchKernelGGL(set_rows_kernel<3>, grid, block, 0, stream, c.codes, c.norms, src,
-                         cell_idx, n_rows, c.n_kv_heads, gph, c.n_cells);
-      break;
-    default:
-      hipLaunchKernelGGL(set_rows_kernel<4>, grid, block, 0, stream, c.codes, c.norms, src,
-                         cell_idx, n_rows, c.n_kv_heads, gph, c.n_cells);
-      break;
+    case TQ_TURBO2: TQ_SR(2); break;
+    case TQ_TURBO3: TQ_SR(3); break;
+    default: TQ_SR(4); break;
   }
+#undef TQ_SR
   return hipGetLastError();
 }
 
