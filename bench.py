@@ -422,6 +422,45 @@ def main():
             extras["decode_8_single_calls_1row_131k_cells"] = {
                 "us_per_layer": round(t_ms * 1e3, 3), "GBps": round(nbytes / (t_ms * 1e-3) / 1e9, 1)}
             del bkc, bvc, bout, sk, sv
+
+        # launch and streaming floors (leg "floor"): what one graph-replayed
+        # launch of an empty kernel costs, and a kernel that only reads the
+        # decode call's bytes once (L distinct buffers, no arithmetic), alone
+        # and followed by a second, tiny launch as the split + merge pair is
+        if want("floor"):
+            import ctypes
+            fl = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(b.__file__)), "lib", "libtq_floor.so"))
+            fl.tqf_empty.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+            fl.tqf_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+            fbufs = [torch.full((kv_bytes_per_call,), i, dtype=torch.uint8, device=dev) for i in range(L)]
+            fout = torch.empty(1024 * 64, dtype=torch.float32, device=dev)
+
+            def fcall(rc):
+                if rc != 0:
+                    raise RuntimeError(f"floor kernel launch failed: hipError {rc}")
+
+            def fs():
+                return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            t_ms = time_graph([lambda: fcall(fl.tqf_empty(256, ctypes.c_void_p(fout.data_ptr()), fs()))] * L)
+            extras["floor_empty_kernel_256wg"] = {"us_per_launch": round(t_ms * 1e3, 3)}
+            for grid in (256, 1024):
+                t_ms = time_graph([lambda i=i: fcall(fl.tqf_read(ctypes.c_void_p(fbufs[i].data_ptr()),
+                                                                  kv_bytes_per_call, grid,
+                                                                  ctypes.c_void_p(fout.data_ptr()), fs()))
+                                   for i in range(L)])
+                gbps = kv_bytes_per_call / (t_ms * 1e-3) / 1e9
+                extras[f"floor_read_{kv_bytes_per_call}B_{grid}wg"] = {
+                    "us_per_call": round(t_ms * 1e3, 3), "GBps": round(gbps, 1),
+                    "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+            t_ms = time_graph([lambda i=i: (fcall(fl.tqf_read(ctypes.c_void_p(fbufs[i].data_ptr()), kv_bytes_per_call,
+                                                              1024, ctypes.c_void_p(fout.data_ptr()), fs())),
+                                            fcall(fl.tqf_empty(32, ctypes.c_void_p(fout.data_ptr()), fs())))
+                               for i in range(L)])
+            gbps = kv_bytes_per_call / (t_ms * 1e-3) / 1e9
+            extras[f"floor_read_{kv_bytes_per_call}B_then_empty_launch"] = {
+                "us_per_call": round(t_ms * 1e3, 3), "GBps": round(gbps, 1),
+                "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+            del fbufs
     log("[bench] extras done")
 
     res = {}

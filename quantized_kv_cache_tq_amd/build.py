@@ -3,7 +3,8 @@
     python -m quantized_kv_cache_tq_amd.build [-j N] [-v]
 
 Objects go to quantized_kv_cache_tq_amd/lib/obj, the library to
-quantized_kv_cache_tq_amd/lib/libtq.so.  Every call recompiles every source.
+quantized_kv_cache_tq_amd/lib/libtq.so, and the benchmark's floor kernels
+(tq_floor.hip) to quantized_kv_cache_tq_amd/lib/libtq_floor.so.  Every call recompiles every source.
 """
 
 from __future__ import annotations
@@ -19,6 +20,9 @@ SRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIB_DIR, "libtq.so")
 SOURCES = ["tq_api.hip", "tq_set_rows.hip", "tq_decode.hip", "tq_prefill.hip", "tq_int8.hip"]
+# benchmark floors (empty launch, one streaming read): not part of libtq
+FLOOR_SOURCE = "tq_floor.hip"
+FLOOR_LIB = os.path.join(LIB_DIR, "libtq_floor.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -64,6 +68,14 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, LIB)
+    # the benchmark's launch and streaming floors: a library of their own
+    fobj = _compile(FLOOR_SOURCE, verbose)
+    tmp = FLOOR_LIB + ".tmp"
+    r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", fobj, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, FLOOR_LIB)
     return LIB
 
 

@@ -398,28 +398,36 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     for (int t = 0; t < T; ++t)
 #pragma unroll
       for (int gv = 0; gv < GV; ++gv) nvq[t][gv] = *reinterpret_cast<const float4 *>(&nv[gv][rg][16 * t + 4 * quad]);
+    // (the dense form without the threshold test when tau is 0: wave-uniform)
+    auto p_tiles = [&](auto sparse_tag) {
+      constexpr bool kSparse = decltype(sparse_tag)::value;
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(sc[t][i] - msafe);
-        lsum += p[i];
-      }
-#pragma unroll
-      for (int gv = 0; gv < GV; ++gv) {
-        const float4 n4 = nvq[t][gv];
-        const float nvv[4] = {n4.x, n4.y, n4.z, n4.w};
-        half4_t pa;
+      for (int t = 0; t < T; ++t) {
+        float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float x = p[i] < tau ? 0.f : p[i] * nvv[i];
-          const _Float16 h = (_Float16)x;
-          pa[i] = (_Float16)__builtin_fmaf(-(float)h, lo_sel, x);
+          p[i] = __builtin_amdgcn_exp2f(sc[t][i] - msafe);
+          lsum += p[i];
         }
-        pbuf[((gv * 4 + rg) * T + t) * 64 + lane] = __builtin_bit_cast(u32x2_t, pa);
+#pragma unroll
+        for (int gv = 0; gv < GV; ++gv) {
+          const float4 n4 = nvq[t][gv];
+          const float nvv[4] = {n4.x, n4.y, n4.z, n4.w};
+          half4_t pa;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = kSparse && p[i] < tau ? 0.f : p[i] * nvv[i];
+            const _Float16 h = (_Float16)x;
+            pa[i] = (_Float16)__builtin_fmaf(-(float)h, lo_sel, x);
+          }
+          pbuf[((gv * 4 + rg) * T + t) * 64 + lane] = __builtin_bit_cast(u32x2_t, pa);
+        }
       }
-    }
+    };
+    if (tau > 0.f)
+      p_tiles(std::true_type{});
+    else
+      p_tiles(std::false_type{});
     lsum += xor_lane<16>(lsum);
     lsum = sum_xor32(lsum);
     if (lane < 8) {
