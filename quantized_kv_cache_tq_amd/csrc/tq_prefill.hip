@@ -198,6 +198,8 @@ __device__ __forceinline__ void load_v(const HeadPtrs &h, int last, int kt, int 
   constexpr int kParts = 128 / D::EV;                 // thread parts per group
   // a part spans two code words unless its bits always fit in one
   constexpr bool kTwo = (B == 3) || (D::EV * B > 32);
+  // the two words of every part lie inside its group: one 8-byte load
+  constexpr bool kPair = kTwo && ((D::EV * B * (kParts - 1)) >> 5) + 1 <= 4 * B - 1;
   const int db = dt >> 4, grp = db / kParts, m = db % kParts;
   const int w0 = (D::EV * B * m) >> 5;
   const int w1 = min(w0 + 1, 4 * B - 1);             // stays inside the group
@@ -205,8 +207,15 @@ __device__ __forceinline__ void load_v(const HeadPtrs &h, int last, int kt, int 
   for (int i = 0; i < 4; ++i) {
     const uint32_t key = (uint32_t)min(kt * kKT + 4 * (dt & 15) + i, last);
     const uint32_t *row = reinterpret_cast<const uint32_t *>(h.vc + key * (16u * B * D::NG) + 16 * B * grp);
-    r.c[i][0] = row[w0];
-    r.c[i][1] = kTwo ? row[w1] : 0u;
+    if constexpr (kPair) {
+      u32x2_t w;
+      __builtin_memcpy(&w, row + w0, sizeof(w));   // 4-byte aligned
+      r.c[i][0] = w.x;
+      r.c[i][1] = w.y;
+    } else {
+      r.c[i][0] = row[w0];
+      r.c[i][1] = kTwo ? row[w1] : 0u;
+    }
     r.n[i] = h.vn[key * (uint32_t)D::NG + grp];
   }
 }
