@@ -41,12 +41,12 @@ FP32_PEAK_TFLOPS = 157.3
 # `rocprofv3 --pmc` passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) over
 # `bench.py --no-cpu-baseline --only decode,copy --steps 2 --warmup 1`, each
 # scaled by what the same counter reads for the 256 MiB device copy of that
-# run (FETCH_SIZE reads 131089.8 KiB for 262144 KiB copied: x1.99973;
+# run (FETCH_SIZE reads 131089.6 KiB for 262144 KiB copied: x1.99973;
 # WRITE_SIZE reads 262144 KiB: x1.0).  Valid only for the decode sources it
 # was taken on (sha256 of tq_decode.hip + tq_common.h); otherwise traffic is
 # reported as null.
-DECODE_TRAFFIC = {"sources_sha256": "e54cc4b5b391baf4badd2357432aa4b71f233bf1651917fffc6be5ddede48fbd",
-                  "fetch_kib": {"decode_split_kernel": 6567.69, "decode_merge_kernel": 574.03},
+DECODE_TRAFFIC = {"sources_sha256": "b814fab647bc898200553d2562825b44f02442f3b9aeac462617a7d64d1d4b47",
+                  "fetch_kib": {"decode_split_kernel": 6575.2, "decode_merge_kernel": 574.0},
                   "write_kib": {"decode_split_kernel": 1088.0, "decode_merge_kernel": 16.0},
                   "fetch_scale": 1.99973, "write_scale": 1.0}
 
