@@ -506,12 +506,26 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
       float4_t o[8];
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) o[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+      // tiles in pairs on the 32-deep product: k-slots (quad, 0..3) hold
+      // the first tile's keys 4 quad + i and (quad, 4..7) the second's, in
+      // both operands, so the sum runs over the same 32 keys; an odd last
+      // tile takes the 16-deep product
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const half4_t pa = __builtin_bit_cast(half4_t, pbuf[((gv * 4 + rg) * T + t) * 64 + lane]);
+      for (int t = 0; t + 1 < T; t += 2) {
+        const u32x2_t p0 = pbuf[((gv * 4 + rg) * T + t) * 64 + lane];
+        const u32x2_t p1 = pbuf[((gv * 4 + rg) * T + t + 1) * 64 + lane];
+        const half8_t pa = __builtin_bit_cast(half8_t, u32x4_t{p0.x, p0.y, p1.x, p1.y});
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const u32x4_t vb = {vbop[t][dt].x, vbop[t][dt].y, vbop[t + 1][dt].x, vbop[t + 1][dt].y};
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(half8_t, vb), o[dt], 0, 0, 0);
+        }
+      }
+      if constexpr (T & 1) {
+        const half4_t pa = __builtin_bit_cast(half4_t, pbuf[((gv * 4 + rg) * T + T - 1) * 64 + lane]);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
-          o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(half4_t, vbop[t][dt]),
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(half4_t, vbop[T - 1][dt]),
                                                        o[dt], 0, 0, 0);
       }
 #pragma unroll
