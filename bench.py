@@ -514,7 +514,7 @@ def main():
 
     # ---------------- CPU baseline: the oracle on a bounded sample
     if not args.no_cpu_baseline and want("decode"):
-        log("[bench] cpu baseline (oracle decode, 2 calls at the 32K shape)")
+        log("[bench] cpu baseline (oracle decode, 8 calls at the 32K shape)")
         import oracle as o
         try:
             from threadpoolctl import threadpool_info
@@ -524,7 +524,7 @@ def main():
         okc, ovc = o.new_cache(3, D, NKV, KV), o.new_cache(3, D, NKV, KV)
         o.set_rows(okc, k_np, np.arange(KV))
         o.set_rows(ovc, v_np, np.arange(KV))
-        reps = 2
+        reps = 8
         t0 = time.perf_counter()
         for _ in range(reps):
             ref = o.attn_decode(okc, ovc, KV, q_np.astype(np.float64), scale_dec)
