@@ -155,17 +155,20 @@ tq_status tq_set_rows(const tq_cache *dst, const float *src, const int64_t *cell
  * TQ_ERR_INVALID_ARG); this build takes head widths of 128 or 256 for each
  * of k and v, which may differ ([PR36] (b): a 192-wide K head padded to 256
  * beside 128-wide V heads, decoded natively; else TQ_ERR_UNSUPPORTED).  A
- * workgroup serves eight q heads of one kv head; more q heads per kv head
- * take more workgroups over the same cells.
+ * workgroup serves P (query row, q head) pairs of one kv head: P = 16 when
+ * a kv head has more than eight pairs (n_pairs = n_rep here, n_rows * n_rep
+ * in the batched call below) and both caches are turbo with 128-wide heads
+ * (the two sets of eight share one decode of the cells), else P = 8; more
+ * pairs take more workgroups over the same cells.
  * sparse_v_tau >= 0 ([PR36] (d) item 3; 0 = off): a key whose weight
  * e^(s - m) is below tau is left out of the value sum and kept in the
  * normalizer, with m the maximum over the aligned block of 16 T keys that
  * one wave scores (at most the true maximum).  T is the plan's: the largest
  * of 8, 4, 2, 1 with T (k->head_dim + v->head_dim) / 128 <= 16 and
- * W(T) = ceil(kv_len / 64T) * n_kv_heads * ceil(n_rep / 8) >= the device's
- * compute units C, else 1; and 4 in place of 8 when W(8) > C or k is TQ_Q8
- * (n_rep = n_q_heads / n_kv_heads; for the batched call below, kv_len is
- * max_kv_len, W is multiplied by n_seq and n_rep by n_rows).
+ * W(T) = ceil(kv_len / 64T) * n_kv_heads * ceil(n_pairs / P) >= the
+ * device's compute units C, else 1; and 4 in place of 8 when W(8) > C, k
+ * is TQ_Q8 or P = 16 (n_rep = n_q_heads / n_kv_heads; for the batched call
+ * below, kv_len is max_kv_len and W is multiplied by n_seq).
  * The output then differs from the dense one by at most
  * sum over {j : e^(s_j - m*) < tau} of (e^(s_j - m*) / sum_i e^(s_i - m*)) |v_j|_2
  * (m* the true maximum).  The products are not skipped, so the call costs

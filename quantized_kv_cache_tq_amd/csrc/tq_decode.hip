@@ -116,24 +116,26 @@ __device__ __forceinline__ SeqExtent seq_extent(const int64_t *seq_start, const 
 // keys.  Waves 0-3 ("key waves") score their range and turn the scores into
 // the matrix-core operand P; waves 4-7 ("value waves") meanwhile decode the
 // V codes of the same ranges into B operands held in registers.  After one
-// barrier every value wave runs its T x 8 value products; the four partial
+// barrier every value wave runs its value products; the four partial
 // outputs are merged in shared memory and written as one split partial.
 // K rows hold GK and V rows GV 128-element groups (head widths 128 GK and
 // 128 GV, which may differ): a score sums its K groups' products, each
 // scaled by that group's norm, and P has one operand per V group (p times
 // that group's norm), the V groups taking their products one after another.
-// The eight heads of a workgroup are (query row, q head) pairs: sequence z =
-// blockIdx.z has n_rows query rows, row r seeing the sequence's cells j <=
-// len - n_rows + r, and a kv head's n_rows * n_rep pairs are cut into
-// head groups of eight (blockIdx.y = kv head * n_hg + head group).  Splits
-// past the sequence's length exit at once and write nothing.
+// The HP (8 or 16) heads of a workgroup are (query row, q head) pairs:
+// sequence z = blockIdx.z has n_rows query rows, row r seeing the sequence's
+// cells j <= len - n_rows + r, and a kv head's n_rows * n_rep pairs are cut
+// into head groups of HP (blockIdx.y = kv head * n_hg + head group).  Sixteen
+// pairs form two column sets of eight that share one decode of the K and V
+// codes, each set with its own score and value products.  Splits past the
+// sequence's length exit at once and write nothing.
 // KQ8: K in the 8-bit block format ([PR36] (b): an asymmetric cache's K in
 // 8-bit blocks beside the turbo V of type B).  Such K is not rotated, so the
 // query is not either; a key row's 32-element blocks map onto the 32 k-slots
 // of one product each (k-slot (lane >> 4, i) of K-step st <-> element 32 st +
 // 8 (lane >> 4) + i), and each product is scaled by its block's scale.
-template <int B, int T, int GK, int GV, bool QBF16, bool KQ8>
-__global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
+template <int B, int T, int GK, int GV, bool QBF16, bool KQ8, int HP>
+__global__ __launch_bounds__(kDecThreads, HP == 16 && B == 3 ? 4 : 2) void decode_split_kernel(
     const uint8_t *__restrict__ kcodes, const uint16_t *__restrict__ knorms,
     const uint8_t *__restrict__ vcodes, const uint16_t *__restrict__ vnorms, int64_t n_cells,
     const int64_t *__restrict__ seq_start, const int32_t *__restrict__ seq_len, int64_t kv_len,
@@ -147,15 +149,17 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
   constexpr int RPL = ceil_div(KPW, 64);       // V rows per lane
   constexpr int NNORM = ceil_div(KPW, 64);
   constexpr int PSTRIDE = DV + 4;              // floats per split partial
+  constexpr int NS = HP / 8;                   // column sets of eight (row, head) pairs
   // One block of shared memory for the V rows of the four ranges (plus one
   // spare dword: a lane's two-dword read of a row may touch the dword after
-  // it), the P operands [GV][4][T][64] and the range outputs [4][8][DV].
-  // With two V groups the outputs reuse the bytes of the rows and operands,
-  // dead by then, so that two workgroups still fit one compute unit.
+  // it), the P operands [GV][4][T][NS][64] and the range outputs [4][HP][DV].
+  // With two V groups or sixteen pairs the outputs reuse the bytes of the
+  // rows and operands, dead by then, so that two workgroups still fit one
+  // compute unit.
   constexpr int kRowWords = (4 * KPW * ROWP + 1 + 3) & ~3;
-  constexpr int kPWords = GV * 4 * T * 64 * 2;
-  constexpr int kOutWords = 4 * 8 * DV;
-  constexpr bool kReuse = GV > 1;
+  constexpr int kPWords = GV * 4 * T * NS * 64 * 2;
+  constexpr int kOutWords = 4 * HP * DV;
+  constexpr bool kReuse = GV > 1 || HP == 16;
   constexpr int kOutOff = kReuse ? 0 : kRowWords + kPWords;
   constexpr int kBlockWords = kReuse ? (kRowWords + kPWords > kOutWords ? kRowWords + kPWords : kOutWords)
                                      : kRowWords + kPWords + kOutWords;
@@ -164,8 +168,8 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
   __shared__ __align__(16) uint32_t block[kBlockWords];
   __shared__ __align__(16) float nk[GK][4][KPW * (KQ8 ? 4 : 1)];   // K norms, or 4 block scales per key
   __shared__ __align__(16) float nv[GV][4][KPW];
-  __shared__ __align__(16) uint32_t qbuf[GK][4 * 64 * 4];   // query operand, [t][lane][8 halves]
-  __shared__ float wm[4][8], wl[4][8];
+  __shared__ __align__(16) uint32_t qbuf[NS][GK][4 * 64 * 4];   // query operand, [t][lane][8 halves]
+  __shared__ float wm[4][HP], wl[4][HP];
   uint32_t *vrows = block;
   u32x2_t *pbuf = reinterpret_cast<u32x2_t *>(block + kRowWords);
   float *obuf = reinterpret_cast<float *>(block + kOutOff);
@@ -199,24 +203,29 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     constexpr int KDW = KQ8 ? 8 : B;                          // K dwords per lane, tile and group
     const uint8_t *kb = kcodes + row0 * KRB;
     const uint16_t *knb = knorms + row0 * (KNS * GK), *vnb = vnorms + row0 * GV;
+    // this lane's query head in column set ns: pair HP hg + 8 ns + qh
     const int qh = 2 * rg + (lane >> 5), qj = lane & 31;
-    const int vq = imin(8 * hg + qh, n_vh - 1);   // (row, head) pair of this lane's head
-    const int vr = n_rows == 1 ? 0 : vq / n_rep;
-    const int64_t qbase = (((int64_t)z * n_rows + vr) * n_q + (int64_t)g * n_rep + (vq - vr * n_rep)) *
-                              (kGroup * GK) + 4 * qj;
-    float qv[GK][4];
+    float qv[NS][GK][4];
 #pragma unroll
-    for (int gk = 0; gk < GK; ++gk) {
-      if constexpr (QBF16) {
-        const u32x2_t b = *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint16_t *>(q) + qbase +
+    for (int ns = 0; ns < NS; ++ns) {
+      const int vq = imin(HP * hg + 8 * ns + qh, n_vh - 1);   // (row, head) pair of this lane's head
+      const int vr = n_rows == 1 ? 0 : vq / n_rep;
+      const int64_t qbase = (((int64_t)z * n_rows + vr) * n_q + (int64_t)g * n_rep + (vq - vr * n_rep)) *
+                                (kGroup * GK) + 4 * qj;
+#pragma unroll
+      for (int gk = 0; gk < GK; ++gk) {
+        if constexpr (QBF16) {
+          const u32x2_t b = *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint16_t *>(q) + qbase +
+                                                               kGroup * gk);
+          qv[ns][gk][0] = __uint_as_float(b.x << 16);
+          qv[ns][gk][1] = __uint_as_float(b.x & 0xffff0000u);
+          qv[ns][gk][2] = __uint_as_float(b.y << 16);
+          qv[ns][gk][3] = __uint_as_float(b.y & 0xffff0000u);
+        } else {
+          const float4 f = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(q) + qbase +
                                                              kGroup * gk);
-        qv[gk][0] = __uint_as_float(b.x << 16);
-        qv[gk][1] = __uint_as_float(b.x & 0xffff0000u);
-        qv[gk][2] = __uint_as_float(b.y << 16);
-        qv[gk][3] = __uint_as_float(b.y & 0xffff0000u);
-      } else {
-        const float4 f = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(q) + qbase + kGroup * gk);
-        qv[gk][0] = f.x; qv[gk][1] = f.y; qv[gk][2] = f.z; qv[gk][3] = f.w;
+          qv[ns][gk][0] = f.x; qv[ns][gk][1] = f.y; qv[ns][gk][2] = f.z; qv[ns][gk][3] = f.w;
+        }
       }
     }
     uint16_t kn[NNORM][GK][KNS], vn[NNORM][GV];
@@ -265,30 +274,34 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     // d = 4qj .. 4qj+3 of head qh; in the MFMA B operand they are slots
     // i = 4(qj&1) .. +3 of K-step t = (qj>>1)&3 in lane 16*(qj>>3) + qh (high
     // half) and 16*(qj>>3) + 8 + qh (low half); for 8-bit block K, of K-step
-    // qj>>3 in lanes 16*((qj>>1)&3) + qh and + 8
+    // qj>>3 in lanes 16*((qj>>1)&3) + qh and + 8 (each column set its own
+    // operand)
 #pragma unroll
-    for (int gk = 0; gk < GK; ++gk) {
-      if constexpr (!KQ8) {
+    for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) qv[gk][i] = flip_sign(qv[gk][i], sign_bit_of(4 * qj + i));
-        wht128_half(qv[gk], qj);
+      for (int gk = 0; gk < GK; ++gk) {
+        if constexpr (!KQ8) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) qv[ns][gk][i] = flip_sign(qv[ns][gk][i], sign_bit_of(4 * qj + i));
+          wht128_half(qv[ns][gk], qj);
+        }
+        const bool live = HP * hg + 8 * ns + qh < n_vh;
+        uint32_t hw[2], lw[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const float x0 = live ? qv[ns][gk][2 * p] * qscale : 0.f;
+          const float x1 = live ? qv[ns][gk][2 * p + 1] * qscale : 0.f;
+          const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+          const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
+          hw[p] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+          lw[p] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+        }
+        const int t = KQ8 ? qj >> 3 : (qj >> 1) & 3, qd = KQ8 ? (qj >> 1) & 3 : qj >> 3;
+        const int half_off = 2 * (qj & 1);
+        *reinterpret_cast<u32x2_t *>(qbuf[ns][gk] + (t * 64 + 16 * qd + qh) * 4 + half_off) = u32x2_t{hw[0], hw[1]};
+        *reinterpret_cast<u32x2_t *>(qbuf[ns][gk] + (t * 64 + 16 * qd + 8 + qh) * 4 + half_off) =
+            u32x2_t{lw[0], lw[1]};
       }
-      const bool live = 8 * hg + qh < n_vh;
-      uint32_t hw[2], lw[2];
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const float x0 = live ? qv[gk][2 * p] * qscale : 0.f;
-        const float x1 = live ? qv[gk][2 * p + 1] * qscale : 0.f;
-        const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-        const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
-        hw[p] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-        lw[p] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
-      }
-      const int t = KQ8 ? qj >> 3 : (qj >> 1) & 3, qd = KQ8 ? (qj >> 1) & 3 : qj >> 3;
-      const int half_off = 2 * (qj & 1);
-      *reinterpret_cast<u32x2_t *>(qbuf[gk] + (t * 64 + 16 * qd + qh) * 4 + half_off) = u32x2_t{hw[0], hw[1]};
-      *reinterpret_cast<u32x2_t *>(qbuf[gk] + (t * 64 + 16 * qd + 8 + qh) * 4 + half_off) = u32x2_t{lw[0], lw[1]};
-    }
     __syncthreads();   // table and query operand complete
 
     // norms of the range (this wave's own slice)
@@ -305,83 +318,103 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
         for (int gv = 0; gv < GV; ++gv) nv[gv][rg][kk] = ok ? half_to_float(vn[i][gv]) : 0.f;
       }
     }
-    // Query operand: column n = lane & 15 -> head n & 7, high (n < 8) or low
-    // half; k-slot (lane >> 4, i) of K-step t <-> element d = 32*(lane>>4) + 8t + i.
-    half8_t qb[GK][4];
+    // Query operand: column n = lane & 15 -> head n & 7 of the set, high
+    // (n < 8) or low half; k-slot (lane >> 4, i) of K-step t <-> element
+    // d = 32*(lane>>4) + 8t + i.
+    half8_t qb[NS][GK][4];
 #pragma unroll
-    for (int gk = 0; gk < GK; ++gk)
+    for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        qb[gk][t] = __builtin_bit_cast(half8_t, reinterpret_cast<const u32x4_t *>(qbuf[gk])[t * 64 + lane]);
+      for (int gk = 0; gk < GK; ++gk)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          qb[ns][gk][t] = __builtin_bit_cast(half8_t, reinterpret_cast<const u32x4_t *>(qbuf[ns][gk])[t * 64 + lane]);
     wave_lds_fence();
 
-    // ---- scores: S^T[key][col] over the range, tile by tile
+    // ---- scores: S^T[key][col] over the range, tile by tile; every column
+    //      set takes the same decoded K operand
     const uint32_t *tab = ptab + lane;
-    float sc[T][4];
+    float sc[T][NS][4];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
 #pragma unroll
       for (int gk = 0; gk < GK; ++gk) {
         if constexpr (KQ8) {
           // one product per 32-element block, each times its block's scale
-          float4_t acc[4];
 #pragma unroll
-          for (int st = 0; st < 4; ++st) {
-            const u32x2_t a0 = i8x4_to_half4(kd[t][gk][2 * st]);
-            const u32x2_t a1 = i8x4_to_half4(kd[t][gk][2 * st + 1]);
-            const u32x4_t av = {a0.x, a0.y, a1.x, a1.y};
-            acc[st] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[gk][st],
-                                                            float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          }
+          for (int ns = 0; ns < NS; ++ns) {
+            float4_t acc[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float4 d4 = *reinterpret_cast<const float4 *>(&nk[gk][rg][4 * (16 * t + 4 * quad + i)]);
-            const float y = acc[0][i] * d4.x + acc[1][i] * d4.y + acc[2][i] * d4.z + acc[3][i] * d4.w;
-            const float x = y + xor_lane<8>(y);
-            sc[t][i] = gk == 0 ? x : sc[t][i] + x;
+            for (int st = 0; st < 4; ++st) {
+              const u32x2_t a0 = i8x4_to_half4(kd[t][gk][2 * st]);
+              const u32x2_t a1 = i8x4_to_half4(kd[t][gk][2 * st + 1]);
+              const u32x4_t av = {a0.x, a0.y, a1.x, a1.y};
+              acc[st] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[ns][gk][st],
+                                                              float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float4 d4 = *reinterpret_cast<const float4 *>(&nk[gk][rg][4 * (16 * t + 4 * quad + i)]);
+              const float y = acc[0][i] * d4.x + acc[1][i] * d4.y + acc[2][i] * d4.z + acc[3][i] * d4.w;
+              const float x = y + xor_lane<8>(y);
+              sc[t][ns][i] = gk == 0 ? x : sc[t][ns][i] + x;
+            }
           }
         } else {
           uint32_t a16[16];
           decode_pairs<B, 32>(kd[t][gk], tab, a16);
-          float4_t acc = {0.f, 0.f, 0.f, 0.f};
+          float4_t acc[NS];
+#pragma unroll
+          for (int ns = 0; ns < NS; ++ns) acc[ns] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int st = 0; st < 4; ++st) {
             const u32x4_t av = {a16[4 * st], a16[4 * st + 1], a16[4 * st + 2], a16[4 * st + 3]};
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[gk][st], acc,
-                                                        0, 0, 0);
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns)
+              acc[ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[ns][gk][st],
+                                                               acc[ns], 0, 0, 0);
           }
           const float4 n4 = *reinterpret_cast<const float4 *>(&nk[gk][rg][16 * t + 4 * quad]);
           const float nkv[4] = {n4.x, n4.y, n4.z, n4.w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x = (acc[i] + xor_lane<8>(acc[i])) * nkv[i];
-            sc[t][i] = gk == 0 ? x : sc[t][i] + x;
-          }
+          for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float x = (acc[ns][i] + xor_lane<8>(acc[ns][i])) * nkv[i];
+              sc[t][ns][i] = gk == 0 ? x : sc[t][ns][i] + x;
+            }
         }
       }
     }
-    // causal limit of this lane's column (head 8hg + (col & 7)): the key
-    // (relative to the range) of its row's last visible cell; only ranges
-    // reaching past the first row's limit mask (wave-uniform)
+    // causal limit of this lane's column (pair HP hg + 8 ns + (col & 7)):
+    // the key (relative to the range) of its row's last visible cell; only
+    // ranges reaching past the first row's limit mask (wave-uniform)
     if (w0 + KPW - 1 > ext.len - n_rows) {
-      const int vc = 8 * hg + (col & 7);
-      const int64_t lim64 = ext.len - n_rows + (vc < n_vh && n_rows > 1 ? vc / n_rep : 0) - w0;
-      const int lim = lim64 < -1 ? -1 : (lim64 > KPW ? KPW : (int)lim64);
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) {
+        const int vc = HP * hg + 8 * ns + (col & 7);
+        const int64_t lim64 = ext.len - n_rows + (vc < n_vh && n_rows > 1 ? vc / n_rep : 0) - w0;
+        const int lim = lim64 < -1 ? -1 : (lim64 > KPW ? KPW : (int)lim64);
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (16 * t + 4 * quad + i > lim) sc[t][ns][i] = -INFINITY;
+      }
+    }
+    // range max per head (log2 domain); -inf for a range without keys
+    float mx[NS], msafe[NS];
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) {
+      float m = -INFINITY;
 #pragma unroll
       for (int t = 0; t < T; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (16 * t + 4 * quad + i > lim) sc[t][i] = -INFINITY;
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, sc[t][ns][i]);
+      m = fmaxf(m, xor_lane<16>(m));
+      mx[ns] = max_xor32(m);
+      msafe[ns] = mx[ns] == -INFINITY ? 0.f : mx[ns];
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[t][i]);
-    // range max per head (log2 domain); -inf for a range without keys
-    mx = fmaxf(mx, xor_lane<16>(mx));
-    mx = max_xor32(mx);
-    const float msafe = mx == -INFINITY ? 0.f : mx;
 
     // ---- P operands: the score layout (lane = column + 16 * key quad) is
     //      the A-operand layout of the value product.  Rows < 8 carry the
@@ -391,7 +424,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     //      3): a key whose weight against the range maximum (<= the true
     //      maximum) is below tau leaves the value sum but stays in lsum.
     const float lo_sel = col >= 8 ? 1.f : 0.f;
-    float lsum = 0.f;
+    float lsum[NS];
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) lsum[ns] = 0.f;
     // every tile's V norms read up front, so the reads' latencies overlap
     float4 nvq[T][GV];
 #pragma unroll
@@ -402,37 +437,42 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     auto p_tiles = [&](auto sparse_tag) {
       constexpr bool kSparse = decltype(sparse_tag)::value;
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        float p[4];
+      for (int t = 0; t < T; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(sc[t][i] - msafe);
-          lsum += p[i];
-        }
-#pragma unroll
-        for (int gv = 0; gv < GV; ++gv) {
-          const float4 n4 = nvq[t][gv];
-          const float nvv[4] = {n4.x, n4.y, n4.z, n4.w};
-          half4_t pa;
+        for (int ns = 0; ns < NS; ++ns) {
+          float p[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float x = kSparse && p[i] < tau ? 0.f : p[i] * nvv[i];
-            const _Float16 h = (_Float16)x;
-            pa[i] = (_Float16)__builtin_fmaf(-(float)h, lo_sel, x);
+            p[i] = __builtin_amdgcn_exp2f(sc[t][ns][i] - msafe[ns]);
+            lsum[ns] += p[i];
           }
-          pbuf[((gv * 4 + rg) * T + t) * 64 + lane] = __builtin_bit_cast(u32x2_t, pa);
+#pragma unroll
+          for (int gv = 0; gv < GV; ++gv) {
+            const float4 n4 = nvq[t][gv];
+            const float nvv[4] = {n4.x, n4.y, n4.z, n4.w};
+            half4_t pa;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float x = kSparse && p[i] < tau ? 0.f : p[i] * nvv[i];
+              const _Float16 h = (_Float16)x;
+              pa[i] = (_Float16)__builtin_fmaf(-(float)h, lo_sel, x);
+            }
+            pbuf[(((gv * 4 + rg) * T + t) * NS + ns) * 64 + lane] = __builtin_bit_cast(u32x2_t, pa);
+          }
         }
-      }
     };
     if (tau > 0.f)
       p_tiles(std::true_type{});
     else
       p_tiles(std::false_type{});
-    lsum += xor_lane<16>(lsum);
-    lsum = sum_xor32(lsum);
-    if (lane < 8) {
-      wm[rg][lane] = mx;
-      wl[rg][lane] = lsum;
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) {
+      float l = lsum[ns] + xor_lane<16>(lsum[ns]);
+      l = sum_xor32(l);
+      if (lane < 8) {
+        wm[rg][8 * ns + lane] = mx[ns];
+        wl[rg][8 * ns + lane] = l;
+      }
     }
     __syncthreads();   // P operands complete
     if constexpr (kReuse) __syncthreads();   // V rows and P operands consumed
@@ -479,7 +519,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     // after the swap, lanes 0-31 hold d-tiles 0-3 and lanes 32-63 d-tiles
     // 4-7, each as high + low; row (head) 4*((lane&31)>>4) + i
     const int qd = (lane & 31) >> 4, dhi = lane >> 5;
-    float4 res[GV][4];
+    float4 res[NS][GV][4];
 #pragma unroll
     for (int gv = 0; gv < GV; ++gv) {
       const uint32_t *vlane = vr + 4 * quad * ROWP + GW * gv + vw0;
@@ -503,58 +543,67 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
       }
       if (gv == 0) __syncthreads();   // P operands complete
 
-      float4_t o[8];
+      // each column set takes the same decoded V operands
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
-      // tiles in pairs on the 32-deep product: k-slots (quad, 0..3) hold
-      // the first tile's keys 4 quad + i and (quad, 4..7) the second's, in
-      // both operands, so the sum runs over the same 32 keys; an odd last
-      // tile takes the 16-deep product
+      for (int ns = 0; ns < NS; ++ns) {
+        float4_t o[8];
 #pragma unroll
-      for (int t = 0; t + 1 < T; t += 2) {
-        const u32x2_t p0 = pbuf[((gv * 4 + rg) * T + t) * 64 + lane];
-        const u32x2_t p1 = pbuf[((gv * 4 + rg) * T + t + 1) * 64 + lane];
-        const half8_t pa = __builtin_bit_cast(half8_t, u32x4_t{p0.x, p0.y, p1.x, p1.y});
+        for (int dt = 0; dt < 8; ++dt) o[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+        // tiles in pairs on the 32-deep product: k-slots (quad, 0..3) hold
+        // the first tile's keys 4 quad + i and (quad, 4..7) the second's, in
+        // both operands, so the sum runs over the same 32 keys; an odd last
+        // tile takes the 16-deep product
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const u32x4_t vb = {vbop[t][dt].x, vbop[t][dt].y, vbop[t + 1][dt].x, vbop[t + 1][dt].y};
-          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(half8_t, vb), o[dt], 0, 0, 0);
+        for (int t = 0; t + 1 < T; t += 2) {
+          const u32x2_t p0 = pbuf[(((gv * 4 + rg) * T + t) * NS + ns) * 64 + lane];
+          const u32x2_t p1 = pbuf[(((gv * 4 + rg) * T + t + 1) * NS + ns) * 64 + lane];
+          const half8_t pa = __builtin_bit_cast(half8_t, u32x4_t{p0.x, p0.y, p1.x, p1.y});
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) {
+            const u32x4_t vb = {vbop[t][dt].x, vbop[t][dt].y, vbop[t + 1][dt].x, vbop[t + 1][dt].y};
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(half8_t, vb), o[dt], 0, 0, 0);
+          }
         }
-      }
-      if constexpr (T & 1) {
-        const half4_t pa = __builtin_bit_cast(half4_t, pbuf[((gv * 4 + rg) * T + T - 1) * 64 + lane]);
+        if constexpr (T & 1) {
+          const half4_t pa =
+              __builtin_bit_cast(half4_t, pbuf[(((gv * 4 + rg) * T + T - 1) * NS + ns) * 64 + lane]);
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-          o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(half4_t, vbop[T - 1][dt]),
-                                                       o[dt], 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float oc[4];
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(o[dt][i]),
-                                                          __float_as_uint(o[dt + 4][i]), false, false);
-          oc[dt] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+          for (int dt = 0; dt < 8; ++dt)
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(half4_t, vbop[T - 1][dt]),
+                                                         o[dt], 0, 0, 0);
         }
-        res[gv][i] = make_float4(oc[0], oc[1], oc[2], oc[3]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float oc[4];
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(o[dt][i]),
+                                                            __float_as_uint(o[dt + 4][i]), false, false);
+            oc[dt] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+          }
+          res[ns][gv][i] = make_float4(oc[0], oc[1], oc[2], oc[3]);
+        }
       }
     }
     if constexpr (kReuse) __syncthreads();   // V rows and P operands consumed
 #pragma unroll
-    for (int gv = 0; gv < GV; ++gv)
+    for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<float4 *>(&obuf[(rg * 8 + 4 * qd + i) * DV + kGroup * gv + 8 * col + 4 * dhi]) =
-            res[gv][i];
+      for (int gv = 0; gv < GV; ++gv)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<float4 *>(
+              &obuf[(rg * HP + 8 * ns + 4 * qd + i) * DV + kGroup * gv + 8 * col + 4 * dhi]) = res[ns][gv][i];
     __syncthreads();   // value products done (partial outputs in obuf)
   }
 
   // ---- merge the four ranges: obuf[r][h][128gv + 8c + t] holds element
-  //      8c + t of group gv of head h, relative to the range's own max
+  //      8c + t of group gv of head h, relative to the range's own max;
+  //      512 / HP threads per head, EPT elements of each group per thread
   {
-    const int h = tid >> 6, d = 2 * (tid & 63);
-    const int vh = 8 * hg + h;
+    constexpr int TPH = kDecThreads / HP, EPT = kGroup / TPH;
+    const int h = tid / TPH, d = EPT * (tid % TPH);
+    const int vh = HP * hg + h;
     if (vh < n_vh) {
       const float M = fmaxf(fmaxf(wm[0][h], wm[1][h]), fmaxf(wm[2][h], wm[3][h]));
       float f[4], L = 0.f;
@@ -570,14 +619,27 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
       float *ph = ws + (qrow * n_split + s) * PSTRIDE;
 #pragma unroll
       for (int gv = 0; gv < GV; ++gv) {
-        float a0 = 0.f, a1 = 0.f;
+        if constexpr (EPT == 2) {
+          float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float2 v = *reinterpret_cast<const float2 *>(&obuf[(r * 8 + h) * DV + kGroup * gv + d]);
-          a0 += f[r] * v.x;
-          a1 += f[r] * v.y;
+          for (int r = 0; r < 4; ++r) {
+            const float2 v = *reinterpret_cast<const float2 *>(&obuf[(r * HP + h) * DV + kGroup * gv + d]);
+            a0 += f[r] * v.x;
+            a1 += f[r] * v.y;
+          }
+          *reinterpret_cast<float2 *>(ph + kGroup * gv + d) = make_float2(a0, a1);
+        } else {
+          float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float4 v = *reinterpret_cast<const float4 *>(&obuf[(r * HP + h) * DV + kGroup * gv + d]);
+            a.x += f[r] * v.x;
+            a.y += f[r] * v.y;
+            a.z += f[r] * v.z;
+            a.w += f[r] * v.w;
+          }
+          *reinterpret_cast<float4 *>(ph + kGroup * gv + d) = a;
         }
-        *reinterpret_cast<float2 *>(ph + kGroup * gv + d) = make_float2(a0, a1);
       }
       if (d == 0) *reinterpret_cast<float2 *>(ph + DV) = make_float2(M, L);
     }
@@ -705,7 +767,12 @@ hipError_t plan_decode(const tq_cache &k, const tq_cache &v, int64_t max_len, in
   const int n_rep = n_q_heads / k.n_kv_heads;
   p->n_rows = n_rows;
   p->n_seq = n_seq;
-  p->head_groups = ceil_div(n_rows * n_rep, 8);
+  // (row, q head) pairs per workgroup: 16 (two column sets over one decode
+  // of the cells) when a kv head has more than eight pairs and both caches
+  // are turbo with 128-wide heads, else 8
+  const int n_pairs = n_rows * n_rep;
+  p->pairs = n_pairs > 8 && k.type != TQ_Q8 && k.head_dim == kGroup && v.head_dim == kGroup ? 16 : 8;
+  p->head_groups = ceil_div(n_pairs, p->pairs);
   // a split covers 4 ranges of 16 * tiles keys.  Tiles per range: the most
   // (1, 2, 4 or 8) with at most 16 group-tiles per range (tiles x (K groups
   // + V groups)) that still give every compute unit a workgroup; 8 only
@@ -716,7 +783,9 @@ hipError_t plan_decode(const tq_cache &k, const tq_cache &v, int64_t max_len, in
   // for 8 sequences of 2 rows).
   const int groups = k.head_dim / kGroup + v.head_dim / kGroup;
   const int64_t wg_per_split = (int64_t)k.n_kv_heads * p->head_groups * n_seq;
-  int tpw = k.type == TQ_Q8 ? 4 : 8;   // 8-bit block K: no 8-tile kernel (its rows are 2.7x wider)
+  // no 8-tile kernel for 8-bit block K (its rows are 2.7x wider) or for 16
+  // pairs (twice the score and value registers)
+  int tpw = k.type == TQ_Q8 || p->pairs == 16 ? 4 : 8;
   while (tpw > 1) {
     const int64_t splits = ceil_div<int64_t>(max_len, 64LL * tpw);
     if (tpw * groups <= 16 && splits * wg_per_split >= n_cu) {
@@ -754,19 +823,33 @@ struct SplitArgs {
 // Tile counts the plan can choose for GK + GV groups (8 only for one turbo
 // group each: the ranges of wider heads would not fit the registers and LDS).
 template <int B, int GK, int GV, bool QBF, bool KQ8>
-hipError_t launch_split(int tpw, dim3 grid, hipStream_t st, const SplitArgs &a) {
+hipError_t launch_split(int tpw, int pairs, dim3 grid, hipStream_t st, const SplitArgs &a) {
   dim3 block(kDecThreads);
-#define TQ_DEC(T)                                                                                   \
-  hipLaunchKernelGGL((decode_split_kernel<B, T, GK, GV, QBF, KQ8>), grid, block, 0, st, a.k->codes, \
-                     a.k->norms, a.v->codes, a.v->norms, a.k->n_cells, a.seq_start, a.seq_len,     \
+#define TQ_DEC(T, HP)                                                                                  \
+  hipLaunchKernelGGL((decode_split_kernel<B, T, GK, GV, QBF, KQ8, HP>), grid, block, 0, st, a.k->codes, \
+                     a.k->norms, a.v->codes, a.v->norms, a.k->n_cells, a.seq_start, a.seq_len,         \
                      a.kv_len, a.q, a.n_q, a.n_rep, a.n_rows, a.n_hg, a.qs, a.tau, a.ws, a.n_split)
+  if (pairs == 16) {
+    // 16 pairs: one turbo group each way, up to 4 tiles
+    if constexpr (GK + GV == 2 && !KQ8) {
+      switch (tpw) {
+        case 1: TQ_DEC(1, 16); break;
+        case 2: TQ_DEC(2, 16); break;
+        case 4: TQ_DEC(4, 16); break;
+        default: return hipErrorNotSupported;
+      }
+      return hipSuccess;
+    } else {
+      return hipErrorNotSupported;
+    }
+  }
   switch (tpw) {
-    case 1: TQ_DEC(1); break;
-    case 2: TQ_DEC(2); break;
-    case 4: TQ_DEC(4); break;
+    case 1: TQ_DEC(1, 8); break;
+    case 2: TQ_DEC(2, 8); break;
+    case 4: TQ_DEC(4, 8); break;
     case 8:
       if constexpr (GK + GV == 2 && !KQ8) {
-        TQ_DEC(8);
+        TQ_DEC(8, 8);
         break;
       } else {
         return hipErrorNotSupported;
@@ -778,21 +861,21 @@ hipError_t launch_split(int tpw, dim3 grid, hipStream_t st, const SplitArgs &a) 
 }
 
 template <int B, int GK, int GV>
-hipError_t launch_split_q(int qbf, int kq8, int tpw, dim3 grid, hipStream_t st, const SplitArgs &a) {
+hipError_t launch_split_q(int qbf, int kq8, int tpw, int pairs, dim3 grid, hipStream_t st, const SplitArgs &a) {
   if (kq8)
-    return qbf ? launch_split<B, GK, GV, true, true>(tpw, grid, st, a)
-               : launch_split<B, GK, GV, false, true>(tpw, grid, st, a);
-  return qbf ? launch_split<B, GK, GV, true, false>(tpw, grid, st, a)
-             : launch_split<B, GK, GV, false, false>(tpw, grid, st, a);
+    return qbf ? launch_split<B, GK, GV, true, true>(tpw, pairs, grid, st, a)
+               : launch_split<B, GK, GV, false, true>(tpw, pairs, grid, st, a);
+  return qbf ? launch_split<B, GK, GV, true, false>(tpw, pairs, grid, st, a)
+             : launch_split<B, GK, GV, false, false>(tpw, pairs, grid, st, a);
 }
 
 template <int B>
-hipError_t launch_split_dims(int gk, int gv, int qbf, int kq8, int tpw, dim3 grid, hipStream_t st,
+hipError_t launch_split_dims(int gk, int gv, int qbf, int kq8, int tpw, int pairs, dim3 grid, hipStream_t st,
                              const SplitArgs &a) {
-  if (gk == 1 && gv == 1) return launch_split_q<B, 1, 1>(qbf, kq8, tpw, grid, st, a);
-  if (gk == 2 && gv == 2) return launch_split_q<B, 2, 2>(qbf, kq8, tpw, grid, st, a);
-  if (gk == 2) return launch_split_q<B, 2, 1>(qbf, kq8, tpw, grid, st, a);
-  return launch_split_q<B, 1, 2>(qbf, kq8, tpw, grid, st, a);
+  if (gk == 1 && gv == 1) return launch_split_q<B, 1, 1>(qbf, kq8, tpw, pairs, grid, st, a);
+  if (gk == 2 && gv == 2) return launch_split_q<B, 2, 2>(qbf, kq8, tpw, pairs, grid, st, a);
+  if (gk == 2) return launch_split_q<B, 2, 1>(qbf, kq8, tpw, pairs, grid, st, a);
+  return launch_split_q<B, 1, 2>(qbf, kq8, tpw, pairs, grid, st, a);
 }
 
 }  // namespace
@@ -826,9 +909,9 @@ hipError_t launch_decode(const tq_cache &k, const tq_cache &v, const int64_t *se
   const int qbf = q_dtype == TQ_BF16 ? 1 : 0;
   hipError_t e;
   switch (v.type) {
-    case TQ_TURBO2: e = launch_split_dims<2>(gk, gv, qbf, kq8, p.tiles_per_wave, grid, stream, a); break;
-    case TQ_TURBO3: e = launch_split_dims<3>(gk, gv, qbf, kq8, p.tiles_per_wave, grid, stream, a); break;
-    default: e = launch_split_dims<4>(gk, gv, qbf, kq8, p.tiles_per_wave, grid, stream, a); break;
+    case TQ_TURBO2: e = launch_split_dims<2>(gk, gv, qbf, kq8, p.tiles_per_wave, p.pairs, grid, stream, a); break;
+    case TQ_TURBO3: e = launch_split_dims<3>(gk, gv, qbf, kq8, p.tiles_per_wave, p.pairs, grid, stream, a); break;
+    default: e = launch_split_dims<4>(gk, gv, qbf, kq8, p.tiles_per_wave, p.pairs, grid, stream, a); break;
   }
   if (e != hipSuccess) return e;
   e = hipGetLastError();

@@ -21,7 +21,8 @@ struct DecodePlan {
   int n_split;           // splits of the longest sequence
   int n_rows;            // query rows per sequence
   int n_seq;             // sequences per call
-  int head_groups;       // workgroups per (split, kv head): eight (row, q head) pairs each
+  int pairs;             // (row, q head) pairs per workgroup: 8 or 16
+  int head_groups;       // workgroups per (split, kv head): `pairs` (row, q head) pairs each
   size_t workspace_bytes;
 };
 // max_len: the longest sequence the call may see (sizes the grid).

@@ -79,7 +79,7 @@ def test_ragged_lengths(kv_len):
     _run(3, q, k, v, kv_len, what=f"ragged kv={kv_len}")
 
 
-@pytest.mark.parametrize("n_q,n_kv", [(1, 1), (2, 1), (4, 2), (8, 1), (12, 3), (32, 4)])
+@pytest.mark.parametrize("n_q,n_kv", [(1, 1), (2, 1), (4, 2), (8, 1), (12, 3), (32, 4), (32, 2), (16, 1), (40, 2)])
 def test_gqa_ratios(n_q, n_kv):
     q, k, v = inputs.small_decode(seed=2, kv_len=3000, n_q=n_q, n_kv=n_kv)
     _run(3, q, k, v, 3000, what=f"gqa {n_q}/{n_kv}")

@@ -205,3 +205,16 @@ def test_batch_many_rows_and_wide_gqa(n_rows, n_q, n_kv):
                                      seed=60 + n_rows + n_q)
     want = o.attn_decode_batch(ok, ov, starts, lens, q.astype(np.float64), scale)
     _check(got, want, f"rows={n_rows} heads={n_q}/{n_kv}")
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("q_bf16", [True, False])
+def test_batch_sixteen_pairs_all_types(bits, q_bf16):
+    """Two rows at 8 q heads per kv head: sixteen (row, head) pairs, served
+    as two column sets of one workgroup over one decode of the cells, for
+    every turbo type and both query dtypes."""
+    starts, lens = [0, 1200, 2500], [1200, 1300, 700]
+    got, q, *_, ok, ov, scale = _run(bits, 3200, 2, 16, 128, 128, starts, lens, 2, 1300, seed=120 + bits,
+                                     q_bf16=q_bf16)
+    want = o.attn_decode_batch(ok, ov, starts, lens, q.astype(np.float64), scale)
+    _check(got, want, f"16 pairs turbo{bits} bf16={q_bf16}")
