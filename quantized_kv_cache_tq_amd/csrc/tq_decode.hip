@@ -135,7 +135,7 @@ __device__ __forceinline__ SeqExtent seq_extent(const int64_t *seq_start, const 
 // of one product each (k-slot (lane >> 4, i) of K-step st <-> element 32 st +
 // 8 (lane >> 4) + i), and each product is scaled by its block's scale.
 template <int B, int T, int GK, int GV, bool QBF16, bool KQ8, int HP>
-__global__ __launch_bounds__(kDecThreads, HP == 16 && B == 3 ? 4 : 2) void decode_split_kernel(
+__global__ __launch_bounds__(kDecThreads, HP == 16 && B == 3 && T <= 4 ? 4 : 2) void decode_split_kernel(
     const uint8_t *__restrict__ kcodes, const uint16_t *__restrict__ knorms,
     const uint8_t *__restrict__ vcodes, const uint16_t *__restrict__ vnorms, int64_t n_cells,
     const int64_t *__restrict__ seq_start, const int32_t *__restrict__ seq_len, int64_t kv_len,
@@ -783,9 +783,8 @@ hipError_t plan_decode(const tq_cache &k, const tq_cache &v, int64_t max_len, in
   // for 8 sequences of 2 rows).
   const int groups = k.head_dim / kGroup + v.head_dim / kGroup;
   const int64_t wg_per_split = (int64_t)k.n_kv_heads * p->head_groups * n_seq;
-  // no 8-tile kernel for 8-bit block K (its rows are 2.7x wider) or for 16
-  // pairs (twice the score and value registers)
-  int tpw = k.type == TQ_Q8 || p->pairs == 16 ? 4 : 8;
+  // no 8-tile kernel for 8-bit block K (its rows are 2.7x wider)
+  int tpw = k.type == TQ_Q8 ? 4 : 8;
   while (tpw > 1) {
     const int64_t splits = ceil_div<int64_t>(max_len, 64LL * tpw);
     if (tpw * groups <= 16 && splits * wg_per_split >= n_cu) {
@@ -836,6 +835,7 @@ hipError_t launch_split(int tpw, int pairs, dim3 grid, hipStream_t st, const Spl
         case 1: TQ_DEC(1, 16); break;
         case 2: TQ_DEC(2, 16); break;
         case 4: TQ_DEC(4, 16); break;
+        case 8: TQ_DEC(8, 16); break;
         default: return hipErrorNotSupported;
       }
       return hipSuccess;
