@@ -422,6 +422,21 @@ def main():
             extras["decode_8_single_calls_1row_131k_cells"] = {
                 "us_per_layer": round(t_ms * 1e3, 3), "GBps": round(nbytes / (t_ms * 1e-3) / 1e9, 1)}
             del bkc, bvc, bout, sk, sv
+            # two rows (speculative verify) over one 32K sequence of the
+            # headline caches: 32 (row, head) pairs, two workgroups of sixteen
+            st2 = torch.tensor([0], dtype=torch.int64, device=dev)
+            ln2 = torch.tensor([KV], dtype=torch.int32, device=dev)
+            q2 = torch.from_numpy(inputs.bf16_round(rng.standard_normal((1, 2, NQ, D)).astype(np.float32)))
+            q2 = q2.to(torch.bfloat16).to(dev)
+            ws2 = torch.empty(b.tq_attn_decode_batch_workspace(kcs[0], vcs[0], 1, 2, KV, NQ), dtype=torch.uint8,
+                              device=dev)
+            out2 = [torch.empty((1, 2, NQ, D), dtype=torch.float32, device=dev) for _ in range(L)]
+            t_ms = time_graph([lambda i=i: b.tq_attn_decode_batch(kcs[i], vcs[i], st2, ln2, KV, q2, scale_dec,
+                                                                  out=out2[i], workspace=ws2) for i in range(L)])
+            gbps = kv_bytes_per_call / (t_ms * 1e-3) / 1e9
+            extras["decode_2rows_32k_gqa8"] = {"us_per_call": round(t_ms * 1e3, 3), "bytes_per_call": kv_bytes_per_call,
+                                               "GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+            del out2, ws2
 
         # launch and streaming floors (leg "floor"): what one graph-replayed
         # launch of an empty kernel costs, and a kernel that only reads the
