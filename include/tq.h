@@ -166,9 +166,9 @@ tq_status tq_set_rows(const tq_cache *dst, const float *src, const int64_t *cell
  * one wave scores (at most the true maximum).  T is the plan's: the largest
  * of 8, 4, 2, 1 with T (k->head_dim + v->head_dim) / 128 <= 16 and
  * W(T) = ceil(kv_len / 64T) * n_kv_heads * ceil(n_pairs / P) >= the
- * device's compute units C, else 1; and 4 in place of 8 when W(8) > C or k
- * is TQ_Q8 (n_rep = n_q_heads / n_kv_heads; for the batched call below,
- * kv_len is max_kv_len and W is multiplied by n_seq).
+ * device's compute units C, else 1; and 4 in place of 8 when W(8) > C
+ * (n_rep = n_q_heads / n_kv_heads; for the batched call below, kv_len is
+ * max_kv_len and W is multiplied by n_seq).
  * The output then differs from the dense one by at most
  * sum over {j : e^(s_j - m*) < tau} of (e^(s_j - m*) / sum_i e^(s_i - m*)) |v_j|_2
  * (m* the true maximum).  The products are not skipped, so the call costs

@@ -783,8 +783,7 @@ hipError_t plan_decode(const tq_cache &k, const tq_cache &v, int64_t max_len, in
   // for 8 sequences of 2 rows).
   const int groups = k.head_dim / kGroup + v.head_dim / kGroup;
   const int64_t wg_per_split = (int64_t)k.n_kv_heads * p->head_groups * n_seq;
-  // no 8-tile kernel for 8-bit block K (its rows are 2.7x wider)
-  int tpw = k.type == TQ_Q8 ? 4 : 8;
+  int tpw = 8;
   while (tpw > 1) {
     const int64_t splits = ceil_div<int64_t>(max_len, 64LL * tpw);
     if (tpw * groups <= 16 && splits * wg_per_split >= n_cu) {
@@ -848,7 +847,7 @@ hipError_t launch_split(int tpw, int pairs, dim3 grid, hipStream_t st, const Spl
     case 2: TQ_DEC(2, 8); break;
     case 4: TQ_DEC(4, 8); break;
     case 8:
-      if constexpr (GK + GV == 2 && !KQ8) {
+      if constexpr (GK + GV == 2) {
         TQ_DEC(8, 8);
         break;
       } else {
