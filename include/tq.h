@@ -233,6 +233,14 @@ tq_status tq_attn_decode_batch(const tq_cache *k, const tq_cache *v, int32_t n_s
  * "Scope / honesty" validates its fast path for turbo3 at head_dim 256 only;
  * the other types use the same kernel with a wider or narrower pair table,
  * head_dim 128 the same kernel with half the products per tile).
+ * Calls of at most 64 rows run the split-key decode kernels instead of the
+ * tiled ones, as one sequence of q_pos0 + n_rows cells whose row r sees
+ * cells <= q_pos0 + r (the tiled kernel has no key split, so a few rows
+ * after a long prefix would occupy a handful of compute units).  [PR28]
+ * "Graph-safe decode" routes only batches of at most two rows to its decode
+ * kernel.  These calls need a workspace; tq_attn_prefill_workspace (same
+ * k, n_rows, n_q_heads and a kv_len >= q_pos0 + n_rows) gives its size,
+ * 0 for the tiled calls.  Both paths meet the same accuracy bar.
  */
 tq_status tq_attn_prefill_workspace(const tq_cache *k, int64_t n_rows, int32_t n_q_heads,
                                     int64_t kv_len, size_t *bytes /*[host]*/);

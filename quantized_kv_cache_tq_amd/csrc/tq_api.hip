@@ -210,11 +210,28 @@ static tq_status prefill_check(const tq_cache *k, int64_t n_rows, int32_t n_q_he
   return TQ_OK;
 }
 
+// Calls of at most this many query rows take the split-key decode kernels:
+// one sequence of q_pos0 + n_rows cells from cell 0 whose row r sees cells
+// <= q_pos0 + r (the same layouts for q and out).  The tiled kernel has one
+// workgroup per two 32-row tiles and kv head and no key split, so a few rows
+// after a long prefix ran on a handful of compute units: measured at 16 q / 8
+// kv heads, head_dim 256, 3 rows after 1024 cells 37.3 us tiled against 8.9
+// us split, after 16384 cells 447 us against 17 us, and 64 rows after 1024
+// cells 75.9 us against 18.4 us.
+constexpr int64_t kPrefillSplitRows = 64;
+
 tq_status tq_attn_prefill_workspace(const tq_cache *k, int64_t n_rows, int32_t n_q_heads,
                                     int64_t kv_len, size_t *bytes) {
   tq_status s = prefill_check(k, n_rows, n_q_heads, kv_len);
   if (s != TQ_OK) return s;
   if (!bytes) return TQ_ERR_INVALID_ARG;
+  if (n_rows >= 1 && n_rows <= kPrefillSplitRows) {
+    // sized for the longest sequence the call may see (q_pos0 + n_rows <= kv_len)
+    DecodePlan dp;
+    if (tq_status st = from_hip(plan_decode(*k, *k, kv_len, n_q_heads, (int)n_rows, 1, &dp))) return st;
+    *bytes = dp.workspace_bytes;
+    return TQ_OK;
+  }
   PrefillPlan p;
   if (plan_prefill(*k, n_rows, n_q_heads, kv_len, &p) != hipSuccess) return TQ_ERR_HIP;
   *bytes = p.workspace_bytes;
@@ -234,6 +251,15 @@ tq_status tq_attn_prefill(const tq_cache *k, const tq_cache *v, int64_t kv_len, 
   if (!(scale == scale)) return TQ_ERR_INVALID_ARG;
   if (n_rows == 0) return TQ_OK;
   if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return TQ_ERR_INVALID_ARG;
+  if (n_rows <= kPrefillSplitRows) {
+    const int64_t len = q_pos0 + n_rows;
+    DecodePlan dp;
+    if (tq_status st = from_hip(plan_decode(*k, *v, len, n_q_heads, (int)n_rows, 1, &dp))) return st;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < dp.workspace_bytes)
+      return TQ_ERR_WORKSPACE;
+    return from_hip(launch_decode(*k, *v, nullptr, nullptr, len, q, q_dtype, n_q_heads, scale, 0.f, out,
+                                  workspace, dp, (hipStream_t)stream));
+  }
   PrefillPlan p;
   if (plan_prefill(*k, n_rows, n_q_heads, kv_len, &p) != hipSuccess) return TQ_ERR_HIP;
   if (p.workspace_bytes && (!workspace || !aligned(workspace, 256) ||

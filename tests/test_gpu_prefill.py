@@ -146,3 +146,36 @@ def test_head_dim_128_causal_1024():
     q, k, v = inputs.prefill(seed=12, rows=1024, n_q=32, n_kv=8, d=128)
     (ma, rl), _ = _run(q, k, v, 1024, 0, what="d128 causal")
     print(f"    max_abs={ma:.3g} rel_l2={rl:.3g}")
+
+
+@pytest.mark.parametrize("rows,kv,q0", [(3, 6000, 5997), (17, 6000, 2000), (64, 6000, 5936), (65, 6000, 5935)])
+def test_few_rows_after_long_prefix(rows, kv, q0):
+    """Calls of at most 64 rows run the split-key kernels (one sequence of
+    q_pos0 + n_rows cells), 65 rows the tiled kernel; both against the oracle,
+    including a prefix that ends before the cache does (q0 + rows < kv)."""
+    q, k, v = inputs.prefill(seed=rows + 7, rows=rows, kv_len=kv)
+    _run(q, k, v, kv, q0, what="long prefix")
+
+
+def test_few_rows_workspace_rule():
+    """The workspace of a split-key call comes from tq_attn_prefill_workspace
+    with a kv_len at least q_pos0 + n_rows; the tiled calls need none."""
+    import torch
+    from quantized_kv_cache_tq_amd import binding as b
+    from gpu_util import bf16_cuda, cuda
+    q, k, v = inputs.prefill(seed=9, rows=5, kv_len=3000, n_q=16, n_kv=8)
+    idx = np.arange(3000)
+    kc, vc = b.new_cache(3, 256, 8, 3000), b.new_cache(3, 256, 8, 3000)
+    b.tq_set_rows(kc, cuda(k), cuda(idx))
+    b.tq_set_rows(vc, cuda(v), cuda(idx))
+    assert b.tq_attn_prefill_workspace(kc, 65, 16, 3000) == 0
+    need = b.tq_attn_prefill_workspace(kc, 5, 16, 3000)
+    assert need > 0
+    assert b.tq_attn_prefill_workspace(kc, 5, 16, 1000) <= need
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = b.tq_attn_prefill(kc, vc, 3000, bf16_cuda(q), 2995, 1.0 / 16.0, workspace=ws)
+    torch.cuda.synchronize()
+    with pytest.raises(b.TQError):
+        b.tq_attn_prefill(kc, vc, 3000, bf16_cuda(q), 2995, 1.0 / 16.0,
+                          workspace=torch.empty(64, dtype=torch.uint8, device="cuda"))
+    assert np.all(np.isfinite(out.cpu().numpy()))
