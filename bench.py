@@ -45,8 +45,8 @@ FP32_PEAK_TFLOPS = 157.3
 # WRITE_SIZE reads 262144 KiB: x1.0).  Valid only for the decode sources it
 # was taken on (sha256 of tq_decode.hip + tq_common.h); otherwise traffic is
 # reported as null.
-DECODE_TRAFFIC = {"sources_sha256": "b814fab647bc898200553d2562825b44f02442f3b9aeac462617a7d64d1d4b47",
-                  "fetch_kib": {"decode_split_kernel": 6575.2, "decode_merge_kernel": 574.0},
+DECODE_TRAFFIC = {"sources_sha256": "839872e0e97b80d0a54e08844a8f259ef6db44cbf28ffa718b6e036a77a242cd",
+                  "fetch_kib": {"decode_split_kernel": 6573.5, "decode_merge_kernel": 561.0},
                   "write_kib": {"decode_split_kernel": 1088.0, "decode_merge_kernel": 16.0},
                   "fetch_scale": 1.99973, "write_scale": 1.0}
 
