@@ -74,7 +74,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=24)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
-                    help="comma list of legs: set_rows,decode,prefill,int8 (default: all); "
+                    help="comma list of legs: set_rows,decode,prefill,int8 (default: all; extras decode_wide, "
+                         "decode_batch, floor, int8_140k); "
                          "'copy' adds a 256 MiB device copy used to calibrate HBM counters")
     return ap.parse_args()
 
@@ -292,6 +293,24 @@ def main():
         tf = prefill["flops"] / (t_ms * 1e-3) / 1e12
         extras["prefill_turbo3_d128_32q8kv"] = {"us": round(t_ms * 1e3, 2), "TFLOPs": round(tf, 2),
                                                 "frac_mfma_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+    if int8 is not None and want("int8_140k"):
+        # the int8 prompt at the longer of the two contexts: 2048 queries at
+        # the end of 140000 cells (leg "int8_140k")
+        d8l = inputs.int8_prompt(seed=1, ctx=140000)
+        tl = {k_: torch.from_numpy(v_).to(dev) for k_, v_ in d8l.items() if not k_.endswith("logical")}
+        nql, nqhl, ddl = d8l["q"].shape
+        q0l = 140000 - nql
+        wsl = torch.empty(max(256, b.tq_attn_int8_prompt_workspace(nql, nqhl, 1, ddl, 140000)), dtype=torch.uint8,
+                          device=dev)
+        outl = torch.empty((nql, nqhl, ddl), dtype=torch.float32, device=dev)
+        t_ms = time_eager(lambda: b.tq_attn_int8_prompt(tl["q"], tl["k8"], tl["v8"], tl["k_scale"], tl["v_scale"],
+                                                        tl["page_table"], 140000, q0l, 1.0 / math.sqrt(ddl),
+                                                        out=outl, workspace=wsl), reps=5)
+        pairs_l = sum(min(140000, q0l + i + 1) for i in range(nql))
+        tf = 4.0 * ddl * nqhl * pairs_l / (t_ms * 1e-3) / 1e12
+        extras["int8_prompt_140k_2048q"] = {"ms": round(t_ms, 4), "TFLOPs": round(tf, 2),
+                                            "frac_mfma_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+        del tl, outl, wsl
     if graph is not None:
         # sparse V at the pages' turbo3 threshold against the dense call, one
         # 32K cache, eager (launch overhead included in both)
