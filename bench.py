@@ -75,7 +75,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
                     help="comma list of legs: set_rows,decode,prefill,int8 (default: all; extras decode_wide, "
-                         "decode_batch, floor, int8_140k); "
+                         "decode_batch, floor, prefill_rows, int8_140k); "
                          "'copy' adds a 256 MiB device copy used to calibrate HBM counters")
     return ap.parse_args()
 
@@ -293,6 +293,25 @@ def main():
         tf = prefill["flops"] / (t_ms * 1e-3) / 1e12
         extras["prefill_turbo3_d128_32q8kv"] = {"us": round(t_ms * 1e3, 2), "TFLOPs": round(tf, 2),
                                                 "frac_mfma_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+    if prefill is not None and want("prefill_rows"):
+        # the other two prompt lengths of the prefill workload, 512 and 4096
+        # causal rows against as many cells (leg "prefill_rows")
+        for R2 in (512, 4096):
+            q2_, k2_, v2_ = inputs.prefill(seed=2, rows=R2)
+            k2c, v2c = b.new_cache(3, PD, PNKV, R2), b.new_cache(3, PD, PNKV, R2)
+            idx2 = torch.arange(R2, dtype=torch.int64, device=dev)
+            b.tq_set_rows(k2c, torch.from_numpy(k2_).to(dev), idx2)
+            b.tq_set_rows(v2c, torch.from_numpy(v2_).to(dev), idx2)
+            q2t = torch.from_numpy(q2_).to(torch.bfloat16).to(dev)
+            o2 = torch.empty((R2, PNQ, PD), dtype=torch.float32, device=dev)
+            w2 = torch.empty(max(256, b.tq_attn_prefill_workspace(k2c, R2, PNQ, R2)), dtype=torch.uint8, device=dev)
+            t_ms = time_eager(lambda: b.tq_attn_prefill(k2c, v2c, R2, q2t, 0, pscale, out=o2, workspace=w2))
+            tf = 4.0 * PD * PNQ * (R2 * (R2 + 1) / 2) / (t_ms * 1e-3) / 1e12
+            extras[f"prefill_turbo3_{R2}rows"] = {"us": round(t_ms * 1e3, 2),
+                                                  "tokens_per_s": round(R2 / (t_ms * 1e-3), 1),
+                                                  "TFLOPs": round(tf, 2),
+                                                  "frac_mfma_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+            del k2c, v2c, q2t, o2, w2
     if int8 is not None and want("int8_140k"):
         # the int8 prompt at the longer of the two contexts: 2048 queries at
         # the end of 140000 cells (leg "int8_140k")
