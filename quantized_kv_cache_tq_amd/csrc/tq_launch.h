@@ -38,6 +38,7 @@ hipError_t launch_decode(const tq_cache &k, const tq_cache &v, const int64_t *se
 struct PrefillPlan {
   int rows_per_tile;     // query rows per workgroup
   int n_row_tiles;
+  int paired;            // 1: tiles p and n_row_tiles - 1 - p share a workgroup
   int keys_per_split;    // key range per workgroup (multiple of the key tile)
   int max_splits;        // splits of the longest row tile
   size_t workspace_bytes;

@@ -35,7 +35,10 @@
 //   A(t): matrix: S(t+1) from K, softmax(t)   decode: write V(t), look up V(t+1)
 //   B(t): matrix: O += V(t) P(t)              decode: decode K(t+2) into K
 // Causal balance: workgroup p processes query tiles p and T-1-p, so every
-// workgroup sees about the same number of key tiles.  After the key loop all
+// workgroup sees about the same number of key tiles; when that grid would
+// not give every compute unit a workgroup, each tile takes its own
+// workgroup instead (one pass: the passes' fixed costs then outweigh the
+// imbalance).  After the key loop all
 // eight waves merge the two key halves and apply the inverse rotation.
 #include "tq_common.h"
 #include "tq_launch.h"
@@ -159,6 +162,7 @@ struct Args {
   const void *q;
   float *out;
   int n_q, n_rep, bq, n_qtiles;
+  int paired;                 // 1: workgroup p also takes query tile n_qtiles - 1 - p
   float qscale;
 };
 
@@ -339,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
 
   for (int pass = 0; pass < 2; ++pass) {
     const int qt = pass == 0 ? (int)blockIdx.x : a.n_qtiles - 1 - (int)blockIdx.x;
-    if (pass == 1 && qt == (int)blockIdx.x) break;
+    if (pass == 1 && (!a.paired || qt == (int)blockIdx.x)) break;
     const int64_t row0 = (int64_t)qt * a.bq;
     const int64_t last_row = lmin(row0 + a.bq, a.n_rows) - 1;
     const int64_t kend = lmin(a.kv_len, a.q_pos0 + last_row + 1);
@@ -677,6 +681,10 @@ hipError_t plan_prefill(const tq_cache &k, int64_t n_rows, int32_t n_q_heads, in
   const int64_t tiles = ceil_div<int64_t>(n_rows, p->rows_per_tile);
   if (tiles > 0x3fffffff) return hipErrorInvalidValue;
   p->n_row_tiles = (int)tiles;
+  int n_cu = 0;
+  const hipError_t e = device_cu_count(&n_cu);
+  if (e != hipSuccess) return e;
+  p->paired = ceil_div<int64_t>(tiles, 2) * k.n_kv_heads >= n_cu ? 1 : 0;
   p->keys_per_split = 0;
   p->max_splits = 1;
   p->workspace_bytes = 0;
@@ -703,9 +711,10 @@ hipError_t launch_prefill(const tq_cache &k, const tq_cache &v, int64_t kv_len, 
   a.n_rep = n_q_heads / k.n_kv_heads;
   a.bq = p.rows_per_tile;
   a.n_qtiles = p.n_row_tiles;
+  a.paired = p.paired;
   // log2 domain; 1/8 for the transform and tile scales (score = H(s.q) . K / 8)
   a.qscale = scale * 1.4426950408889634f / 8.0f;
-  dim3 grid((unsigned)ceil_div(p.n_row_tiles, 2), (unsigned)k.n_kv_heads);
+  dim3 grid((unsigned)(p.paired ? ceil_div(p.n_row_tiles, 2) : p.n_row_tiles), (unsigned)k.n_kv_heads);
   dim3 block(pf::kThreads);
 #define TQ_PF(B, KD)                                                                  \
   do {                                                                                \
