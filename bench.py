@@ -75,7 +75,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
                     help="comma list of legs: set_rows,decode,prefill,int8 (default: all; extras decode_wide, "
-                         "decode_batch, floor, prefill_rows, int8_140k); "
+                         "decode_types, decode_batch, floor, prefill_rows, int8_140k); "
                          "'copy' adds a 256 MiB device copy used to calibrate HBM counters")
     return ap.parse_args()
 
@@ -407,6 +407,35 @@ def main():
                 "us_per_call": round(t_ms * 1e3, 3), "bytes_per_call": nbytes, "GBps": round(gbps, 1),
                 "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
             del akc, aws
+
+        # turbo2 and turbo4 decode at the headline's heads, 8192 and 32768
+        # cells (leg "decode_types"), over L distinct caches each
+        if want("decode_types"):
+            for bits in (2, 4):
+                xkc = [b.new_cache(bits, D, NKV, KV) for _ in range(L)]
+                xvc = [b.new_cache(bits, D, NKV, KV) for _ in range(L)]
+                b.tq_set_rows(xkc[0], k_src, idx)
+                b.tq_set_rows(xvc[0], v_src, idx)
+                for i in range(1, L):
+                    xkc[i].codes.copy_(xkc[0].codes); xkc[i].norms.copy_(xkc[0].norms)
+                    xvc[i].codes.copy_(xvc[0].codes); xvc[i].norms.copy_(xvc[0].norms)
+                xws = torch.empty(b.tq_attn_decode_workspace(xkc[0], xvc[0], KV, NQ), dtype=torch.uint8, device=dev)
+                for kvl in (8192, KV):
+                    t_ms = time_graph([lambda i=i, kvl=kvl: b.tq_attn_decode(xkc[i], xvc[i], kvl, q_dec, scale_dec,
+                                                                             out=outs[i], workspace=xws)
+                                       for i in range(L)])
+                    nbytes = 2 * NKV * kvl * (16 * bits + 2)
+                    gbps = nbytes / (t_ms * 1e-3) / 1e9
+                    extras[f"decode_turbo{bits}_{kvl}_gqa8"] = {
+                        "us_per_call": round(t_ms * 1e3, 3), "bytes_per_call": nbytes, "GBps": round(gbps, 1),
+                        "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+                del xkc, xvc, xws
+            t_ms = time_graph([lambda i=i: b.tq_attn_decode(kcs[i], vcs[i], 8192, q_dec, scale_dec, out=outs[i],
+                                                            workspace=ws) for i in range(L)])
+            nbytes = 2 * NKV * 8192 * 50
+            gbps = nbytes / (t_ms * 1e-3) / 1e9
+            extras["decode_turbo3_8192_gqa8"] = {"us_per_call": round(t_ms * 1e3, 3), "bytes_per_call": nbytes,
+                                                 "GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
 
         # batched decode (leg "decode_batch"): 8 sequences of mixed lengths
         # (131,072 cells in all), 2 query rows each, 32 q / 4 kv heads, one
