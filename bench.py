@@ -312,6 +312,19 @@ def main():
                                                   "TFLOPs": round(tf, 2),
                                                   "frac_mfma_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
             del k2c, v2c, q2t, o2, w2
+        # the speculative-verify batch: 3 rows at the end of 1024 cells
+        q3_, k3_, v3_ = inputs.prefill(seed=3, rows=3, kv_len=1024)
+        k3c, v3c = b.new_cache(3, PD, PNKV, 1024), b.new_cache(3, PD, PNKV, 1024)
+        idx3 = torch.arange(1024, dtype=torch.int64, device=dev)
+        b.tq_set_rows(k3c, torch.from_numpy(k3_).to(dev), idx3)
+        b.tq_set_rows(v3c, torch.from_numpy(v3_).to(dev), idx3)
+        q3t = torch.from_numpy(q3_).to(torch.bfloat16).to(dev)
+        o3 = torch.empty((3, PNQ, PD), dtype=torch.float32, device=dev)
+        w3 = torch.empty(max(256, b.tq_attn_prefill_workspace(k3c, 3, PNQ, 1024)), dtype=torch.uint8, device=dev)
+        t_ms = time_eager(lambda: b.tq_attn_prefill(k3c, v3c, 1024, q3t, 1021, pscale, out=o3, workspace=w3),
+                          reps=50)
+        extras["prefill_turbo3_spec_verify_3rows_1024_eager"] = {"us": round(t_ms * 1e3, 2)}
+        del k3c, v3c, q3t, o3, w3
     if int8 is not None and want("int8_140k"):
         # the int8 prompt at the longer of the two contexts: 2048 queries at
         # the end of 140000 cells (leg "int8_140k")
