@@ -92,6 +92,16 @@ def test_turbo2_turbo4_one_head(bits, kv_len):
     _run(bits, q, k, v, kv_len, what="turbo2/4 one head")
 
 
+@pytest.mark.parametrize("kv_len,n_q", [(131072, 8), (100003, 16)])
+def test_long_context(kv_len, n_q):
+    """128K cells on one kv head (256 splits of 512 keys) and a ragged 100003
+    cells with 16 q heads per kv head (sixteen pairs per workgroup, 391
+    splits of 256 keys): the 512-thread merge takes several load rounds per
+    lane group."""
+    q, k, v = inputs.outlier_decode(seed=kv_len % 97, kv_len=kv_len, n_q=n_q, n_kv=1)
+    _run(3, q, k, v, kv_len, q_bf16=True, what="long context")
+
+
 @pytest.mark.parametrize("bits", [3, 2, 4])
 def test_outlier_gqa8_32k(bits):
     q, k, v = inputs.outlier_decode(seed=0)
