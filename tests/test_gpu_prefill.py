@@ -157,6 +157,15 @@ def test_few_rows_after_long_prefix(rows, kv, q0):
     _run(q, k, v, kv, q0, what="long prefix")
 
 
+@pytest.mark.parametrize("d,n_q,n_kv", [(256, 16, 2), (128, 32, 4)])
+def test_few_rows_wide_gqa(d, n_q, n_kv):
+    """64 rows at 8 q heads per kv head through the split-key kernels: 512
+    (row, head) pairs per kv head, 64 head groups of eight (256-wide heads) or
+    32 of sixteen (128-wide)."""
+    q, k, v = inputs.prefill(seed=d + n_q, rows=64, kv_len=2000, n_q=n_q, n_kv=n_kv, d=d)
+    _run(q, k, v, 2000, 1936, what=f"wide gqa {n_q}/{n_kv} d{d}")
+
+
 def test_few_rows_workspace_rule():
     """The workspace of a split-key call comes from tq_attn_prefill_workspace
     with a kv_len at least q_pos0 + n_rows; the tiled calls need none."""
