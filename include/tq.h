@@ -236,7 +236,8 @@ tq_status tq_attn_decode_batch(const tq_cache *k, const tq_cache *v, int32_t n_s
  * Calls of at most 64 rows run the split-key decode kernels instead of the
  * tiled ones, as one sequence of q_pos0 + n_rows cells whose row r sees
  * cells <= q_pos0 + r (the tiled kernel has no key split, so a few rows
- * after a long prefix would occupy a handful of compute units).  [PR28]
+ * after a long prefix would occupy a handful of compute units), as long as
+ * their split partials for kv_len cells fit 256 MiB.  [PR28]
  * "Graph-safe decode" routes only batches of at most two rows to its decode
  * kernel.  These calls need a workspace; tq_attn_prefill_workspace (same
  * k, n_rows, n_q_heads and a kv_len >= q_pos0 + n_rows) gives its size,

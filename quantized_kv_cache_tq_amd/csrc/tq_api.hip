@@ -219,17 +219,37 @@ static tq_status prefill_check(const tq_cache *k, int64_t n_rows, int32_t n_q_he
 // us split, after 16384 cells 447 us against 17 us, and 64 rows after 1024
 // cells 75.9 us against 18.4 us.
 constexpr int64_t kPrefillSplitRows = 64;
+// ... as long as their split partials, sized for kv_len, stay within this
+// many bytes (else the tiled kernel, which needs none)
+constexpr size_t kPrefillSplitMaxWorkspace = size_t(256) << 20;
+
+// Whether a prefill call takes the split-key kernels; the decision depends
+// only on arguments the workspace query also has (kv_len, not q_pos0), so
+// the query and the call agree.
+static tq_status prefill_split_plan(const tq_cache &k, int64_t n_rows, int32_t n_q_heads, int64_t kv_len,
+                                    bool *split, size_t *bytes) {
+  *split = false;
+  *bytes = 0;
+  if (n_rows < 1 || n_rows > kPrefillSplitRows) return TQ_OK;
+  DecodePlan dp;
+  if (tq_status st = from_hip(plan_decode(k, k, kv_len, n_q_heads, (int)n_rows, 1, &dp))) return st;
+  if (dp.workspace_bytes > kPrefillSplitMaxWorkspace) return TQ_OK;
+  *split = true;
+  *bytes = dp.workspace_bytes;
+  return TQ_OK;
+}
 
 tq_status tq_attn_prefill_workspace(const tq_cache *k, int64_t n_rows, int32_t n_q_heads,
                                     int64_t kv_len, size_t *bytes) {
   tq_status s = prefill_check(k, n_rows, n_q_heads, kv_len);
   if (s != TQ_OK) return s;
   if (!bytes) return TQ_ERR_INVALID_ARG;
-  if (n_rows >= 1 && n_rows <= kPrefillSplitRows) {
+  bool split = false;
+  size_t split_bytes = 0;
+  if (tq_status st = prefill_split_plan(*k, n_rows, n_q_heads, kv_len, &split, &split_bytes)) return st;
+  if (split) {
     // sized for the longest sequence the call may see (q_pos0 + n_rows <= kv_len)
-    DecodePlan dp;
-    if (tq_status st = from_hip(plan_decode(*k, *k, kv_len, n_q_heads, (int)n_rows, 1, &dp))) return st;
-    *bytes = dp.workspace_bytes;
+    *bytes = split_bytes;
     return TQ_OK;
   }
   PrefillPlan p;
@@ -251,7 +271,10 @@ tq_status tq_attn_prefill(const tq_cache *k, const tq_cache *v, int64_t kv_len, 
   if (!(scale == scale)) return TQ_ERR_INVALID_ARG;
   if (n_rows == 0) return TQ_OK;
   if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return TQ_ERR_INVALID_ARG;
-  if (n_rows <= kPrefillSplitRows) {
+  bool split = false;
+  size_t split_bytes = 0;
+  if (tq_status st = prefill_split_plan(*k, n_rows, n_q_heads, kv_len, &split, &split_bytes)) return st;
+  if (split) {
     const int64_t len = q_pos0 + n_rows;
     DecodePlan dp;
     if (tq_status st = from_hip(plan_decode(*k, *v, len, n_q_heads, (int)n_rows, 1, &dp))) return st;

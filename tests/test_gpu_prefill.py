@@ -178,6 +178,11 @@ def test_few_rows_workspace_rule():
     b.tq_set_rows(kc, cuda(k), cuda(idx))
     b.tq_set_rows(vc, cuda(v), cuda(idx))
     assert b.tq_attn_prefill_workspace(kc, 65, 16, 3000) == 0
+    # 64 rows at 64 q heads over 65536 cells: partials beyond 256 MiB, so the
+    # tiled kernel (no workspace)
+    big = b.new_cache(3, 256, 8, 65536)
+    assert b.tq_attn_prefill_workspace(big, 64, 64, 65536) == 0
+    assert 0 < b.tq_attn_prefill_workspace(big, 64, 64, 2000) <= 256 << 20
     need = b.tq_attn_prefill_workspace(kc, 5, 16, 3000)
     assert need > 0
     assert b.tq_attn_prefill_workspace(kc, 5, 16, 1000) <= need
