@@ -522,9 +522,14 @@ def main():
         # launch of an empty kernel costs, and a kernel that only reads the
         # decode call's bytes once (L distinct buffers, no arithmetic), alone
         # and followed by a second, tiny launch as the split + merge pair is
+        fl = None
         if want("floor"):
             import ctypes
-            fl = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(b.__file__)), "lib", "libtq_floor.so"))
+            try:
+                fl = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(b.__file__)), "lib", "libtq_floor.so"))
+            except OSError as e:
+                log(f"[bench] floor leg skipped (build the package first): {e}")
+        if fl is not None:
             fl.tqf_empty.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
             fl.tqf_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
             fbufs = [torch.full((kv_bytes_per_call,), i, dtype=torch.uint8, device=dev) for i in range(L)]
