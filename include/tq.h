@@ -239,9 +239,12 @@ tq_status tq_attn_decode_batch(const tq_cache *k, const tq_cache *v, int32_t n_s
  * after a long prefix would occupy a handful of compute units), as long as
  * their split partials for kv_len cells fit 256 MiB.  [PR28]
  * "Graph-safe decode" routes only batches of at most two rows to its decode
- * kernel.  These calls need a workspace; tq_attn_prefill_workspace (same
- * k, n_rows, n_q_heads and a kv_len >= q_pos0 + n_rows) gives its size,
- * 0 for the tiled calls.  Both paths meet the same accuracy bar.
+ * kernel.  A tiled call whose grid would occupy at most half the compute
+ * units while kv_len spans at least 16 key tiles of 64 splits the key range
+ * too, merging the partials in a second kernel.  Such calls need a
+ * workspace; tq_attn_prefill_workspace (same k, n_rows, n_q_heads and a
+ * kv_len >= q_pos0 + n_rows) gives its size, at most 256 MiB, and 0 when
+ * none is needed.  Every path meets the same accuracy bar.
  */
 tq_status tq_attn_prefill_workspace(const tq_cache *k, int64_t n_rows, int32_t n_q_heads,
                                     int64_t kv_len, size_t *bytes /*[host]*/);

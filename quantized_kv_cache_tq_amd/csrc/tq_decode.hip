@@ -759,6 +759,22 @@ hipError_t device_cu_count(int *n_cu) {
   return hipSuccess;
 }
 
+hipError_t launch_split_merge(const float *ws, int n_split, int split_log2, int dv, int64_t rows_out,
+                              float *out, hipStream_t stream) {
+  if (n_split < 1 || rows_out < 1 || rows_out > 0x7fffffff || dv % kGroup) return hipErrorInvalidValue;
+  const dim3 mgrid((unsigned)rows_out, dv / kGroup);
+  // every split is read (length n_split << split_log2 from cell 0); empty
+  // ones carry maximum -inf, which the masked chain skips
+  const int64_t len = (int64_t)n_split << split_log2;
+  if (n_split <= 64)
+    hipLaunchKernelGGL((decode_merge_kernel<true, 256>), mgrid, dim3(256), 0, stream, ws, n_split, split_log2, dv,
+                       nullptr, nullptr, len, len, 1, out);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<true, 512>), mgrid, dim3(512), 0, stream, ws, n_split, split_log2, dv,
+                       nullptr, nullptr, len, len, 1, out);
+  return hipGetLastError();
+}
+
 hipError_t plan_decode(const tq_cache &k, const tq_cache &v, int64_t max_len, int32_t n_q_heads,
                        int n_rows, int n_seq, DecodePlan *p) {
   int n_cu = 0;

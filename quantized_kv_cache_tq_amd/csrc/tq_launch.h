@@ -45,6 +45,12 @@ struct PrefillPlan {
 };
 hipError_t plan_prefill(const tq_cache &k, int64_t n_rows, int32_t n_q_heads, int64_t kv_len,
                         PrefillPlan *p);
+// Merge n_split partials [rows_out][n_split][dv + 4] (16 x unnormalized
+// rotated sums, log2-domain maximum, weight sum; maximum -inf for an empty
+// one) into out [rows_out][dv] with the inverse rotation; a split holds
+// 2^split_log2 keys.
+hipError_t launch_split_merge(const float *ws, int n_split, int split_log2, int dv, int64_t rows_out,
+                              float *out, hipStream_t stream);
 hipError_t launch_prefill(const tq_cache &k, const tq_cache &v, int64_t kv_len, const void *q,
                           int q_dtype, int64_t n_rows, int32_t n_q_heads, int64_t q_pos0,
                           float scale, float *out, void *workspace, const PrefillPlan &p,

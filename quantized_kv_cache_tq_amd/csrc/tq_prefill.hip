@@ -163,6 +163,12 @@ struct Args {
   float *out;
   int n_q, n_rep, bq, n_qtiles;
   int paired;                 // 1: workgroup p also takes query tile n_qtiles - 1 - p
+  // key splits (kSplit): workgroup z takes key tiles [z ks_tiles, (z+1) ks_tiles)
+  // of each of its query tiles and writes partials [row][q head][split][KD + 4]
+  // (16 * unnormalized rotated output, then the log2-domain maximum and the
+  // weight sum) for the decode merge kernel
+  int ks_tiles, n_split;
+  float *ws;
   float qscale;
 };
 
@@ -317,7 +323,7 @@ __device__ __forceinline__ void wht_in_regs(float (&x)[N]) {
       }
 }
 
-template <int B, int KD, bool QBF16>
+template <int B, int KD, bool QBF16, bool kSplit>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
   using D = Dims<KD>;
   // aligned to its size, so a lookup address is (entry << 8) | (lane << 2)
@@ -350,6 +356,23 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
     const int n_kt = (int)ceil_div<int64_t>(kend, kKT);
     // tiles past this key need the causal mask (the first row sees keys <= pos_min)
     const int64_t pos_min = lmin(a.q_pos0 + row0, a.kv_len - 1);
+    // this workgroup's key tiles [kt0, kt1)
+    const int kt0 = kSplit ? (int)blockIdx.z * a.ks_tiles : 0;
+    const int kt1 = kSplit ? min(kt0 + a.ks_tiles, n_kt) : n_kt;
+    if (kSplit && kt0 >= kt1) {
+      // no key of this range: an empty partial (maximum -inf, weight 0) per row
+      constexpr int EE = D::EE, PE = 128 / EE;
+      const int j = tid % PE, c = (tid / PE) & 63, grp = tid / (PE * 64);
+      const int64_t r = row0 + c % a.bq;
+      if (r < a.n_rows) {
+        float *pr = a.ws + ((r * a.n_q + g * a.n_rep + c / a.bq) * a.n_split + blockIdx.z) * (KD + 4);
+#pragma unroll
+        for (int v = 0; v < EE / 4; ++v)
+          reinterpret_cast<float4 *>(pr + 128 * grp + EE * j)[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (j == 0 && grp == 0) *reinterpret_cast<float2 *>(pr + KD) = make_float2(-INFINITY, 0.f);
+      }
+      continue;
+    }
 
     if (wave < 4) {
       // ================================================= matrix waves
@@ -537,9 +560,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
         }
         __syncthreads();   // V tile kt consumed; K tile kt+2 written
       };
-      for (int kt = 0; kt < n_kt; kt += 2) {
+      for (int kt = kt0; kt < kt1; kt += 2) {
         step(kt, sa, sb);
-        if (kt + 1 < n_kt) step(kt + 1, sb, sa);
+        if (kt + 1 < kt1) step(kt + 1, sb, sa);
       }
 
       // ---- merge the key halves: khalf 1 hands its partial output to
@@ -564,8 +587,21 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
         const float M = fmaxf(m_run, m2);
         const float f1 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
         const float f2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
-        const float rinv = 1.0f / (8.0f * (l_run * f1 + l2 * f2));
-        const float g1 = f1 * rinv, g2 = f2 * rinv;
+        // a split keeps 16 x the unnormalized sum and its statistics (the
+        // merge divides by 128 L: the output's 1 / (8 L))
+        float g1, g2;
+        if constexpr (kSplit) {
+          g1 = 16.f * f1;
+          g2 = 16.f * f2;
+          if (hl == 0) {
+            mst[0][qrow] = M;
+            lst[0][qrow] = l_run * f1 + l2 * f2;
+          }
+        } else {
+          const float rinv = 1.0f / (8.0f * (l_run * f1 + l2 * f2));
+          g1 = f1 * rinv;
+          g2 = f2 * rinv;
+        }
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
@@ -589,28 +625,28 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
       KRaw<B, KD> kr0, kr1;
       VRaw<B> vr;
       uint32_t vw[KD / 32][4];
-      load_k<B, KD>(hp, last, 0, dt, kr0);
-      load_k<B, KD>(hp, last, 1, dt, kr1);
-      load_v<B, KD>(hp, last, 0, dt, vr);
+      load_k<B, KD>(hp, last, kt0, dt, kr0);
+      load_k<B, KD>(hp, last, min(kt0 + 1, kt1 - 1), dt, kr1);
+      load_v<B, KD>(hp, last, kt0, dt, vr);
       store_k<B, KD>(kr0, dt, tab, vbuf);   // K tile 0 goes where V tile 0 will
       store_k<B, KD>(kr1, dt, tab, kbuf);
       lookup_v<B, KD>(vr, dt, tab, vw);
       // loads are unconditional (tile index clamped): a conditional load
       // would merge into the loop-carried registers through copies that wait
       // for the data
-      load_k<B, KD>(hp, last, min(2, n_kt - 1), dt, kr0);
-      load_v<B, KD>(hp, last, min(1, n_kt - 1), dt, vr);
+      load_k<B, KD>(hp, last, min(kt0 + 2, kt1 - 1), dt, kr0);
+      load_v<B, KD>(hp, last, min(kt0 + 1, kt1 - 1), dt, vr);
       __syncthreads();   // query rows, K tiles 0 (in the V^T buffer) and 1 ready
       __syncthreads();   // K tile 0 read: the V^T buffer may take V tile 0
-      for (int kt = 0; kt < n_kt; ++kt) {
+      for (int kt = kt0; kt < kt1; ++kt) {
         // phase A: V tile kt into the buffer, look up V tile kt+1
         write_v<KD>(vw, dt, vbuf);
         lookup_v<B, KD>(vr, dt, tab, vw);   // past the end: never written
-        load_v<B, KD>(hp, last, min(kt + 2, n_kt - 1), dt, vr);
+        load_v<B, KD>(hp, last, min(kt + 2, kt1 - 1), dt, vr);
         __syncthreads();   // V tile kt written; K tile kt+1 read
         // phase B: K tile kt+2 into the (now free) K buffer
-        if (kt + 2 < n_kt) store_k<B, KD>(kr0, dt, tab, kbuf);
-        load_k<B, KD>(hp, last, min(kt + 3, n_kt - 1), dt, kr0);
+        if (kt + 2 < kt1) store_k<B, KD>(kr0, dt, tab, kbuf);
+        load_k<B, KD>(hp, last, min(kt + 3, kt1 - 1), dt, kr0);
         __syncthreads();   // V tile kt consumed; K tile kt+2 written
       }
       __syncthreads();   // partial outputs and statistics in shared memory
@@ -638,6 +674,19 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
           x[8 * rq + 4 * hh + 2] = u.z;
           x[8 * rq + 4 * hh + 3] = u.w;
         }
+      if constexpr (kSplit) {
+        const int64_t r = row0 + c % a.bq;
+        if (r < a.n_rows) {
+          float *pr = a.ws + ((r * a.n_q + g * a.n_rep + c / a.bq) * a.n_split + blockIdx.z) * (KD + 4);
+#pragma unroll
+          for (int v = 0; v < EE / 4; ++v)
+            reinterpret_cast<float4 *>(pr + 128 * grp + EE * j)[v] =
+                make_float4(x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]);
+          if (j == 0 && grp == 0) *reinterpret_cast<float2 *>(pr + KD) = make_float2(mst[0][c], lst[0][c]);
+        }
+        __syncthreads();   // merge buffer read: the tiles may be overwritten
+        continue;
+      }
       wht_in_regs<EE>(x);
 #pragma unroll
       for (int e = 0; e < EE; ++e) x[e] = bfly_lane<1>(x[e], (j & 1) != 0);
@@ -672,7 +721,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
 
 hipError_t plan_prefill(const tq_cache &k, int64_t n_rows, int32_t n_q_heads, int64_t kv_len,
                         PrefillPlan *p) {
-  (void)kv_len;
+
   const int n_rep = n_q_heads / k.n_kv_heads;
   if (n_rep < 1 || pf::kQRows % n_rep != 0) return hipErrorNotSupported;
   // key offsets inside one head are 32-bit
@@ -688,6 +737,29 @@ hipError_t plan_prefill(const tq_cache &k, int64_t n_rows, int32_t n_q_heads, in
   p->keys_per_split = 0;
   p->max_splits = 1;
   p->workspace_bytes = 0;
+  // Key splits when the grid leaves most compute units idle and the rows see
+  // many key tiles (rows after a long prefix): each split takes a
+  // power-of-two number (>= 8) of key tiles, partials merged by a second
+  // kernel; sized for kv_len and capped at 256 MiB of partials.
+  const int64_t base = (p->paired ? ceil_div<int64_t>(tiles, 2) : tiles) * k.n_kv_heads;
+  const int64_t max_kt = ceil_div<int64_t>(kv_len, pf::kKT);
+  if (2 * base <= n_cu && max_kt >= 16) {
+    int64_t want = n_cu / base;   // the split grid stays one round
+    if (want > max_kt / 8) want = max_kt / 8;
+    int64_t ks = 8;
+    while (ks * want < max_kt) ks *= 2;
+    const size_t per_split = (size_t)n_rows * (size_t)n_q_heads * (size_t)(k.head_dim + 4) * sizeof(float);
+    int64_t n_split = ceil_div<int64_t>(max_kt, ks);
+    while (n_split > 1 && (size_t)n_split * per_split > (size_t(256) << 20)) {
+      ks *= 2;
+      n_split = ceil_div<int64_t>(max_kt, ks);
+    }
+    if (n_split > 1 && n_split <= 65535) {
+      p->keys_per_split = (int)(ks * pf::kKT);
+      p->max_splits = (int)n_split;
+      p->workspace_bytes = ((size_t)n_split * per_split + 255) & ~(size_t)255;
+    }
+  }
   return hipSuccess;
 }
 
@@ -695,7 +767,7 @@ hipError_t launch_prefill(const tq_cache &k, const tq_cache &v, int64_t kv_len, 
                           int q_dtype, int64_t n_rows, int32_t n_q_heads, int64_t q_pos0,
                           float scale, float *out, void *workspace, const PrefillPlan &p,
                           hipStream_t stream) {
-  (void)workspace;
+
   pf::Args a;
   a.kcodes = k.codes;
   a.knorms = k.norms;
@@ -712,16 +784,28 @@ hipError_t launch_prefill(const tq_cache &k, const tq_cache &v, int64_t kv_len, 
   a.bq = p.rows_per_tile;
   a.n_qtiles = p.n_row_tiles;
   a.paired = p.paired;
+  const bool split = p.max_splits > 1;
+  a.n_split = p.max_splits;
+  a.ks_tiles = split ? p.keys_per_split / pf::kKT : 0;
+  a.ws = reinterpret_cast<float *>(workspace);
   // log2 domain; 1/8 for the transform and tile scales (score = H(s.q) . K / 8)
   a.qscale = scale * 1.4426950408889634f / 8.0f;
-  dim3 grid((unsigned)(p.paired ? ceil_div(p.n_row_tiles, 2) : p.n_row_tiles), (unsigned)k.n_kv_heads);
+  dim3 grid((unsigned)(p.paired ? ceil_div(p.n_row_tiles, 2) : p.n_row_tiles), (unsigned)k.n_kv_heads,
+            (unsigned)p.max_splits);
   dim3 block(pf::kThreads);
-#define TQ_PF(B, KD)                                                                  \
-  do {                                                                                \
-    if (q_dtype == TQ_BF16)                                                           \
-      hipLaunchKernelGGL((pf::prefill_kernel<B, KD, true>), grid, block, 0, stream, a); \
-    else                                                                              \
-      hipLaunchKernelGGL((pf::prefill_kernel<B, KD, false>), grid, block, 0, stream, a); \
+#define TQ_PF_Q(B, KD, QB)                                                                        \
+  do {                                                                                            \
+    if (split)                                                                                    \
+      hipLaunchKernelGGL((pf::prefill_kernel<B, KD, QB, true>), grid, block, 0, stream, a);      \
+    else                                                                                          \
+      hipLaunchKernelGGL((pf::prefill_kernel<B, KD, QB, false>), grid, block, 0, stream, a);     \
+  } while (0)
+#define TQ_PF(B, KD)                       \
+  do {                                     \
+    if (q_dtype == TQ_BF16)                \
+      TQ_PF_Q(B, KD, true);                \
+    else                                   \
+      TQ_PF_Q(B, KD, false);               \
   } while (0)
 #define TQ_PF_TYPES(KD)                  \
   switch (k.type) {                      \
@@ -738,7 +822,11 @@ hipError_t launch_prefill(const tq_cache &k, const tq_cache &v, int64_t kv_len, 
     return hipErrorNotSupported;
 #undef TQ_PF_TYPES
 #undef TQ_PF
-  return hipGetLastError();
+#undef TQ_PF_Q
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !split) return e;
+  return launch_split_merge(a.ws, p.max_splits, __builtin_ctz((unsigned)p.keys_per_split), k.head_dim,
+                            n_rows * n_q_heads, out, stream);
 }
 
 }  // namespace tq

@@ -168,7 +168,8 @@ def test_few_rows_wide_gqa(d, n_q, n_kv):
 
 def test_few_rows_workspace_rule():
     """The workspace of a split-key call comes from tq_attn_prefill_workspace
-    with a kv_len at least q_pos0 + n_rows; the tiled calls need none."""
+    with a kv_len at least q_pos0 + n_rows; a fresh prompt's tiled call needs
+    none."""
     import torch
     from quantized_kv_cache_tq_amd import binding as b
     from gpu_util import bf16_cuda, cuda
@@ -177,11 +178,15 @@ def test_few_rows_workspace_rule():
     kc, vc = b.new_cache(3, 256, 8, 3000), b.new_cache(3, 256, 8, 3000)
     b.tq_set_rows(kc, cuda(k), cuda(idx))
     b.tq_set_rows(vc, cuda(v), cuda(idx))
-    assert b.tq_attn_prefill_workspace(kc, 65, 16, 3000) == 0
-    # 64 rows at 64 q heads over 65536 cells: partials beyond 256 MiB, so the
-    # tiled kernel (no workspace)
+    # 65 rows: the tiled kernel, whose key splits (a few row tiles after a
+    # long prefix) also take a workspace of at most 256 MiB
+    assert b.tq_attn_prefill_workspace(kc, 65, 16, 3000) <= 256 << 20
+    assert b.tq_attn_prefill_workspace(kc, 65, 16, 65) == 0
+    # 64 rows at 64 q heads over 65536 cells: the split-key decode path's
+    # partials exceed 256 MiB, so the tiled kernel runs (its own partials
+    # capped at 256 MiB)
     big = b.new_cache(3, 256, 8, 65536)
-    assert b.tq_attn_prefill_workspace(big, 64, 64, 65536) == 0
+    assert b.tq_attn_prefill_workspace(big, 64, 64, 65536) <= 256 << 20
     assert 0 < b.tq_attn_prefill_workspace(big, 64, 64, 2000) <= 256 << 20
     need = b.tq_attn_prefill_workspace(kc, 5, 16, 3000)
     assert need > 0
@@ -193,3 +198,24 @@ def test_few_rows_workspace_rule():
         b.tq_attn_prefill(kc, vc, 3000, bf16_cuda(q), 2995, 1.0 / 16.0,
                           workspace=torch.empty(64, dtype=torch.uint8, device="cuda"))
     assert np.all(np.isfinite(out.cpu().numpy()))
+
+
+@pytest.mark.parametrize("rows,kv,q0,d,n_q,n_kv,bits", [
+    (100, 6000, 5900, 256, 16, 8, 3), (256, 9000, 8744, 256, 16, 8, 3), (65, 4000, 1000, 256, 16, 8, 3),
+    (130, 5000, 4870, 128, 32, 8, 3), (96, 7000, 6904, 256, 16, 2, 2), (80, 3000, 2920, 128, 16, 4, 4)])
+def test_key_split_after_long_prefix(rows, kv, q0, d, n_q, n_kv, bits):
+    """More than 64 rows after a long prefix: a grid of few row tiles splits
+    the key range (power-of-two tiles per split, partials merged by a second
+    kernel), including a prefix that ends before the cache does."""
+    q, k, v = inputs.prefill(seed=rows + kv, rows=rows, kv_len=kv, n_q=n_q, n_kv=n_kv, d=d)
+    _run(q, k, v, kv, q0, q_bf16=(bits != 2), what=f"key split d{d}", bits=bits)
+
+
+def test_key_split_workspace():
+    """The split plan's workspace comes from tq_attn_prefill_workspace (kv_len
+    sizes it); fresh prompts and full grids need none."""
+    from quantized_kv_cache_tq_amd import binding as b
+    kc = b.new_cache(3, 256, 8, 9000)
+    assert b.tq_attn_prefill_workspace(kc, 256, 16, 9000) > 0
+    assert b.tq_attn_prefill_workspace(kc, 2048, 16, 9000) == 0
+    assert b.tq_attn_prefill_workspace(kc, 512, 16, 512) == 0
