@@ -41,14 +41,14 @@ FP32_PEAK_TFLOPS = 157.3
 # `rocprofv3 --pmc` passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) over
 # `bench.py --no-cpu-baseline --only decode,copy --steps 2 --warmup 1`, each
 # scaled by what the same counter reads for the 256 MiB device copy of that
-# run (FETCH_SIZE reads 131089.6 KiB for 262144 KiB copied: x1.99973;
+# run (FETCH_SIZE reads 131088.1 KiB for 262144 KiB copied: x1.99975;
 # WRITE_SIZE reads 262144 KiB: x1.0).  Valid only for the decode sources it
 # was taken on (sha256 of tq_decode.hip + tq_common.h); otherwise traffic is
 # reported as null.
-DECODE_TRAFFIC = {"sources_sha256": "839872e0e97b80d0a54e08844a8f259ef6db44cbf28ffa718b6e036a77a242cd",
-                  "fetch_kib": {"decode_split_kernel": 6573.5, "decode_merge_kernel": 561.0},
+DECODE_TRAFFIC = {"sources_sha256": "51750abbe791ce3fa51c83a9ed6b71129dd26df5e03323973a6fab912f3df795",
+                  "fetch_kib": {"decode_split_kernel": 6565.2, "decode_merge_kernel": 561.0},
                   "write_kib": {"decode_split_kernel": 1088.0, "decode_merge_kernel": 16.0},
-                  "fetch_scale": 1.99973, "write_scale": 1.0}
+                  "fetch_scale": 1.99975, "write_scale": 1.0}
 
 
 def decode_traffic_bytes():
