@@ -103,8 +103,9 @@ tq_status tq_cache_plane_bytes(int type, int32_t head_dim, int32_t n_kv_heads, i
  * levels; these are chosen values, identical for K, V and Q):
  *   code_values[2^b]       reconstruction level of each code: +-magnitude, the
  *                          magnitudes being the Lloyd-Max levels of N(0,1)
- *                          rounded to float16;
- *   mag_thresholds[2^(b-1)-1]  midpoints between neighbouring magnitudes;
+ *                          (computed in double precision) rounded to float32;
+ *   mag_thresholds[2^(b-1)-1]  the midpoints of neighbouring double-precision
+ *                          levels, rounded to float32;
  *   sign_words[2]          the random sign flip: element d of a group is
  *                          negated iff bit d%64 of sign_words[d/64] is set
  *                          (the first two SplitMix64 outputs from state 0).
@@ -242,9 +243,11 @@ tq_status tq_attn_decode_batch(const tq_cache *k, const tq_cache *v, int32_t n_s
  * kernel.  A tiled call whose grid would occupy at most half the compute
  * units while kv_len spans at least 16 key tiles of 64 splits the key range
  * too, merging the partials in a second kernel.  Such calls need a
- * workspace; tq_attn_prefill_workspace (same k, n_rows, n_q_heads and a
- * kv_len >= q_pos0 + n_rows) gives its size, at most 256 MiB, and 0 when
- * none is needed.  Every path meets the same accuracy bar.
+ * workspace; tq_attn_prefill_workspace with the call's k, n_rows, n_q_heads
+ * and kv_len gives its size (any q_pos0), at most 256 MiB, and 0 when none
+ * is needed.  When n_q_heads / n_kv_heads does not divide 64 (3, 5, 6, 7), a
+ * 64-qrow tile of the tiled kernel holds floor(64 / n_rep) rows of each
+ * head.  Every path meets the same accuracy bar.
  */
 tq_status tq_attn_prefill_workspace(const tq_cache *k, int64_t n_rows, int32_t n_q_heads,
                                     int64_t kv_len, size_t *bytes /*[host]*/);

@@ -73,13 +73,14 @@ def lloyd_max_normal(n_levels: int, tol: float = 1e-13, max_iter: int = 100000) 
 def code_magnitudes(bits: int) -> np.ndarray:
     """Positive reconstruction magnitudes of a b-bit code, ascending, float32.
 
-    Reading: the levels of ``lloyd_max_normal(2**bits)`` rounded once to
-    float16 (round-to-nearest-even), so that the stored codebook is exactly
-    the 16-bit value the attention kernels feed their matrix units.  The
-    rounding moves a level by at most 2^-11 of its size.
+    Reading: the levels of ``lloyd_max_normal(2**bits)`` (the Lloyd-Max
+    quantizer of a unit normal source), rounded once to float32, the precision
+    of the quantizer's own arithmetic.  They are not rounded to any narrower
+    type: how a GPU kernel represents a level in its matrix products is that
+    kernel's approximation, checked against these values.
     """
     lv = lloyd_max_normal(2 ** bits)
-    return lv[2 ** (bits - 1):].astype(np.float16).astype(np.float32)
+    return lv[2 ** (bits - 1):].astype(np.float32)
 
 
 def code_values(bits: int) -> np.ndarray:
@@ -98,16 +99,14 @@ def code_values(bits: int) -> np.ndarray:
 
 
 def mag_thresholds(bits: int) -> np.ndarray:
-    """Decision thresholds between neighbouring magnitudes, float32 (exact).
+    """Decision thresholds between neighbouring magnitudes, float32.
 
-    The midpoint of two float16 values is exact in float32, so the
-    nearest-magnitude rule below is exact with respect to the stored levels.
+    Reading: a level's cell ends halfway to its neighbour (the Lloyd-Max
+    condition that makes the rule "nearest level"); each threshold is the
+    midpoint of the two float64 levels, rounded once to float32.
     """
-    m = code_magnitudes(bits).astype(np.float64)
-    t = 0.5 * (m[1:] + m[:-1])
-    t32 = t.astype(np.float32)
-    assert np.all(t32.astype(np.float64) == t)
-    return t32
+    lv = lloyd_max_normal(2 ** bits)[2 ** (bits - 1):]
+    return (0.5 * (lv[1:] + lv[:-1])).astype(np.float32)
 
 
 def splitmix64(seed: int, n: int) -> list:

@@ -12,35 +12,57 @@ namespace tq {
 constexpr int kGroup = 128;  // elements per quantization group
 
 // Positive reconstruction magnitudes, ascending: the Lloyd-Max levels of a
-// unit normal source with 2^b levels, rounded to float16 (so they are exact
-// 16-bit matrix-core operands).  A code is qs | sign << (b-1), value
+// unit normal source with 2^b levels (computed in double precision),
+// rounded to float32.  A code is qs | sign << (b-1), value
 // (sign ? -1 : +1) * mag[qs].
 __host__ __device__ constexpr float mag2(int i) {
-  return i == 0 ? 0x1.cfcp-2f : 0x1.82cp+0f;
+  return i == 0 ? 0x1.cfa592p-2f : 0x1.82aabap+0f;
 }
 __host__ __device__ constexpr float mag3(int i) {
-  return i == 0 ? 0x1.f6p-3f : i == 1 ? 0x1.83p-1f : i == 2 ? 0x1.58p+0f : 0x1.138p+1f;
+  return i == 0 ? 0x1.f5f3f0p-3f : i == 1 ? 0x1.831320p-1f : i == 2 ? 0x1.580a70p+0f : 0x1.1372f4p+1f;
 }
 __host__ __device__ constexpr float mag4(int i) {
-  return i == 0 ? 0x1.07p-3f
-       : i == 1 ? 0x1.8d4p-2f
-       : i == 2 ? 0x1.504p-1f
-       : i == 3 ? 0x1.e28p-1f
-       : i == 4 ? 0x1.418p+0f
-       : i == 5 ? 0x1.9e4p+0f
-       : i == 6 ? 0x1.08cp+1f
-                : 0x1.5dcp+1f;
+  return i == 0 ? 0x1.06f3fap-3f
+       : i == 1 ? 0x1.8d5c88p-2f
+       : i == 2 ? 0x1.5042bcp-1f
+       : i == 3 ? 0x1.e27a72p-1f
+       : i == 4 ? 0x1.41985ep+0f
+       : i == 5 ? 0x1.9e384ap+0f
+       : i == 6 ? 0x1.08d58ep+1f
+                : 0x1.5dc57ep+1f;
 }
 template <int B>
 __host__ __device__ constexpr float magnitude(int i) {
   return B == 2 ? mag2(i) : B == 3 ? mag3(i) : mag4(i);
 }
-// Decision threshold between magnitudes k-1 and k (k >= 1); the midpoint of
-// two float16 values is exact in float32.
+// Decision threshold between magnitudes k-1 and k (k >= 1): the midpoint of
+// the two double-precision levels, rounded to float32.
+__host__ __device__ constexpr float thr2(int) { return 0x1.f6941ep-1f; }
+__host__ __device__ constexpr float thr3(int k) {
+  return k == 1 ? 0x1.00480ep-1f : k == 2 ? 0x1.0cca00p+0f : 0x1.bf782ep+0f;
+}
+__host__ __device__ constexpr float thr4(int k) {
+  return k == 1 ? 0x1.086b42p-2f
+       : k == 2 ? 0x1.0b7880p-1f
+       : k == 3 ? 0x1.995e96p-1f
+       : k == 4 ? 0x1.196accp+0f
+       : k == 5 ? 0x1.6fe854p+0f
+       : k == 6 ? 0x1.d7f1b4p+0f
+                : 0x1.334d86p+1f;
+}
 template <int B>
 __host__ __device__ constexpr float threshold(int k) {
-  return 0.5f * (magnitude<B>(k - 1) + magnitude<B>(k));
+  return B == 2 ? thr2(k) : B == 3 ? thr3(k) : thr4(k);
 }
+template <int B>
+__host__ __device__ constexpr bool thresholds_between_levels() {
+  for (int k = 1; k < (1 << (B - 1)); ++k)
+    if (!(threshold<B>(k) > magnitude<B>(k - 1) && threshold<B>(k) < magnitude<B>(k))) return false;
+  return true;
+}
+static_assert(thresholds_between_levels<2>() && thresholds_between_levels<3>() &&
+                  thresholds_between_levels<4>(),
+              "each threshold lies between its two levels");
 // Value of code c.
 template <int B>
 __host__ __device__ constexpr float code_value(int c) {
@@ -48,125 +70,112 @@ __host__ __device__ constexpr float code_value(int c) {
                         : magnitude<B>(c & ((1 << (B - 1)) - 1));
 }
 
-// float16 bit pattern of a float that is an exact normal float16 value.
-__host__ __device__ constexpr uint16_t f16_bits_exact(float v) {
+// float16 bits of a finite float below 65520 in magnitude, rounded to
+// nearest even (subnormal results included).
+__host__ __device__ constexpr uint16_t f16_bits_rne(float v) {
   const uint32_t u = __builtin_bit_cast(uint32_t, v);
   const uint32_t sign = (u >> 16) & 0x8000u;
-  const uint32_t e = ((u >> 23) & 0xffu) - 127u + 15u;
-  return (uint16_t)(sign | (e << 10) | ((u >> 13) & 0x3ffu));
+  const int ex = (int)((u >> 23) & 0xffu);
+  if (ex == 0) return (uint16_t)sign;          // float32 zero or subnormal: below float16's range
+  const int e = ex - 127;
+  const uint32_t m = (u & 0x7fffffu) | 0x800000u;   // value = m * 2^(e - 23)
+  const int ulp_e = e >= -14 ? e - 10 : -24;        // the float16 ulp at this magnitude
+  const int sh = ulp_e - (e - 23);                  // right shift from m to float16 ulps (>= 13)
+  if (sh > 25) return (uint16_t)sign;
+  uint32_t q = m >> sh;
+  const uint32_t rem = m & ((1u << sh) - 1u), half = 1u << (sh - 1);
+  if (rem > half || (rem == half && (q & 1u))) ++q;
+  // normal: the implicit bit of q adds one to the biased exponent field,
+  // and a carry out of the significand moves on to the next exponent
+  const uint32_t bits = e >= -14 ? ((uint32_t)(e + 14) << 10) + q : q;
+  return (uint16_t)(sign | bits);
+}
+// float value of float16 bits (finite).
+__host__ __device__ constexpr float f16_value(uint16_t h) {
+  const uint32_t e = (h >> 10) & 0x1fu, m = h & 0x3ffu;
+  const float a = e == 0 ? (float)m * 0x1p-24f
+                         : __builtin_bit_cast(float, ((e - 15u + 127u) << 23) | (m << 13));
+  return (h & 0x8000u) ? -a : a;
+}
+// The matrix cores take 16-bit operands, so a level enters a product as two
+// float16 parts: hi = float16(level), lo = float16(level - hi) (the
+// difference is exact in float32).  hi + lo carries about 22 bits of the
+// level.
+template <int B>
+__host__ __device__ constexpr uint16_t mag_bits(int i, bool lo) {
+  return lo ? f16_bits_rne(magnitude<B>(i) - f16_value(f16_bits_rne(magnitude<B>(i))))
+            : f16_bits_rne(magnitude<B>(i));
 }
 template <int B>
-__host__ __device__ constexpr bool levels_are_f16() {
+__host__ __device__ constexpr bool split_is_close() {
   for (int i = 0; i < (1 << (B - 1)); ++i) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, magnitude<B>(i));
-    if (u & 0x1fffu) return false;
+    const double m = magnitude<B>(i);
+    const double h = f16_value(mag_bits<B>(i, false)), l = f16_value(mag_bits<B>(i, true));
+    const double err = m - h - l;
+    if ((err < 0 ? -err : err) > m * 0x1p-21) return false;
   }
   return true;
 }
-static_assert(levels_are_f16<2>() && levels_are_f16<3>() && levels_are_f16<4>(),
-              "levels must be exact float16 values");
+static_assert(split_is_close<2>() && split_is_close<3>() && split_is_close<4>(),
+              "hi + lo float16 parts reproduce each level to 2^-21");
 
-// Level table for the attention kernels: entry idx decodes the U codes
-// packed in idx (code u in bits [B*u, B*u+B)) to U float16 levels, two per
-// dword (code 2p in the low half).  U = 4 for 2- and 3-bit codes (8/12-bit
-// index), U = 2 for 4-bit codes (8-bit index).
-template <int B>
-struct UnitCfg {
-  static constexpr int U = (B == 4) ? 2 : 4;
-  static constexpr int IBITS = U * B;
-  static constexpr int N = 1 << IBITS;
-  static constexpr int DW = U / 2;
-  static constexpr int WORDS = N * DW;
-};
-template <int B>
-struct alignas(16) LevelTable {
-  uint32_t w[UnitCfg<B>::WORDS];
-  constexpr LevelTable() : w{} {
-    using C = UnitCfg<B>;
-    for (int idx = 0; idx < C::N; ++idx)
-      for (int p = 0; p < C::DW; ++p) {
-        const int c0 = (idx >> (B * (2 * p))) & ((1 << B) - 1);
-        const int c1 = (idx >> (B * (2 * p + 1))) & ((1 << B) - 1);
-        w[idx * C::DW + p] = (uint32_t)f16_bits_exact(code_value<B>(c0)) |
-                             ((uint32_t)f16_bits_exact(code_value<B>(c1)) << 16);
-      }
-  }
-};
-
-// float16 bits of magnitudes 2k and 2k+1 (low, high half).
-template <int B>
+// float16 bits (hi or lo part) of magnitudes 2k and 2k+1 (low, high half).
+template <int B, bool LO>
 __host__ __device__ constexpr uint32_t mag_word(int k) {
-  return (uint32_t)f16_bits_exact(magnitude<B>(2 * k)) |
-         ((2 * k + 1 < (1 << (B - 1))) ? (uint32_t)f16_bits_exact(magnitude<B>(2 * k + 1)) << 16 : 0u);
+  return (uint32_t)mag_bits<B>(2 * k, LO) |
+         ((2 * k + 1 < (1 << (B - 1))) ? (uint32_t)mag_bits<B>(2 * k + 1, LO) << 16 : 0u);
 }
 
-// float16 levels of codes c0 (low half) and c1 (high half): the magnitudes
-// are picked by v_perm_b32 from the constant magnitude words (byte selector
-// 2q, 2q+1 per half), then the sign bits are applied.
-template <int B>
+// float16 parts (hi or lo) of the levels of codes c0 (low half) and c1 (high
+// half): the magnitudes are picked by v_perm_b32 from the constant magnitude
+// words (byte selector 2q, 2q+1 per half), then the sign bits are applied
+// (the parts of -level are the negated parts of level).
+template <int B, bool LO = false>
 __device__ __forceinline__ uint32_t level_pair(uint32_t c0, uint32_t c1) {
-  constexpr uint32_t QM = (1u << (B - 1)) - 1u;
   const uint32_t sgn = ((c0 >> (B - 1)) << 15) | ((c1 >> (B - 1)) << 31);
-  const uint32_t q0 = c0 & QM & 3u, q1 = c1 & QM & 3u;
+  const uint32_t q0 = c0 & 3u, q1 = c1 & 3u;
   const uint32_t sel = 0x01000100u + (q0 | (q1 << 16)) * 0x202u;
   if constexpr (B == 2) {
-    return __builtin_amdgcn_perm(mag_word<2>(0), mag_word<2>(0), sel) ^ sgn;
+    return __builtin_amdgcn_perm(mag_word<2, LO>(0), mag_word<2, LO>(0), sel) ^ sgn;
   } else if constexpr (B == 3) {
-    return __builtin_amdgcn_perm(mag_word<3>(1), mag_word<3>(0), sel) ^ sgn;
+    return __builtin_amdgcn_perm(mag_word<3, LO>(1), mag_word<3, LO>(0), sel) ^ sgn;
   } else {
-    const uint32_t lo = __builtin_amdgcn_perm(mag_word<4>(1), mag_word<4>(0), sel);
-    const uint32_t hi = __builtin_amdgcn_perm(mag_word<4>(3), mag_word<4>(2), sel);
+    const uint32_t lo = __builtin_amdgcn_perm(mag_word<4, LO>(1), mag_word<4, LO>(0), sel);
+    const uint32_t hi = __builtin_amdgcn_perm(mag_word<4, LO>(3), mag_word<4, LO>(2), sel);
     const uint32_t m = ((c0 & 4u) ? 0xffffu : 0u) | ((c1 & 4u) ? 0xffff0000u : 0u);
     return ((hi & m) | (lo & ~m)) ^ sgn;
   }
 }
 
-// Writes the level table (the layout of LevelTable<B>) to shared memory
-// with NT threads; computed from the magnitudes, no global memory read.
-template <int B, int NT>
-__device__ __forceinline__ void build_level_table(uint32_t *lut, int tid) {
-  using C = UnitCfg<B>;
-  constexpr uint32_t CM = (1u << B) - 1u;
-#pragma unroll
-  for (int j = 0; j < (C::N + NT - 1) / NT; ++j) {
-    const uint32_t e = (uint32_t)tid + (uint32_t)NT * j;
-    if (C::N % NT == 0 || e < (uint32_t)C::N) {
-      if constexpr (C::DW == 2) {
-        const uint32_t lo = level_pair<B>(e & CM, (e >> B) & CM);
-        const uint32_t hi = level_pair<B>((e >> (2 * B)) & CM, (e >> (3 * B)) & CM);
-        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-        *reinterpret_cast<u32x2_t *>(lut + 2 * e) = u32x2_t{lo, hi};
-      } else {
-        lut[e] = level_pair<B>(e & CM, (e >> B) & CM);
-      }
-    }
-  }
-}
-
 // Pair table for the decode kernels: entry e (the 2B-bit concatenation of
-// two codes, first code in the low bits) holds their two float16 levels
-// (first in the low half).  It is stored in 64 copies with copy c of entry e
-// at dword 64e + c, and lane l of a wave always reads copy l: whatever the
-// indices, the 64 lanes of one lookup touch 64 consecutive banks' worth of
-// distinct dwords (no bank conflicts), unlike a single-copy table whose
-// random lookups pile onto the same banks.
+// two codes, first code in the low bits) holds the float16 hi parts of their
+// two levels (first in the low half) in its first dword and the lo parts in
+// its second.  It is stored in 32 copies with copy c of entry e at 8-byte
+// slot 32e + c, and lane l of a wave always reads copy l % 32: the lanes an
+// LDS read serves together touch distinct copies, so distinct banks,
+// whatever the indices (a single-copy table's random lookups pile onto the
+// same banks).  Reading only one part is a 4-byte read at dword 2(32e+c) (+1
+// for lo).
 template <int B>
 struct PairCfg {
   static constexpr int BITS = 2 * B;
   static constexpr int N = 1 << BITS;
-  static constexpr int WORDS = N * 64;
+  static constexpr int COPIES = 32;
+  static constexpr int WORDS = N * COPIES * 2;
 };
 
 template <int B, int NT>
 __device__ __forceinline__ void build_pair_table(uint32_t *tab, int tid) {
   using P = PairCfg<B>;
   constexpr uint32_t CM = (1u << B) - 1u;
-  static_assert(P::WORDS % NT == 0 && NT % 64 == 0, "pair table fill");
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  static_assert((P::N * P::COPIES) % NT == 0 && NT % 64 == 0, "pair table fill");
 #pragma unroll
-  for (int j = 0; j < P::WORDS / NT; ++j) {
-    // entry (tid + NT j) / 64 is the same for a whole wave
-    const uint32_t e = (uint32_t)__builtin_amdgcn_readfirstlane((tid >> 6) + (NT / 64) * j);
-    tab[tid + NT * j] = level_pair<B>(e & CM, e >> B);
+  for (int j = 0; j < P::N * P::COPIES / NT; ++j) {
+    // entry (tid + NT j) / 32 is the same for each half of a wave
+    const uint32_t slot = (uint32_t)tid + NT * j, e = slot / P::COPIES;
+    reinterpret_cast<u32x2_t *>(tab)[slot] =
+        u32x2_t{level_pair<B, false>(e & CM, e >> B), level_pair<B, true>(e & CM, e >> B)};
   }
 }
 

@@ -4,10 +4,11 @@
 // memory (one shared read per element and head).  With eight query heads per
 // kv head that is eight table reads per cache element, far more LDS traffic
 // than the packed stream itself.  On CDNA4 the eight heads are one dense
-// contraction instead: every packed code is decoded ONCE per kv head into a
-// float16 level through a table in LDS (indexed by the concatenated codes of
-// 2 or 4 neighbouring elements, so one LDS read yields 2-4 levels), and the
-// matrix cores do Q.K^T and P.V for all heads of the kv head at once.
+// contraction instead: every packed code is decoded ONCE per kv head into
+// the float16 hi and lo parts of its level through a table in LDS (indexed
+// by the concatenated codes of 2 neighbouring elements, so one LDS read
+// yields both parts of 2 levels), and the matrix cores do Q.K^T and P.V for
+// all heads of the kv head at once.
 //
 // One 16-key tile in a wave (v_mfma_f32_16x16x32_f16 for scores,
 // v_mfma_f32_16x16x16_f16 for values):
@@ -18,7 +19,9 @@
 //           p * vnorm, rows >= 8 the low half.  V's 8 d-tiles take element
 //           8n + t in column n of tile t, so a lane decodes 8 consecutive
 //           elements of 4 keys.
-// The levels are float16-exact, so the only roundings are float32
+// A level (a float32 value) enters both products as its float16 hi and lo
+// parts, one product each into the same accumulator, so every operand
+// carries about 22 bits and the roundings that matter are float32
 // accumulation and the exponential.
 //
 // Work split ([PR36] (d) raised occupancy to hide load latency; on MI355X the
@@ -56,15 +59,27 @@ __device__ __forceinline__ uint32_t bits_at(const uint32_t *dw, int pos, int nbi
   return nbits == 32 ? x : (x & ((1u << nbits) - 1u));
 }
 
-// Decode NEL consecutive elements held in dw (first element in bit 0) into
-// float16 pairs out[0 .. NEL/2) through the pair table; tab points at this
-// lane's copy (dword lane of the table).
+// Decode NEL consecutive elements held in dw (first element in bit 0)
+// through the pair table into float16 pairs: hi[0 .. NEL/2) and lo[0 ..
+// NEL/2) hold the hi and lo parts of the levels.  tab points at this lane's
+// copy (8-byte slot lane % 32 of the table).
 template <int B, int NEL>
-__device__ __forceinline__ void decode_pairs(const uint32_t *dw, const uint32_t *tab,
-                                             uint32_t *out) {
+__device__ __forceinline__ void decode_pairs_hl(const uint32_t *dw, const u32x2_t *tab, uint32_t *hi,
+                                                uint32_t *lo) {
   constexpr int PB = 2 * B;
 #pragma unroll
-  for (int j = 0; j < NEL / 2; ++j) out[j] = tab[bits_at(dw, PB * j, PB) * 64];
+  for (int j = 0; j < NEL / 2; ++j) {
+    const u32x2_t v = tab[bits_at(dw, PB * j, PB) * PairCfg<B>::COPIES];
+    hi[j] = v.x;
+    lo[j] = v.y;
+  }
+}
+// One part only (tab: this lane's hi dword, or lo dword, of the table).
+template <int B, int NEL>
+__device__ __forceinline__ void decode_pairs(const uint32_t *dw, const uint32_t *tab, uint32_t *out) {
+  constexpr int PB = 2 * B;
+#pragma unroll
+  for (int j = 0; j < NEL / 2; ++j) out[j] = tab[bits_at(dw, PB * j, PB) * (2 * PairCfg<B>::COPIES)];
 }
 
 __device__ __forceinline__ float half_to_float(uint16_t h) {
@@ -135,7 +150,7 @@ __device__ __forceinline__ SeqExtent seq_extent(const int64_t *seq_start, const 
 // of one product each (k-slot (lane >> 4, i) of K-step st <-> element 32 st +
 // 8 (lane >> 4) + i), and each product is scaled by its block's scale.
 template <int B, int T, int GK, int GV, bool QBF16, bool KQ8, int HP>
-__global__ __launch_bounds__(kDecThreads, HP == 16 && B == 3 && T <= 4 ? 4 : 2) void decode_split_kernel(
+__global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
     const uint8_t *__restrict__ kcodes, const uint16_t *__restrict__ knorms,
     const uint8_t *__restrict__ vcodes, const uint16_t *__restrict__ vnorms, int64_t n_cells,
     const int64_t *__restrict__ seq_start, const int32_t *__restrict__ seq_len, int64_t kv_len,
@@ -333,7 +348,7 @@ __global__ __launch_bounds__(kDecThreads, HP == 16 && B == 3 && T <= 4 ? 4 : 2) 
 
     // ---- scores: S^T[key][col] over the range, tile by tile; every column
     //      set takes the same decoded K operand
-    const uint32_t *tab = ptab + lane;
+    const u32x2_t *tab = reinterpret_cast<const u32x2_t *>(ptab) + (lane & 31);
     float sc[T][NS][4];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -361,18 +376,24 @@ __global__ __launch_bounds__(kDecThreads, HP == 16 && B == 3 && T <= 4 ? 4 : 2) 
             }
           }
         } else {
-          uint32_t a16[16];
-          decode_pairs<B, 32>(kd[t][gk], tab, a16);
+          // the level's hi and lo parts in two products over the same query
+          // operand: (Kh + Kl) (Qh + Ql)
+          uint32_t a16[16], l16[16];
+          decode_pairs_hl<B, 32>(kd[t][gk], tab, a16, l16);
           float4_t acc[NS];
 #pragma unroll
           for (int ns = 0; ns < NS; ++ns) acc[ns] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int st = 0; st < 4; ++st) {
             const u32x4_t av = {a16[4 * st], a16[4 * st + 1], a16[4 * st + 2], a16[4 * st + 3]};
+            const u32x4_t al = {l16[4 * st], l16[4 * st + 1], l16[4 * st + 2], l16[4 * st + 3]};
 #pragma unroll
-            for (int ns = 0; ns < NS; ++ns)
+            for (int ns = 0; ns < NS; ++ns) {
               acc[ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[ns][gk][st],
                                                                acc[ns], 0, 0, 0);
+              acc[ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, al), qb[ns][gk][st],
+                                                               acc[ns], 0, 0, 0);
+            }
           }
           const float4 n4 = *reinterpret_cast<const float4 *>(&nk[gk][rg][16 * t + 4 * quad]);
           const float nkv[4] = {n4.x, n4.y, n4.z, n4.w};
@@ -515,75 +536,99 @@ __global__ __launch_bounds__(kDecThreads, HP == 16 && B == 3 && T <= 4 ? 4 : 2) 
     constexpr int VBITS = 8 * B;
     const int vpos = VBITS * col;
     const int vw0 = vpos >> 5, vsh = vpos & 31;
-    const uint32_t *tab = ptab + lane;
+    // this lane's hi dword of the pair table (its lo dword follows)
+    const uint32_t *tabw = ptab + 2 * (lane & 31);
     // after the swap, lanes 0-31 hold d-tiles 0-3 and lanes 32-63 d-tiles
     // 4-7, each as high + low; row (head) 4*((lane&31)>>4) + i
     const int qd = (lane & 31) >> 4, dhi = lane >> 5;
+    // B operands of tile t from one part of the levels (tb: the hi or lo
+    // dword of this lane's table copy)
+    auto v_tile = [&](const uint32_t *vlane, int t, const uint32_t *tb, u32x2_t (&ops)[8]) {
+      uint32_t vv[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t *row = vlane + (16 * t + i) * ROWP;
+        const uint32_t run[1] = {__builtin_amdgcn_alignbit(row[1], row[0], vsh)};
+        decode_pairs<B, 8>(run, tb, vv[i]);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const int w = dt >> 1;
+        const uint32_t sel = (dt & 1) ? 0x07060302u : 0x05040100u;
+        ops[dt] = u32x2_t{__builtin_amdgcn_perm(vv[1][w], vv[0][w], sel),
+                          __builtin_amdgcn_perm(vv[3][w], vv[2][w], sel)};
+      }
+    };
     float4 res[NS][GV][4];
 #pragma unroll
     for (int gv = 0; gv < GV; ++gv) {
       const uint32_t *vlane = vr + 4 * quad * ROWP + GW * gv + vw0;
+      // hi parts of every tile before the barrier; lo parts tile pair by
+      // tile pair beside the products
       u32x2_t vbop[T][8];
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        uint32_t vv[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t *row = vlane + (16 * t + i) * ROWP;
-          const uint32_t run[1] = {__builtin_amdgcn_alignbit(row[1], row[0], vsh)};
-          decode_pairs<B, 8>(run, tab, vv[i]);
-        }
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const int w = dt >> 1;
-          const uint32_t sel = (dt & 1) ? 0x07060302u : 0x05040100u;
-          vbop[t][dt] = u32x2_t{__builtin_amdgcn_perm(vv[1][w], vv[0][w], sel),
-                                __builtin_amdgcn_perm(vv[3][w], vv[2][w], sel)};
-        }
-      }
+      for (int t = 0; t < T; ++t) v_tile(vlane, t, tabw, vbop[t]);
       if (gv == 0) __syncthreads();   // P operands complete
 
-      // each column set takes the same decoded V operands
+      // each column set takes the same decoded V operands; the products run
+      // (Ph + Pl)(Vh + Vl) as two products per d-tile into one accumulator
+      float4_t o[NS][8];
 #pragma unroll
-      for (int ns = 0; ns < NS; ++ns) {
-        float4_t o[8];
+      for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
-        // tiles in pairs on the 32-deep product: k-slots (quad, 0..3) hold
-        // the first tile's keys 4 quad + i and (quad, 4..7) the second's, in
-        // both operands, so the sum runs over the same 32 keys; an odd last
-        // tile takes the 16-deep product
+        for (int dt = 0; dt < 8; ++dt) o[ns][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+      // tiles in pairs on the 32-deep product: k-slots (quad, 0..3) hold
+      // the first tile's keys 4 quad + i and (quad, 4..7) the second's, in
+      // both operands, so the sum runs over the same 32 keys; an odd last
+      // tile takes the 16-deep product
 #pragma unroll
-        for (int t = 0; t + 1 < T; t += 2) {
+      for (int t = 0; t + 1 < T; t += 2) {
+        u32x2_t l0[8], l1[8];
+        v_tile(vlane, t, tabw + 1, l0);
+        v_tile(vlane, t + 1, tabw + 1, l1);
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
           const u32x2_t p0 = pbuf[(((gv * 4 + rg) * T + t) * NS + ns) * 64 + lane];
           const u32x2_t p1 = pbuf[(((gv * 4 + rg) * T + t + 1) * NS + ns) * 64 + lane];
           const half8_t pa = __builtin_bit_cast(half8_t, u32x4_t{p0.x, p0.y, p1.x, p1.y});
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) {
-            const u32x4_t vb = {vbop[t][dt].x, vbop[t][dt].y, vbop[t + 1][dt].x, vbop[t + 1][dt].y};
-            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(half8_t, vb), o[dt], 0, 0, 0);
+            const u32x4_t vh = {vbop[t][dt].x, vbop[t][dt].y, vbop[t + 1][dt].x, vbop[t + 1][dt].y};
+            const u32x4_t vl = {l0[dt].x, l0[dt].y, l1[dt].x, l1[dt].y};
+            o[ns][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(half8_t, vh), o[ns][dt], 0, 0, 0);
+            o[ns][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(half8_t, vl), o[ns][dt], 0, 0, 0);
           }
         }
-        if constexpr (T & 1) {
+      }
+      if constexpr (T & 1) {
+        u32x2_t l0[8];
+        v_tile(vlane, T - 1, tabw + 1, l0);
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
           const half4_t pa =
               __builtin_bit_cast(half4_t, pbuf[(((gv * 4 + rg) * T + T - 1) * NS + ns) * 64 + lane]);
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt)
-            o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(half4_t, vbop[T - 1][dt]),
-                                                         o[dt], 0, 0, 0);
+          for (int dt = 0; dt < 8; ++dt) {
+            o[ns][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(half4_t, vbop[T - 1][dt]),
+                                                             o[ns][dt], 0, 0, 0);
+            o[ns][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(half4_t, l0[dt]),
+                                                             o[ns][dt], 0, 0, 0);
+          }
         }
+      }
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float oc[4];
 #pragma unroll
           for (int dt = 0; dt < 4; ++dt) {
-            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(o[dt][i]),
-                                                            __float_as_uint(o[dt + 4][i]), false, false);
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(o[ns][dt][i]),
+                                                            __float_as_uint(o[ns][dt + 4][i]), false, false);
             oc[dt] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
           }
           res[ns][gv][i] = make_float4(oc[0], oc[1], oc[2], oc[3]);
         }
-      }
     }
     if constexpr (kReuse) __syncthreads();   // V rows and P operands consumed
 #pragma unroll
@@ -799,7 +844,9 @@ hipError_t plan_decode(const tq_cache &k, const tq_cache &v, int64_t max_len, in
   // for 8 sequences of 2 rows).
   const int groups = k.head_dim / kGroup + v.head_dim / kGroup;
   const int64_t wg_per_split = (int64_t)k.n_kv_heads * p->head_groups * n_seq;
-  int tpw = 8;
+  // (sixteen pairs hold two column sets of value accumulators beside the
+  // tiles' hi operands: at most 4 tiles fit the registers)
+  int tpw = p->pairs == 16 ? 4 : 8;
   while (tpw > 1) {
     const int64_t splits = ceil_div<int64_t>(max_len, 64LL * tpw);
     if (tpw * groups <= 16 && splits * wg_per_split >= n_cu) {
@@ -850,7 +897,6 @@ hipError_t launch_split(int tpw, int pairs, dim3 grid, hipStream_t st, const Spl
         case 1: TQ_DEC(1, 16); break;
         case 2: TQ_DEC(2, 16); break;
         case 4: TQ_DEC(4, 16); break;
-        case 8: TQ_DEC(8, 16); break;
         default: return hipErrorNotSupported;
       }
       return hipSuccess;

@@ -123,16 +123,21 @@ def test_lloyd_max_fixed_point_by_quadrature(levels):
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
-def test_stored_codebook_is_fp16_of_lloyd_max(bits):
-    """Stored magnitudes are float16 values within half an fp16 ulp of the
-    quadrature-checked Lloyd-Max levels, and thresholds are exact midpoints."""
+def test_stored_codebook_is_fp32_of_lloyd_max(bits):
+    """Stored magnitudes are the quadrature-checked Lloyd-Max levels rounded
+    once to float32 (within half a float32 ulp, no narrower rounding), and
+    every threshold is within half a float32 ulp of the float64 midpoint of
+    its two levels, strictly between them."""
     m = o.code_magnitudes(bits)
+    assert m.dtype == np.float32
     lv = o.lloyd_max_normal(2 ** bits)[2 ** (bits - 1):]
-    assert np.all(m.astype(np.float16).astype(np.float32) == m)
-    ulp = np.spacing(m.astype(np.float16)).astype(np.float64)
-    assert np.all(np.abs(m.astype(np.float64) - lv) <= 0.5 * ulp)
+    assert np.all(np.abs(m.astype(np.float64) - lv) <= 0.5 * np.spacing(m).astype(np.float64))
+    # not float16-rounded: at least one level is not a float16 value
+    assert np.any(m.astype(np.float16).astype(np.float32) != m)
     t = o.mag_thresholds(bits)
-    assert np.all(t.astype(np.float64) * 2 == m[1:].astype(np.float64) + m[:-1])
+    mid = 0.5 * (lv[1:] + lv[:-1])
+    assert np.all(np.abs(t.astype(np.float64) - mid) <= 0.5 * np.spacing(t).astype(np.float64))
+    assert np.all((t > m[:-1]) & (t < m[1:]))
     v = o.code_values(bits)
     half = 2 ** (bits - 1)
     np.testing.assert_array_equal(v[:half], m)
@@ -197,11 +202,15 @@ def test_quantizer_impulse_closed_form(bits, qs_star):
         want = np.zeros(128)
         want[j] = float(level) * float(np.float16(abs(alpha))) * np.sign(alpha)
         np.testing.assert_allclose(xh, want, atol=1e-12)
-    # the worked number for turbo3, alpha = -3: 0.7558594 * 3
+    # the worked number for turbo3, alpha = -3: three times the second
+    # 3-bit level, 0.7560 in Max's table (four decimals), so x_hat_0 is
+    # -2.2680 to within 3 * 5e-5
     if bits == 3:
         x = np.zeros(128, F32); x[0] = -3.0
         c, n = o.quantize_groups(x, 3)
-        assert abs(o.dequant(c, n, 3)[0] + 2.267578125) < 1e-12
+        xh0 = o.dequant(c, n, 3)[0]
+        assert abs(xh0 + 3 * 0.7560) < 3 * 5e-5
+        assert abs(xh0 + 3 * float(o.code_magnitudes(3)[1])) < 1e-12
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
