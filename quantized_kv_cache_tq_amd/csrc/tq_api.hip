@@ -275,9 +275,13 @@ tq_status tq_attn_prefill(const tq_cache *k, const tq_cache *v, int64_t kv_len, 
   size_t split_bytes = 0;
   if (tq_status st = prefill_split_plan(*k, n_rows, n_q_heads, kv_len, &split, &split_bytes)) return st;
   if (split) {
+    // planned for kv_len, as the workspace query sizes it (the tile count of
+    // the plan is not monotone in the length, so a plan for the shorter
+    // sequence could need more splits than the query provided); its grid
+    // covers the sequence and splits past its q_pos0 + n_rows cells exit
     const int64_t len = q_pos0 + n_rows;
     DecodePlan dp;
-    if (tq_status st = from_hip(plan_decode(*k, *v, len, n_q_heads, (int)n_rows, 1, &dp))) return st;
+    if (tq_status st = from_hip(plan_decode(*k, *v, kv_len, n_q_heads, (int)n_rows, 1, &dp))) return st;
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < dp.workspace_bytes)
       return TQ_ERR_WORKSPACE;
     return from_hip(launch_decode(*k, *v, nullptr, nullptr, len, q, q_dtype, n_q_heads, scale, 0.f, out,

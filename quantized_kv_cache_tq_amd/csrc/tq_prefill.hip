@@ -162,6 +162,7 @@ struct Args {
   const void *q;
   float *out;
   int n_q, n_rep, bq, n_qtiles;
+  int n_live;                 // live qrows per tile: n_rep * bq (<= 64)
   int paired;                 // 1: workgroup p also takes query tile n_qtiles - 1 - p
   // key splits (kSplit): workgroup z takes key tiles [z ks_tiles, (z+1) ks_tiles)
   // of each of its query tiles and writes partials [row][q head][split][KD + 4]
@@ -364,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
       constexpr int EE = D::EE, PE = 128 / EE;
       const int j = tid % PE, c = (tid / PE) & 63, grp = tid / (PE * 64);
       const int64_t r = row0 + c % a.bq;
-      if (r < a.n_rows) {
+      if (r < a.n_rows && c < a.n_live) {
         float *pr = a.ws + ((r * a.n_q + g * a.n_rep + c / a.bq) * a.n_split + blockIdx.z) * (KD + 4);
 #pragma unroll
         for (int v = 0; v < EE / 4; ++v)
@@ -383,7 +384,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
         //      EQ pi .. EQ pi + EQ - 1 of group grp of qrow c
         constexpr int EQ = D::EQ, PP = 128 / EQ;
         const int pi = tid % PP, c = (tid / PP) & 63, grp = tid / (PP * 64);
-        const int hq = c / a.bq, rq = c % a.bq;
+        // (a qrow past the last live one, when n_rep does not divide 64, reads
+        // a live head's row and its result is never stored)
+        const int hq = min(c / a.bq, a.n_rep - 1), rq = c % a.bq;
         const int64_t rr = lmin(row0 + rq, a.n_rows - 1);
         const int64_t off = (rr * a.n_q + g * a.n_rep + hq) * KD + 128 * grp + EQ * pi;
         float x[EQ];
@@ -676,7 +679,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
         }
       if constexpr (kSplit) {
         const int64_t r = row0 + c % a.bq;
-        if (r < a.n_rows) {
+        if (r < a.n_rows && c < a.n_live) {
           float *pr = a.ws + ((r * a.n_q + g * a.n_rep + c / a.bq) * a.n_split + blockIdx.z) * (KD + 4);
 #pragma unroll
           for (int v = 0; v < EE / 4; ++v)
@@ -698,7 +701,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
       }
       const int hq = c / a.bq;
       const int64_t r = row0 + c % a.bq;
-      if (r < a.n_rows) {
+      if (r < a.n_rows && c < a.n_live) {
         uint32_t sw = sign_word32((EE * j) >> 5) >> ((EE * j) & 31);
         asm volatile("" : "+v"(sw));   // formed here, not hoisted and spilled
         float *orow = a.out + (r * a.n_q + g * a.n_rep + hq) * KD + d0;
@@ -723,9 +726,11 @@ hipError_t plan_prefill(const tq_cache &k, int64_t n_rows, int32_t n_q_heads, in
                         PrefillPlan *p) {
 
   const int n_rep = n_q_heads / k.n_kv_heads;
-  if (n_rep < 1 || pf::kQRows % n_rep != 0) return hipErrorNotSupported;
+  if (n_rep < 1 || n_rep > 8) return hipErrorNotSupported;
   // key offsets inside one head are 32-bit
   if (k.n_cells > (int64_t)(0xffffffffu / (32u * 4))) return hipErrorNotSupported;
+  // query rows per tile: the tile's 64 qrows hold bq rows of n_rep heads;
+  // when n_rep does not divide 64 the last 64 - n_rep bq qrows are idle
   p->rows_per_tile = pf::kQRows / n_rep;
   const int64_t tiles = ceil_div<int64_t>(n_rows, p->rows_per_tile);
   if (tiles > 0x3fffffff) return hipErrorInvalidValue;
@@ -782,6 +787,7 @@ hipError_t launch_prefill(const tq_cache &k, const tq_cache &v, int64_t kv_len, 
   a.n_q = n_q_heads;
   a.n_rep = n_q_heads / k.n_kv_heads;
   a.bq = p.rows_per_tile;
+  a.n_live = a.n_rep * a.bq;
   a.n_qtiles = p.n_row_tiles;
   a.paired = p.paired;
   const bool split = p.max_splits > 1;

@@ -219,3 +219,26 @@ def test_key_split_workspace():
     assert b.tq_attn_prefill_workspace(kc, 256, 16, 9000) > 0
     assert b.tq_attn_prefill_workspace(kc, 2048, 16, 9000) == 0
     assert b.tq_attn_prefill_workspace(kc, 512, 16, 512) == 0
+
+
+@pytest.mark.parametrize("rows,kv,q0", [(3, 8192, 7933), (3, 8192, 4100), (40, 16384, 15000)])
+def test_few_rows_workspace_for_kv_len(rows, kv, q0):
+    """The split-key path runs with the plan for kv_len, the length its
+    workspace query was given: a plan for the shorter q_pos0 + n_rows cells
+    can pick fewer keys per split (more splits) than the one for kv_len
+    (3 rows after 7933 of 8192 cells at 16 q / 8 kv heads), so it would not
+    fit the workspace the query returned."""
+    q, k, v = inputs.prefill(seed=rows + q0, rows=rows, kv_len=kv)
+    _run(q, k, v, kv, q0, what="plan for kv_len")
+
+
+@pytest.mark.parametrize("rows,kv,q0,d,n_q,n_kv", [
+    (200, 300, 100, 256, 24, 8), (130, 130, 0, 256, 12, 2), (150, 400, 250, 128, 5, 1),
+    (100, 160, 60, 128, 14, 2), (100, 6000, 5900, 256, 6, 2)])
+def test_gqa_not_dividing_tile(rows, kv, q0, d, n_q, n_kv):
+    """3, 5, 6 and 7 q heads per kv head in the tiled kernel (more than 64
+    rows): a tile holds floor(64 / n_rep) rows of every head and its last
+    64 - n_rep floor(64 / n_rep) qrows are idle; the last case also splits
+    the key range (few row tiles after a long prefix)."""
+    q, k, v = inputs.prefill(seed=rows + n_q, rows=rows, kv_len=kv, n_q=n_q, n_kv=n_kv, d=d)
+    _run(q, k, v, kv, q0, q_bf16=(d == 256), what=f"gqa {n_q}/{n_kv} d{d}")
