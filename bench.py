@@ -74,7 +74,7 @@ def parse():
     ap.add_argument("--layers", type=int, default=24)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
-                    help="comma list of legs: set_rows,decode,prefill,int8 (default: all; extras decode_wide, "
+                    help="comma list of legs: set_rows,decode,prefill,int8 (default: all; extras decode_wide, decode_long, "
                          "decode_types, decode_batch, floor, prefill_rows, int8_140k); "
                          "'copy' adds a 256 MiB device copy used to calibrate HBM counters")
     return ap.parse_args()
@@ -104,10 +104,130 @@ class Leg:
         b.record()
         self.pairs.append((a, b))
 
+    def times_ms(self):
+        return [a.elapsed_time(b) for a, b in self.pairs]
+
     def mean_ms(self):
         if not self.pairs:
             return None
-        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
+        return float(np.mean(self.times_ms()))
+
+    def median_ms(self):
+        if not self.pairs:
+            return None
+        return float(np.median(self.times_ms()))
+
+
+def host_info():
+    """Host cores the CPU baseline can use and what it ran on."""
+    info = {"os_cpu_count": os.cpu_count()}
+    try:
+        info["affinity_cpus"] = len(os.sched_getaffinity(0))
+    except AttributeError:
+        info["affinity_cpus"] = None
+    try:
+        from threadpoolctl import threadpool_info
+        info["blas_threads"] = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        info["blas_threads"] = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            info["cpu_model"] = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        info["cpu_model"] = None
+    return info
+
+
+def max_abs_rel_l2(got, want):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64).astype(np.float32).astype(np.float64)
+    d = got - want
+    return float(np.abs(d).max()), float(np.linalg.norm(d) / max(np.linalg.norm(want), 1e-300))
+
+
+def oracle_leg(b, torch, dev, inputs, k_np, v_np, q_np, kc0, vc0, q_dec, ws, scale_dec, kv_bytes_per_call,
+               prefill, int8, snap, pf_inputs, d8):
+    """The oracle timed on bounded samples of each workload on the host cores,
+    and the parity of the GPU results of this run against it."""
+    import oracle as o
+    log("[bench] cpu baseline: oracle set_rows, decode, prefill and int8 samples")
+    host = host_info()
+    legs = {}
+    parity = {}
+    KV, NKV, D = k_np.shape
+    # set_rows: the 32K x 4-head K and V caches (vectorized float32 numpy)
+    t0 = time.perf_counter()
+    okc, ovc = o.new_cache(3, D, NKV, KV), o.new_cache(3, D, NKV, KV)
+    o.set_rows(okc, k_np, np.arange(KV))
+    o.set_rows(ovc, v_np, np.arange(KV))
+    dt = time.perf_counter() - t0
+    sr_bytes = 2 * (KV * NKV * D * 4 + KV * NKV * 50)
+    legs["set_rows_32k_KV_pair"] = {"s": round(dt, 3), "GBps": round(sr_bytes / dt / 1e9, 4)}
+    # decode: two calls at the 32K / GQA-8 shape
+    reps = 2
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        ref = o.attn_decode(okc, ovc, KV, q_np.astype(np.float64), scale_dec)
+    dt_dec = (time.perf_counter() - t0) / reps
+    legs["decode_32k_gqa8"] = {"s_per_call": round(dt_dec, 3), "GBps": round(kv_bytes_per_call / dt_dec / 1e9, 6)}
+    # decode parity: one call into a buffer of its own, right before the compare
+    chk = torch.empty((q_np.shape[0], D), dtype=torch.float32, device=dev)
+    b.tq_attn_decode(kc0, vc0, KV, q_dec, scale_dec, out=chk, workspace=ws)
+    torch.cuda.synchronize()
+    ma, rl = max_abs_rel_l2(chk.cpu().numpy(), ref)
+    parity["decode_32k"] = {"max_abs": ma, "rel_l2": rl}
+    # sparse V at the pages' turbo3 threshold: the order-free bound B of the
+    # skipped terms and the share of (head, key) weights below tau
+    tau = 5e-3
+    bnd, n_small = o.sparse_v_bound(okc, ovc, KV, q_np.astype(np.float64), scale_dec, tau)
+    chk_s = torch.empty_like(chk)
+    b.tq_attn_decode(kc0, vc0, KV, q_dec, scale_dec, out=chk_s, workspace=ws, sparse_v_tau=tau)
+    torch.cuda.synchronize()
+    dev_s = np.abs(chk_s.cpu().numpy().astype(np.float64) - ref).max(axis=1)
+    parity["decode_32k_sparse_v"] = {"tau": tau, "bound_B_max": float(bnd.max()),
+                                     "skippable_fraction": float(n_small.sum() / (KV * len(n_small))),
+                                     "max_abs_vs_dense_oracle": float(dev_s.max()),
+                                     "within_B_plus_2e-3": bool(np.all(dev_s <= bnd + 2e-3))}
+    del okc, ovc
+    if prefill is not None and pf_inputs is not None:
+        # prefill: the last 256 of the 2048 causal rows (dequantize the cache,
+        # then float64 attention), against the timed call's output
+        pq, pk, pv = pf_inputs
+        R, _, PD = pq.shape
+        t0 = time.perf_counter()
+        pkc, pvc = o.new_cache(3, PD, pk.shape[1], R), o.new_cache(3, PD, pk.shape[1], R)
+        o.set_rows(pkc, pk, np.arange(R))
+        o.set_rows(pvc, pv, np.arange(R))
+        t1 = time.perf_counter()
+        n_s = 256
+        want = o.attn_prefill(pkc, pvc, R, pq[R - n_s:].astype(np.float64), R - n_s, 1.0 / math.sqrt(PD))
+        dt = time.perf_counter() - t1
+        legs["prefill_2048_last_256_rows"] = {"s": round(dt, 3), "tokens_per_s": round(n_s / dt, 1),
+                                             "quantize_s": round(t1 - t0, 3)}
+        ma, rl = max_abs_rel_l2(snap["prefill"][R - n_s:], want)
+        parity["prefill_2048_last_256_rows"] = {"max_abs": ma, "rel_l2": rl}
+    if int8 is not None and d8 is not None:
+        # int8 prompt: the last 64 of the 2048 queries at 40000 cells
+        ctx = int8["ctx"]
+        n_q8 = d8["q"].shape[0]
+        n_s = 64
+        t0 = time.perf_counter()
+        want = o.attn_int8_prompt(d8["q"][n_q8 - n_s:].astype(np.float64), d8["k8"], d8["v8"], d8["k_scale"],
+                                  d8["v_scale"], d8["page_table"], ctx, ctx - n_s, 1.0 / math.sqrt(d8["q"].shape[2]))
+        dt = time.perf_counter() - t0
+        pairs = n_s * ctx - n_s * (n_s - 1) // 2
+        legs["int8_40k_last_64_queries"] = {"s": round(dt, 3),
+                                           "GFLOPs": round(4.0 * 128 * d8["q"].shape[1] * pairs / dt / 1e9, 2)}
+        ma, rl = max_abs_rel_l2(snap["int8"][n_q8 - n_s:], want)
+        parity["int8_40k_last_64_queries"] = {"max_abs": ma, "rel_l2": rl}
+    cores = host["blas_threads"] or 1
+    return {"cpu_baseline": {"value": legs["decode_32k_gqa8"]["GBps"], "unit": "GB/s", "cores": cores,
+                             "kind": "oracle",
+                             "sample": f"{reps} numpy decode calls at the 32K / GQA-8 turbo3 shape "
+                                       f"({dt_dec:.2f} s per call: unpack, dequantize, float64 attention "
+                                       f"through BLAS with {cores} threads); the other legs in 'legs'",
+                             "host": host, "legs": legs},
+            "parity_check": parity}
 
 
 def main():
@@ -272,6 +392,13 @@ def main():
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / max(1, args.steps)
     log("[bench] timed region done")
+    # the timed calls' outputs, before any extra reuses their buffers (the
+    # parity check below compares samples of them with the oracle)
+    snap = {}
+    if prefill is not None:
+        snap["prefill"] = pout.cpu().numpy()
+    if int8 is not None:
+        snap["int8"] = out8.cpu().numpy()
 
     # ---------------- extras, timed after the steps (not part of a step)
     def time_eager(fn, reps=10):
@@ -421,6 +548,32 @@ def main():
                 "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
             del akc, aws
 
+        # one query row over a long sequence (leg "decode_long"): 131072
+        # cells, 32 q / 4 kv heads, turbo3, L distinct caches (52 MB each),
+        # so the launch cost is spread over four times the headline's bytes
+        if want("decode_long"):
+            LK = 131072
+            lq, lk, lv = inputs.outlier_decode(seed=11, kv_len=LK)
+            lidx = torch.arange(LK, dtype=torch.int64, device=dev)
+            lkc = [b.new_cache(3, D, NKV, LK) for _ in range(L)]
+            lvc = [b.new_cache(3, D, NKV, LK) for _ in range(L)]
+            b.tq_set_rows(lkc[0], torch.from_numpy(lk).to(dev), lidx)
+            b.tq_set_rows(lvc[0], torch.from_numpy(lv).to(dev), lidx)
+            del lk, lv
+            for i in range(1, L):
+                lkc[i].codes.copy_(lkc[0].codes); lkc[i].norms.copy_(lkc[0].norms)
+                lvc[i].codes.copy_(lvc[0].codes); lvc[i].norms.copy_(lvc[0].norms)
+            lqt = torch.from_numpy(lq).to(torch.bfloat16).to(dev)
+            lws = torch.empty(b.tq_attn_decode_workspace(lkc[0], lvc[0], LK, NQ), dtype=torch.uint8, device=dev)
+            t_ms = time_graph([lambda i=i: b.tq_attn_decode(lkc[i], lvc[i], LK, lqt, scale_dec, out=outs[i],
+                                                            workspace=lws) for i in range(L)])
+            nbytes = 2 * NKV * LK * 50
+            gbps = nbytes / (t_ms * 1e-3) / 1e9
+            extras["decode_turbo3_131072_gqa8"] = {"us_per_call": round(t_ms * 1e3, 3), "bytes_per_call": nbytes,
+                                                   "GBps": round(gbps, 1),
+                                                   "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+            del lkc, lvc, lws
+
         # turbo2 and turbo4 decode at the headline's heads, 8192 and 32768
         # cells (leg "decode_types"), over L distinct caches each
         if want("decode_types"):
@@ -563,12 +716,14 @@ def main():
             del fbufs
     log("[bench] extras done")
 
-    res = {}
-    ms = {n: legs[n].mean_ms() for n in legs}
+    # every leg's time is the median over the timed steps (its mean beside it)
+    ms = {n: legs[n].median_ms() for n in legs}
+    ms_mean = {n: legs[n].mean_ms() for n in legs}
     step_ms = sum(v_ for n_, v_ in ms.items() if v_ is not None and n_ != "copy")
     out = {"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True,
-           "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+           "scaling": "weak", "vs_baseline": None,
+           "dtype": "f16 hi+lo split operands, f32 accumulate (prefill: single f16 operands)",
            "data": "synthetic",
            "config": {"workload": f"turbo3 decode: 32 q / 4 kv heads, head_dim 128, kv 32768, bf16 q, "
                                   f"{L} layers' caches per step; + set_rows of one 32768-row cache, "
@@ -582,7 +737,7 @@ def main():
         out["value"] = round(gbps, 2)
         out["decode"] = {"us_per_call": round(per_call_us, 3), "kv_bytes_per_call": kv_bytes_per_call,
                          "GBps": round(gbps, 2), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
-                         "layers_per_step": L}
+                         "layers_per_step": L, "us_per_call_mean": round(ms_mean["decode"] * 1e3 / L, 3)}
         out["roofline"] = {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
                            "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                            "traffic": decode_traffic_bytes(),
@@ -602,40 +757,24 @@ def main():
     if ms["int8"] is not None:
         t_s = ms["int8"] * 1e-3
         tflops = int8["flops"] / t_s / 1e12
+        # the products run on float16 matrix cores with hi and lo operand
+        # parts: twice the algorithmic flops are executed
         out["int8_prompt"] = {"ctx": int8["ctx"], "n_q": int8["n_q"], "ms": round(ms["int8"], 4),
                               "TFLOPs": round(tflops, 2),
                               "frac_mfma_f16_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                              "frac_fp32_peak": round(tflops / FP32_PEAK_TFLOPS, 4)}
+                              "frac_mfma_f16_peak_executed": round(2 * tflops / MFMA_F16_PEAK_TFLOPS, 4)}
 
     if ms["copy"] is not None:
         out["calibration_copy"] = {"bytes_read": copy["nbytes"], "bytes_written": copy["nbytes"],
                                    "us": round(ms["copy"] * 1e3, 2),
                                    "GBps_read_plus_write": round(2 * copy["nbytes"] / (ms["copy"] * 1e-3) / 1e9, 1)}
 
-    # ---------------- CPU baseline: the oracle on a bounded sample
+    # ---------------- CPU baseline and parity: the oracle on bounded samples
     if not args.no_cpu_baseline and want("decode"):
-        log("[bench] cpu baseline (oracle decode, 8 calls at the 32K shape)")
-        import oracle as o
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-        except Exception:
-            cores = 1
-        okc, ovc = o.new_cache(3, D, NKV, KV), o.new_cache(3, D, NKV, KV)
-        o.set_rows(okc, k_np, np.arange(KV))
-        o.set_rows(ovc, v_np, np.arange(KV))
-        reps = 8
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            ref = o.attn_decode(okc, ovc, KV, q_np.astype(np.float64), scale_dec)
-        dt = (time.perf_counter() - t0) / reps
-        got = outs[0].cpu().numpy()
-        out["cpu_baseline"] = {"value": round(kv_bytes_per_call / dt / 1e9, 6), "unit": "GB/s",
-                               "cores": cores, "kind": "oracle",
-                               "sample": f"{reps} decode calls at the 32K/GQA-8 turbo3 shape "
-                                         f"(numpy: unpack, dequantize, float64 attention); "
-                                         f"{dt:.2f} s per call"}
-        out["parity_check"] = {"decode_max_abs_vs_oracle": float(np.abs(got - ref).max())}
+        out.update(oracle_leg(b, torch, dev, inputs, k_np, v_np, q_np, kcs[0], vcs[0], q_dec, ws,
+                              scale_dec, kv_bytes_per_call, prefill, int8, snap,
+                              (pq, pk, pv) if prefill is not None else None,
+                              d8 if int8 is not None else None))
     if extras:
         out["extras"] = extras
     out["wall_s_total"] = round(time.time() - t_wall0, 1)
