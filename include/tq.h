@@ -185,6 +185,23 @@ tq_status tq_attn_decode(const tq_cache *k, const tq_cache *v, int64_t kv_len, c
                          float *out, void *workspace, size_t workspace_bytes, tq_stream_t stream);
 
 /*
+ * Decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments, requirements and
+ * result as tq_attn_decode, with the split partials kept in a device array
+ * that the library owns, TQ_STATIC_SCRATCH_BYTES on every GPU the library
+ * runs on, held until the process ends.  The call allocates nothing.  A
+ * call whose partials (the size tq_attn_decode_workspace reports) exceed the
+ * array returns TQ_ERR_WORKSPACE and enqueues nothing.  Every call on a GPU
+ * shares that GPU's array: calls that may overlap on one GPU (other streams
+ * or threads) race and must be ordered by the caller.
+ */
+#define TQ_STATIC_SCRATCH_BYTES (16u << 20)
+tq_status tq_attn_decode_static(const tq_cache *k, const tq_cache *v, int64_t kv_len, const void *q,
+                                int q_dtype, int32_t n_q_heads, float scale, float sparse_v_tau,
+                                float *out, tq_stream_t stream);
+
+/*
  * Batched decode: n_seq sequences with n_rows (1..16) query rows each, in
  * one call ([PR28] "Graph-safe decode": query batches of at most two rows
  * take the single-row decode kernel, not the tile kernel; here any number

@@ -19,6 +19,9 @@ LIB_PATH = os.path.join(_PKG, "lib", "libtq.so")
 
 TQ_TURBO2, TQ_TURBO3, TQ_TURBO4, TQ_Q8 = 2, 3, 4, 8
 TQ_F32, TQ_BF16 = 0, 1
+TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP = 0, -1, -2, -3, -4
+# size of the device array behind tq_attn_decode_static (TQ_STATIC_SCRATCH_BYTES)
+STATIC_SCRATCH_BYTES = 16 << 20
 TYPE_BY_NAME = {"turbo2": 2, "turbo3": 3, "turbo4": 4, "q8": 8}
 
 
@@ -46,6 +49,8 @@ _SIGS = {
                                          POINTER(c_size_t)]),
     "tq_attn_decode": (c_int, [POINTER(TQCache), POINTER(TQCache), c_int64, c_void_p, c_int, c_int32,
                                c_float, c_float, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "tq_attn_decode_static": (c_int, [POINTER(TQCache), POINTER(TQCache), c_int64, c_void_p, c_int, c_int32,
+                                      c_float, c_float, c_void_p, c_void_p]),
     "tq_attn_decode_batch_workspace": (c_int, [POINTER(TQCache), POINTER(TQCache), c_int32, c_int32, c_int64,
                                                c_int32, POINTER(c_size_t)]),
     "tq_attn_decode_batch": (c_int, [POINTER(TQCache), POINTER(TQCache), c_int32, c_int32, c_void_p, c_void_p,
@@ -209,6 +214,27 @@ def tq_attn_decode(k: TQCacheTensors, v: TQCacheTensors, kv_len: int, q: torch.T
     _check(load_library().tq_attn_decode(ctypes.byref(k.struct), ctypes.byref(v.struct), kv_len,
                                          q.data_ptr(), qd, n_q, scale, sparse_v_tau, out.data_ptr(),
                                          ws.data_ptr(), ws.numel(), _stream(stream)), "tq_attn_decode")
+    return out
+
+
+def tq_attn_decode_static(k: TQCacheTensors, v: TQCacheTensors, kv_len: int, q: torch.Tensor, scale: float,
+                          out: torch.Tensor | None = None, sparse_v_tau: float = 0.0, stream=None) -> torch.Tensor:
+    """tq_attn_decode with the split partials in the library's own device
+    array (no workspace argument; nothing is allocated but `out` when it is
+    not given)."""
+    qd = _q_dtype(q)
+    _dev_tensor(q, q.dtype, "q")
+    if q.dim() != 2 or q.shape[1] != k.head_dim:
+        raise ValueError("q must be [n_q_heads, k.head_dim]")
+    n_q = q.shape[0]
+    if out is None:
+        out = torch.empty((n_q, v.head_dim), dtype=torch.float32, device=q.device)
+    _dev_tensor(out, torch.float32, "out")
+    if tuple(out.shape) != (n_q, v.head_dim):
+        raise ValueError("out must be [n_q_heads, v.head_dim]")
+    _check(load_library().tq_attn_decode_static(ctypes.byref(k.struct), ctypes.byref(v.struct), kv_len,
+                                                q.data_ptr(), qd, n_q, scale, sparse_v_tau, out.data_ptr(),
+                                                _stream(stream)), "tq_attn_decode_static")
     return out
 
 

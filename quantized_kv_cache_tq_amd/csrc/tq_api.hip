@@ -3,6 +3,8 @@
 // device memory; every check happens before the first HIP call.
 #include <string.h>
 
+#include <mutex>
+
 #include "tq_common.h"
 #include "tq_launch.h"
 
@@ -112,6 +114,38 @@ tq_status tq_set_rows(const tq_cache *dst, const float *src, const int64_t *cell
 
 // ---------------------------------------------------------------- decode
 
+// The scratch array of tq_attn_decode_static: one copy per GPU (the code
+// object's device globals), holding a call's split partials.  Host code
+// never passes the array's name to a kernel (on the host it names a stand-in,
+// not device memory): each device's address comes from hipGetSymbolAddress,
+// taken once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[TQ_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// This device's address of the scratch array (looked up on the first call on
+// the device, kept afterwards).
+hipError_t scratch_address(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
 static tq_status decode_check(const tq_cache *k, const tq_cache *v, int64_t kv_len,
                               int32_t n_q_heads) {
   tq_status s = check_pair(k, v, /*same_width=*/false, /*q8_k=*/true);
@@ -164,6 +198,26 @@ tq_status tq_attn_decode(const tq_cache *k, const tq_cache *v, int64_t kv_len, c
   if (s != TQ_OK) return s;
   return decode_call(k, v, 1, 1, nullptr, nullptr, kv_len, q, q_dtype, n_q_heads, scale, sparse_v_tau,
                      out, workspace, workspace_bytes, stream);
+}
+
+tq_status tq_attn_decode_static(const tq_cache *k, const tq_cache *v, int64_t kv_len, const void *q,
+                                int q_dtype, int32_t n_q_heads, float scale, float sparse_v_tau,
+                                float *out, tq_stream_t stream) {
+  tq_status s = decode_check(k, v, kv_len, n_q_heads);
+  if (s != TQ_OK) return s;
+  if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return TQ_ERR_INVALID_ARG;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
+  if (!(scale == scale) || !(sparse_v_tau == sparse_v_tau) || sparse_v_tau < 0.f)
+    return TQ_ERR_INVALID_ARG;
+  DecodePlan p;
+  if (tq_status st = from_hip(plan_decode(*k, *v, kv_len, n_q_heads, 1, 1, &p))) return st;
+  if (p.workspace_bytes > (size_t)TQ_STATIC_SCRATCH_BYTES) return TQ_ERR_WORKSPACE;
+  void *ws = nullptr;
+  if (tq_status st = from_hip(scratch_address(&ws))) return st;
+  // every split the merge reads is written by the split kernel first, so
+  // nothing in the array needs clearing
+  return from_hip(launch_decode(*k, *v, nullptr, nullptr, kv_len, q, q_dtype, n_q_heads, scale, sparse_v_tau,
+                                out, ws, p, (hipStream_t)stream));
 }
 
 tq_status tq_attn_decode_batch_workspace(const tq_cache *k, const tq_cache *v, int32_t n_seq,

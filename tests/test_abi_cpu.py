@@ -231,3 +231,13 @@ def test_int8_rejects_bad_arguments():
     assert call(npp=0) == -1
     assert call(q=FAKE + 4) == -1
     assert call(nq=0, q0=0) == 0
+
+
+def test_static_scratch_size_matches_header():
+    """The binding's size of the allocation-free decode's device array is the
+    header's TQ_STATIC_SCRATCH_BYTES."""
+    import re
+    from quantized_kv_cache_tq_amd import binding
+    hdr = open(os.path.join(ROOT, "include", "tq.h")).read()
+    m = re.search(r"#define TQ_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == binding.STATIC_SCRATCH_BYTES
