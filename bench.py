@@ -74,7 +74,7 @@ def parse():
     ap.add_argument("--layers", type=int, default=24)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
-                    help="comma list of legs: set_rows,decode,prefill,int8 (default: all; extras decode_wide, decode_long, "
+                    help="comma list of legs: set_rows,decode,prefill,int8 (default: all; extras decode_wide, decode_long, decode_paths, "
                          "decode_types, decode_batch, floor, prefill_rows, int8_140k); "
                          "'copy' adds a 256 MiB device copy used to calibrate HBM counters")
     return ap.parse_args()
@@ -573,6 +573,35 @@ def main():
                                                    "GBps": round(gbps, 1),
                                                    "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
             del lkc, lvc, lws
+
+        # the two decode kernels side by side (leg "decode_paths"): the
+        # matrix-core path and the Q x centroid table path of the decode
+        # design on the pages, at 1, 2 and 8 q heads per kv head over 32768
+        # cells and at one head over 256 cells
+        if want("decode_paths"):
+            for n_qh, n_kvh, kvl, LL in ((1, 1, 256, L), (8, 8, 32768, 12), (16, 8, 32768, 12), (NQ, NKV, KV, L)):
+                pq_, pk_, pv_ = inputs.outlier_decode(seed=12, kv_len=kvl, n_q=n_qh, n_kv=n_kvh)
+                pidx = torch.arange(kvl, dtype=torch.int64, device=dev)
+                pkc = [b.new_cache(3, D, n_kvh, kvl) for _ in range(LL)]
+                pvc = [b.new_cache(3, D, n_kvh, kvl) for _ in range(LL)]
+                b.tq_set_rows(pkc[0], torch.from_numpy(pk_).to(dev), pidx)
+                b.tq_set_rows(pvc[0], torch.from_numpy(pv_).to(dev), pidx)
+                for i in range(1, LL):
+                    pkc[i].codes.copy_(pkc[0].codes); pkc[i].norms.copy_(pkc[0].norms)
+                    pvc[i].codes.copy_(pvc[0].codes); pvc[i].norms.copy_(pvc[0].norms)
+                pqt = torch.from_numpy(pq_).to(torch.bfloat16).to(dev)
+                pout = [torch.empty((n_qh, D), dtype=torch.float32, device=dev) for _ in range(LL)]
+                nbytes = 2 * n_kvh * kvl * 50
+                row = {"bytes_per_call": nbytes}
+                for pname, path in (("matrix", b.TQ_DECODE_MATRIX), ("table", b.TQ_DECODE_TABLE)):
+                    pws = torch.empty(b.tq_attn_decode_path_workspace(pkc[0], pvc[0], kvl, n_qh, path),
+                                      dtype=torch.uint8, device=dev)
+                    t_ms = time_graph([lambda i=i, path=path, pws=pws: b.tq_attn_decode_path(
+                        pkc[i], pvc[i], kvl, pqt, scale_dec, path, out=pout[i], workspace=pws) for i in range(LL)])
+                    row[f"{pname}_us"] = round(t_ms * 1e3, 3)
+                    row[f"{pname}_GBps"] = round(nbytes / (t_ms * 1e-3) / 1e9, 1)
+                extras[f"decode_paths_turbo3_{n_qh}q{n_kvh}kv_{kvl}"] = row
+                del pkc, pvc, pout
 
         # turbo2 and turbo4 decode at the headline's heads, 8192 and 32768
         # cells (leg "decode_types"), over L distinct caches each

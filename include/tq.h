@@ -163,17 +163,26 @@ tq_status tq_set_rows(const tq_cache *dst, const float *src, const int64_t *cell
  * pairs take more workgroups over the same cells.
  * sparse_v_tau >= 0 ([PR36] (d) item 3; 0 = off): a key whose weight
  * e^(s - m) is below tau is left out of the value sum and kept in the
- * normalizer, with m the maximum over the aligned block of 16 T keys that
- * one wave scores (at most the true maximum).  T is the plan's: the largest
- * of 8, 4, 2, 1 with T (k->head_dim + v->head_dim) / 128 <= 16 and
- * W(T) = ceil(kv_len / 64T) * n_kv_heads * ceil(n_pairs / P) >= the
- * device's compute units C, else 1; and 4 in place of 8 when W(8) > C
- * (n_rep = n_q_heads / n_kv_heads; for the batched call below, kv_len is
- * max_kv_len and W is multiplied by n_seq).
+ * normalizer, with m a reference no larger than the true maximum.  When
+ * both caches are turbo with 128-wide heads and a kv head has at most eight
+ * pairs, a wave scores aligned blocks of 16 tb keys in turn, tb the largest
+ * of 4, 2, 1 with W(tb) = ceil(kv_len / 128 tb) * n_kv_heads >= C, C the
+ * device's compute units (else 1), and m is the maximum of the keys it has
+ * scored up to and including the key's block: that block's own maximum
+ * while W(tb) < 2C (one block per wave; for the batched call below, kv_len
+ * is max_kv_len and W is multiplied by n_seq).  Otherwise m is the maximum
+ * over the
+ * aligned block of 16 T keys that one wave scores, T the largest of 8, 4,
+ * 2, 1 with T (k->head_dim + v->head_dim) / 128 <= 16 and
+ * W(T) = ceil(kv_len / 64T) * n_kv_heads * ceil(n_pairs / P) >= C, else 1;
+ * and 4 in place of 8 when W(8) > C (n_rep = n_q_heads / n_kv_heads; for
+ * the batched call below, kv_len is max_kv_len and W is multiplied by
+ * n_seq).
  * The output then differs from the dense one by at most
  * sum over {j : e^(s_j - m*) < tau} of (e^(s_j - m*) / sum_i e^(s_i - m*)) |v_j|_2
- * (m* the true maximum).  The products are not skipped, so the call costs
- * the same as a dense one.  A NaN or negative tau is TQ_ERR_INVALID_ARG.
+ * (m* the true maximum).  In the first case above, a 16-key tile whose
+ * weights are all left out also skips its value products.  A NaN or negative tau
+ * is TQ_ERR_INVALID_ARG.
  * The workspace holds per-split partial results; its size comes from
  * tq_attn_decode_workspace for the same caches and arguments on the same
  * device (it grows with v->head_dim).
@@ -183,6 +192,35 @@ tq_status tq_attn_decode_workspace(const tq_cache *k, const tq_cache *v, int64_t
 tq_status tq_attn_decode(const tq_cache *k, const tq_cache *v, int64_t kv_len, const void *q,
                          int q_dtype, int32_t n_q_heads, float scale, float sparse_v_tau,
                          float *out, void *workspace, size_t workspace_bytes, tq_stream_t stream);
+
+/*
+ * Decode with an explicit choice of kernel ([PR36] (c): the decode reads a
+ * per-query-head table of query x level products in shared memory).  Same
+ * arguments, requirements and result as tq_attn_decode, plus path:
+ *   TQ_DECODE_AUTO    the route tq_attn_decode takes;
+ *   TQ_DECODE_MATRIX  every code decoded once per kv head to its level,
+ *                     scores and values on the matrix cores for all the kv
+ *                     head's q heads at once;
+ *   TQ_DECODE_TABLE   the table of [PR36] (c): per split, lut[h][p][e] =
+ *                     q_h[2p] c[e0] + q_h[2p+1] c[e1] in float32 for the
+ *                     code pair e = (e0, e1) of elements 2p, 2p+1, a key's
+ *                     score 64 table reads per q head; values accumulated
+ *                     in float32 per (head, element).  Requires turbo2 or
+ *                     turbo3 caches with 128-wide K and V heads and at most 8
+ *                     q heads per kv head (else TQ_ERR_UNSUPPORTED).  The
+ *                     sparse-V reference of a key is the maximum of its
+ *                     256-key split.
+ * An unknown path is TQ_ERR_INVALID_ARG.  The workspace size depends on the
+ * path: it comes from tq_attn_decode_path_workspace with the same path.
+ * TQ_DECODE_AUTO never picks the table: measured on MI355X it is slower at
+ * every shape tried (1 to 8 q heads per kv head).
+ */
+typedef enum { TQ_DECODE_AUTO = 0, TQ_DECODE_MATRIX = 1, TQ_DECODE_TABLE = 2 } tq_decode_path;
+tq_status tq_attn_decode_path_workspace(const tq_cache *k, const tq_cache *v, int64_t kv_len,
+                                        int32_t n_q_heads, int path, size_t *bytes /*[host]*/);
+tq_status tq_attn_decode_path(const tq_cache *k, const tq_cache *v, int64_t kv_len, const void *q,
+                              int q_dtype, int32_t n_q_heads, float scale, float sparse_v_tau, int path,
+                              float *out, void *workspace, size_t workspace_bytes, tq_stream_t stream);
 
 /*
  * Decode without a workspace argument, for callers that cannot allocate

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_PKG, "lib", "libtq.so")
 TQ_TURBO2, TQ_TURBO3, TQ_TURBO4, TQ_Q8 = 2, 3, 4, 8
 TQ_F32, TQ_BF16 = 0, 1
 TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP = 0, -1, -2, -3, -4
+TQ_DECODE_AUTO, TQ_DECODE_MATRIX, TQ_DECODE_TABLE = 0, 1, 2
 # size of the device array behind tq_attn_decode_static (TQ_STATIC_SCRATCH_BYTES)
 STATIC_SCRATCH_BYTES = 16 << 20
 TYPE_BY_NAME = {"turbo2": 2, "turbo3": 3, "turbo4": 4, "q8": 8}
@@ -49,6 +50,10 @@ _SIGS = {
                                          POINTER(c_size_t)]),
     "tq_attn_decode": (c_int, [POINTER(TQCache), POINTER(TQCache), c_int64, c_void_p, c_int, c_int32,
                                c_float, c_float, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "tq_attn_decode_path_workspace": (c_int, [POINTER(TQCache), POINTER(TQCache), c_int64, c_int32, c_int,
+                                              POINTER(c_size_t)]),
+    "tq_attn_decode_path": (c_int, [POINTER(TQCache), POINTER(TQCache), c_int64, c_void_p, c_int, c_int32,
+                                    c_float, c_float, c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
     "tq_attn_decode_static": (c_int, [POINTER(TQCache), POINTER(TQCache), c_int64, c_void_p, c_int, c_int32,
                                       c_float, c_float, c_void_p, c_void_p]),
     "tq_attn_decode_batch_workspace": (c_int, [POINTER(TQCache), POINTER(TQCache), c_int32, c_int32, c_int64,
@@ -214,6 +219,37 @@ def tq_attn_decode(k: TQCacheTensors, v: TQCacheTensors, kv_len: int, q: torch.T
     _check(load_library().tq_attn_decode(ctypes.byref(k.struct), ctypes.byref(v.struct), kv_len,
                                          q.data_ptr(), qd, n_q, scale, sparse_v_tau, out.data_ptr(),
                                          ws.data_ptr(), ws.numel(), _stream(stream)), "tq_attn_decode")
+    return out
+
+
+def tq_attn_decode_path_workspace(k: TQCacheTensors, v: TQCacheTensors, kv_len: int, n_q_heads: int,
+                                  path: int) -> int:
+    b = c_size_t()
+    _check(load_library().tq_attn_decode_path_workspace(ctypes.byref(k.struct), ctypes.byref(v.struct), kv_len,
+                                                        n_q_heads, path, ctypes.byref(b)),
+           "tq_attn_decode_path_workspace")
+    return b.value
+
+
+def tq_attn_decode_path(k: TQCacheTensors, v: TQCacheTensors, kv_len: int, q: torch.Tensor, scale: float,
+                        path: int, out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                        sparse_v_tau: float = 0.0, stream=None) -> torch.Tensor:
+    """tq_attn_decode through the kernel `path` names (TQ_DECODE_AUTO,
+    TQ_DECODE_MATRIX or TQ_DECODE_TABLE)."""
+    qd = _q_dtype(q)
+    _dev_tensor(q, q.dtype, "q")
+    if q.dim() != 2 or q.shape[1] != k.head_dim:
+        raise ValueError("q must be [n_q_heads, k.head_dim]")
+    n_q = q.shape[0]
+    if out is None:
+        out = torch.empty((n_q, v.head_dim), dtype=torch.float32, device=q.device)
+    _dev_tensor(out, torch.float32, "out")
+    if tuple(out.shape) != (n_q, v.head_dim):
+        raise ValueError("out must be [n_q_heads, v.head_dim]")
+    ws = _workspace(tq_attn_decode_path_workspace(k, v, kv_len, n_q, path), q.device, workspace)
+    _check(load_library().tq_attn_decode_path(ctypes.byref(k.struct), ctypes.byref(v.struct), kv_len,
+                                              q.data_ptr(), qd, n_q, scale, sparse_v_tau, path, out.data_ptr(),
+                                              ws.data_ptr(), ws.numel(), _stream(stream)), "tq_attn_decode_path")
     return out
 
 

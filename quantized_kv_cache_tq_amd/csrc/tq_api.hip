@@ -166,13 +166,13 @@ static tq_status decode_call(const tq_cache *k, const tq_cache *v, int32_t n_seq
                              const int64_t *seq_start, const int32_t *seq_len, int64_t kv_len,
                              const void *q, int q_dtype, int32_t n_q_heads, float scale,
                              float sparse_v_tau, float *out, void *workspace,
-                             size_t workspace_bytes, tq_stream_t stream) {
+                             size_t workspace_bytes, tq_stream_t stream, int path = TQ_DECODE_AUTO) {
   if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return TQ_ERR_INVALID_ARG;
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
   if (!(scale == scale) || !(sparse_v_tau == sparse_v_tau) || sparse_v_tau < 0.f)
     return TQ_ERR_INVALID_ARG;
   DecodePlan p;
-  if (tq_status st = from_hip(plan_decode(*k, *v, kv_len, n_q_heads, n_rows, n_seq, &p))) return st;
+  if (tq_status st = from_hip(plan_decode(*k, *v, kv_len, n_q_heads, n_rows, n_seq, &p, path))) return st;
   if (!workspace || !aligned(workspace, 256) || workspace_bytes < p.workspace_bytes)
     return TQ_ERR_WORKSPACE;
   return from_hip(launch_decode(*k, *v, seq_start, seq_len, kv_len, q, q_dtype, n_q_heads, scale,
@@ -198,6 +198,28 @@ tq_status tq_attn_decode(const tq_cache *k, const tq_cache *v, int64_t kv_len, c
   if (s != TQ_OK) return s;
   return decode_call(k, v, 1, 1, nullptr, nullptr, kv_len, q, q_dtype, n_q_heads, scale, sparse_v_tau,
                      out, workspace, workspace_bytes, stream);
+}
+
+tq_status tq_attn_decode_path_workspace(const tq_cache *k, const tq_cache *v, int64_t kv_len,
+                                        int32_t n_q_heads, int path, size_t *bytes) {
+  tq_status s = decode_check(k, v, kv_len, n_q_heads);
+  if (s != TQ_OK) return s;
+  if (!bytes) return TQ_ERR_INVALID_ARG;
+  DecodePlan p;
+  if (tq_status st = from_hip(plan_decode(*k, *v, kv_len, n_q_heads, 1, 1, &p, path)))
+    return st == TQ_ERR_HIP ? TQ_ERR_INVALID_ARG : st;
+  *bytes = p.workspace_bytes;
+  return TQ_OK;
+}
+
+tq_status tq_attn_decode_path(const tq_cache *k, const tq_cache *v, int64_t kv_len, const void *q,
+                              int q_dtype, int32_t n_q_heads, float scale, float sparse_v_tau, int path,
+                              float *out, void *workspace, size_t workspace_bytes, tq_stream_t stream) {
+  tq_status s = decode_check(k, v, kv_len, n_q_heads);
+  if (s != TQ_OK) return s;
+  if (path != TQ_DECODE_AUTO && path != TQ_DECODE_MATRIX && path != TQ_DECODE_TABLE) return TQ_ERR_INVALID_ARG;
+  return decode_call(k, v, 1, 1, nullptr, nullptr, kv_len, q, q_dtype, n_q_heads, scale, sparse_v_tau,
+                     out, workspace, workspace_bytes, stream, path);
 }
 
 tq_status tq_attn_decode_static(const tq_cache *k, const tq_cache *v, int64_t kv_len, const void *q,

@@ -168,14 +168,25 @@ template <int B, int NT>
 __device__ __forceinline__ void build_pair_table(uint32_t *tab, int tid) {
   using P = PairCfg<B>;
   constexpr uint32_t CM = (1u << B) - 1u;
-  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-  static_assert((P::N * P::COPIES) % NT == 0 && NT % 64 == 0, "pair table fill");
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  // NT threads over N entries: each thread computes entries e (its entry,
+  // then e + NT / TPE, ...) once and writes CPT consecutive copies of each
+  // as 16-byte stores (two copies per store)
+  constexpr int TPE = NT >= P::N ? (NT / P::N < P::COPIES / 2 ? NT / P::N : P::COPIES / 2) : 1;
+  constexpr int CPT = P::COPIES / TPE;                    // copies per thread
+  constexpr int WORK = P::N * TPE;                        // (entry, copy run) tasks
+  constexpr int EPT = (WORK + NT - 1) / NT;               // tasks per thread
+  static_assert(TPE * CPT == P::COPIES && CPT % 2 == 0 && (WORK % NT == 0 || WORK < NT), "pair table fill");
 #pragma unroll
-  for (int j = 0; j < P::N * P::COPIES / NT; ++j) {
-    // entry (tid + NT j) / 32 is the same for each half of a wave
-    const uint32_t slot = (uint32_t)tid + NT * j, e = slot / P::COPIES;
-    reinterpret_cast<u32x2_t *>(tab)[slot] =
-        u32x2_t{level_pair<B, false>(e & CM, e >> B), level_pair<B, true>(e & CM, e >> B)};
+  for (int k = 0; k < EPT; ++k) {
+    const int task = tid + NT * k;
+    if (WORK < NT && task >= WORK) break;
+    const uint32_t e = (uint32_t)(task / TPE);
+    const uint32_t c0 = (uint32_t)(task % TPE) * CPT;
+    const uint32_t hi = level_pair<B, false>(e & CM, e >> B), lo = level_pair<B, true>(e & CM, e >> B);
+    u32x4_t *dst = reinterpret_cast<u32x4_t *>(tab + 2 * (P::COPIES * e + c0));
+#pragma unroll
+    for (int c = 0; c < CPT / 2; ++c) dst[c] = u32x4_t{hi, lo, hi, lo};
   }
 }
 
@@ -186,6 +197,11 @@ constexpr uint64_t kSignWord1 = 0x6e789e6aa1b965f4ull;
 
 __device__ __forceinline__ uint32_t sign_bit_of(int d) {
   return (uint32_t)((d < 64 ? kSignWord0 >> d : kSignWord1 >> (d - 64)) & 1u);
+}
+// Sign bits of elements 4j .. 4j+3 (j < 32) as a nibble, element 4j in bit 0.
+__device__ __forceinline__ uint32_t sign_nibble(int j) {
+  const uint64_t w = j < 16 ? kSignWord0 : kSignWord1;
+  return (uint32_t)(w >> (4 * (j & 15))) & 0xfu;
 }
 
 // ---------------------------------------------------------------- lane exchanges

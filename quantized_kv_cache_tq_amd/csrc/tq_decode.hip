@@ -691,6 +691,587 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
   }
 }
 
+// ---------------------------------------------------------------- fused decode
+//
+// decode_fused_kernel: the single-group (128-wide K and V, both turbo) decode
+// with at most eight (query row, q head) pairs per kv head.  Workgroup
+// (split s, kv head g) has eight waves; wave w takes the blocks of KPB = 16 TB
+// keys numbered 8b + w (b = 0 .. nb-1) of the split and runs each block
+// through the whole chain itself: scores, the running maximum, P kept in
+// registers (the score accumulator's lane layout is the A-operand layout of
+// the value product), the V rows staged in the wave's own LDS rows, and the
+// value products.  No barrier separates the waves until the eight partial
+// results are merged into the split partial, so the waves take their blocks
+// as their loads arrive; with nb > 1 each wave loads its next block while it
+// computes the current one, and the running maximum rescales the
+// accumulators (wave-uniform test) when it moves.
+//
+// Operand layouts (v_mfma_f32_16x16x32_f16; a level enters as its float16 hi
+// and lo parts, the query and P as theirs):
+//   scores  K-step st (0..7), lane (col, quad): k-slots hold hi(e0) hi(e1)
+//           lo(e0) lo(e1) hi(e2) hi(e3) lo(e2) lo(e3) of the key's elements
+//           e = 32 quad + 4 st + 0..3, i.e. two pair-table entries read as
+//           they are; the query operand repeats each element twice (column
+//           c < 8: the high part of pair c's rotated query, 8 + c its low part)
+//   values  per 16-key tile and d-tile dt, lane (n, quad): k-slots hold
+//           keys 4 quad + (0, 1) hi, (0, 1) lo, (2, 3) hi, (2, 3) lo of element
+//           8n + dt; P repeats each key twice (rows < 8: the high part of
+//           p * vnorm, rows >= 8 the low part).
+// Sparse V ([PR36] (d) item 3): P entries below tau become 0, and a tile whose
+// entries are all 0 skips its value decode and products.
+template <int B>
+__device__ __forceinline__ uint32_t pair_field_at8(const uint32_t *dw, int pos) {
+  // the 2B-bit field at bit pos of dw (pos compile-time), moved to bit 8
+  const int w = pos >> 5, sh = pos & 31;
+  if (sh >= 8)
+    return sh + 2 * B <= 32 ? dw[w] >> (sh - 8) : __builtin_amdgcn_alignbit(dw[w + 1], dw[w], sh - 8);
+  return w == 0 ? dw[0] << (8 - sh) : __builtin_amdgcn_alignbit(dw[w], dw[w - 1], 24 + sh);
+}
+// Byte offset of a pair-table entry (in bits 8 .. 8 + 2B of x) in this
+// lane's copy: entry e, copy c at byte 256 e + 8 c.
+template <int B>
+__device__ __forceinline__ uint32_t pair_byte(uint32_t x, uint32_t lane8) {
+  return (x & (((1u << (2 * B)) - 1u) << 8)) | lane8;
+}
+__device__ __forceinline__ u32x2_t lds_u32x2(const uint32_t *base, uint32_t byte) {
+  return *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const char *>(base) + byte);
+}
+
+// PF: the next block's loads are issued before the current block is
+// computed (waves with several blocks); without it a block is loaded when
+// its turn comes.
+template <int B, int TB, bool QBF16, bool PF>
+__global__ __launch_bounds__(kDecThreads, 2) void decode_fused_kernel(
+    const uint8_t *__restrict__ kcodes, const uint16_t *__restrict__ knorms,
+    const uint8_t *__restrict__ vcodes, const uint16_t *__restrict__ vnorms, int64_t n_cells,
+    const int64_t *__restrict__ seq_start, const int32_t *__restrict__ seq_len, int64_t kv_len,
+    const void *__restrict__ q, int n_q, int n_rep, int n_rows, int nb, float qscale, float tau,
+    float *__restrict__ ws, int n_split) {
+  constexpr int KPB = 16 * TB;                 // keys per wave block
+  constexpr int GW = 4 * B;                    // code dwords per key row
+  constexpr int ROWP = GW + 1;                 // padded LDS V row
+  constexpr int NCH = KPB * B;                 // 16-byte V chunks per block
+  constexpr int CPL = ceil_div(NCH, 64);       // chunks per lane
+  constexpr int PSTRIDE = kGroup + 4;
+  constexpr int kVstWords = (KPB * ROWP + 1 + 3) & ~3;   // + a spare dword (two-dword row reads)
+  constexpr int kStageWords = 8 * (kVstWords + 2 * KPB);
+  constexpr int kOutWords = 8 * 8 * kGroup;
+  constexpr int kBlockWords = kStageWords > kOutWords ? kStageWords : kOutWords;
+  __shared__ __align__(256) uint32_t ptab[PairCfg<B>::WORDS];   // pair table, 32 copies
+  __shared__ __align__(16) uint32_t qbuf[8 * 64 * 4];            // query operand [st][lane][8 halves]
+  // per wave: V rows and the block's K and V norms; after the last block the
+  // same bytes take the eight waves' outputs [wave][pair][128]
+  __shared__ __align__(16) uint32_t blk[kBlockWords];
+  __shared__ float wm[8][8], wl[8][8];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, quad = lane >> 4;
+  const int s = blockIdx.x, g = blockIdx.y, z = blockIdx.z;
+  const SeqExtent ext = seq_extent(seq_start, seq_len, z, kv_len, n_cells);
+  const int64_t kps = (int64_t)8 * nb * KPB;
+  if ((int64_t)s * kps >= ext.len) return;     // uniform: the whole workgroup
+  const int n_vh = n_rows * n_rep;             // (row, head) pairs of the kv head (<= 8)
+  const int64_t kbase = (int64_t)g * n_cells + ext.start;
+  uint32_t *vst = blk + wave * (kVstWords + 2 * KPB);
+  float *nk = reinterpret_cast<float *>(vst + kVstWords), *nv = nk + KPB;
+
+  // raw global loads of block b: K codes of the lane's 32 elements (lane
+  // (col, quad) of tile t: dwords B quad .. B quad + B - 1 of key 16t + col),
+  // V rows as consecutive 16-byte chunks, one norm of each per lane (key =
+  // lane)
+  struct Raw {
+    uint32_t k[TB][B];
+    u32x4_t v[CPL];
+    uint16_t kn, vn;
+  };
+  auto block_keys = [&](int b, int64_t &w0) {
+    w0 = (int64_t)s * kps + (int64_t)(b * 8 + wave) * KPB;
+    const int64_t left = ext.len - w0;
+    return (int)(left <= 0 ? 0 : (left < KPB ? left : KPB));
+  };
+  auto load = [&](int b, Raw &r) {
+    int64_t w0;
+    const int wk = block_keys(b, w0);
+    const int wlast = wk > 0 ? wk - 1 : 0;
+    const int64_t row0 = kbase + (wk > 0 ? w0 : ext.len - 1);
+    const uint8_t *kb = kcodes + row0 * (16 * B);
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      const uint32_t key = (uint32_t)imin(16 * t + col, wlast);
+      const uint32_t *row = reinterpret_cast<const uint32_t *>(kb + key * (16u * B) + 4u * B * quad);
+#pragma unroll
+      for (int i = 0; i < B; ++i) r.k[t][i] = row[i];
+    }
+    const uint8_t *vb = vcodes + row0 * (16 * B);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = imin(lane + 64 * j, NCH - 1);
+      const int rr = c / B, part = c - rr * B;
+      r.v[j] = *reinterpret_cast<const u32x4_t *>(vb + (uint32_t)imin(rr, wlast) * (16u * B) + 16u * part);
+    }
+    const uint32_t kk = (uint32_t)imin(lane, wlast);
+    r.kn = knorms[row0 + kk];
+    r.vn = vnorms[row0 + kk];
+  };
+
+  Raw cur;
+  load(0, cur);
+  build_pair_table<B, kDecThreads>(ptab, tid);
+  // rotate + split the query of pairs 2w, 2w+1 (waves 0-3): thread (qh, qj)
+  // holds d = 4qj .. 4qj+3 of pair qh, which is the element chunk of quad
+  // qj >> 3 and K-step qj & 7: it writes that chunk's high parts to lane
+  // 16 (qj >> 3) + qh and its low parts to lane 16 (qj >> 3) + 8 + qh
+  if (wave < 4) {
+    const int qh = 2 * wave + (lane >> 5), qj = lane & 31;
+    const int vq = imin(qh, n_vh - 1);
+    const int vr = n_rows == 1 ? 0 : vq / n_rep;
+    const int64_t qbase =
+        (((int64_t)z * n_rows + vr) * n_q + (int64_t)g * n_rep + (vq - vr * n_rep)) * kGroup + 4 * qj;
+    float qv[4];
+    if constexpr (QBF16) {
+      const u32x2_t bw = *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint16_t *>(q) + qbase);
+      qv[0] = __uint_as_float(bw.x << 16);
+      qv[1] = __uint_as_float(bw.x & 0xffff0000u);
+      qv[2] = __uint_as_float(bw.y << 16);
+      qv[3] = __uint_as_float(bw.y & 0xffff0000u);
+    } else {
+      const float4 f = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(q) + qbase);
+      qv[0] = f.x; qv[1] = f.y; qv[2] = f.z; qv[3] = f.w;
+    }
+    const uint32_t sn = sign_nibble(qj);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qv[i] = flip_sign(qv[i], (sn >> i) & 1u);
+    wht128_half(qv, qj);
+    const bool live = qh < n_vh;
+    uint32_t hw[2], lw[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const float x0 = live ? qv[2 * p] * qscale : 0.f;
+      const float x1 = live ? qv[2 * p + 1] * qscale : 0.f;
+      const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+      const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
+      hw[p] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+      lw[p] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+    }
+    const int st = qj & 7, qd = qj >> 3;
+    reinterpret_cast<u32x4_t *>(qbuf)[st * 64 + 16 * qd + qh] = u32x4_t{hw[0], hw[0], hw[1], hw[1]};
+    reinterpret_cast<u32x4_t *>(qbuf)[st * 64 + 16 * qd + 8 + qh] = u32x4_t{lw[0], lw[0], lw[1], lw[1]};
+  }
+  __syncthreads();   // pair table and query operand complete
+  half8_t qb[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) qb[st] = __builtin_bit_cast(half8_t, reinterpret_cast<const u32x4_t *>(qbuf)[st * 64 + lane]);
+
+  const uint32_t lane8 = 8u * (uint32_t)(lane & 31);   // this lane's table copy
+  // this lane's score column: pair col & 7 -> causal offset of its row
+  const int vcol = col & 7;
+  const int row_off = vcol < n_vh && n_rows > 1 ? vcol / n_rep : 0;
+  const float lo_sel = col >= 8 ? 1.f : 0.f;
+  // V: lane (n, quad) of tile t decodes elements 8n .. 8n+7 of keys
+  // 16t + 4quad + i (i = 0..3), the 8B-bit run at bit 8Bn of each row
+  const int vpos = 8 * B * col;
+  const int vw0 = vpos >> 5, vsh = vpos & 31;
+  const uint32_t *vlane = vst + 4 * quad * ROWP + vw0;
+
+  float4_t o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;   // of this lane's column
+
+  for (int b = 0; b < nb; ++b) {
+    int64_t w0;
+    const int wk = block_keys(b, w0);
+    if (wk == 0) break;                        // wave-uniform: later blocks are empty too
+    if (!PF && b > 0) load(b, cur);
+    // stage the V rows and norms of the block in the wave's own LDS
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j;
+      if (NCH % 64 == 0 || c < NCH) {
+        const int rr = c / B, part = c - rr * B;
+        uint32_t *d = vst + rr * ROWP + 4 * part;
+        d[0] = cur.v[j].x;
+        d[1] = cur.v[j].y;
+        d[2] = cur.v[j].z;
+        d[3] = cur.v[j].w;
+      }
+    }
+    if (lane < KPB) {
+      nk[lane] = lane < wk ? half_to_float(cur.kn) : 0.f;
+      nv[lane] = lane < wk ? half_to_float(cur.vn) : 0.f;
+    }
+    uint32_t kr[TB][B];
+#pragma unroll
+    for (int t = 0; t < TB; ++t)
+#pragma unroll
+      for (int i = 0; i < B; ++i) kr[t][i] = cur.k[t][i];
+    if (PF && b + 1 < nb) load(b + 1, cur);     // the next block's loads fly over this one
+    wave_lds_fence();
+
+    // ---- scores of the block's tiles
+    float sc[TB][4];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      u32x2_t lv[16];   // (hi pair, lo pair) of the lane's element pairs 2j, 2j+1
+#pragma unroll
+      for (int j = 0; j < 16; ++j) lv[j] = lds_u32x2(ptab, pair_byte<B>(pair_field_at8<B>(kr[t], 2 * B * j), lane8));
+      float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const u32x4_t av = {lv[2 * st].x, lv[2 * st].y, lv[2 * st + 1].x, lv[2 * st + 1].y};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[st], acc, 0, 0, 0);
+      }
+      const float4 n4 = *reinterpret_cast<const float4 *>(nk + 16 * t + 4 * quad);
+      const float nkv[4] = {n4.x, n4.y, n4.z, n4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[t][i] = (acc[i] + xor_lane<8>(acc[i])) * nkv[i];
+      // (keeps the next tile's lookups below this one's products)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // causal limit of this lane's column (relative to the block), only for
+    // blocks reaching past the first row's last cell (wave-uniform)
+    if (w0 + KPB - 1 > ext.len - n_rows) {
+      const int64_t lim64 = ext.len - n_rows + row_off - w0;
+      const int lim = lim64 < -1 ? -1 : (lim64 > KPB ? KPB : (int)lim64);
+#pragma unroll
+      for (int t = 0; t < TB; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (16 * t + 4 * quad + i > lim) sc[t][i] = -INFINITY;
+    }
+    // running maximum of the column (log2 domain)
+    float mb = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < TB; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mb = fmaxf(mb, sc[t][i]);
+    mb = fmaxf(mb, xor_lane<16>(mb));
+    mb = max_xor32(mb);
+    const float m_new = fmaxf(m_run, mb);
+    if (b > 0 && __builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+      // rescale: the factor of pair c lives in lanes c, c + 8 (any quad);
+      // value row 4 quad + i is pair 4 (quad & 1) + i
+      const float a = m_new > m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      l_run *= a;
+      float ar[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        ar[i] = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (4 * (quad & 1) + i), __float_as_int(a)));
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[dt][i] *= ar[i];
+    }
+    m_run = m_new;
+    const float msafe = m_new == -INFINITY ? 0.f : m_new;
+
+    // ---- P in registers (rows < 8: high part of p * vnorm, rows >= 8: low
+    //      part), then the value products tile by tile
+    auto tiles = [&](auto sparse_tag) {
+      constexpr bool kSparse = decltype(sparse_tag)::value;
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        const float4 n4 = *reinterpret_cast<const float4 *>(nv + 16 * t + 4 * quad);
+        const float nvv[4] = {n4.x, n4.y, n4.z, n4.w};
+        bool any = false;
+        uint32_t pw[2];
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2) {
+          _Float16 ph[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int i = 2 * i2 + e;
+            const float p = __builtin_amdgcn_exp2f(sc[t][i] - msafe);
+            l_run += p;
+            const float x = kSparse && p < tau ? 0.f : p * nvv[i];
+            any |= x != 0.f;
+            const _Float16 h = (_Float16)x;
+            ph[e] = (_Float16)__builtin_fmaf(-(float)h, lo_sel, x);
+          }
+          pw[i2] = (uint32_t)__builtin_bit_cast(uint16_t, ph[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, ph[1]) << 16);
+        }
+        if (kSparse && __builtin_amdgcn_ballot_w64(any) == 0) continue;   // wave-uniform
+        const half8_t pp = __builtin_bit_cast(half8_t, u32x4_t{pw[0], pw[0], pw[1], pw[1]});
+        // the (hi pair, lo pair) of elements 8n + 2j, +1 of the lane's four keys
+        u32x2_t hl[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t *row = vlane + (16 * t + i) * ROWP;
+          const uint32_t run = __builtin_amdgcn_alignbit(row[1], row[0], vsh);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t x = 2 * B * j >= 8 ? run >> (2 * B * j - 8) : run << (8 - 2 * B * j);
+            hl[i][j] = lds_u32x2(ptab, pair_byte<B>(x, lane8));
+          }
+        }
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const int w = dt >> 1;
+          const uint32_t sel = (dt & 1) ? 0x07060302u : 0x05040100u;
+          const u32x4_t vb = {__builtin_amdgcn_perm(hl[1][w].x, hl[0][w].x, sel),
+                              __builtin_amdgcn_perm(hl[1][w].y, hl[0][w].y, sel),
+                              __builtin_amdgcn_perm(hl[3][w].x, hl[2][w].x, sel),
+                              __builtin_amdgcn_perm(hl[3][w].y, hl[2][w].y, sel)};
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pp, __builtin_bit_cast(half8_t, vb), o[dt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if (tau > 0.f)
+      tiles(std::true_type{});
+    else
+      tiles(std::false_type{});
+    wave_lds_fence();   // the block's V rows read before the next block overwrites them
+  }
+
+  // ---- merge the eight waves: value row 4 quad + i holds pair (4quad+i) & 7,
+  //      high rows in lanes 0-31 and low rows in lanes 32-63; after the swap
+  //      lanes 0-31 hold d-tiles 0-3 and lanes 32-63 d-tiles 4-7 of pair
+  //      4((lane&31)>>4) + i as high + low
+  float l = l_run + xor_lane<16>(l_run);
+  l = sum_xor32(l);
+  float4 res[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float oc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(o[dt][i]), __float_as_uint(o[dt + 4][i]),
+                                                      false, false);
+      oc[dt] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    res[i] = make_float4(oc[0], oc[1], oc[2], oc[3]);
+  }
+  __syncthreads();   // every wave is done with its LDS rows: they take the outputs now
+  float *obuf = reinterpret_cast<float *>(blk);
+  const int qd = (lane & 31) >> 4, dhi = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<float4 *>(&obuf[(wave * 8 + 4 * qd + i) * kGroup + 8 * col + 4 * dhi]) = res[i];
+  if (lane < 8) {
+    wm[wave][lane] = m_run;
+    wl[wave][lane] = l;
+  }
+  __syncthreads();
+  // the weight of wave w's partial of pair h, exp2(m_w - M_h), once per
+  // (w, h) by the first wave (wm then holds the weights, wl[0] L and
+  // wl[1] M)
+  if (wave == 0) {
+    const int h = lane & 7, w = lane >> 3;
+    float M = wm[0][h];
+#pragma unroll
+    for (int v = 1; v < 8; ++v) M = fmaxf(M, wm[v][h]);
+    const float mw = wm[w][h];
+    const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+    float fl = f * wl[w][h];
+    fl += __shfl_xor(fl, 8);
+    fl += __shfl_xor(fl, 16);
+    fl += __shfl_xor(fl, 32);
+    wave_lds_fence();
+    wm[w][h] = f;
+    if (w == 0) {
+      wl[0][h] = fl;
+      wl[1][h] = M;
+    }
+  }
+  __syncthreads();
+  {
+    const int h = tid >> 6, d = 2 * (tid & 63);
+    if (h < n_vh) {
+      const float L = wl[0][h], M = wl[1][h];
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const float f = wm[w][h];
+        const float2 v = *reinterpret_cast<const float2 *>(&obuf[(w * 8 + h) * kGroup + d]);
+        a0 += f * v.x;
+        a1 += f * v.y;
+      }
+      const int vr = n_rows == 1 ? 0 : h / n_rep;
+      const int64_t qrow = ((int64_t)z * n_rows + vr) * n_q + (int64_t)g * n_rep + (h - vr * n_rep);
+      float *ph = ws + (qrow * n_split + s) * PSTRIDE;
+      *reinterpret_cast<float2 *>(ph + d) = make_float2(a0, a1);
+      if (d == 0) *reinterpret_cast<float2 *>(ph + kGroup) = make_float2(M, L);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- LUT decode
+//
+// decode_lut_kernel: the decode of [PR36] (c), a Q x centroid lookup table
+// in LDS built once per split, for one query row, 128-wide turbo2/turbo3
+// heads and NREP (1..8) q heads per kv head.  The table is indexed by the
+// code pair of two neighbouring elements: lut[h][dp][e] = q[2dp] c[e0] +
+// q[2dp+1] c[e1] (float32, q the rotated query of head h, e0 and e1 the two
+// codes packed in e, c the float32 levels), so a key's score is 64 table
+// reads per head.  Workgroup (split s, kv head g), 256 threads, 256 keys:
+//   scores  thread j takes key j; every thread reads row dp of the table at
+//           the same time, so the lanes of a read hit distinct banks or
+//           broadcast one dword (no conflict, no padding needed);
+//   values  thread (slot, d) accumulates p * vnorm * c[code] of element d
+//           over the keys (V code rows staged in LDS): slot = key half for
+//           one head, else the head parity;
+// and the split partial (unnormalized rotated sum, log2 maximum, weight sum)
+// goes to the merge kernel like the other decode paths' partials.
+template <int B, int NREP, bool QBF16>
+__global__ __launch_bounds__(256) void decode_lut_kernel(
+    const uint8_t *__restrict__ kcodes, const uint16_t *__restrict__ knorms,
+    const uint8_t *__restrict__ vcodes, const uint16_t *__restrict__ vnorms, int64_t n_cells,
+    int64_t kv_len, const void *__restrict__ q, int n_q, int n_rep, float qscale, float tau,
+    float *__restrict__ ws, int n_split) {
+  constexpr int NE = 1 << (2 * B);             // code-pair entries
+  constexpr int KPS = 256;                     // keys per split
+  constexpr int RW = 4 * B;                    // code dwords per row
+  constexpr int RWP = RW + 1;                  // padded LDS row
+  constexpr int PSTRIDE = kGroup + 4;
+  constexpr int CM = (1 << B) - 1;
+  __shared__ float lut[NREP][64][NE];
+  __shared__ float qr[NREP][kGroup];
+  __shared__ uint32_t vrow[KPS * RWP + 1];
+  __shared__ float pv[NREP][KPS];
+  __shared__ float lvl[1 << B];
+  __shared__ float red_m[4][NREP], red_l[4][NREP];
+  __shared__ float obuf2[NREP == 1 ? kGroup : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int s = blockIdx.x, g = blockIdx.y;
+  const int64_t w0 = (int64_t)s * KPS;
+  if (w0 >= kv_len) return;
+  const int nk = (int)(kv_len - w0 < KPS ? kv_len - w0 : KPS);
+  const int64_t row0 = (int64_t)g * n_cells + w0;
+  const int key = imin(tid, nk - 1);
+
+  // loads: this thread's K and V rows (16-byte chunks) and norms
+  uint32_t kw[RW], vw[RW];
+#pragma unroll
+  for (int c = 0; c < B; ++c) {
+    const u32x4_t a = reinterpret_cast<const u32x4_t *>(kcodes + (row0 + key) * (16 * B))[c];
+    const u32x4_t b = reinterpret_cast<const u32x4_t *>(vcodes + (row0 + key) * (16 * B))[c];
+    kw[4 * c] = a.x; kw[4 * c + 1] = a.y; kw[4 * c + 2] = a.z; kw[4 * c + 3] = a.w;
+    vw[4 * c] = b.x; vw[4 * c + 1] = b.y; vw[4 * c + 2] = b.z; vw[4 * c + 3] = b.w;
+  }
+  const float kn = half_to_float(knorms[row0 + key]);
+  const float vn = half_to_float(vnorms[row0 + key]);
+  // rotated query of the NREP heads: lanes 0-31 / 32-63 of wave w hold heads
+  // 2w / 2w + 1, lane j elements 4j .. 4j+3
+  if (wave < (NREP + 1) / 2) {
+    const int h = 2 * wave + (lane >> 5), j = lane & 31;
+    if (h < NREP) {
+      const int64_t qb = ((int64_t)g * n_rep + h) * kGroup + 4 * j;
+      float x[4];
+      if constexpr (QBF16) {
+        const u32x2_t bw = *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint16_t *>(q) + qb);
+        x[0] = __uint_as_float(bw.x << 16);
+        x[1] = __uint_as_float(bw.x & 0xffff0000u);
+        x[2] = __uint_as_float(bw.y << 16);
+        x[3] = __uint_as_float(bw.y & 0xffff0000u);
+      } else {
+        const float4 f = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(q) + qb);
+        x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
+      }
+      const uint32_t sn = sign_nibble(j);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = flip_sign(x[i], (sn >> i) & 1u);
+      wht128_half(x, j);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qr[h][4 * j + i] = x[i];
+    }
+  }
+  if (tid <= CM) lvl[tid] = code_value<B>(tid);
+#pragma unroll
+  for (int w = 0; w < RW; ++w) vrow[tid * RWP + w] = vw[w];
+  __syncthreads();
+  // the table: entry e of dim pair dp packs the codes of elements 2dp (low
+  // bits) and 2dp + 1
+#pragma unroll 4
+  for (int i = tid; i < NREP * 64 * NE; i += 256) {
+    const int h = i / (64 * NE), dp = (i / NE) % 64, e = i % NE;
+    lut[h][dp][e] = qr[h][2 * dp] * lvl[e & CM] + qr[h][2 * dp + 1] * lvl[e >> B];
+  }
+  __syncthreads();
+
+  // ---- scores (log2 domain): key tid
+  float sc[NREP];
+#pragma unroll
+  for (int h = 0; h < NREP; ++h) sc[h] = 0.f;
+#pragma unroll
+  for (int dp = 0; dp < 64; ++dp) {
+    const int pos = 2 * B * dp, w = pos >> 5, sh = pos & 31;
+    const uint32_t x = sh + 2 * B <= 32 ? kw[w] >> sh : __builtin_amdgcn_alignbit(kw[w + 1], kw[w], sh);
+    const int e = (int)(x & (NE - 1));
+#pragma unroll
+    for (int h = 0; h < NREP; ++h) sc[h] += lut[h][dp][e];
+  }
+#pragma unroll
+  for (int h = 0; h < NREP; ++h) sc[h] = tid < nk ? sc[h] * kn * qscale : -INFINITY;
+  // split maximum and weight sum per head
+  float M[NREP];
+#pragma unroll
+  for (int h = 0; h < NREP; ++h) {
+    float m = sc[h];
+    m = fmaxf(m, xor_lane<1>(m));
+    m = fmaxf(m, xor_lane<2>(m));
+    m = fmaxf(m, xor_lane<4>(m));
+    m = fmaxf(m, xor_lane<8>(m));
+    m = fmaxf(m, xor_lane<16>(m));
+    m = max_xor32(m);
+    if (lane == 0) red_m[wave][h] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < NREP; ++h) M[h] = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
+#pragma unroll
+  for (int h = 0; h < NREP; ++h) {
+    const float p = __builtin_amdgcn_exp2f(sc[h] - M[h]);   // 0 for a masked key
+    pv[h][tid] = tau > 0.f && p < tau ? 0.f : p * vn;
+    float l = p;
+    l += xor_lane<1>(l);
+    l += xor_lane<2>(l);
+    l += xor_lane<4>(l);
+    l += xor_lane<8>(l);
+    l += xor_lane<16>(l);
+    l = sum_xor32(l);
+    if (lane == 0) red_l[wave][h] = l;
+  }
+  __syncthreads();
+
+  // ---- values: thread (slot, d), element d's code at bit B d of each row
+  const int d = tid & (kGroup - 1), slot = tid >> 7;
+  const int vwi = (B * d) >> 5, vsh = (B * d) & 31;
+  auto code_of = [&](int j) {
+    const uint32_t *r = vrow + j * RWP + vwi;
+    const uint32_t x = vsh + B <= 32 ? r[0] >> vsh : __builtin_amdgcn_alignbit(r[1], r[0], vsh);
+    return (int)(x & CM);
+  };
+  if constexpr (NREP == 1) {
+    // one head: the two slots take the two key halves
+    float o = 0.f;
+    const int j0 = slot * (KPS / 2), j1 = imin(j0 + KPS / 2, nk);
+#pragma unroll 4
+    for (int j = j0; j < j1; ++j) o += pv[0][j] * lvl[code_of(j)];
+    if (slot == 1) obuf2[d] = o;
+    __syncthreads();
+    if (slot == 0) {
+      o += obuf2[d];
+      const float L = (red_l[0][0] + red_l[1][0]) + (red_l[2][0] + red_l[3][0]);
+      float *ph = ws + (((int64_t)g * n_rep) * n_split + s) * PSTRIDE;
+      ph[d] = o;
+      if (d == 0) *reinterpret_cast<float2 *>(ph + kGroup) = make_float2(M[0], L);
+    }
+  } else {
+    for (int h = slot; h < NREP; h += 2) {
+      float o = 0.f;
+#pragma unroll 4
+      for (int j = 0; j < nk; ++j) o += pv[h][j] * lvl[code_of(j)];
+      const float L = (red_l[0][h] + red_l[1][h]) + (red_l[2][h] + red_l[3][h]);
+      float *ph = ws + (((int64_t)g * n_rep + h) * n_split + s) * PSTRIDE;
+      ph[d] = o;
+      if (d == 0) *reinterpret_cast<float2 *>(ph + kGroup) = make_float2(M[h], L);
+    }
+  }
+}
+
 // Merge the split partials of one 128-element group (blockIdx.y) of one
 // output row (blockIdx.x: (sequence, query row, q head)), undo the rotation
 // and write that part of the float32 row: out = s (.) H O / (128 L).  Only
@@ -820,8 +1401,16 @@ hipError_t launch_split_merge(const float *ws, int n_split, int split_log2, int 
   return hipGetLastError();
 }
 
+// Most q heads per kv head for which automatic routing takes the Q x
+// centroid table kernel: none.  Measured on one MI355X (turbo3, graph
+// replay, us per call, matrix path against table path): 1 q / 1 kv head
+// over 256 cells 6.9 / 18.1; over 32768 cells 8 q / 8 kv 18.9 / 27.4, 16 q /
+// 8 kv 19.1 / 63.2, 32 q / 4 kv 14.5 / 227.5.  The table path stays
+// available by request (TQ_DECODE_TABLE).
+constexpr int kTableMaxRepAuto = 0;
+
 hipError_t plan_decode(const tq_cache &k, const tq_cache &v, int64_t max_len, int32_t n_q_heads,
-                       int n_rows, int n_seq, DecodePlan *p) {
+                       int n_rows, int n_seq, DecodePlan *p, int path) {
   int n_cu = 0;
   hipError_t e = device_cu_count(&n_cu);
   if (e != hipSuccess) return e;
@@ -857,6 +1446,45 @@ hipError_t plan_decode(const tq_cache &k, const tq_cache &v, int64_t max_len, in
   }
   p->tiles_per_wave = tpw;
   p->keys_per_split = 64 * tpw;
+  p->fused = 0;
+  p->nb = 1;
+  p->lut = 0;
+  const bool table_ok = n_rows == 1 && n_seq == 1 && n_rep <= 8 && (k.type == TQ_TURBO2 || k.type == TQ_TURBO3) &&
+                        k.type == v.type && k.head_dim == kGroup && v.head_dim == kGroup;
+  if (path == TQ_DECODE_TABLE && !table_ok) return hipErrorNotSupported;
+  if (path != TQ_DECODE_AUTO && path != TQ_DECODE_MATRIX && path != TQ_DECODE_TABLE) return hipErrorInvalidValue;
+  if (table_ok && (path == TQ_DECODE_TABLE || (path == TQ_DECODE_AUTO && n_rep <= kTableMaxRepAuto))) {
+    p->lut = 1;
+    p->pairs = n_rep;
+    p->head_groups = 1;
+    p->tiles_per_wave = 1;
+    p->keys_per_split = 256;
+  } else
+  // One 128-wide group each way, both caches turbo, at most eight pairs per
+  // kv head: the fused kernel, eight waves of blocks of 16 tb keys.  tb: the
+  // most (4, 2, 1) that still gives every compute unit a workgroup; nb
+  // blocks per wave: as many (a power of two) as keep the grid at least one
+  // full round, so long sequences stream through one round of workgroups
+  // (then with blocks of at most 2 tiles, the next block's loads in flight
+  // beside the current one).
+  if (k.type != TQ_Q8 && k.type == v.type && k.head_dim == kGroup && v.head_dim == kGroup && n_pairs <= 8) {
+    const int64_t wg = (int64_t)k.n_kv_heads * n_seq;
+    int tb = 4;
+    while (tb > 1 && ceil_div<int64_t>(max_len, 128LL * tb) * wg < n_cu) tb >>= 1;
+    int64_t per = ceil_div<int64_t>(max_len, 128LL * tb) * wg;
+    if (tb == 4 && per >= 2 * n_cu) {
+      tb = 2;
+      per = ceil_div<int64_t>(max_len, 256LL) * wg;
+    }
+    int nb = 1;
+    while (nb < (1 << 20) && (int64_t)nb * 2 * n_cu <= per) nb *= 2;
+    p->fused = 1;
+    p->pairs = 8;
+    p->head_groups = 1;
+    p->tiles_per_wave = tb;
+    p->nb = nb;
+    p->keys_per_split = 128 * tb * nb;
+  }
   const int64_t n_split = ceil_div<int64_t>(max_len, p->keys_per_split);
   if (n_split > 0x7fffffff || (int64_t)k.n_kv_heads * p->head_groups > 65535 || n_seq > 65535)
     return hipErrorInvalidValue;
@@ -939,6 +1567,73 @@ hipError_t launch_split_dims(int gk, int gv, int qbf, int kq8, int tpw, int pair
   return launch_split_q<B, 1, 2>(qbf, kq8, tpw, pairs, grid, st, a);
 }
 
+template <int B, bool QBF>
+hipError_t launch_fused_tb(int tb, dim3 grid, hipStream_t st, const SplitArgs &a, int nb) {
+  dim3 block(kDecThreads);
+#define TQ_FUSED(TB, PF)                                                                               \
+  hipLaunchKernelGGL((decode_fused_kernel<B, TB, QBF, PF>), grid, block, 0, st, a.k->codes, a.k->norms, \
+                     a.v->codes, a.v->norms, a.k->n_cells, a.seq_start, a.seq_len, a.kv_len, a.q, a.n_q, \
+                     a.n_rep, a.n_rows, nb, a.qs, a.tau, a.ws, a.n_split)
+  // several blocks per wave: prefetching variants (at most 2 tiles per
+  // block, the prefetch registers beside them)
+  if (nb > 1) {
+    switch (tb) {
+      case 1: TQ_FUSED(1, true); break;
+      case 2: TQ_FUSED(2, true); break;
+      default: return hipErrorNotSupported;
+    }
+  } else {
+    switch (tb) {
+      case 1: TQ_FUSED(1, false); break;
+      case 2: TQ_FUSED(2, false); break;
+      case 4: TQ_FUSED(4, false); break;
+      default: return hipErrorNotSupported;
+    }
+  }
+#undef TQ_FUSED
+  return hipSuccess;
+}
+
+template <int B, int R, bool QBF>
+hipError_t launch_lut_r(dim3 grid, hipStream_t st, const SplitArgs &a) {
+  hipLaunchKernelGGL((decode_lut_kernel<B, R, QBF>), grid, dim3(256), 0, st, a.k->codes, a.k->norms,
+                     a.v->codes, a.v->norms, a.k->n_cells, a.kv_len, a.q, a.n_q, a.n_rep, a.qs, a.tau, a.ws,
+                     a.n_split);
+  return hipSuccess;
+}
+
+template <int B, bool QBF>
+hipError_t launch_lut_b(int n_rep, dim3 grid, hipStream_t st, const SplitArgs &a) {
+  switch (n_rep) {
+    case 1: return launch_lut_r<B, 1, QBF>(grid, st, a);
+    case 2: return launch_lut_r<B, 2, QBF>(grid, st, a);
+    case 3: return launch_lut_r<B, 3, QBF>(grid, st, a);
+    case 4: return launch_lut_r<B, 4, QBF>(grid, st, a);
+    case 5: return launch_lut_r<B, 5, QBF>(grid, st, a);
+    case 6: return launch_lut_r<B, 6, QBF>(grid, st, a);
+    case 7: return launch_lut_r<B, 7, QBF>(grid, st, a);
+    case 8: return launch_lut_r<B, 8, QBF>(grid, st, a);
+    default: return hipErrorNotSupported;
+  }
+}
+
+hipError_t launch_lut(int type, int n_rep, int qbf, dim3 grid, hipStream_t st, const SplitArgs &a) {
+  switch (type) {
+    case TQ_TURBO2: return qbf ? launch_lut_b<2, true>(n_rep, grid, st, a) : launch_lut_b<2, false>(n_rep, grid, st, a);
+    case TQ_TURBO3: return qbf ? launch_lut_b<3, true>(n_rep, grid, st, a) : launch_lut_b<3, false>(n_rep, grid, st, a);
+    default: return hipErrorNotSupported;
+  }
+}
+
+hipError_t launch_fused(int type, int tb, int qbf, dim3 grid, hipStream_t st, const SplitArgs &a, int nb) {
+  switch (type) {
+    case TQ_TURBO2: return qbf ? launch_fused_tb<2, true>(tb, grid, st, a, nb) : launch_fused_tb<2, false>(tb, grid, st, a, nb);
+    case TQ_TURBO3: return qbf ? launch_fused_tb<3, true>(tb, grid, st, a, nb) : launch_fused_tb<3, false>(tb, grid, st, a, nb);
+    case TQ_TURBO4: return qbf ? launch_fused_tb<4, true>(tb, grid, st, a, nb) : launch_fused_tb<4, false>(tb, grid, st, a, nb);
+    default: return hipErrorNotSupported;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_decode(const tq_cache &k, const tq_cache &v, const int64_t *seq_start,
@@ -969,10 +1664,17 @@ hipError_t launch_decode(const tq_cache &k, const tq_cache &v, const int64_t *se
   dim3 grid(p.n_split, k.n_kv_heads * p.head_groups, p.n_seq);
   const int qbf = q_dtype == TQ_BF16 ? 1 : 0;
   hipError_t e;
+  if (p.lut) {
+    if (seq_start || seq_len) return hipErrorInvalidValue;
+    e = launch_lut(v.type, a.n_rep, qbf, dim3(p.n_split, k.n_kv_heads, 1), stream, a);
+  } else if (p.fused) {
+    e = launch_fused(v.type, p.tiles_per_wave, qbf, grid, stream, a, p.nb);
+  } else {
   switch (v.type) {
     case TQ_TURBO2: e = launch_split_dims<2>(gk, gv, qbf, kq8, p.tiles_per_wave, p.pairs, grid, stream, a); break;
     case TQ_TURBO3: e = launch_split_dims<3>(gk, gv, qbf, kq8, p.tiles_per_wave, p.pairs, grid, stream, a); break;
     default: e = launch_split_dims<4>(gk, gv, qbf, kq8, p.tiles_per_wave, p.pairs, grid, stream, a); break;
+  }
   }
   if (e != hipSuccess) return e;
   e = hipGetLastError();

@@ -23,11 +23,17 @@ struct DecodePlan {
   int n_seq;             // sequences per call
   int pairs;             // (row, q head) pairs per workgroup: 8 or 16
   int head_groups;       // workgroups per (split, kv head): `pairs` (row, q head) pairs each
+  int fused;             // 1: the fused kernel (tiles_per_wave = tiles per wave block)
+  int nb;                // fused kernel: blocks per wave
+  int lut;               // 1: the Q x centroid table kernel (256 keys per split)
   size_t workspace_bytes;
 };
-// max_len: the longest sequence the call may see (sizes the grid).
+// max_len: the longest sequence the call may see (sizes the grid).  path: a
+// tq_decode_path; TQ_DECODE_TABLE needs one row of one sequence from cell 0
+// (no device length arrays), 128-wide turbo2/turbo3 heads and at most 8 q
+// heads per kv head, else hipErrorNotSupported.
 hipError_t plan_decode(const tq_cache &k, const tq_cache &v, int64_t max_len, int32_t n_q_heads,
-                       int n_rows, int n_seq, DecodePlan *p);
+                       int n_rows, int n_seq, DecodePlan *p, int path = TQ_DECODE_AUTO);
 // seq_start / seq_len: device arrays [n_seq] (null: one sequence of kv_len
 // cells from cell 0); kv_len is otherwise the largest length allowed.
 hipError_t launch_decode(const tq_cache &k, const tq_cache &v, const int64_t *seq_start,

@@ -35,12 +35,22 @@ def _caches(bits, k, v, kv_len=None):
     return kc, vc, ok, ov
 
 
-def _plan_block(kv, n_kv, dk, dv):
-    """Keys one wave scores (16 T), T as tq.h states the plan picks it: the
-    largest of 8, 4, 2, 1 with T (dk + dv) / 128 <= 16 and at least one
-    workgroup per compute unit, 4 in place of 8 past one round."""
+def _plan_block(kv, n_kv, dk, dv, n_pairs=8):
+    """The keys whose maximum is a key's sparse-V reference, as tq.h states
+    the plan: 128-wide K and V with at most eight pairs per kv head take
+    blocks of 16 tb keys, tb the largest of 4, 2, 1 giving every compute
+    unit a workgroup, one block per wave while that grid is below two rounds
+    (else a running maximum over several blocks: None, no block rule); other
+    shapes take 16 T keys, T the largest of 8, 4, 2, 1
+    with T (dk + dv) / 128 <= 16 and at least one workgroup per compute unit,
+    4 in place of 8 past one round."""
     import torch
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    if dk == 128 and dv == 128 and n_pairs <= 8:
+        tb = 4
+        while tb > 1 and -(-kv // (128 * tb)) * n_kv < n_cu:
+            tb //= 2
+        return 16 * tb if -(-kv // (128 * tb)) * n_kv < 2 * n_cu else None
     groups = (dk + dv) // 128
     tpw = 8
     while tpw > 1 and not (tpw * groups <= 16 and -(-kv // (64 * tpw)) * n_kv >= n_cu):
@@ -179,9 +189,10 @@ def test_sparse_v_within_bound(bits, tau):
     # tight check: the kernel's own rule, a skip against the maximum of each
     # block of keys one wave scores (16 * tiles-per-wave keys, from the plan)
     block = _plan_block(kv, k.shape[1], k.shape[2], v.shape[2])
-    want = o.attn_decode_sparse_v(ok, ov, kv, q.astype(np.float64), scale, tau, ref_block=block)
-    from gpu_util import assert_attention_close
-    assert_attention_close(got, want, what=f"sparse-V block rule, block {block}")
+    if block is not None:
+        want = o.attn_decode_sparse_v(ok, ov, kv, q.astype(np.float64), scale, tau, ref_block=block)
+        from gpu_util import assert_attention_close
+        assert_attention_close(got, want, what=f"sparse-V block rule, block {block}")
 
 
 def test_sparse_v_limits_on_gpu():
@@ -254,3 +265,76 @@ def test_sparse_v_wide_heads(dk, dv, tau):
     block = _plan_block(kv, k.shape[1], dk, dv)
     want = o.attn_decode_sparse_v(ok, ov, kv, qd, scale, tau, ref_block=block)
     assert_attention_close(got, want, what=f"sparse-V {dk}/{dv} block rule, block {block}")
+
+
+# ---------------------------------------------------------------- Q x centroid table path
+
+def _run_path(bits, q, k, v, kv_len, path, q_bf16=False, what="", tau=0.0):
+    import torch
+    from quantized_kv_cache_tq_amd import binding as b
+    from gpu_util import bf16_cuda, cuda
+    kc, vc, ok, ov = _caches(bits, k, v)
+    scale = 1.0 / math.sqrt(q.shape[1])
+    print(f"[decode] {what} path={path} bits={bits} n_q={q.shape[0]} n_kv={k.shape[1]} kv={kv_len}", flush=True)
+    qt = bf16_cuda(q) if q_bf16 else cuda(q)
+    got = b.tq_attn_decode_path(kc, vc, kv_len, qt, scale, path, sparse_v_tau=tau)
+    torch.cuda.synchronize()
+    return got.cpu().numpy(), kc, vc, ok, ov, qt, scale
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("n_q,n_kv", [(1, 1), (4, 4), (2, 1), (8, 4), (8, 1)])
+@pytest.mark.parametrize("kv_len", [1, 17, 256, 257, 3000, 32768])
+def test_table_path(bits, n_q, n_kv, kv_len):
+    """The Q x centroid table kernel of [PR36] (c) (TQ_DECODE_TABLE):
+    1, 2 and 8 q heads per kv head, outlier-channel K and V, lengths from one
+    key to 128 splits with ragged tails, bf16 and f32 queries."""
+    from quantized_kv_cache_tq_amd import binding as b
+    from gpu_util import assert_attention_close
+    q, k, v = inputs.outlier_decode(seed=40 + bits + n_q, kv_len=max(kv_len, 256), n_q=n_q, n_kv=n_kv)
+    got, _, _, ok, ov, _, scale = _run_path(bits, q, k, v, kv_len, b.TQ_DECODE_TABLE, q_bf16=(kv_len % 2 == 0),
+                                            what=f"table {n_q}/{n_kv}")
+    want = o.attn_decode(ok, ov, kv_len, q.astype(np.float64), scale)
+    assert_attention_close(got, want, what=f"table {n_q}/{n_kv} kv={kv_len}")
+
+
+def test_decode_paths_auto_matrix_and_refusals():
+    """TQ_DECODE_AUTO and TQ_DECODE_MATRIX give tq_attn_decode's bits; the
+    table path refuses turbo4, 256-wide heads and more than 8 q heads per kv
+    head, and an unknown path is an invalid argument."""
+    from quantized_kv_cache_tq_amd import binding as b
+    q, k, v = inputs.outlier_decode(seed=48, kv_len=5000, n_q=16, n_kv=2)
+    got_auto, kc, vc, _, _, qt, scale = _run_path(3, q, k, v, 5000, b.TQ_DECODE_AUTO, q_bf16=True, what="auto")
+    got_mat = b.tq_attn_decode_path(kc, vc, 5000, qt, scale, b.TQ_DECODE_MATRIX).cpu().numpy()
+    plain = b.tq_attn_decode(kc, vc, 5000, qt, scale).cpu().numpy()
+    np.testing.assert_array_equal(got_auto, plain)
+    np.testing.assert_array_equal(got_mat, plain)
+    with pytest.raises(b.TQError) as e:
+        b.tq_attn_decode_path(kc, vc, 5000, qt, scale, 7)
+    assert e.value.status == b.TQ_ERR_INVALID_ARG
+    for bits, n_q, n_kv, d in [(4, 2, 1, 128), (3, 16, 1, 128), (3, 2, 1, 256)]:
+        kc2, vc2 = b.new_cache(bits, d, n_kv, 64), b.new_cache(bits, d, n_kv, 64)
+        with pytest.raises(b.TQError) as e:
+            b.tq_attn_decode_path_workspace(kc2, vc2, 64, n_q, b.TQ_DECODE_TABLE)
+        assert e.value.status == b.TQ_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("bits,tau", [(2, 1e-2), (3, 5e-3)])
+def test_table_sparse_v_within_bound(bits, tau):
+    """The table kernel's value skip: within the oracle's bound of the dense
+    output (its reference is the maximum of each 256-key split, at most the
+    true maximum), and at the bar against the split-block emulation."""
+    from quantized_kv_cache_tq_amd import binding as b
+    from gpu_util import assert_attention_close
+    kv = 8192
+    q, k, v = inputs.outlier_decode(seed=44 + bits, kv_len=kv, n_q=8, n_kv=4)
+    got, _, _, ok, ov, _, scale = _run_path(bits, q, k, v, kv, b.TQ_DECODE_TABLE, q_bf16=True, what="table sparse",
+                                            tau=tau)
+    qd = q.astype(np.float64)
+    dense = o.attn_decode(ok, ov, kv, qd, scale)
+    bound, n_t = o.sparse_v_bound(ok, ov, kv, qd, scale, tau)
+    err = np.abs(got - dense).max(axis=1)
+    assert n_t.sum() > 0
+    assert np.all(err <= bound + 2e-3), (err - bound).max()
+    want = o.attn_decode_sparse_v(ok, ov, kv, qd, scale, tau, ref_block=256)
+    assert_attention_close(got, want, what="table sparse-V, 256-key blocks")

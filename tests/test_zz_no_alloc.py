@@ -52,7 +52,8 @@ def test_static_decode_two_calls_second_smaller():
 def test_static_decode_refuses_oversized_partials():
     import torch
     from quantized_kv_cache_tq_amd import binding as b
-    kv, n_q, n_kv = 262144, 64, 8
+    # 16 q heads per kv head: each kv head's splits hold sixteen pairs' partials
+    kv, n_q, n_kv = 262144, 128, 8
     kc, vc = b.new_cache(3, 128, n_kv, kv), b.new_cache(3, 128, n_kv, kv)
     need = b.tq_attn_decode_workspace(kc, vc, kv, n_q)
     assert need > b.STATIC_SCRATCH_BYTES
