@@ -37,18 +37,18 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak
 FP32_PEAK_TFLOPS = 157.3
 
-# HBM traffic of one decode call (split + merge kernels), from two
+# HBM traffic of one decode call (fused split kernel + merge kernel), from two
 # `rocprofv3 --pmc` passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) over
 # `bench.py --no-cpu-baseline --only decode,copy --steps 2 --warmup 1`, each
 # scaled by what the same counter reads for the 256 MiB device copy of that
-# run (FETCH_SIZE reads 131088.1 KiB for 262144 KiB copied: x1.99975;
+# run (FETCH_SIZE reads 131088.8 KiB for 262144 KiB copied: x1.99974;
 # WRITE_SIZE reads 262144 KiB: x1.0).  Valid only for the decode sources it
 # was taken on (sha256 of tq_decode.hip + tq_common.h); otherwise traffic is
 # reported as null.
-DECODE_TRAFFIC = {"sources_sha256": "51750abbe791ce3fa51c83a9ed6b71129dd26df5e03323973a6fab912f3df795",
-                  "fetch_kib": {"decode_split_kernel": 6565.2, "decode_merge_kernel": 561.0},
-                  "write_kib": {"decode_split_kernel": 1088.0, "decode_merge_kernel": 16.0},
-                  "fetch_scale": 1.99975, "write_scale": 1.0}
+DECODE_TRAFFIC = {"sources_sha256": "068e8819bd51167a8ee7de33d860a2099afea848467fe68ec48d15aabebe48d0",
+                  "fetch_kib": {"decode_fused_kernel": 6536.8, "decode_merge_kernel": 568.5},
+                  "write_kib": {"decode_fused_kernel": 1088.0, "decode_merge_kernel": 16.0},
+                  "fetch_scale": 1.99974, "write_scale": 1.0}
 
 
 def decode_traffic_bytes():
@@ -770,7 +770,7 @@ def main():
         out["roofline"] = {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
                            "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                            "traffic": decode_traffic_bytes(),
-                           "kernel": "decode call (decode_split_kernel + decode_merge_kernel), "
+                           "kernel": "decode call (decode_fused_kernel + decode_merge_kernel), "
                                      "algorithmic bytes = packed K+V codes and norms"}
     if ms["set_rows"] is not None:
         per_cache_us = ms["set_rows"] * 1e3
