@@ -625,32 +625,43 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
       hp.vc = a.vcodes + head_base * (16 * B * D::NG);
       hp.kn = a.knorms + head_base * D::NG;
       hp.vn = a.vnorms + head_base * D::NG;
-      KRaw<B, KD> kr0, kr1;
-      VRaw<B> vr;
+      // raw codes in two register sets that swap roles every tile (the loop
+      // runs two tiles per trip), so a load never targets registers whose
+      // previous contents are still to be used: with one set, the compiler
+      // issued each load into fresh registers and copied them back at the
+      // end of the phase, which waited for the load there
+      KRaw<B, KD> kra, krb;
+      VRaw<B> vra, vrb;
       uint32_t vw[KD / 32][4];
-      load_k<B, KD>(hp, last, kt0, dt, kr0);
-      load_k<B, KD>(hp, last, min(kt0 + 1, kt1 - 1), dt, kr1);
-      load_v<B, KD>(hp, last, kt0, dt, vr);
-      store_k<B, KD>(kr0, dt, tab, vbuf);   // K tile 0 goes where V tile 0 will
-      store_k<B, KD>(kr1, dt, tab, kbuf);
-      lookup_v<B, KD>(vr, dt, tab, vw);
+      load_k<B, KD>(hp, last, kt0, dt, kra);
+      load_k<B, KD>(hp, last, min(kt0 + 1, kt1 - 1), dt, krb);
+      load_v<B, KD>(hp, last, kt0, dt, vra);
+      store_k<B, KD>(kra, dt, tab, vbuf);   // K tile 0 goes where V tile 0 will
+      store_k<B, KD>(krb, dt, tab, kbuf);
+      lookup_v<B, KD>(vra, dt, tab, vw);
       // loads are unconditional (tile index clamped): a conditional load
       // would merge into the loop-carried registers through copies that wait
       // for the data
-      load_k<B, KD>(hp, last, min(kt0 + 2, kt1 - 1), dt, kr0);
-      load_v<B, KD>(hp, last, min(kt0 + 1, kt1 - 1), dt, vr);
+      load_k<B, KD>(hp, last, min(kt0 + 2, kt1 - 1), dt, kra);
+      load_v<B, KD>(hp, last, min(kt0 + 1, kt1 - 1), dt, vra);
       __syncthreads();   // query rows, K tiles 0 (in the V^T buffer) and 1 ready
       __syncthreads();   // K tile 0 read: the V^T buffer may take V tile 0
-      for (int kt = kt0; kt < kt1; ++kt) {
+      // one tile: vc holds V tile kt+1, kc K tile kt+2; vn and kn receive
+      // V tile kt+2 and K tile kt+3
+      auto tile = [&](int kt, VRaw<B> &vc, VRaw<B> &vn, KRaw<B, KD> &kc, KRaw<B, KD> &kn) {
         // phase A: V tile kt into the buffer, look up V tile kt+1
         write_v<KD>(vw, dt, vbuf);
-        lookup_v<B, KD>(vr, dt, tab, vw);   // past the end: never written
-        load_v<B, KD>(hp, last, min(kt + 2, kt1 - 1), dt, vr);
+        lookup_v<B, KD>(vc, dt, tab, vw);   // past the end: never written
+        load_v<B, KD>(hp, last, min(kt + 2, kt1 - 1), dt, vn);
         __syncthreads();   // V tile kt written; K tile kt+1 read
         // phase B: K tile kt+2 into the (now free) K buffer
-        if (kt + 2 < kt1) store_k<B, KD>(kr0, dt, tab, kbuf);
-        load_k<B, KD>(hp, last, min(kt + 3, kt1 - 1), dt, kr0);
+        if (kt + 2 < kt1) store_k<B, KD>(kc, dt, tab, kbuf);
+        load_k<B, KD>(hp, last, min(kt + 3, kt1 - 1), dt, kn);
         __syncthreads();   // V tile kt consumed; K tile kt+2 written
+      };
+      for (int kt = kt0; kt < kt1; kt += 2) {
+        tile(kt, vra, vrb, kra, krb);
+        if (kt + 1 < kt1) tile(kt + 1, vrb, vra, krb, kra);
       }
       __syncthreads();   // partial outputs and statistics in shared memory
     }

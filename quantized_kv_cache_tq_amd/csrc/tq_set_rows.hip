@@ -4,135 +4,227 @@
 // [PR36] (a), the llama-cpp-turboquant SET_ROWS butterfly commit, describes
 // the kernel as a sign flip and a 128-point butterfly (h = 1..64) per group;
 // the CUDA kernel spread a group over several 32-wide warps and kept block
-// barriers for h = 32 and 64.  On CDNA4 half a wave64 holds a whole group:
-// lane j owns elements 4j..4j+3 (one 16-byte load), stages h = 1 and 2 are
-// in-register and h = 4..64 are DPP / swizzle exchanges inside the 32 lanes,
-// so no barrier or LDS round trip is needed anywhere in the transform.  Each
-// wave quantizes 2 x kRounds groups and issues all their loads first, so
-// enough bytes are in flight to stream from HBM.
+// barriers for h = 32 and 64.  Here a pair of lanes quantizes one group: lane
+// half h = lane & 1 holds elements 64h .. 64h + 63 in registers, so the sum of
+// squares, the butterfly stages h = 1 .. 32, the codes and the bit packing
+// are per-lane arithmetic, and only the last stage (h = 64) and the last step
+// of the sum exchange values between the two lanes (one DPP read each).
+// Every instruction of a wave thus advances 32 groups.  (With a group spread
+// over 32 lanes the per-group work -- the correctly rounded square root and
+// division, the gathering of the packed words -- ran on all 32 lanes, and
+// every butterfly stage across lanes took an exchange and a select: about
+// three times the vector instructions per group.  With one lane per group
+// the compiler's schedule of the 128-value transform ran out of registers.)
+// A wave takes 32 consecutive rows of one (kv head, group) column: its loads
+// read whole 256-byte half groups and its stores write consecutive cells'
+// code blocks when the cell indices are consecutive.
 //
 // Bit-exact contract (float32, no contraction): see tq_set_rows in tq.h.
 #include "tq_common.h"
 
 namespace tq {
 
-constexpr int kSrWaves = 4;
-constexpr int kSrRounds = 4;                              // groups per half-wave
-constexpr int kSrGroupsPerBlock = kSrWaves * 2 * kSrRounds;
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// kSmall: fewer than 2^31 groups in the call, so the one division that
-// places a lane's first group is 32-bit.
-template <int B, bool kSmall>
+constexpr int kSrWaves = 4;                 // waves per workgroup
+constexpr int kSrHalf = kGroup / 2;         // elements per lane
+constexpr int kSrRows = 32;                 // rows (groups) per task
+constexpr int kSrTasks = 1;                 // tasks per wave
+
+// qs = #{k : a > threshold k} by binary search over the sorted thresholds:
+// each step compares with the middle threshold of the range left, chosen by
+// the earlier steps' outcomes.
+template <int B>
+__device__ __forceinline__ uint32_t mag_index(float a) {
+  if constexpr (B == 2) {
+    return a > threshold<2>(1) ? 1u : 0u;
+  } else if constexpr (B == 3) {
+    const bool c2 = a > threshold<3>(2);
+    const bool c1 = a > (c2 ? threshold<3>(3) : threshold<3>(1));
+    return (c2 ? 2u : 0u) | (c1 ? 1u : 0u);
+  } else {
+    static_assert(B == 4, "2, 3 or 4 bits");
+    const bool c4 = a > threshold<4>(4);
+    const bool c2 = a > (c4 ? threshold<4>(6) : threshold<4>(2));
+    const float t1 = c4 ? (c2 ? threshold<4>(7) : threshold<4>(5)) : (c2 ? threshold<4>(3) : threshold<4>(1));
+    const bool c1 = a > t1;
+    return (c4 ? 4u : 0u) | (c2 ? 2u : 0u) | (c1 ? 1u : 0u);
+  }
+}
+
+template <int B>
 __global__ __launch_bounds__(64 * kSrWaves) void set_rows_kernel(
     uint8_t *__restrict__ codes, uint16_t *__restrict__ norms, const float *__restrict__ src,
     const int64_t *__restrict__ cell_idx, int64_t n_rows, int32_t n_kv, int32_t n_groups_per_head,
     int64_t n_cells) {
 #pragma clang fp contract(off)
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int half = lane >> 5, j = lane & 31;
-  const int64_t groups_per_row = (int64_t)n_kv * n_groups_per_head;
-  const int64_t total = n_rows * groups_per_row;
-  const int64_t gbase = ((int64_t)blockIdx.x * kSrWaves + wave) * (2 * kSrRounds) + half;
+  // sign masks of the random flip (bit 31 set where an element is negated)
+  __shared__ __align__(16) uint32_t smask[kGroup];
+  if (threadIdx.x < kGroup) smask[threadIdx.x] = sign_bit_of(threadIdx.x) << 31;
+  __syncthreads();
 
-  // the lane's groups gbase, gbase + 2, ...: row, kv head and group of the
-  // first by one division, the later ones stepped from it (the group index
-  // grows by 2, so each carry loop runs at most twice)
-  int64_t row;
-  int head, grp;
-  if constexpr (kSmall) {
-    const uint32_t g32 = (uint32_t)gbase, gpr = (uint32_t)groups_per_row;
-    const uint32_t r32 = g32 / gpr, rem = g32 - r32 * gpr;
-    row = r32;
-    head = (int)(rem / (uint32_t)n_groups_per_head);
-    grp = (int)(rem - (uint32_t)head * (uint32_t)n_groups_per_head);
-  } else {
-    row = gbase / groups_per_row;
-    const int64_t rem = gbase - row * groups_per_row;
-    head = (int)(rem / n_groups_per_head);
-    grp = (int)(rem - (int64_t)head * n_groups_per_head);
-  }
-  int64_t rrow[kSrRounds];
-  int rhead[kSrRounds], rgrp[kSrRounds];
-#pragma unroll
-  for (int r = 0; r < kSrRounds; ++r) {
-    rrow[r] = row;
-    rhead[r] = head;
-    rgrp[r] = grp;
-    grp += 2;
-    while (grp >= n_groups_per_head) {
-      grp -= n_groups_per_head;
-      ++head;
-    }
-    while (head >= n_kv) {
-      head -= n_kv;
-      ++row;
-    }
-  }
-  // issue every load first
-  float4 x[kSrRounds];
-  int64_t cell[kSrRounds];
-#pragma unroll
-  for (int r = 0; r < kSrRounds; ++r) {
-    const int64_t gi = gbase + 2 * r;
-    if (gi < total) {
-      x[r] = reinterpret_cast<const float4 *>(src + gi * kGroup)[j];
-      cell[r] = cell_idx[rrow[r]];
-    } else {
-      x[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-      cell[r] = -1;
-    }
-  }
-  uint32_t neg[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) neg[i] = sign_bit_of(4 * j + i);
+  const int lane = threadIdx.x & 63, h = lane & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int cols = n_kv * n_groups_per_head;                 // (kv head, group) columns of a row
+  const int64_t n_tasks = ceil_div<int64_t>(n_rows, kSrRows) * cols;
+  const int64_t task0 = ((int64_t)blockIdx.x * kSrWaves + wave) * kSrTasks;
+  if (task0 >= n_tasks) return;                              // uniform: the whole wave
 
+  // (row tile, column) of the wave's tasks: one division, then steps
+  int64_t ttile[kSrTasks];
+  int tcol[kSrTasks];
+  {
+    int64_t tile = task0 / cols;
+    int col = (int)(task0 - tile * cols);
 #pragma unroll
-  for (int r = 0; r < kSrRounds; ++r) {
-    const int64_t gi = gbase + 2 * r;
-    float u[4] = {x[r].x, x[r].y, x[r].z, x[r].w};
-    // 1. norm: sum of squares in the butterfly's pairing order
-    const float n2 = sum_squares_half(u);
-    const float norm = __builtin_sqrtf(n2);             // correctly rounded
-    const float inv = norm > 0.f ? 1.0f / norm : 0.f;   // correctly rounded
-    // 2. sign flip, 3. butterfly, 4. unit-variance coordinates, 5. codes
+    for (int k = 0; k < kSrTasks; ++k) {
+      ttile[k] = tile;
+      tcol[k] = col;
+      if (++col == cols) {
+        col = 0;
+        ++tile;
+      }
+    }
+  }
+
+  // loads of task k (kSrRows rows of one column); a task past the end
+  // reloads valid rows and stores nothing
+  auto load = [&](int k, float (&u)[kSrHalf], int64_t &cell) {
+    const int64_t tile = task0 + k < n_tasks ? ttile[k] : ttile[0];
+    const int col = task0 + k < n_tasks ? tcol[k] : tcol[0];
+    const int64_t row = tile * kSrRows + (lane >> 1);
+    const int64_t lrow = row < n_rows ? row : n_rows - 1;    // a dead lane loads a valid row
+    const float4 *g = reinterpret_cast<const float4 *>(src + (lrow * cols + col) * kGroup);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) u[i] = flip_sign(u[i], neg[i]);
-    wht128_half(u, j);
-    uint32_t field = 0;
+    for (int v = 0; v < kSrHalf / 4; ++v) {
+      const float4 f = g[2 * v + h];
+      u[4 * v] = f.x; u[4 * v + 1] = f.y; u[4 * v + 2] = f.z; u[4 * v + 3] = f.w;
+    }
+    cell = cell_idx[lrow];
+  };
+
+  auto quantize = [&](int k, float (&u)[kSrHalf], int64_t cell) {
+    const int64_t tile = ttile[k];
+    const int col = tcol[k];
+    const int head = col / n_groups_per_head, grp = col - head * n_groups_per_head;
+    const bool live = task0 + k < n_tasks && tile * kSrRows + (lane >> 1) < n_rows;
+
+    // 1. norm: the sum of squares added in the butterfly's pairing order
+    //    (neighbours, then partials at distance 2, 4, .., 64).  Distances 1
+    //    and 2 stay inside a lane's chunk, distance 4 adds the two lanes'
+    //    chunk partials (both lanes get the same bits: the operands meet
+    //    commuted), distances 8 .. 64 pair the lane's chunks in order: pend[l]
+    //    holds a finished left partial until its right sibling is done
+    float pend[5];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float y = u[i] * inv;
+    for (int v = 0; v < kSrHalf / 4; ++v) {
+      const float s01 = u[4 * v] * u[4 * v] + u[4 * v + 1] * u[4 * v + 1];
+      const float s23 = u[4 * v + 2] * u[4 * v + 2] + u[4 * v + 3] * u[4 * v + 3];
+      const float q = s01 + s23;
+      float t = q + xor_lane<1>(q);
+      int l = 0;
+#pragma unroll
+      for (; (v >> l) & 1; ++l) t = pend[l] + t;
+      pend[l] = t;
+    }
+    const float n2 = pend[4];
+    const float norm = __builtin_sqrtf(n2);                  // correctly rounded
+    const float inv = norm > 0.f ? 1.0f / norm : 0.f;        // correctly rounded
+
+    // 2. sign flip, 3. butterfly stages in order: h = 1, 2 inside a chunk,
+    //    h = 4 between the two lanes, h = 8 .. 64 between the lane's chunks.
+    //    The lane stage is x + c p with p the partner's value and c = +1 in
+    //    the lower lane, -1 in the upper (the product by +-1 is exact, so the
+    //    fused form rounds like the plain add or subtract): the upper lane so
+    //    holds b - a, the butterfly's a - b negated, and the later stages keep
+    //    that sign on all its values (both operands of each carry it); its
+    //    factor 1/norm is negated to match, so y below is exactly the
+    //    transform over norm
+    const u32x4_t *sm = reinterpret_cast<const u32x4_t *>(smask);
+#pragma unroll
+    for (int v = 0; v < kSrHalf / 4; ++v) {
+      const u32x4_t m = sm[2 * v + h];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) u[4 * v + k] = __uint_as_float(__float_as_uint(u[4 * v + k]) ^ m[k]);
+    }
+    auto local_stage = [&](int d) {   // pairs (i, i + d) of the lane's values
+#pragma unroll
+      for (int i = 0; i < kSrHalf; ++i)
+        if (!(i & d)) {
+          const float a = u[i], b = u[i + d];
+          u[i] = a + b;
+          u[i + d] = a - b;
+        }
+    };
+    local_stage(1);
+    local_stage(2);
+    const float c4 = h ? -1.f : 1.f;
+#pragma unroll
+    for (int i = 0; i < kSrHalf; ++i) u[i] = __builtin_fmaf(xor_lane<1>(u[i]), c4, u[i]);
+    local_stage(4);
+    local_stage(8);
+    local_stage(16);
+    local_stage(32);
+    const float inv_s = flip_sign(inv, (uint32_t)h);
+
+    // 4. unit-variance coordinates, 5. codes, 6. pack: element e's code at
+    //    bits B e .. B e + B - 1 of the group's little-endian bit stream.  The
+    //    lane places its own elements' codes into an image of the whole
+    //    group's 4B dwords, ORs in the partner's image and stores its half
+    uint32_t word[4 * B];
+#pragma unroll
+    for (int w = 0; w < 4 * B; ++w) word[w] = 0u;
+#pragma unroll
+    for (int i = 0; i < kSrHalf; ++i) {
+      const float y = u[i] * inv_s;
       const float a = __builtin_fabsf(y);
-      uint32_t qs = 0;
-#pragma unroll
-      for (int k = 1; k < (1 << (B - 1)); ++k) qs += a > threshold<B>(k) ? 1u : 0u;
-      const uint32_t c = qs | ((y < 0.f ? 1u : 0u) << (B - 1));
-      field |= c << (B * i);
+      const uint32_t c = mag_index<B>(a) | (y < 0.f ? 1u << (B - 1) : 0u);
+      // element 8v + 4h + r of the group (i = 4v + r); the lane-dependent
+      // part 4h B of its bit position is applied below, as a shift of the
+      // lane's 4B-bit chunk fields
+      const int v = i >> 2, r = i & 3;
+      const int bit = 8 * B * v + B * r, w = bit >> 5, sh = bit & 31;
+      word[w] |= c << sh;
+      if (sh + B > 32) word[w + 1] |= c >> (32 - sh);
     }
-    // 6. pack: lane j's 4B-bit field sits at stream bit 4B*j; lane w < 4B
-    //    assembles output dword w from the (at most KMAX) fields it overlaps.
-    constexpr int FB = 4 * B;
-    constexpr int KMAX = (B == 4) ? 2 : 4;
-    const int w = j;
-    const int j0 = (32 * w) / FB;
-    const int j1 = (32 * w + 31) / FB;
-    uint32_t word = 0;
+    // the upper lane's chunk fields sit 4B bits higher: shift its image
+    // (a funnel shift across the dwords)
+    uint32_t img[4 * B];
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-      const int jj = j0 + k;
-      const int srcl = (half << 5) + (jj < 32 ? jj : 31);
-      const uint32_t f = (uint32_t)__shfl((int)field, srcl, 64);
-      const int pos = FB * jj - 32 * w;
-      if (jj <= j1) word |= pos >= 0 ? (f << pos) : (f >> (-pos));
+    for (int w = 4 * B - 1; w >= 0; --w) {
+      const uint32_t lo = w > 0 ? word[w - 1] : 0u;
+      const uint32_t shifted = (4 * B == 32) ? lo : __builtin_amdgcn_alignbit(word[w], lo, 32 - 4 * B);
+      img[w] = h ? shifted : word[w];
     }
-    const int64_t c = cell[r];
-    if (gi < total && c >= 0 && c < n_cells) {
-      const int64_t slot = ((int64_t)rhead[r] * n_cells + c) * n_groups_per_head + rgrp[r];
-      if (w < FB) reinterpret_cast<uint32_t *>(codes + slot * (16 * B))[w] = word;
-      if (j == 0) {
+#pragma unroll
+    for (int w = 0; w < 4 * B; ++w) img[w] |= (uint32_t)__float_as_int(xor_lane<1>(__int_as_float((int)img[w])));
+    if (live && cell >= 0 && cell < n_cells) {
+      const int64_t slot = ((int64_t)head * n_cells + cell) * n_groups_per_head + grp;
+      uint8_t *dst = codes + slot * (16 * B) + 8 * B * h;     // this lane's 8B bytes (8-byte aligned)
+#pragma unroll
+      for (int v = 0; v < B; ++v)
+        reinterpret_cast<u32x2_t *>(dst)[v] =
+            u32x2_t{h ? img[2 * B + 2 * v] : img[2 * v], h ? img[2 * B + 2 * v + 1] : img[2 * v + 1]};
+      if (h == 0) {
         const _Float16 h16 = (_Float16)norm;
         norms[slot] = __builtin_bit_cast(uint16_t, h16);
       }
+    }
+  };
+
+  // two register sets: the next task's loads are in flight while the current
+  // one is computed
+  float ua[kSrHalf], ub[kSrHalf];
+  int64_t ca, cb;
+  load(0, ua, ca);
+#pragma unroll
+  for (int k = 0; k < kSrTasks; k += 2) {
+    if (k + 1 < kSrTasks) load(k + 1, ub, cb);
+    quantize(k, ua, ca);
+    if (k + 1 < kSrTasks) {
+      if (k + 2 < kSrTasks) load(k + 2, ua, ca);
+      quantize(k + 1, ub, cb);
     }
   }
 }
@@ -195,27 +287,24 @@ hipError_t launch_set_rows(const tq_cache &c, const float *src, const int64_t *c
     return hipGetLastError();
   }
   const int32_t gph = c.head_dim / kGroup;
-  const int64_t total = n_rows * (int64_t)c.n_kv_heads * gph;
-  const int64_t blocks = ceil_div<int64_t>(total, kSrGroupsPerBlock);
+  const int64_t tasks = ceil_div<int64_t>(n_rows, kSrRows) * (int64_t)c.n_kv_heads * gph;
+  const int64_t blocks = ceil_div<int64_t>(tasks, kSrWaves * kSrTasks);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   dim3 grid((unsigned)blocks), block(64 * kSrWaves);
-  // a lane's first group index stays below total + the groups of one block
-  const bool small = total + kSrGroupsPerBlock < 0x7fffffffLL;
-#define TQ_SR(B)                                                                                   \
-  do {                                                                                             \
-    if (small)                                                                                     \
-      hipLaunchKernelGGL((set_rows_kernel<B, true>), grid, block, 0, stream, c.codes, c.norms, src, \
-                         cell_idx, n_rows, c.n_kv_heads, gph, c.n_cells);                          \
-    else                                                                                           \
-      hipLaunchKernelGGL((set_rows_kernel<B, false>), grid, block, 0, stream, c.codes, c.norms,    \
-                         src, cell_idx, n_rows, c.n_kv_heads, gph, c.n_cells);                     \
-  } while (0)
   switch (c.type) {
-    case TQ_TURBO2: TQ_SR(2); break;
-    case TQ_TURBO3: TQ_SR(3); break;
-    default: TQ_SR(4); break;
+    case TQ_TURBO2:
+      hipLaunchKernelGGL((set_rows_kernel<2>), grid, block, 0, stream, c.codes, c.norms, src, cell_idx, n_rows,
+                         c.n_kv_heads, gph, c.n_cells);
+      break;
+    case TQ_TURBO3:
+      hipLaunchKernelGGL((set_rows_kernel<3>), grid, block, 0, stream, c.codes, c.norms, src, cell_idx, n_rows,
+                         c.n_kv_heads, gph, c.n_cells);
+      break;
+    default:
+      hipLaunchKernelGGL((set_rows_kernel<4>), grid, block, 0, stream, c.codes, c.norms, src, cell_idx, n_rows,
+                         c.n_kv_heads, gph, c.n_cells);
+      break;
   }
-#undef TQ_SR
   return hipGetLastError();
 }
 
