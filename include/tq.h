@@ -156,18 +156,21 @@ tq_status tq_set_rows(const tq_cache *dst, const float *src, const int64_t *cell
  * TQ_ERR_INVALID_ARG); this build takes head widths of 128 or 256 for each
  * of k and v, which may differ ([PR36] (b): a 192-wide K head padded to 256
  * beside 128-wide V heads, decoded natively; else TQ_ERR_UNSUPPORTED).  A
- * workgroup serves P (query row, q head) pairs of one kv head: P = 16 when
- * a kv head has more than eight pairs (n_pairs = n_rep here, n_rows * n_rep
- * in the batched call below) and both caches are turbo with 128-wide heads
- * (the two sets of eight share one decode of the cells), else P = 8; more
- * pairs take more workgroups over the same cells.
+ * workgroup serves P (query row, q head) pairs of one kv head (n_pairs =
+ * n_rep here, n_rows * n_rep in the batched call below).  When both caches
+ * are turbo with 128-wide heads and either n_pairs <= 8 or there is one
+ * sequence (the "fused" case), P = 8 and a kv head's pairs take
+ * ceil(n_pairs / 8) pair groups of workgroups over the same cells.
+ * Otherwise P = 16 when n_pairs > 8 and both caches are turbo with 128-wide
+ * heads (the two sets of eight share one decode of the cells), else P = 8;
+ * more pairs take more workgroups over the same cells.
  * sparse_v_tau >= 0 ([PR36] (d) item 3; 0 = off): a key whose weight
  * e^(s - m) is below tau is left out of the value sum and kept in the
- * normalizer, with m a reference no larger than the true maximum.  When
- * both caches are turbo with 128-wide heads and a kv head has at most eight
- * pairs, a wave scores aligned blocks of 16 tb keys in turn, tb the largest
- * of 4, 2, 1 with W(tb) = ceil(kv_len / 128 tb) * n_kv_heads >= C, C the
- * device's compute units (else 1), and m is the maximum of the keys it has
+ * normalizer, with m a reference no larger than the true maximum.  In the
+ * fused case a wave scores aligned blocks of 16 tb keys in turn, tb the
+ * largest of 4, 2, 1 with W(tb) = ceil(kv_len / 128 tb) * n_kv_heads *
+ * ceil(n_pairs / 8) >= C, C the device's compute units (else 1), and m is
+ * the maximum of the keys it has
  * scored up to and including the key's block: that block's own maximum
  * while W(tb) < 2C (one block per wave; for the batched call below, kv_len
  * is max_kv_len and W is multiplied by n_seq).  Otherwise m is the maximum

@@ -745,7 +745,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_fused_kernel(
     const uint8_t *__restrict__ kcodes, const uint16_t *__restrict__ knorms,
     const uint8_t *__restrict__ vcodes, const uint16_t *__restrict__ vnorms, int64_t n_cells,
     const int64_t *__restrict__ seq_start, const int32_t *__restrict__ seq_len, int64_t kv_len,
-    const void *__restrict__ q, int n_q, int n_rep, int n_rows, int nb, float qscale, float tau,
+    const void *__restrict__ q, int n_q, int n_rep, int n_rows, int n_hg, int nb, float qscale, float tau,
     float *__restrict__ ws, int n_split) {
   constexpr int KPB = 16 * TB;                 // keys per wave block
   constexpr int GW = 4 * B;                    // code dwords per key row
@@ -767,11 +767,14 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_fused_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, quad = lane >> 4;
-  const int s = blockIdx.x, g = blockIdx.y, z = blockIdx.z;
+  const int s = blockIdx.x, z = blockIdx.z;
+  const int g = (int)blockIdx.y / n_hg, hg = (int)blockIdx.y - g * n_hg;   // kv head, pair group
   const SeqExtent ext = seq_extent(seq_start, seq_len, z, kv_len, n_cells);
   const int64_t kps = (int64_t)8 * nb * KPB;
   if ((int64_t)s * kps >= ext.len) return;     // uniform: the whole workgroup
-  const int n_vh = n_rows * n_rep;             // (row, head) pairs of the kv head (<= 8)
+  // (row, head) pairs 8 hg .. 8 hg + n_vh - 1 of the kv head's n_rows n_rep
+  const int p0 = 8 * hg;
+  const int n_vh = imin(8, n_rows * n_rep - p0);
   const int64_t kbase = (int64_t)g * n_cells + ext.start;
   uint32_t *vst = blk + wave * (kVstWords + 2 * KPB);
   float *nk = reinterpret_cast<float *>(vst + kVstWords), *nv = nk + KPB;
@@ -824,7 +827,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_fused_kernel(
   // 16 (qj >> 3) + qh and its low parts to lane 16 (qj >> 3) + 8 + qh
   if (wave < 4) {
     const int qh = 2 * wave + (lane >> 5), qj = lane & 31;
-    const int vq = imin(qh, n_vh - 1);
+    const int vq = p0 + imin(qh, n_vh - 1);
     const int vr = n_rows == 1 ? 0 : vq / n_rep;
     const int64_t qbase =
         (((int64_t)z * n_rows + vr) * n_q + (int64_t)g * n_rep + (vq - vr * n_rep)) * kGroup + 4 * qj;
@@ -866,7 +869,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_fused_kernel(
   const uint32_t lane8 = 8u * (uint32_t)(lane & 31);   // this lane's table copy
   // this lane's score column: pair col & 7 -> causal offset of its row
   const int vcol = col & 7;
-  const int row_off = vcol < n_vh && n_rows > 1 ? vcol / n_rep : 0;
+  const int row_off = vcol < n_vh && n_rows > 1 ? (p0 + vcol) / n_rep : 0;
   const float lo_sel = col >= 8 ? 1.f : 0.f;
   // V: lane (n, quad) of tile t decodes elements 8n .. 8n+7 of keys
   // 16t + 4quad + i (i = 0..3), the 8B-bit run at bit 8Bn of each row
@@ -1088,8 +1091,9 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_fused_kernel(
         a0 += f * v.x;
         a1 += f * v.y;
       }
-      const int vr = n_rows == 1 ? 0 : h / n_rep;
-      const int64_t qrow = ((int64_t)z * n_rows + vr) * n_q + (int64_t)g * n_rep + (h - vr * n_rep);
+      const int gh = p0 + h;
+      const int vr = n_rows == 1 ? 0 : gh / n_rep;
+      const int64_t qrow = ((int64_t)z * n_rows + vr) * n_q + (int64_t)g * n_rep + (gh - vr * n_rep);
       float *ph = ws + (qrow * n_split + s) * PSTRIDE;
       *reinterpret_cast<float2 *>(ph + d) = make_float2(a0, a1);
       if (d == 0) *reinterpret_cast<float2 *>(ph + kGroup) = make_float2(M, L);
@@ -1460,15 +1464,27 @@ hipError_t plan_decode(const tq_cache &k, const tq_cache &v, int64_t max_len, in
     p->tiles_per_wave = 1;
     p->keys_per_split = 256;
   } else
-  // One 128-wide group each way, both caches turbo, at most eight pairs per
-  // kv head: the fused kernel, eight waves of blocks of 16 tb keys.  tb: the
-  // most (4, 2, 1) that still gives every compute unit a workgroup; nb
-  // blocks per wave: as many (a power of two) as keep the grid at least one
-  // full round, so long sequences stream through one round of workgroups
-  // (then with blocks of at most 2 tiles, the next block's loads in flight
-  // beside the current one).
-  if (k.type != TQ_Q8 && k.type == v.type && k.head_dim == kGroup && v.head_dim == kGroup && n_pairs <= 8) {
-    const int64_t wg = (int64_t)k.n_kv_heads * n_seq;
+  // One 128-wide group each way, both caches turbo, and at most eight
+  // (row, q head) pairs per kv head or a single sequence: the fused kernel,
+  // eight waves of blocks of 16 tb keys, eight pairs per workgroup (more
+  // pairs take more pair groups over the same cells).  tb: the most (4, 2,
+  // 1) that still gives every compute unit a workgroup; nb blocks per wave:
+  // as many (a power of two) as keep the grid at least one full round, so
+  // long sequences stream through one round of workgroups (then with blocks
+  // of at most 2 tiles, the next block's loads in flight beside the current
+  // one).  Batches of several sequences with more than eight pairs keep the
+  // sixteen-pair split kernel: the fused kernel holds a compute unit per
+  // workgroup, and when the batch's lengths (which live on the device) are
+  // mixed, the split kernel's two workgroups per compute unit overlap its
+  // several rounds.  Measured, 8 sequences x 2 rows, 32 q / 4 kv heads,
+  // graph replay, us per call, split kernel against fused pair groups:
+  // lengths 2000 - 32768 (131,072 cells) 77.0 / 84.0; all 16384: 63.3 / 48.2
+  // (with the fused grid sized for one sequence of max_len cells instead of
+  // all of them: 105 / 69).
+  if (k.type != TQ_Q8 && k.type == v.type && k.head_dim == kGroup && v.head_dim == kGroup &&
+      (n_pairs <= 8 || n_seq == 1)) {
+    const int n_hg = ceil_div(n_pairs, 8);
+    const int64_t wg = (int64_t)k.n_kv_heads * n_hg * n_seq;
     int tb = 4;
     while (tb > 1 && ceil_div<int64_t>(max_len, 128LL * tb) * wg < n_cu) tb >>= 1;
     int64_t per = ceil_div<int64_t>(max_len, 128LL * tb) * wg;
@@ -1480,7 +1496,7 @@ hipError_t plan_decode(const tq_cache &k, const tq_cache &v, int64_t max_len, in
     while (nb < (1 << 20) && (int64_t)nb * 2 * n_cu <= per) nb *= 2;
     p->fused = 1;
     p->pairs = 8;
-    p->head_groups = 1;
+    p->head_groups = n_hg;
     p->tiles_per_wave = tb;
     p->nb = nb;
     p->keys_per_split = 128 * tb * nb;
@@ -1573,7 +1589,7 @@ hipError_t launch_fused_tb(int tb, dim3 grid, hipStream_t st, const SplitArgs &a
 #define TQ_FUSED(TB, PF)                                                                               \
   hipLaunchKernelGGL((decode_fused_kernel<B, TB, QBF, PF>), grid, block, 0, st, a.k->codes, a.k->norms, \
                      a.v->codes, a.v->norms, a.k->n_cells, a.seq_start, a.seq_len, a.kv_len, a.q, a.n_q, \
-                     a.n_rep, a.n_rows, nb, a.qs, a.tau, a.ws, a.n_split)
+                     a.n_rep, a.n_rows, a.n_hg, nb, a.qs, a.tau, a.ws, a.n_split)
   // several blocks per wave: prefetching variants (at most 2 tiles per
   // block, the prefetch registers beside them)
   if (nb > 1) {

@@ -37,20 +37,21 @@ def _caches(bits, k, v, kv_len=None):
 
 def _plan_block(kv, n_kv, dk, dv, n_pairs=8):
     """The keys whose maximum is a key's sparse-V reference, as tq.h states
-    the plan: 128-wide K and V with at most eight pairs per kv head take
-    blocks of 16 tb keys, tb the largest of 4, 2, 1 giving every compute
-    unit a workgroup, one block per wave while that grid is below two rounds
-    (else a running maximum over several blocks: None, no block rule); other
-    shapes take 16 T keys, T the largest of 8, 4, 2, 1
+    the plan for one sequence: 128-wide K and V take blocks of 16 tb keys,
+    tb the largest of 4, 2, 1 giving every compute unit a workgroup (counting
+    the pair groups of eight), one block per wave while that grid is below
+    two rounds (else a running maximum over several blocks: None, no block
+    rule); other shapes take 16 T keys, T the largest of 8, 4, 2, 1
     with T (dk + dv) / 128 <= 16 and at least one workgroup per compute unit,
     4 in place of 8 past one round."""
     import torch
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
-    if dk == 128 and dv == 128 and n_pairs <= 8:
+    if dk == 128 and dv == 128:
+        wg = n_kv * -(-n_pairs // 8)
         tb = 4
-        while tb > 1 and -(-kv // (128 * tb)) * n_kv < n_cu:
+        while tb > 1 and -(-kv // (128 * tb)) * wg < n_cu:
             tb //= 2
-        return 16 * tb if -(-kv // (128 * tb)) * n_kv < 2 * n_cu else None
+        return 16 * tb if -(-kv // (128 * tb)) * wg < 2 * n_cu else None
     groups = (dk + dv) // 128
     tpw = 8
     while tpw > 1 and not (tpw * groups <= 16 and -(-kv // (64 * tpw)) * n_kv >= n_cu):

@@ -52,13 +52,14 @@ def test_static_decode_two_calls_second_smaller():
 def test_static_decode_refuses_oversized_partials():
     import torch
     from quantized_kv_cache_tq_amd import binding as b
-    # 16 q heads per kv head: each kv head's splits hold sixteen pairs' partials
-    kv, n_q, n_kv = 262144, 128, 8
-    kc, vc = b.new_cache(3, 128, n_kv, kv), b.new_cache(3, 128, n_kv, kv)
+    # 256-wide K and V heads take splits of at most 256 keys: 1024 splits of
+    # 16 q heads x 260 floats over 262144 cells, 17 MB of partials
+    kv, n_q, n_kv, d = 262144, 16, 2, 256
+    kc, vc = b.new_cache(3, d, n_kv, kv), b.new_cache(3, d, n_kv, kv)
     need = b.tq_attn_decode_workspace(kc, vc, kv, n_q)
     assert need > b.STATIC_SCRATCH_BYTES
-    q = torch.zeros((n_q, 128), dtype=torch.float32, device="cuda")
-    out = torch.full((n_q, 128), 7.0, dtype=torch.float32, device="cuda")
+    q = torch.zeros((n_q, d), dtype=torch.float32, device="cuda")
+    out = torch.full((n_q, d), 7.0, dtype=torch.float32, device="cuda")
     with pytest.raises(b.TQError) as e:
         b.tq_attn_decode_static(kc, vc, kv, q, 1.0, out=out)
     assert e.value.status == b.TQ_ERR_WORKSPACE
