@@ -38,7 +38,7 @@ constexpr int kQRows = 64;
 constexpr int kKT = 64;              // keys per tile (two 32-cell pages)
 constexpr int kPage = 32;
 constexpr int kKsStride = kD + 8;    // halves per K row
-constexpr int kVtStride = kKT + 8;   // halves per V^T row
+constexpr int kVtStride = kKT + 4;   // halves per V^T row (136 B: the value products' row reads hit distinct banks)
 constexpr int kPartStride = kD + 4;  // o[128], m, l, pad
 constexpr float kPTop = 15.f;         // P = p * scale stays below 2^kPTop
 constexpr float kPSet = 9.f;          // a moved reference puts the tile's top at 2^kPSet
@@ -274,16 +274,22 @@ __global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
     if (kt + 1 < kt1) load_tile<kOff32>(a, g, kt + 1, tid, raw);
     __syncthreads();
 
-    f32x16_t s;
+    // the high and low query parts accumulate apart (two independent chains
+    // of products, so consecutive products do not wait on each other)
+    f32x16_t s, s_lo;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) s[rr] = 0.f;
+    for (int rr = 0; rr < 16; ++rr) {
+      s[rr] = 0.f;
+      s_lo[rr] = 0.f;
+    }
     const _Float16 *krow = ksm + (32 * khalf + ql) * kKsStride + 8 * hl;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const half8_t av = *reinterpret_cast<const half8_t *>(krow + 16 * t);
       s = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qhi[t], s, 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qlo[t], s, 0, 0, 0);
+      s_lo = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qlo[t], s_lo, 0, 0, 0);
     }
+    s += s_lo;
     const int64_t lim64 = pos - (kt * kKT + 32 * khalf);   // keys past lim are masked
     const int lim = lim64 > 64 ? 64 : (int)lim64;
     // m_run is a reference, not the running maximum: p = exp2(s - m_run)
@@ -350,17 +356,22 @@ __global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) o[dt][rr] *= alpha;
     }
+    // products in the order (key step, P part, d-tile): consecutive ones
+    // update different accumulators
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const _Float16 *vrow = vt + (32 * dt + ql) * kVtStride + 32 * khalf + 4 * hl;
+    for (int ga = 0; ga < 2; ++ga) {
+      half8_t av[4];
 #pragma unroll
-      for (int ga = 0; ga < 2; ++ga) {
-        const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vrow + 16 * ga);
-        const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vrow + 16 * ga + 8);
-        const half8_t av = __builtin_bit_cast(half8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, phi[ga], o[dt], 0, 0, 0);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, plo[ga], o[dt], 0, 0, 0);
+      for (int dt = 0; dt < 4; ++dt) {
+        const _Float16 *vrow = vt + (32 * dt + ql) * kVtStride + 32 * khalf + 4 * hl + 16 * ga;
+        const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vrow);
+        const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vrow + 8);
+        av[dt] = __builtin_bit_cast(half8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
       }
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[dt], phi[ga], o[dt], 0, 0, 0);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[dt], plo[ga], o[dt], 0, 0, 0);
     }
     __syncthreads();
   }
