@@ -5,8 +5,8 @@
 // whole cache as float16 temporaries on every step; the fast path decodes the
 // 3-bit K/V codes while loading each tile into shared memory.  Here each
 // 64-key tile is decoded through the LDS pair table straight into two LDS
-// tiles, K as [key][d] and V transposed as [d][key] (the layouts the matrix
-// cores read), as float16 values level * norm / 16: the group norm is folded
+// tiles, K and V both as [key][d], as float16 values level * norm / 16: the
+// group norm is folded
 // into the tile, so the products need no per-key scaling.  Such a value is at
 // most 2.8 * 65504 / 16 in magnitude, so it never overflows float16.  Nothing
 // is written back to global memory but the output.
@@ -18,7 +18,10 @@
 //
 // Products (v_mfma_f32_32x32x16_f16, fp32 accumulate):
 //   S^T[key][qrow] = K[key][:] . Qrot[qrow][:]   A = K tile, B = rotated query
-//   O^T[d][qrow]  += V^T[d][key] P^T[key][qrow]  A = V^T tile, B = P
+//   O^T[d][qrow]  += V^T[d][key] P^T[key][qrow]  A = V^T, B = P
+// The V^T operand comes from the [key][d] tile by transposing LDS reads
+// (ds_read_b64_tr_b16: within 16 lanes, lane j points at four consecutive d
+// of one key and lane i receives d0 + i of four consecutive keys).
 // A "qrow" is one (query row, query head) pair; the accumulator layout of S^T
 // (one query column per lane pair) is the B-operand layout P needs, so the
 // softmax never leaves registers.
@@ -52,13 +55,13 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kHalf = kThreads / 2;   // matrix threads; the rest decode
 constexpr int kQRows = 64;            // qrows per workgroup
 constexpr int kKT = 64;               // keys per tile
-constexpr int kVtStride = kKT + 4;    // halves per V^T row (136 B: conflict-free both ways)
 // key-half merge: per qrow half [d-tile][4 regs][64 lanes][4], d-tile
 // stride padded by 16 floats so the reads of four d-tiles hit distinct banks
 constexpr int kEDt = 16 * 64 + 16;
@@ -70,19 +73,21 @@ struct Dims {
   static_assert(KD == 128 || KD == 256, "head_dim 128 or 256");
   static constexpr int NG = KD / 128;              // groups per key
   static constexpr int KsStride = KD + 8;          // halves per K row and per query row
+  // halves per V row: 16 B of padding puts the four rows of a transposing
+  // read's lane group 32 B apart in the banks
+  static constexpr int VsStride = KD + 16;
   static constexpr int KsHalves = kKT * KsStride;
-  static constexpr int VtHalves = KD * kVtStride;
+  static constexpr int VsHalves = kKT * VsStride;
   static constexpr int QsHalves = kQRows * KsStride;
-  static constexpr int TileHalves = KsHalves + VtHalves + QsHalves;
+  static constexpr int TileHalves = KsHalves + VsHalves + QsHalves;
   static constexpr int NS = KD / 16;               // products per score tile
   static constexpr int ND = KD / 32;               // 32-row d-tiles of the output
   static constexpr int EK = KD / 4;                // K elements per decode thread (one key)
-  static constexpr int EV = KD / 16;               // V elements per key per decode thread
   static constexpr int EQ = KD / 4;                // query elements per matrix thread
   static constexpr int EE = KD / 8;                // output elements per thread
   static constexpr int EWave = ND * kEDt;          // merge floats per qrow half
   static_assert(2 * EWave * 4 <= TileHalves * 2, "merge buffer must fit in the tile buffers");
-  static_assert(KsHalves <= VtHalves, "K tile 0 is staged in the V^T buffer");
+  static_assert(KsHalves <= VsHalves, "K tile 0 is staged in the V buffer");
 };
 
 // 32 sign bits of a group starting at element 32w (w = 0..3).
@@ -139,18 +144,12 @@ __device__ __forceinline__ uint32_t norm_pair(uint16_t h) {
   return b | (b << 16);
 }
 
-// Codes of one key tile for a decode thread dt (0..255).  K: key dt & 63,
-// elements EK q .. EK q + EK - 1 with q = dt >> 6 (its decode wave); V: keys
-// 4(dt & 15) + i, elements EV(dt >> 4) .. EV(dt >> 4) + EV - 1.
+// Codes of one key tile (K or V) for a decode thread dt (0..255): key
+// dt & 63, elements EK q .. EK q + EK - 1 with q = dt >> 6 (its decode wave).
 template <int B, int KD>
 struct KRaw {
   uint32_t c[KD * B / 128];
   uint16_t n;
-};
-template <int B>
-struct VRaw {
-  uint32_t c[4][2];
-  uint16_t n[4];
 };
 
 struct Args {
@@ -184,11 +183,12 @@ struct HeadPtrs {
 // valid rows, and their scores are masked).  A key's codes are its groups'
 // codes back to back, so element e of the key starts at bit e * B.
 template <int B, int KD>
-__device__ __forceinline__ void load_k(const HeadPtrs &h, int last, int kt, int dt, KRaw<B, KD> &r) {
+__device__ __forceinline__ void load_row(const uint8_t *codes, const uint16_t *norms, int last, int kt, int dt,
+                                         KRaw<B, KD> &r) {
   using D = Dims<KD>;
   const int q = dt >> 6;
   const uint32_t key = (uint32_t)min(kt * kKT + (dt & 63), last);
-  const uint8_t *src = h.kc + key * (16u * B * D::NG) + (D::EK * B / 8) * q;
+  const uint8_t *src = codes + key * (16u * B * D::NG) + (D::EK * B / 8) * q;
   if constexpr (KD == 256) {
 #pragma unroll
     for (int i = 0; i < B; ++i) {
@@ -200,99 +200,38 @@ __device__ __forceinline__ void load_k(const HeadPtrs &h, int last, int kt, int 
 #pragma unroll
     for (int i = 0; i < B; ++i) r.c[i] = reinterpret_cast<const uint32_t *>(src)[i];
   }
-  r.n = h.kn[key * (uint32_t)D::NG + (D::EK * q) / 128];
+  r.n = norms[key * (uint32_t)D::NG + (D::EK * q) / 128];
 }
 
+// Rows of one tile (K or V): EK elements of one key, every pair-table read
+// first (held in h), then written as 16-byte stores at row stride `stride`.
 template <int B, int KD>
-__device__ __forceinline__ void load_v(const HeadPtrs &h, int last, int kt, int dt, VRaw<B> &r) {
-  using D = Dims<KD>;
-  constexpr int kParts = 128 / D::EV;                 // thread parts per group
-  // a part spans two code words unless its bits always fit in one
-  constexpr bool kTwo = (B == 3) || (D::EV * B > 32);
-  // the two words of every part lie inside its group: one 8-byte load
-  constexpr bool kPair = kTwo && ((D::EV * B * (kParts - 1)) >> 5) + 1 <= 4 * B - 1;
-  const int db = dt >> 4, grp = db / kParts, m = db % kParts;
-  const int w0 = (D::EV * B * m) >> 5;
-  const int w1 = min(w0 + 1, 4 * B - 1);             // stays inside the group
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t key = (uint32_t)min(kt * kKT + 4 * (dt & 15) + i, last);
-    const uint32_t *row = reinterpret_cast<const uint32_t *>(h.vc + key * (16u * B * D::NG) + 16 * B * grp);
-    if constexpr (kPair) {
-      u32x2_t w;
-      __builtin_memcpy(&w, row + w0, sizeof(w));   // 4-byte aligned
-      r.c[i][0] = w.x;
-      r.c[i][1] = w.y;
-    } else {
-      r.c[i][0] = row[w0];
-      r.c[i][1] = kTwo ? row[w1] : 0u;
-    }
-    r.n[i] = h.vn[key * (uint32_t)D::NG + grp];
-  }
-}
-
-// K part: EK elements of one key -> its K row part, every pair-table read
-// first, then 16-byte writes.
-template <int B, int KD>
-__device__ __forceinline__ void store_k(const KRaw<B, KD> &r, int dt, const uint32_t *tab, _Float16 *ks) {
+__device__ __forceinline__ void lookup_row(const KRaw<B, KD> &r, const uint32_t *tab,
+                                           uint32_t (&h)[Dims<KD>::EK / 2]) {
   using D = Dims<KD>;
   const uint32_t n2 = norm_pair(r.n);
-  uint32_t h[D::EK / 2];
 #pragma unroll
   for (int j = 0; j < D::EK / 2; ++j) h[j] = pair_scaled<B>(tab, bits_at(r.c, 2 * B * j, 2 * B), n2);
-  u32x4_t *dst = reinterpret_cast<u32x4_t *>(ks + (dt & 63) * D::KsStride + D::EK * (dt >> 6));
+}
+
+template <int KD>
+__device__ __forceinline__ void write_row(const uint32_t (&h)[Dims<KD>::EK / 2], int dt, _Float16 *buf, int stride) {
+  using D = Dims<KD>;
+  u32x4_t *dst = reinterpret_cast<u32x4_t *>(buf + (dt & 63) * stride + D::EK * (dt >> 6));
 #pragma unroll
   for (int v = 0; v < D::EK / 8; ++v) dst[v] = u32x4_t{h[4 * v], h[4 * v + 1], h[4 * v + 2], h[4 * v + 3]};
 }
 
-// V part, transposed: 4 keys x EV elements -> V^T rows d = EV db + j, four
-// keys per 8-byte write.  Looked up into w (held until the V buffer is
-// free), written by write_v.
 template <int B, int KD>
-__device__ __forceinline__ void lookup_v(const VRaw<B> &r, int dt, const uint32_t *tab,
-                                         uint32_t (&w)[KD / 32][4]) {
-  using D = Dims<KD>;
-  const int m = (dt >> 4) % (128 / D::EV);
-  const int sh = (D::EV * B * m) & 31;
-  // parts of a whole number of words start on a word boundary
-  constexpr bool kAligned = (D::EV * B) % 32 == 0;
-  uint32_t run[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (kAligned) {
-      run[i][0] = r.c[i][0];
-      run[i][1] = r.c[i][1];
-    } else {
-      run[i][0] = __builtin_amdgcn_alignbit(r.c[i][1], r.c[i][0], sh);
-      run[i][1] = sh ? (r.c[i][1] >> sh) : r.c[i][1];
-    }
-  }
-  uint32_t n2[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) n2[i] = norm_pair(r.n[i]);
-  uint32_t prs[D::EV / 2][4];
-#pragma unroll
-  for (int u = 0; u < D::EV / 2; ++u)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) prs[u][i] = pair_scaled<B>(tab, bits_at(run[i], 2 * B * u, 2 * B), n2[i]);
-#pragma unroll
-  for (int u = 0; u < D::EV / 2; ++u) {
-    w[u][0] = __builtin_amdgcn_perm(prs[u][1], prs[u][0], 0x05040100u);
-    w[u][1] = __builtin_amdgcn_perm(prs[u][3], prs[u][2], 0x05040100u);
-    w[u][2] = __builtin_amdgcn_perm(prs[u][1], prs[u][0], 0x07060302u);
-    w[u][3] = __builtin_amdgcn_perm(prs[u][3], prs[u][2], 0x07060302u);
-  }
+__device__ __forceinline__ void store_k(const KRaw<B, KD> &r, int dt, const uint32_t *tab, _Float16 *ks) {
+  uint32_t h[Dims<KD>::EK / 2];
+  lookup_row<B, KD>(r, tab, h);
+  write_row<KD>(h, dt, ks, Dims<KD>::KsStride);
 }
 
-template <int KD>
-__device__ __forceinline__ void write_v(const uint32_t (&w)[KD / 32][4], int dt, _Float16 *vt) {
-  constexpr int EV = Dims<KD>::EV;
-  _Float16 *base = vt + (EV * (dt >> 4)) * kVtStride + 4 * (dt & 15);
-#pragma unroll
-  for (int u = 0; u < EV / 2; ++u) {
-    *reinterpret_cast<u32x2_t *>(base + (2 * u) * kVtStride) = u32x2_t{w[u][0], w[u][1]};
-    *reinterpret_cast<u32x2_t *>(base + (2 * u + 1) * kVtStride) = u32x2_t{w[u][2], w[u][3]};
-  }
+// Four 16-bit values by a transposing LDS read (see the header).
+__device__ __forceinline__ s16x4_t read_tr16(const _Float16 *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t *)p);
 }
 
 // S^T of this wave's 32 keys x 32 qrows over all KD dimensions.
@@ -341,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
   const int64_t head_base = (int64_t)g * a.n_cells;
   _Float16 *kbuf = tiles;
   _Float16 *vbuf = tiles + D::KsHalves;
-  _Float16 *qbuf = vbuf + D::VtHalves;
+  _Float16 *qbuf = vbuf + D::VsHalves;
   float *ebuf = reinterpret_cast<float *>(tiles);
   const uint32_t *tab = ptab + lane % PfTable<B>::C;   // this lane's pair-table copy
 
@@ -443,9 +382,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
       const int64_t pos = lmin(a.q_pos0 + r, a.kv_len - 1);   // last key this column sees
       const _Float16 *qrow_p = qbuf + qrow * D::KsStride + 8 * hl;
       const int koff = (32 * khalf + ql) * D::KsStride + 8 * hl;
-      __syncthreads();   // query rows, K tiles 0 (in the V^T buffer) and 1 ready
+      __syncthreads();   // query rows, K tiles 0 (in the V buffer) and 1 ready
       f32x16_t sa = scores<KD>(vbuf + koff, qrow_p), sb;
-      __syncthreads();   // K tile 0 read: the V^T buffer may take V tile 0
+      __syncthreads();   // K tile 0 read: the V buffer may take V tile 0
 
       constexpr int ND = D::ND, NS = D::NS;
       f32x16_t o[ND];
@@ -544,13 +483,19 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
         // phase B: O^T += V^T P^T; k-slot (hl, i) of step ga <-> key
         // 16ga + 8(i>>2) + 4hl + (i&3).  Products in the order (ga, dt), so
         // no two consecutive ones share an accumulator; V^T operands three
-        // products ahead.
-        const _Float16 *vt = vbuf + ql * kVtStride + 32 * khalf + 4 * hl;
+        // products ahead.  An operand is two transposing reads of the
+        // [key][d] tile: lane j of each 16-lane group points at d 16 (g & 1)
+        // + 4 (j & 3) .. + 3 of key 4 hl + (j >> 2) (g = lane >> 4), so lane
+        // i of the group receives d 16 (g & 1) + i, that is ql, of the four
+        // keys of its k-slots 4r .. 4r + 3
+        const int trg = lane >> 4, trj = lane & 15;
+        const _Float16 *vtr =
+            vbuf + (32 * khalf + 4 * hl + (trj >> 2)) * D::VsStride + 16 * (trg & 1) + 4 * (trj & 3);
         auto vop = [&](int idx) {
-          const _Float16 *vr = vt + 32 * (idx % ND) * kVtStride + 16 * (idx / ND);
-          const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vr);
-          const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vr + 8);
-          return __builtin_bit_cast(half8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+          const _Float16 *vr = vtr + 16 * (idx / ND) * D::VsStride + 32 * (idx % ND);
+          const s16x4_t lo = read_tr16(vr);                      // keys 16 ga + 4 hl + 0..3
+          const s16x4_t hi = read_tr16(vr + 8 * D::VsStride);    // keys 16 ga + 8 + 4 hl + 0..3
+          return __builtin_bit_cast(half8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         };
         half8_t va[4];
 #pragma unroll
@@ -630,33 +575,32 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
       // previous contents are still to be used: with one set, the compiler
       // issued each load into fresh registers and copied them back at the
       // end of the phase, which waited for the load there
-      KRaw<B, KD> kra, krb;
-      VRaw<B> vra, vrb;
-      uint32_t vw[KD / 32][4];
-      load_k<B, KD>(hp, last, kt0, dt, kra);
-      load_k<B, KD>(hp, last, min(kt0 + 1, kt1 - 1), dt, krb);
-      load_v<B, KD>(hp, last, kt0, dt, vra);
+      KRaw<B, KD> kra, krb, vra, vrb;
+      uint32_t vw[D::EK / 2];
+      load_row<B, KD>(hp.kc, hp.kn, last, kt0, dt, kra);
+      load_row<B, KD>(hp.kc, hp.kn, last, min(kt0 + 1, kt1 - 1), dt, krb);
+      load_row<B, KD>(hp.vc, hp.vn, last, kt0, dt, vra);
       store_k<B, KD>(kra, dt, tab, vbuf);   // K tile 0 goes where V tile 0 will
       store_k<B, KD>(krb, dt, tab, kbuf);
-      lookup_v<B, KD>(vra, dt, tab, vw);
+      lookup_row<B, KD>(vra, tab, vw);
       // loads are unconditional (tile index clamped): a conditional load
       // would merge into the loop-carried registers through copies that wait
       // for the data
-      load_k<B, KD>(hp, last, min(kt0 + 2, kt1 - 1), dt, kra);
-      load_v<B, KD>(hp, last, min(kt0 + 1, kt1 - 1), dt, vra);
-      __syncthreads();   // query rows, K tiles 0 (in the V^T buffer) and 1 ready
-      __syncthreads();   // K tile 0 read: the V^T buffer may take V tile 0
+      load_row<B, KD>(hp.kc, hp.kn, last, min(kt0 + 2, kt1 - 1), dt, kra);
+      load_row<B, KD>(hp.vc, hp.vn, last, min(kt0 + 1, kt1 - 1), dt, vra);
+      __syncthreads();   // query rows, K tiles 0 (in the V buffer) and 1 ready
+      __syncthreads();   // K tile 0 read: the V buffer may take V tile 0
       // one tile: vc holds V tile kt+1, kc K tile kt+2; vn and kn receive
       // V tile kt+2 and K tile kt+3
-      auto tile = [&](int kt, VRaw<B> &vc, VRaw<B> &vn, KRaw<B, KD> &kc, KRaw<B, KD> &kn) {
+      auto tile = [&](int kt, KRaw<B, KD> &vc, KRaw<B, KD> &vn, KRaw<B, KD> &kc, KRaw<B, KD> &kn) {
         // phase A: V tile kt into the buffer, look up V tile kt+1
-        write_v<KD>(vw, dt, vbuf);
-        lookup_v<B, KD>(vc, dt, tab, vw);   // past the end: never written
-        load_v<B, KD>(hp, last, min(kt + 2, kt1 - 1), dt, vn);
+        write_row<KD>(vw, dt, vbuf, D::VsStride);
+        lookup_row<B, KD>(vc, tab, vw);   // past the end: never written
+        load_row<B, KD>(hp.vc, hp.vn, last, min(kt + 2, kt1 - 1), dt, vn);
         __syncthreads();   // V tile kt written; K tile kt+1 read
         // phase B: K tile kt+2 into the (now free) K buffer
         if (kt + 2 < kt1) store_k<B, KD>(kc, dt, tab, kbuf);
-        load_k<B, KD>(hp, last, min(kt + 3, kt1 - 1), dt, kn);
+        load_row<B, KD>(hp.kc, hp.kn, last, min(kt + 3, kt1 - 1), dt, kn);
         __syncthreads();   // V tile kt consumed; K tile kt+2 written
       };
       for (int kt = kt0; kt < kt1; kt += 2) {
