@@ -88,6 +88,7 @@ struct Dims {
   static constexpr int EWave = ND * kEDt;          // merge floats per qrow half
   static_assert(2 * EWave * 4 <= TileHalves * 2, "merge buffer must fit in the tile buffers");
   static_assert(KsHalves <= VsHalves, "K tile 0 is staged in the V buffer");
+  static_assert(kQRows * (KD + 4) * 4 <= TileHalves * 2, "the output staging must fit in the tile buffers");
 };
 
 // 32 sign bits of a group starting at element 32w (w = 0..3).
@@ -654,12 +655,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
 #pragma unroll
         for (int e = 0; e < EE; ++e) x[e] = bfly_lane<4>(x[e], (j & 4) != 0);
       }
-      const int hq = c / a.bq;
-      const int64_t r = row0 + c % a.bq;
-      if (r < a.n_rows && c < a.n_live) {
+      // the finished rows go through LDS ([qrow][KD + 4] floats over the
+      // tile buffers) so that each store instruction writes whole output
+      // rows: stored straight from this layout, an instruction covered 16
+      // rows in 16-byte pieces 128 bytes apart (measured: the output stores
+      // cost 10 us of a 2048-row call)
+      __syncthreads();   // every thread has read its part of the merge buffer
+      constexpr int SS = KD + 4;   // staging row stride (floats)
+      float *stg = reinterpret_cast<float *>(tiles);
+      {
         uint32_t sw = sign_word32((EE * j) >> 5) >> ((EE * j) & 31);
         asm volatile("" : "+v"(sw));   // formed here, not hoisted and spilled
-        float *orow = a.out + (r * a.n_q + g * a.n_rep + hq) * KD + d0;
+        float4 *dst = reinterpret_cast<float4 *>(stg + c * SS + d0);
 #pragma unroll
         for (int v = 0; v < EE / 4; ++v) {
           float4 f;
@@ -667,7 +674,19 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
           f.y = flip_sign(x[4 * v + 1], (sw >> (4 * v + 1)) & 1u);
           f.z = flip_sign(x[4 * v + 2], (sw >> (4 * v + 2)) & 1u);
           f.w = flip_sign(x[4 * v + 3], (sw >> (4 * v + 3)) & 1u);
-          reinterpret_cast<float4 *>(orow)[v] = f;
+          dst[v] = f;
+        }
+      }
+      __syncthreads();   // staged rows complete
+      // wave w stores qrows 8w .. 8w + 7, RPI rows per instruction
+      constexpr int RPI = 256 / KD, LPR = 64 / RPI;
+#pragma unroll
+      for (int i = 0; i < 8 / RPI; ++i) {
+        const int cc = 8 * wave + RPI * i + lane / LPR;
+        const int64_t rr = row0 + cc % a.bq;
+        if (rr < a.n_rows && cc < a.n_live) {
+          const float4 f = *reinterpret_cast<const float4 *>(stg + cc * SS + 4 * (lane % LPR));
+          reinterpret_cast<float4 *>(a.out + (rr * a.n_q + g * a.n_rep + cc / a.bq) * KD)[lane % LPR] = f;
         }
       }
     }
