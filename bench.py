@@ -41,14 +41,14 @@ FP32_PEAK_TFLOPS = 157.3
 # `rocprofv3 --pmc` passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) over
 # `bench.py --no-cpu-baseline --only decode,copy --steps 2 --warmup 1`, each
 # scaled by what the same counter reads for the 256 MiB device copy of that
-# run (FETCH_SIZE reads 131088.8 KiB for 262144 KiB copied: x1.99974;
+# run (FETCH_SIZE reads 131087.6 KiB for 262144 KiB copied: x1.99976;
 # WRITE_SIZE reads 262144 KiB: x1.0).  Valid only for the decode sources it
 # was taken on (sha256 of tq_decode.hip + tq_common.h); otherwise traffic is
 # reported as null.
-DECODE_TRAFFIC = {"sources_sha256": "068e8819bd51167a8ee7de33d860a2099afea848467fe68ec48d15aabebe48d0",
-                  "fetch_kib": {"decode_fused_kernel": 6536.8, "decode_merge_kernel": 568.5},
+DECODE_TRAFFIC = {"sources_sha256": "4e0d2c8bdc94ac02d678b0fb369b296f046e2d56a7f6ec8a5c2801b50c02a3c4",
+                  "fetch_kib": {"decode_fused_kernel": 6542.7, "decode_merge_kernel": 568.5},
                   "write_kib": {"decode_fused_kernel": 1088.0, "decode_merge_kernel": 16.0},
-                  "fetch_scale": 1.99974, "write_scale": 1.0}
+                  "fetch_scale": 1.99976, "write_scale": 1.0}
 
 
 def decode_traffic_bytes():
