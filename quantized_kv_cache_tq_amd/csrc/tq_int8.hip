@@ -14,10 +14,12 @@
 // The output depends only on the logical key order: physical page placement
 // changes which bytes are read, never the arithmetic.
 //
-// Workgroup: 64 qrows (64/n_rep queries x n_rep heads of one kv head), four
-// waves = 2 qrow halves x 2 key halves of each tile, merged at the end.  For
-// few queries the key range is split over workgroups and merged by a second
-// kernel.
+// Workgroup: 128 qrows (128/n_rep queries x n_rep heads of one kv head),
+// eight waves = 4 qrow quarters x 2 key halves of each tile, merged at the
+// end.  Each key tile is gathered and converted once for all 128 qrows (with
+// 64 qrows per workgroup the conversion and the gather addressing were a
+// quarter of the loop's vector instructions).  For few queries the key range
+// is split over workgroups and merged by a second kernel.
 #include "tq_common.h"
 #include "tq_launch.h"
 
@@ -31,10 +33,11 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+constexpr int kQBlocks = 4;              // 32-qrow blocks per workgroup
+constexpr int kWaves = 2 * kQBlocks;     // x 2 key halves
 constexpr int kThreads = 64 * kWaves;
 constexpr int kD = 128;
-constexpr int kQRows = 64;
+constexpr int kQRows = 32 * kQBlocks;
 constexpr int kKT = 64;              // keys per tile (two 32-cell pages)
 constexpr int kPage = 32;
 constexpr int kKsStride = kD + 8;    // halves per K row
@@ -73,10 +76,10 @@ __device__ __forceinline__ float half_to_float(uint16_t h) {
 }
 
 struct TileRaw {
-  u32x4_t k[2];       // K: key t>>2, bytes 32*(t&3) .. +31
-  uint32_t v[4][2];   // V: keys 4*(t&15)+i, bytes 8*(t>>4) .. +7
+  u32x4_t k;          // K: key t>>3, bytes 16*(t&7) .. +15
+  uint32_t v[2][2];   // V: keys 2*(t&31)+i, bytes 8*(t>>5) .. +7
   uint16_t scl;       // scale: t < 64 -> K of key t, 64 <= t < 128 -> V of key t-64
-  bool page_ok;       // this thread's V/K keys' pages exist
+  bool page_ok;       // this thread's scale key's page exists
 };
 
 // The two pages of key tile kt (wave-uniform, so the page-table entries are
@@ -125,25 +128,23 @@ __device__ __forceinline__ void load_tile(const Args &a, int g, int64_t kt, int 
   const TilePages t = tile_pages(a, kt);
   bool ok;
   {
-    const int64_t e = key_row<kOff32>(a, t, g, tid >> 2, ok);
-    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(a.k + row_bytes<kOff32>(e) + 32 * (tid & 3));
-    r.k[0] = src[0];
-    r.k[1] = src[1];
+    const int64_t e = key_row<kOff32>(a, t, g, tid >> 3, ok);
+    r.k = *reinterpret_cast<const u32x4_t *>(a.k + row_bytes<kOff32>(e) + 16 * (tid & 7));
   }
   {
-    const int db = tid >> 4;
+    const int db = tid >> 5;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t e = key_row<kOff32>(a, t, g, 4 * (tid & 15) + i, ok);
+    for (int i = 0; i < 2; ++i) {
+      const int64_t e = key_row<kOff32>(a, t, g, 2 * (tid & 31) + i, ok);
       const u32x2_t w = *reinterpret_cast<const u32x2_t *>(a.v + row_bytes<kOff32>(e) + 8 * db);
       r.v[i][0] = w.x;
       r.v[i][1] = w.y;
     }
   }
-  {
+  if (tid < 2 * kKT) {
     const int64_t e = key_row<kOff32>(a, t, g, tid & 63, ok);
     r.page_ok = ok;
-    r.scl = (tid < 64) ? a.ks[e] : a.vs[e];
+    r.scl = (tid < kKT) ? a.ks[e] : a.vs[e];
   }
 }
 
@@ -151,31 +152,28 @@ __device__ __forceinline__ void store_tile(const Args &a, int64_t kt, int tid, c
                                            _Float16 *ksm, _Float16 *vt, float *sk, float *sv,
                                            float *ve, int *kval) {
   {
-    // 32 K bytes -> 32 halves; byte pairs (2m, 2m+1) of dword m/2
-    uint32_t h[16];
+    // 16 K bytes -> 16 halves; byte pairs (2m, 2m+1) of dword m/2
+    uint32_t h[8];
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t x = r.k[c][w];
-        h[8 * c + 2 * w] = bytes_to_half2(__builtin_amdgcn_perm(0u, x, 0x0c010c00u));
-        h[8 * c + 2 * w + 1] = bytes_to_half2(__builtin_amdgcn_perm(0u, x, 0x0c030c02u));
-      }
-    u32x4_t *dst = reinterpret_cast<u32x4_t *>(ksm + (tid >> 2) * kKsStride + 32 * (tid & 3));
-#pragma unroll
-    for (int v = 0; v < 4; ++v) dst[v] = u32x4_t{h[4 * v], h[4 * v + 1], h[4 * v + 2], h[4 * v + 3]};
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t x = r.k[w];
+      h[2 * w] = bytes_to_half2(__builtin_amdgcn_perm(0u, x, 0x0c010c00u));
+      h[2 * w + 1] = bytes_to_half2(__builtin_amdgcn_perm(0u, x, 0x0c030c02u));
+    }
+    u32x4_t *dst = reinterpret_cast<u32x4_t *>(ksm + (tid >> 3) * kKsStride + 16 * (tid & 7));
+    dst[0] = u32x4_t{h[0], h[1], h[2], h[3]};
+    dst[1] = u32x4_t{h[4], h[5], h[6], h[7]};
   }
   {
-    // 4 keys x 8 d -> V^T rows d = 8*db + e: (key0, key1) and (key2, key3) pairs
-    const int db = tid >> 4;
-    _Float16 *base = vt + (8 * db) * kVtStride + 4 * (tid & 15);
+    // 2 keys x 8 d -> V^T rows d = 8*db + e: one (key0, key1) pair each
+    const int db = tid >> 5;
+    _Float16 *base = vt + (8 * db) * kVtStride + 2 * (tid & 31);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int w = e >> 2, b = e & 3;
       const uint32_t sel = 0x0c000c00u | ((uint32_t)(4 + b) << 16) | (uint32_t)b;
-      const uint32_t p01 = bytes_to_half2(__builtin_amdgcn_perm(r.v[1][w], r.v[0][w], sel));
-      const uint32_t p23 = bytes_to_half2(__builtin_amdgcn_perm(r.v[3][w], r.v[2][w], sel));
-      *reinterpret_cast<u32x2_t *>(base + e * kVtStride) = u32x2_t{p01, p23};
+      *reinterpret_cast<uint32_t *>(base + e * kVtStride) =
+          bytes_to_half2(__builtin_amdgcn_perm(r.v[1][w], r.v[0][w], sel));
     }
   }
   if (tid < 2 * kKT) {
@@ -199,21 +197,22 @@ __device__ __forceinline__ void split_hl(float x, _Float16 &hi, _Float16 &lo) {
 
 template <bool kOff32>
 __global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
-  constexpr int kArenaHalves = kKT * kKsStride + kD * kVtStride;
-  static_assert(kArenaHalves * 2 >= 2 * 4 * 16 * 64 * 4, "merge buffer must fit");
+  constexpr int kTileHalves = kKT * kKsStride + kD * kVtStride;
+  constexpr int kMergeHalves = kQBlocks * 4 * 16 * 64 * 2;   // o of the key-half-1 waves, float32
+  constexpr int kArenaHalves = kTileHalves > kMergeHalves ? kTileHalves : kMergeHalves;
   __shared__ __align__(16) _Float16 arena[kArenaHalves];
   __shared__ __align__(16) float sk[kKT], sv[kKT];
   __shared__ __align__(16) float ve[kKT];   // binary exponent of each V scale
-  __shared__ float mstat[2][32], lstat[2][32];
+  __shared__ float mstat[kQBlocks][32], lstat[kQBlocks][32];
   __shared__ int kval[kKT];   // key exists (in context, page in range)
   _Float16 *ksm = arena;
   _Float16 *vt = arena + kKT * kKsStride;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int qhalf = wave & 1, khalf = wave >> 1;
+  const int qblk = wave & (kQBlocks - 1), khalf = wave / kQBlocks;
   const int qt = blockIdx.x, split = blockIdx.y, g = blockIdx.z;
   const int ql = lane & 31, hl = lane >> 5;
-  const int qrow = 32 * qhalf + ql;
+  const int qrow = 32 * qblk + ql;
   const int head_local = qrow / a.bq, row_local = qrow % a.bq;
   const int head = g * a.n_rep + head_local;
   const int64_t q0 = (int64_t)qt * a.bq;
@@ -383,15 +382,15 @@ __global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) mbuf[((qhalf * 4 + dt) * 16 + rr) * 64 + lane] = o[dt][rr];
+      for (int rr = 0; rr < 16; ++rr) mbuf[((qblk * 4 + dt) * 16 + rr) * 64 + lane] = o[dt][rr];
     if (hl == 0) {
-      mstat[qhalf][ql] = m_run;
-      lstat[qhalf][ql] = l_run;
+      mstat[qblk][ql] = m_run;
+      lstat[qblk][ql] = l_run;
     }
   }
   __syncthreads();
   if (khalf != 0) return;
-  const float m2 = mstat[qhalf][ql], l2 = lstat[qhalf][ql];
+  const float m2 = mstat[qblk][ql], l2 = lstat[qblk][ql];
   const float M = fmaxf(m_run, m2);
   const float f1 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
   const float f2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
@@ -400,7 +399,7 @@ __global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr)
-      o[dt][rr] = o[dt][rr] * f1 + mbuf[((qhalf * 4 + dt) * 16 + rr) * 64 + lane] * f2;
+      o[dt][rr] = o[dt][rr] * f1 + mbuf[((qblk * 4 + dt) * 16 + rr) * 64 + lane] * f2;
   if (qi >= a.n_q) return;
   // O^T register rr of tile dt <-> d = 32dt + 8(rr/4) + 4hl + rr%4
   if (a.n_split == 1) {
@@ -466,10 +465,20 @@ hipError_t plan_int8(int64_t n_q, int32_t n_q_heads, int32_t n_kv_heads, int64_t
   if (q_tiles > 0x7fffffff) return hipErrorInvalidValue;
   p->n_q_tiles = (int)q_tiles;
   const int64_t max_tiles = ceil_div<int64_t>(ctx_len, i8::kKT);
-  int64_t n_split = 1;
+  // one workgroup fills a compute unit (two waves per SIMD): split the key
+  // range so that there is a workgroup for every compute unit, or, with more
+  // workgroups than compute units, until their last round is 85% full
   const int64_t wgs = q_tiles * n_kv_heads;
-  // two resident workgroups per compute unit: one computes while the other waits
-  if (wgs < 2LL * n_cu) n_split = ceil_div<int64_t>(2LL * n_cu, wgs);
+  int64_t n_split = 1;
+  if (wgs < n_cu) {
+    n_split = ceil_div<int64_t>(n_cu, wgs);
+  } else {
+    while (n_split < 16) {
+      const int64_t w = wgs * n_split, rounds = ceil_div<int64_t>(w, n_cu);
+      if (w * 100 >= rounds * n_cu * 85) break;
+      ++n_split;
+    }
+  }
   if (n_split > max_tiles) n_split = max_tiles;
   if (n_split > 65535) n_split = 65535;
   const int64_t tps = ceil_div<int64_t>(max_tiles, n_split);
