@@ -149,8 +149,8 @@ __device__ __forceinline__ void load_tile(const Args &a, int g, int64_t kt, int 
 }
 
 __device__ __forceinline__ void store_tile(const Args &a, int64_t kt, int tid, const TileRaw &r,
-                                           _Float16 *ksm, _Float16 *vt, float *sk, float *sv,
-                                           float *ve, int *kval) {
+                                           _Float16 *ksm, _Float16 *vt, float (*skq)[kKT], float *sv,
+                                           float *ve_max, int *kval, const int *qexp_s) {
   {
     // 16 K bytes -> 16 halves; byte pairs (2m, 2m+1) of dword m/2
     uint32_t h[8];
@@ -181,11 +181,21 @@ __device__ __forceinline__ void store_tile(const Args &a, int64_t kt, int tid, c
     const bool ok = j < a.ctx_len && r.page_ok;
     const float s = ok ? half_to_float(r.scl) : 0.f;
     if (tid < kKT) {
-      sk[tid] = s;
+      // the K scale times each row block's 2^-qexp (exact: a power of two)
+#pragma unroll
+      for (int q = 0; q < kQBlocks; ++q) skq[q][tid] = __builtin_amdgcn_ldexpf(s, -qexp_s[q]);
       kval[tid] = ok ? 1 : 0;
     } else {
       sv[tid - kKT] = s;
-      ve[tid - kKT] = (float)__builtin_amdgcn_frexp_expf(s);   // s < 2^ve
+      // the tile's largest binary exponent of a V scale (every s < 2^e)
+      float e = (float)__builtin_amdgcn_frexp_expf(s);
+      e = fmaxf(e, xor_lane<1>(e));
+      e = fmaxf(e, xor_lane<2>(e));
+      e = fmaxf(e, xor_lane<4>(e));
+      e = fmaxf(e, xor_lane<8>(e));
+      e = fmaxf(e, xor_lane<16>(e));
+      e = fmaxf(e, xor_lane<32>(e));
+      if (tid == kKT) *ve_max = e;
     }
   }
 }
@@ -201,8 +211,9 @@ __global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
   constexpr int kMergeHalves = kQBlocks * 4 * 16 * 64 * 2;   // o of the key-half-1 waves, float32
   constexpr int kArenaHalves = kTileHalves > kMergeHalves ? kTileHalves : kMergeHalves;
   __shared__ __align__(16) _Float16 arena[kArenaHalves];
-  __shared__ __align__(16) float sk[kKT], sv[kKT];
-  __shared__ __align__(16) float ve[kKT];   // binary exponent of each V scale
+  __shared__ __align__(16) float skq[kQBlocks][kKT], sv[kKT];
+  __shared__ float ve_max;                  // largest binary exponent of the tile's V scales
+  __shared__ int qexp_s[kQBlocks];
   __shared__ float mstat[kQBlocks][32], lstat[kQBlocks][32];
   __shared__ int kval[kKT];   // key exists (in context, page in range)
   _Float16 *ksm = arena;
@@ -226,9 +237,10 @@ __global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
   const int64_t pos = a.q_pos0 + qi_c;
 
   // query operand: d = 16t + 8hl + i, high and low float16 parts of
-  // q * qscale * 2^qexp, the power of two putting the row's largest element
-  // just under 2^14 (both parts clear of float16 overflow and subnormals);
-  // the scores are scaled back by 2^-qexp
+  // q * qscale * 2^qexp, the power of two putting the largest element of the
+  // wave's 32 rows just under 2^14 (no float16 overflow; the low parts keep
+  // an absolute error of at most 2^-25 of that scale); the K scales stored
+  // for this row block carry the 2^-qexp back
   half8_t qhi[8], qlo[8];
   int qexp;
   {
@@ -246,8 +258,14 @@ __global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
         amax = fmaxf(amax, fabsf(x[t][i]));
       }
     }
+    amax = fmaxf(amax, xor_lane<1>(amax));
+    amax = fmaxf(amax, xor_lane<2>(amax));
+    amax = fmaxf(amax, xor_lane<4>(amax));
+    amax = fmaxf(amax, xor_lane<8>(amax));
+    amax = fmaxf(amax, xor_lane<16>(amax));
     amax = fmaxf(amax, xor_lane<32>(amax));
     qexp = 14 - __builtin_amdgcn_frexp_expf(amax);   // amax * 2^qexp < 2^14
+    if (khalf == 0 && lane == 0) qexp_s[qblk] = qexp;
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
@@ -266,36 +284,34 @@ __global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
     for (int rr = 0; rr < 16; ++rr) o[dt][rr] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
+  __syncthreads();   // qexp_s
   TileRaw raw;
   if (kt0 < kt1) load_tile<kOff32>(a, g, kt0, tid, raw);
   for (int64_t kt = kt0; kt < kt1; ++kt) {
-    store_tile(a, kt, tid, raw, ksm, vt, sk, sv, ve, kval);
+    store_tile(a, kt, tid, raw, ksm, vt, skq, sv, &ve_max, kval, qexp_s);
     if (kt + 1 < kt1) load_tile<kOff32>(a, g, kt + 1, tid, raw);
     __syncthreads();
 
-    // the high and low query parts accumulate apart (two independent chains
-    // of products, so consecutive products do not wait on each other)
-    f32x16_t s, s_lo;
+    // one chain of products over the high and low query parts (two chains
+    // and their sum cost 16 more registers and vector additions per tile,
+    // which measured slower)
+    f32x16_t s;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      s[rr] = 0.f;
-      s_lo[rr] = 0.f;
-    }
+    for (int rr = 0; rr < 16; ++rr) s[rr] = 0.f;
     const _Float16 *krow = ksm + (32 * khalf + ql) * kKsStride + 8 * hl;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const half8_t av = *reinterpret_cast<const half8_t *>(krow + 16 * t);
       s = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qhi[t], s, 0, 0, 0);
-      s_lo = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qlo[t], s_lo, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qlo[t], s, 0, 0, 0);
     }
-    s += s_lo;
     const int64_t lim64 = pos - (kt * kKT + 32 * khalf);   // keys past lim are masked
     const int lim = lim64 > 64 ? 64 : (int)lim64;
     // m_run is a reference, not the running maximum: p = exp2(s - m_run)
     // and P = p * (V scale) goes to float16 as a high and a low part.  With
-    // e the binary exponent of a key's V scale, P < 2^(s + e - m_run); the
-    // reference moves only when some key would reach 2^kPTop, and then to put
-    // the tile's top at 2^kPSet.  So P never overflows, its parts stay clear
+    // e the largest binary exponent of the tile's V scales,
+    // P < 2^(s + e - m_run); the reference moves only when some key could
+    // reach 2^kPTop, and then to put the tile's bound at 2^kPSet.  So P never overflows, its parts stay clear
     // of float16 subnormals, and the accumulators are rescaled rarely.
     // Softmax does not depend on the reference.
     // a tile whose 64 keys all exist (in context, pages in range) and whose
@@ -309,16 +325,15 @@ __global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int k0 = 8 * g4 + 4 * hl;   // keys k0 .. k0+3 of the half <-> registers 4 g4 .. 4 g4 + 3
-        const float4 sk4 = *reinterpret_cast<const float4 *>(&sk[32 * khalf + k0]);
-        const float4 ve4 = *reinterpret_cast<const float4 *>(&ve[32 * khalf + k0]);
-        const float skv[4] = {sk4.x, sk4.y, sk4.z, sk4.w}, vev[4] = {ve4.x, ve4.y, ve4.z, ve4.w};
+        const float4 sk4 = *reinterpret_cast<const float4 *>(&skq[qblk][32 * khalf + k0]);
+        const float skv[4] = {sk4.x, sk4.y, sk4.z, sk4.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int rr = 4 * g4 + i, kk = k0 + i;
-          float v = __builtin_amdgcn_ldexpf(s[rr], -qexp) * skv[i];
+          float v = s[rr] * skv[i];
           if (kMask && (kk > lim || !kval[32 * khalf + kk])) v = -INFINITY;  // causal / no such key
           s[rr] = v;
-          tref = fmaxf(tref, v + vev[i]);
+          tref = fmaxf(tref, v);
         }
       }
     };
@@ -326,7 +341,7 @@ __global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
       scale_scores(std::false_type{});
     else
       scale_scores(std::true_type{});
-    tref = fmaxf(tref, xor_lane<32>(tref));
+    tref = fmaxf(tref, xor_lane<32>(tref)) + ve_max;
     const float m_new = tref > m_run + kPTop ? tref - kPSet : m_run;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
