@@ -4,8 +4,8 @@
 // K and V rows are scattered in memory, prefetching the next chunk while the
 // current one computes.  On CDNA4 the same walk becomes 64-key tiles (two
 // pages) gathered through the page table straight into LDS, converted to
-// float16 on the way (int8 is exact in float16), and multiplied on the matrix
-// cores:
+// float16 on the way (int8 is exact in float16; K and V both stored [key][d],
+// V read transposed for its product), and multiplied on the matrix cores:
 //   S^T[key][qrow] = K[key][:] . Q[qrow][:]      (then x k_scale[key])
 //   O^T[d][qrow]  += V^T[d][key] P^T[key][qrow]   (P already x v_scale[key])
 // The float32 query and P are each split into a high and a low float16 part
@@ -32,6 +32,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kQBlocks = 4;              // 32-qrow blocks per workgroup
 constexpr int kWaves = 2 * kQBlocks;     // x 2 key halves
@@ -41,7 +42,7 @@ constexpr int kQRows = 32 * kQBlocks;
 constexpr int kKT = 64;              // keys per tile (two 32-cell pages)
 constexpr int kPage = 32;
 constexpr int kKsStride = kD + 8;    // halves per K row
-constexpr int kVtStride = kKT + 4;   // halves per V^T row (136 B: the value products' row reads hit distinct banks)
+constexpr int kVsStride = kD + 16;   // halves per V row (288 B: a transposing read's four rows hit distinct banks)
 constexpr int kPartStride = kD + 4;  // o[128], m, l, pad
 constexpr float kPTop = 15.f;         // P = p * scale stays below 2^kPTop
 constexpr float kPSet = 9.f;          // a moved reference puts the tile's top at 2^kPSet
@@ -62,13 +63,28 @@ struct Args {
 
 __device__ __forceinline__ int64_t lmin(int64_t a, int64_t b) { return a < b ? a : b; }
 
-// float16 pair (x0, x1) of two signed bytes placed in the low bytes of the
-// two halves of w (high bytes zero): 0x6400 | (b ^ 0x80) is 1024 + b + 128,
-// exactly representable, so subtracting 1152 leaves b exactly.
-__device__ __forceinline__ uint32_t bytes_to_half2(uint32_t w) {
-  const half2_t h = __builtin_bit_cast(half2_t, w ^ 0x64806480u);
+// 16 signed bytes -> 16 float16 values, in order.  With every byte's top bit
+// flipped (b ^ 0x80 = b + 128 as an unsigned byte), the float16 bit pattern
+// 0x64 : (b ^ 0x80) is 1024 + b + 128, exact, so subtracting 1152 leaves b
+// exactly.  A byte permute places two flipped bytes under 0x64 high bytes.
+__device__ __forceinline__ void bytes16_to_halves(const u32x4_t &x, uint32_t (&h)[8]) {
   const half2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-  return __builtin_bit_cast(uint32_t, h - bias);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t y = x[w] ^ 0x80808080u;
+    const uint32_t p0 = __builtin_amdgcn_perm(0x64646464u, y, 0x04010400u);   // bytes 0, 1
+    const uint32_t p1 = __builtin_amdgcn_perm(0x64646464u, y, 0x04030402u);   // bytes 2, 3
+    h[2 * w] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p0) - bias);
+    h[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p1) - bias);
+  }
+}
+
+// Four 16-bit values by a transposing LDS read: within each 16-lane group,
+// lane j gives the address of four consecutive values of row j / 4 of a
+// 4 x 16 block (columns 4 (j % 4) .. + 3), and lane i receives column i of
+// the block's four rows.
+__device__ __forceinline__ s16x4_t read_tr16(const _Float16 *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t *)p);
 }
 
 __device__ __forceinline__ float half_to_float(uint16_t h) {
@@ -77,7 +93,7 @@ __device__ __forceinline__ float half_to_float(uint16_t h) {
 
 struct TileRaw {
   u32x4_t k;          // K: key t>>3, bytes 16*(t&7) .. +15
-  uint32_t v[2][2];   // V: keys 2*(t&31)+i, bytes 8*(t>>5) .. +7
+  u32x4_t v;          // V: key t>>3, bytes 16*(t&7) .. +15
   uint16_t scl;       // scale: t < 64 -> K of key t, 64 <= t < 128 -> V of key t-64
   bool page_ok;       // this thread's scale key's page exists
 };
@@ -132,14 +148,8 @@ __device__ __forceinline__ void load_tile(const Args &a, int g, int64_t kt, int 
     r.k = *reinterpret_cast<const u32x4_t *>(a.k + row_bytes<kOff32>(e) + 16 * (tid & 7));
   }
   {
-    const int db = tid >> 5;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t e = key_row<kOff32>(a, t, g, 2 * (tid & 31) + i, ok);
-      const u32x2_t w = *reinterpret_cast<const u32x2_t *>(a.v + row_bytes<kOff32>(e) + 8 * db);
-      r.v[i][0] = w.x;
-      r.v[i][1] = w.y;
-    }
+    const int64_t e = key_row<kOff32>(a, t, g, tid >> 3, ok);
+    r.v = *reinterpret_cast<const u32x4_t *>(a.v + row_bytes<kOff32>(e) + 16 * (tid & 7));
   }
   if (tid < 2 * kKT) {
     const int64_t e = key_row<kOff32>(a, t, g, tid & 63, ok);
@@ -151,30 +161,20 @@ __device__ __forceinline__ void load_tile(const Args &a, int g, int64_t kt, int 
 __device__ __forceinline__ void store_tile(const Args &a, int64_t kt, int tid, const TileRaw &r,
                                            _Float16 *ksm, _Float16 *vt, float (*skq)[kKT], float *sv,
                                            float *ve_max, int *kval, const int *qexp_s) {
+  // K and V rows alike: [key][d], 16 bytes -> 16 halves per thread
   {
-    // 16 K bytes -> 16 halves; byte pairs (2m, 2m+1) of dword m/2
     uint32_t h[8];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t x = r.k[w];
-      h[2 * w] = bytes_to_half2(__builtin_amdgcn_perm(0u, x, 0x0c010c00u));
-      h[2 * w + 1] = bytes_to_half2(__builtin_amdgcn_perm(0u, x, 0x0c030c02u));
-    }
+    bytes16_to_halves(r.k, h);
     u32x4_t *dst = reinterpret_cast<u32x4_t *>(ksm + (tid >> 3) * kKsStride + 16 * (tid & 7));
     dst[0] = u32x4_t{h[0], h[1], h[2], h[3]};
     dst[1] = u32x4_t{h[4], h[5], h[6], h[7]};
   }
   {
-    // 2 keys x 8 d -> V^T rows d = 8*db + e: one (key0, key1) pair each
-    const int db = tid >> 5;
-    _Float16 *base = vt + (8 * db) * kVtStride + 2 * (tid & 31);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 2, b = e & 3;
-      const uint32_t sel = 0x0c000c00u | ((uint32_t)(4 + b) << 16) | (uint32_t)b;
-      *reinterpret_cast<uint32_t *>(base + e * kVtStride) =
-          bytes_to_half2(__builtin_amdgcn_perm(r.v[1][w], r.v[0][w], sel));
-    }
+    uint32_t h[8];
+    bytes16_to_halves(r.v, h);
+    u32x4_t *dst = reinterpret_cast<u32x4_t *>(vt + (tid >> 3) * kVsStride + 16 * (tid & 7));
+    dst[0] = u32x4_t{h[0], h[1], h[2], h[3]};
+    dst[1] = u32x4_t{h[4], h[5], h[6], h[7]};
   }
   if (tid < 2 * kKT) {
     const int64_t j = kt * kKT + (tid & 63);
@@ -207,7 +207,7 @@ __device__ __forceinline__ void split_hl(float x, _Float16 &hi, _Float16 &lo) {
 
 template <bool kOff32>
 __global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
-  constexpr int kTileHalves = kKT * kKsStride + kD * kVtStride;
+  constexpr int kTileHalves = kKT * kKsStride + kKT * kVsStride;
   constexpr int kMergeHalves = kQBlocks * 4 * 16 * 64 * 2;   // o of the key-half-1 waves, float32
   constexpr int kArenaHalves = kTileHalves > kMergeHalves ? kTileHalves : kMergeHalves;
   __shared__ __align__(16) _Float16 arena[kArenaHalves];
@@ -371,16 +371,22 @@ __global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
       for (int rr = 0; rr < 16; ++rr) o[dt][rr] *= alpha;
     }
     // products in the order (key step, P part, d-tile): consecutive ones
-    // update different accumulators
+    // update different accumulators.  The V^T operand (d = 32 dt + ql, k-slots
+    // 8 hl + i <-> keys 16 ga + 8 (i >> 2) + 4 hl + (i & 3), as P's) is two
+    // transposing reads of the [key][d] tile: lane j of 16-lane group gq
+    // points at d 16 (gq & 1) + 4 (j & 3) of key 4 hl + (j >> 2), so lane i
+    // of the group receives d 16 (gq & 1) + i, that is ql, of four keys
+    const int gq = lane >> 4, tj = lane & 15;
+    const _Float16 *vtr = vt + (32 * khalf + 4 * hl + (tj >> 2)) * kVsStride + 16 * (gq & 1) + 4 * (tj & 3);
 #pragma unroll
     for (int ga = 0; ga < 2; ++ga) {
       half8_t av[4];
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const _Float16 *vrow = vt + (32 * dt + ql) * kVtStride + 32 * khalf + 4 * hl + 16 * ga;
-        const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vrow);
-        const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vrow + 8);
-        av[dt] = __builtin_bit_cast(half8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+        const _Float16 *vr = vtr + 16 * ga * kVsStride + 32 * dt;
+        const s16x4_t lo = read_tr16(vr);                    // keys 16 ga + 4 hl + 0..3
+        const s16x4_t hi = read_tr16(vr + 8 * kVsStride);    // keys 16 ga + 8 + 4 hl + 0..3
+        av[dt] = __builtin_bit_cast(half8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[dt], phi[ga], o[dt], 0, 0, 0);
