@@ -818,29 +818,41 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_fused_kernel(
     r.vn = vnorms[row0 + kk];
   };
 
-  Raw cur;
-  load(0, cur);
-  build_pair_table<B, kDecThreads>(ptab, tid);
   // rotate + split the query of pairs 2w, 2w+1 (waves 0-3): thread (qh, qj)
   // holds d = 4qj .. 4qj+3 of pair qh, which is the element chunk of quad
   // qj >> 3 and K-step qj & 7: it writes that chunk's high parts to lane
-  // 16 (qj >> 3) + qh and its low parts to lane 16 (qj >> 3) + 8 + qh
+  // 16 (qj >> 3) + qh and its low parts to lane 16 (qj >> 3) + 8 + qh.
+  // The query load is issued before the block's K/V loads: loads retire in
+  // order, so issued after them it could only be used once they had all
+  // arrived, and the rotation would wait for the whole block
+  const int qh = 2 * wave + (lane >> 5), qj = lane & 31;
+  u32x4_t qraw = {0u, 0u, 0u, 0u};   // the lane's 4 query values as loaded (bf16 pairs or fp32)
   if (wave < 4) {
-    const int qh = 2 * wave + (lane >> 5), qj = lane & 31;
     const int vq = p0 + imin(qh, n_vh - 1);
     const int vr = n_rows == 1 ? 0 : vq / n_rep;
     const int64_t qbase =
         (((int64_t)z * n_rows + vr) * n_q + (int64_t)g * n_rep + (vq - vr * n_rep)) * kGroup + 4 * qj;
-    float qv[4];
     if constexpr (QBF16) {
       const u32x2_t bw = *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint16_t *>(q) + qbase);
-      qv[0] = __uint_as_float(bw.x << 16);
-      qv[1] = __uint_as_float(bw.x & 0xffff0000u);
-      qv[2] = __uint_as_float(bw.y << 16);
-      qv[3] = __uint_as_float(bw.y & 0xffff0000u);
+      qraw.x = bw.x;
+      qraw.y = bw.y;
     } else {
-      const float4 f = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(q) + qbase);
-      qv[0] = f.x; qv[1] = f.y; qv[2] = f.z; qv[3] = f.w;
+      qraw = *reinterpret_cast<const u32x4_t *>(reinterpret_cast<const float *>(q) + qbase);
+    }
+  }
+  Raw cur;
+  load(0, cur);
+  build_pair_table<B, kDecThreads>(ptab, tid);
+  if (wave < 4) {
+    float qv[4];
+    if constexpr (QBF16) {
+      qv[0] = __uint_as_float(qraw.x << 16);
+      qv[1] = __uint_as_float(qraw.x & 0xffff0000u);
+      qv[2] = __uint_as_float(qraw.y << 16);
+      qv[3] = __uint_as_float(qraw.y & 0xffff0000u);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qv[i] = __uint_as_float(qraw[i]);
     }
     const uint32_t sn = sign_nibble(qj);
 #pragma unroll
