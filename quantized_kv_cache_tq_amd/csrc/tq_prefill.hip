@@ -73,9 +73,12 @@ struct Dims {
   static_assert(KD == 128 || KD == 256, "head_dim 128 or 256");
   static constexpr int NG = KD / 128;              // groups per key
   static constexpr int KsStride = KD + 8;          // halves per K row and per query row
-  // halves per V row: 16 B of padding puts the four rows of a transposing
-  // read's lane group 32 B apart in the banks
-  static constexpr int VsStride = KD + 16;
+  // halves per V row: 80 B of padding puts consecutive rows 20 banks apart.
+  // The decode waves' row writes (one row per lane, 16 rows served together)
+  // then hit distinct banks, and a transposing read's four rows overlap at
+  // most pairwise, as they did 8 banks apart (32 B of padding), where the
+  // writes conflicted pairwise too
+  static constexpr int VsStride = KD + 40;
   static constexpr int KsHalves = kKT * KsStride;
   static constexpr int VsHalves = kKT * VsStride;
   static constexpr int QsHalves = kQRows * KsStride;
