@@ -45,10 +45,10 @@ FP32_PEAK_TFLOPS = 157.3
 # WRITE_SIZE reads 262144 KiB: x1.0).  Valid only for the decode sources it
 # was taken on (sha256 of tq_decode.hip + tq_common.h); otherwise traffic is
 # reported as null.
-DECODE_TRAFFIC = {"sources_sha256": "4e0d2c8bdc94ac02d678b0fb369b296f046e2d56a7f6ec8a5c2801b50c02a3c4",
-                  "fetch_kib": {"decode_fused_kernel": 6542.7, "decode_merge_kernel": 568.5},
+DECODE_TRAFFIC = {"sources_sha256": "a385a3ba7f82192d9af3758843701d176bb05371c59bae3eb6854e7b9b20906d",
+                  "fetch_kib": {"decode_fused_kernel": 6541.6, "decode_merge_kernel": 568.5},
                   "write_kib": {"decode_fused_kernel": 1088.0, "decode_merge_kernel": 16.0},
-                  "fetch_scale": 1.99976, "write_scale": 1.0}
+                  "fetch_scale": 1.99974, "write_scale": 1.0}
 
 
 def decode_traffic_bytes():
