@@ -103,3 +103,17 @@ def test_large_scales_and_sharp_scores():
     d = inputs.int8_prompt(seed=11, ctx=2048, n_q=256, v_mult=1e5, k_mult=4.0)
     got, want = _gpu(d, 2048, 2048 - 256), _oracle(d, 2048, 2048 - 256)
     _check(got / 1e5, want / 1e5, "large scales")
+
+
+def test_query_rows_of_very_different_size():
+    """The query's power-of-two scale is shared by each 32-row block (4
+    queries x 8 heads share a block here): queries 1000x smaller and 30x
+    larger than unit size sit in the same blocks, so the small rows' low
+    float16 parts carry an absolute error bounded by the block's largest
+    row.  Their softmax still has to meet the same bar."""
+    d = inputs.int8_prompt(seed=12, ctx=2048, n_q=96)
+    q = d["q"].copy()
+    q[0::3] *= 1e-3
+    q[1::3] *= 30.0
+    d = dict(d, q=q)
+    _check(_gpu(d, 2048, 2048 - 96), _oracle(d, 2048, 2048 - 96), "mixed query magnitudes")
