@@ -357,8 +357,11 @@ __global__ __launch_bounds__(kThreads, 2) void int8_prompt_kernel(Args a) {
         const int rr = 4 * g4 + i;
         const float p = __builtin_amdgcn_exp2f(s[rr] - m_use);
         psum += p;
-        _Float16 h, l;
-        split_hl(p * svv[i], h, l);
+        // P = p * (V scale) split into float16 parts straight from the exact
+        // product: hi = RN(P), lo = RN(P - hi) (fused multiply-adds with a
+        // float16 result, no float32 rounding of P in between)
+        const _Float16 h = (_Float16)__builtin_fmaf(p, svv[i], 0.f);
+        const _Float16 l = (_Float16)__builtin_fmaf(p, svv[i], -(float)h);
         phi[rr >> 3][rr & 7] = h;
         plo[rr >> 3][rr & 7] = l;
       }
