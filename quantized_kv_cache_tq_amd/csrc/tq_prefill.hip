@@ -101,13 +101,6 @@ __device__ __forceinline__ uint32_t sign_word32(int w) {
 
 __device__ __forceinline__ int64_t lmin(int64_t a, int64_t b) { return a < b ? a : b; }
 
-// nbits-bit field at bit pos of dw (pos, nbits compile-time after unrolling).
-__device__ __forceinline__ uint32_t bits_at(const uint32_t *dw, int pos, int nbits) {
-  const int w = pos >> 5, sh = pos & 31;
-  if (sh + nbits <= 32) return __builtin_amdgcn_ubfe(dw[w], sh, nbits);
-  return __builtin_amdgcn_alignbit(dw[w + 1], dw[w], sh) & ((1u << nbits) - 1u);
-}
-
 // Pair table: entry e (two B-bit codes, the first in the low bits) holds
 // their two float16 levels, in C = 32 copies with copy c of entry e at dword
 // 32e + c.  Lane l reads copy l % 32; an LDS 32-bit read serves 32 lanes at
@@ -133,11 +126,33 @@ __device__ __forceinline__ void build_pf_table(uint32_t *tab, int tid) {
   }
 }
 
-// Pair-table entry e of this lane's copy (tab = table + copy), scaled by the
-// float16 pair n2 (the group norm / 16 in both halves).
-template <int B>
-__device__ __forceinline__ uint32_t pair_scaled(const uint32_t *tab, uint32_t e, uint32_t n2) {
-  const uint32_t lv = tab[e * PfTable<B>::C];
+// A lane's view of the pair table: the table base and the byte offset of the
+// lane's copy (4 c, below 128).  The byte offset of entry e in that copy,
+// 128 e + 4 c, is formed with an OR: the 2B-bit code field (pos, NB
+// compile-time after unrolling) is shifted straight to bit 7 and masked,
+// then OR'ed with the lane's offset, two instructions per lookup.
+struct TabRef {
+  const uint32_t *base;
+  uint32_t lane_off;
+};
+
+// Byte offset of the entry whose index is the nb-bit field at bit pos of dw.
+template <int NB>
+__device__ __forceinline__ uint32_t entry_off(const uint32_t *dw, int pos, uint32_t lane_off) {
+  constexpr uint32_t M = ((1u << NB) - 1u) << 7;
+  const int w = pos >> 5, sh = pos & 31;
+  uint32_t x;
+  if (sh + NB <= 32)
+    x = sh >= 7 ? dw[w] >> (sh - 7) : dw[w] << (7 - sh);
+  else
+    x = __builtin_amdgcn_alignbit(dw[w + 1], dw[w], sh - 7);   // sh > 32 - NB >= 24
+  return (x & M) | lane_off;
+}
+
+// The pair-table entry at byte offset off, scaled by the float16 pair n2 (the
+// group norm / 16 in both halves).
+__device__ __forceinline__ uint32_t pair_scaled(const TabRef &tab, uint32_t off, uint32_t n2) {
+  const uint32_t lv = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(tab.base) + off);
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, lv) * __builtin_bit_cast(half2_t, n2));
 }
 
@@ -210,12 +225,12 @@ __device__ __forceinline__ void load_row(const uint8_t *codes, const uint16_t *n
 // Rows of one tile (K or V): EK elements of one key, every pair-table read
 // first (held in h), then written as 16-byte stores at row stride `stride`.
 template <int B, int KD>
-__device__ __forceinline__ void lookup_row(const KRaw<B, KD> &r, const uint32_t *tab,
+__device__ __forceinline__ void lookup_row(const KRaw<B, KD> &r, const TabRef &tab,
                                            uint32_t (&h)[Dims<KD>::EK / 2]) {
   using D = Dims<KD>;
   const uint32_t n2 = norm_pair(r.n);
 #pragma unroll
-  for (int j = 0; j < D::EK / 2; ++j) h[j] = pair_scaled<B>(tab, bits_at(r.c, 2 * B * j, 2 * B), n2);
+  for (int j = 0; j < D::EK / 2; ++j) h[j] = pair_scaled(tab, entry_off<2 * B>(r.c, 2 * B * j, tab.lane_off), n2);
 }
 
 template <int KD>
@@ -227,7 +242,7 @@ __device__ __forceinline__ void write_row(const uint32_t (&h)[Dims<KD>::EK / 2],
 }
 
 template <int B, int KD>
-__device__ __forceinline__ void store_k(const KRaw<B, KD> &r, int dt, const uint32_t *tab, _Float16 *ks) {
+__device__ __forceinline__ void store_k(const KRaw<B, KD> &r, int dt, const TabRef &tab, _Float16 *ks) {
   uint32_t h[Dims<KD>::EK / 2];
   lookup_row<B, KD>(r, tab, h);
   write_row<KD>(h, dt, ks, Dims<KD>::KsStride);
@@ -286,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
   _Float16 *vbuf = tiles + D::KsHalves;
   _Float16 *qbuf = vbuf + D::VsHalves;
   float *ebuf = reinterpret_cast<float *>(tiles);
-  const uint32_t *tab = ptab + lane % PfTable<B>::C;   // this lane's pair-table copy
+  const TabRef tab = {ptab, 4u * (uint32_t)(lane % PfTable<B>::C)};   // this lane's pair-table copy
 
   build_pf_table<B, kThreads>(ptab, tid);
   __syncthreads();
