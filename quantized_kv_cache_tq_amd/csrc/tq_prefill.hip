@@ -33,7 +33,7 @@
 //     tile t, so the exponentials overlap the matrix products.
 //   * decode waves 4-7: turn the codes of later tiles into the float16 tiles
 //     in the phase that does not read them (V looked up one tile ahead into
-//     registers).
+//     registers, the codes of each tile loaded two tiles ahead).
 // Two barriers per tile separate the phases; each tile buffer is single:
 //   A(t): matrix: S(t+1) from K, softmax(t)   decode: write V(t), look up V(t+1)
 //   B(t): matrix: O += V(t) P(t)              decode: decode K(t+2) into K
@@ -285,8 +285,8 @@ __device__ __forceinline__ void wht_in_regs(float (&x)[N]) {
 template <int B, int KD, bool QBF16, bool kSplit>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
   using D = Dims<KD>;
-  // aligned to its size, so a lookup address is (entry << 8) | (lane << 2)
-  // on top of the table base with no carries
+  // (aligned to its size, which places it first, at LDS address 0: a
+  // lookup's address is then its byte offset, with nothing added)
   __shared__ __align__(PfTable<B>::WORDS * 4) uint32_t ptab[PfTable<B>::WORDS];
   // the K tile, the V^T tile, the rotated query rows; after the key loop the
   // same bytes hold the key-half merge
@@ -589,42 +589,58 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Args a) {
       hp.vc = a.vcodes + head_base * (16 * B * D::NG);
       hp.kn = a.knorms + head_base * D::NG;
       hp.vn = a.vnorms + head_base * D::NG;
-      // raw codes in two register sets that swap roles every tile (the loop
-      // runs two tiles per trip), so a load never targets registers whose
-      // previous contents are still to be used: with one set, the compiler
-      // issued each load into fresh registers and copied them back at the
-      // end of the phase, which waited for the load there
-      KRaw<B, KD> kra, krb, vra, vrb;
+      // raw codes in three register sets per cache that rotate roles every
+      // tile (the loop runs three tiles per trip): a tile's codes are loaded
+      // two tiles before their lookups, and a load never targets registers
+      // whose previous contents are still to be used (with one set, the
+      // compiler issued each load into fresh registers and copied them back
+      // at the end of the phase, which waited for the load there).  Loads
+      // retire in order; the issue order V(j), K(j+1), V(j+1), ... lets each
+      // phase wait for its own tile's codes with the next two tiles' loads
+      // still in flight
+      KRaw<B, KD> ka, kb, kc, va, vb, vc;
       uint32_t vw[D::EK / 2];
-      load_row<B, KD>(hp.kc, hp.kn, last, kt0, dt, kra);
-      load_row<B, KD>(hp.kc, hp.kn, last, min(kt0 + 1, kt1 - 1), dt, krb);
-      load_row<B, KD>(hp.vc, hp.vn, last, kt0, dt, vra);
-      store_k<B, KD>(kra, dt, tab, vbuf);   // K tile 0 goes where V tile 0 will
-      store_k<B, KD>(krb, dt, tab, kbuf);
-      lookup_row<B, KD>(vra, tab, vw);
+      load_row<B, KD>(hp.kc, hp.kn, last, kt0, dt, ka);
+      load_row<B, KD>(hp.kc, hp.kn, last, min(kt0 + 1, kt1 - 1), dt, kb);
+      load_row<B, KD>(hp.vc, hp.vn, last, kt0, dt, va);
+      store_k<B, KD>(ka, dt, tab, vbuf);   // K tile 0 goes where V tile 0 will
+      store_k<B, KD>(kb, dt, tab, kbuf);
+      lookup_row<B, KD>(va, tab, vw);
       // loads are unconditional (tile index clamped): a conditional load
       // would merge into the loop-carried registers through copies that wait
       // for the data
-      load_row<B, KD>(hp.kc, hp.kn, last, min(kt0 + 2, kt1 - 1), dt, kra);
-      load_row<B, KD>(hp.vc, hp.vn, last, min(kt0 + 1, kt1 - 1), dt, vra);
+      load_row<B, KD>(hp.vc, hp.vn, last, min(kt0 + 1, kt1 - 1), dt, va);
+      load_row<B, KD>(hp.kc, hp.kn, last, min(kt0 + 2, kt1 - 1), dt, ka);
+      load_row<B, KD>(hp.vc, hp.vn, last, min(kt0 + 2, kt1 - 1), dt, vb);
+      load_row<B, KD>(hp.kc, hp.kn, last, min(kt0 + 3, kt1 - 1), dt, kb);
       __syncthreads();   // query rows, K tiles 0 (in the V buffer) and 1 ready
       __syncthreads();   // K tile 0 read: the V buffer may take V tile 0
-      // one tile: vc holds V tile kt+1, kc K tile kt+2; vn and kn receive
-      // V tile kt+2 and K tile kt+3
-      auto tile = [&](int kt, KRaw<B, KD> &vc, KRaw<B, KD> &vn, KRaw<B, KD> &kc, KRaw<B, KD> &kn) {
+      // one tile: vcur holds V tile kt+1, kcur K tile kt+2; vnew and knew
+      // receive V tile kt+3 and K tile kt+4
+      auto tile = [&](int kt, KRaw<B, KD> &vcur, KRaw<B, KD> &vnew, KRaw<B, KD> &kcur, KRaw<B, KD> &knew) {
         // phase A: V tile kt into the buffer, look up V tile kt+1
         write_row<KD>(vw, dt, vbuf, D::VsStride);
-        lookup_row<B, KD>(vc, tab, vw);   // past the end: never written
-        load_row<B, KD>(hp.vc, hp.vn, last, min(kt + 2, kt1 - 1), dt, vn);
+        lookup_row<B, KD>(vcur, tab, vw);   // past the end: never written
+        load_row<B, KD>(hp.vc, hp.vn, last, min(kt + 3, kt1 - 1), dt, vnew);
         __syncthreads();   // V tile kt written; K tile kt+1 read
         // phase B: K tile kt+2 into the (now free) K buffer
-        if (kt + 2 < kt1) store_k<B, KD>(kc, dt, tab, kbuf);
-        load_row<B, KD>(hp.kc, hp.kn, last, min(kt + 3, kt1 - 1), dt, kn);
+        if (kt + 2 < kt1) store_k<B, KD>(kcur, dt, tab, kbuf);
+        load_row<B, KD>(hp.kc, hp.kn, last, min(kt + 4, kt1 - 1), dt, knew);
         __syncthreads();   // V tile kt consumed; K tile kt+2 written
       };
-      for (int kt = kt0; kt < kt1; kt += 2) {
-        tile(kt, vra, vrb, kra, krb);
-        if (kt + 1 < kt1) tile(kt + 1, vrb, vra, krb, kra);
+      // whole trips only, so the loop is entered and re-entered with the
+      // same loads in flight in the same order (the wait before each lookup
+      // then leaves the later tiles' loads outstanding); then the 0-2 tiles
+      // left
+      int kt = kt0;
+      for (; kt + 3 <= kt1; kt += 3) {
+        tile(kt, va, vc, ka, kc);
+        tile(kt + 1, vb, va, kb, ka);
+        tile(kt + 2, vc, vb, kc, kb);
+      }
+      if (kt < kt1) {
+        tile(kt, va, vc, ka, kc);
+        if (kt + 1 < kt1) tile(kt + 1, vb, va, kb, ka);
       }
       __syncthreads();   // partial outputs and statistics in shared memory
     }
