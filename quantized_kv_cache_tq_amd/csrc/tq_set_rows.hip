@@ -115,39 +115,48 @@ __global__ __launch_bounds__(64 * kSrWaves) void set_rows_kernel(
     //    and 2 stay inside a lane's chunk, distance 4 adds the two lanes'
     //    chunk partials (both lanes get the same bits: the operands meet
     //    commuted), distances 8 .. 64 pair the lane's chunks in order: pend[l]
-    //    holds a finished left partial until its right sibling is done
+    //    holds a finished left partial until its right sibling is done.
+    // 2. sign flip, 3. the butterfly stages that stay inside one chunk pair
+    //    of lanes: h = 1, 2 inside the chunk, h = 4 between the two lanes.
+    //    Both run chunk by chunk in load order, so each chunk's share is
+    //    computed while the later chunks are still arriving.  The lane stage
+    //    is x + c p with p the partner's value and c = +1 in the lower lane,
+    //    -1 in the upper (the product by +-1 is exact, so the fused form
+    //    rounds like the plain add or subtract): the upper lane so holds
+    //    b - a, the butterfly's a - b negated, and the later stages keep that
+    //    sign on all its values (both operands of each carry it); its factor
+    //    1/norm is negated to match, so y below is exactly the transform over
+    //    norm
+    const u32x4_t *sm = reinterpret_cast<const u32x4_t *>(smask);
+    const float c4 = h ? -1.f : 1.f;
     float pend[5];
 #pragma unroll
     for (int v = 0; v < kSrHalf / 4; ++v) {
-      const float s01 = u[4 * v] * u[4 * v] + u[4 * v + 1] * u[4 * v + 1];
-      const float s23 = u[4 * v + 2] * u[4 * v + 2] + u[4 * v + 3] * u[4 * v + 3];
+      float *x = u + 4 * v;
+      const float s01 = x[0] * x[0] + x[1] * x[1];
+      const float s23 = x[2] * x[2] + x[3] * x[3];
       const float q = s01 + s23;
       float t = q + xor_lane<1>(q);
       int l = 0;
 #pragma unroll
       for (; (v >> l) & 1; ++l) t = pend[l] + t;
       pend[l] = t;
+      const u32x4_t m = sm[2 * v + h];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[k] = __uint_as_float(__float_as_uint(x[k]) ^ m[k]);
+      const float a0 = x[0] + x[1], a1 = x[0] - x[1], a2 = x[2] + x[3], a3 = x[2] - x[3];
+      x[0] = a0 + a2;
+      x[1] = a1 + a3;
+      x[2] = a0 - a2;
+      x[3] = a1 - a3;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[k] = __builtin_fmaf(xor_lane<1>(x[k]), c4, x[k]);
     }
     const float n2 = pend[4];
     const float norm = __builtin_sqrtf(n2);                  // correctly rounded
     const float inv = norm > 0.f ? 1.0f / norm : 0.f;        // correctly rounded
 
-    // 2. sign flip, 3. butterfly stages in order: h = 1, 2 inside a chunk,
-    //    h = 4 between the two lanes, h = 8 .. 64 between the lane's chunks.
-    //    The lane stage is x + c p with p the partner's value and c = +1 in
-    //    the lower lane, -1 in the upper (the product by +-1 is exact, so the
-    //    fused form rounds like the plain add or subtract): the upper lane so
-    //    holds b - a, the butterfly's a - b negated, and the later stages keep
-    //    that sign on all its values (both operands of each carry it); its
-    //    factor 1/norm is negated to match, so y below is exactly the
-    //    transform over norm
-    const u32x4_t *sm = reinterpret_cast<const u32x4_t *>(smask);
-#pragma unroll
-    for (int v = 0; v < kSrHalf / 4; ++v) {
-      const u32x4_t m = sm[2 * v + h];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) u[4 * v + k] = __uint_as_float(__float_as_uint(u[4 * v + k]) ^ m[k]);
-    }
+    // 3. (cont.) stages h = 8 .. 64 between the lane's chunks
     auto local_stage = [&](int d) {   // pairs (i, i + d) of the lane's values
 #pragma unroll
       for (int i = 0; i < kSrHalf; ++i)
@@ -157,11 +166,6 @@ __global__ __launch_bounds__(64 * kSrWaves) void set_rows_kernel(
           u[i + d] = a - b;
         }
     };
-    local_stage(1);
-    local_stage(2);
-    const float c4 = h ? -1.f : 1.f;
-#pragma unroll
-    for (int i = 0; i < kSrHalf; ++i) u[i] = __builtin_fmaf(xor_lane<1>(u[i]), c4, u[i]);
     local_stage(4);
     local_stage(8);
     local_stage(16);
