@@ -53,6 +53,37 @@ __device__ __forceinline__ uint32_t mag_index(float a) {
   }
 }
 
+// 2 acc + bit as one add with the comparison's lane mask as its carry-in
+// (written as plain C the compiler selects the bit into a register first).
+__device__ __forceinline__ uint32_t push_bit(uint32_t acc, bool bit) {
+  const uint64_t m = __builtin_amdgcn_ballot_w64(bit);
+  uint32_t r;
+  uint64_t co;
+  asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(co) : "v"(acc), "s"(m));
+  return r;
+}
+
+// Bit b of the code of y (b = B - 1: the sign; below it the magnitude
+// index of mag_index, from its comparisons, most significant first).
+template <int B>
+__device__ __forceinline__ bool code_bit(float y, int b) {
+  if (b == B - 1) return y < 0.f;
+  const float a = __builtin_fabsf(y);
+  if constexpr (B == 2) {
+    return a > threshold<2>(1);
+  } else if constexpr (B == 3) {
+    const bool c2 = a > threshold<3>(2);
+    if (b == 1) return c2;
+    return a > (c2 ? threshold<3>(3) : threshold<3>(1));
+  } else {
+    const bool c4 = a > threshold<4>(4);
+    if (b == 2) return c4;
+    const bool c2 = a > (c4 ? threshold<4>(6) : threshold<4>(2));
+    if (b == 1) return c2;
+    return a > (c4 ? (c2 ? threshold<4>(7) : threshold<4>(5)) : (c2 ? threshold<4>(3) : threshold<4>(1)));
+  }
+}
+
 template <int B>
 __global__ __launch_bounds__(64 * kSrWaves) void set_rows_kernel(
     uint8_t *__restrict__ codes, uint16_t *__restrict__ norms, const float *__restrict__ src,
@@ -175,22 +206,35 @@ __global__ __launch_bounds__(64 * kSrWaves) void set_rows_kernel(
     // 4. unit-variance coordinates, 5. codes, 6. pack: element e's code at
     //    bits B e .. B e + B - 1 of the group's little-endian bit stream.  The
     //    lane places its own elements' codes into an image of the whole
-    //    group's 4B dwords, ORs in the partner's image and stores its half
+    //    group's 4B dwords (as the lower lane's elements 8v + r, r < 4, i =
+    //    4v + r; the upper lane's sit 4B bits higher, applied below), ORs in
+    //    the partner's image and stores its half.  Each dword is built from
+    //    its top bit down, one bit per instruction: w = 2 w + bit takes the
+    //    bit as the carry-in of one add, and a run of the partner's bits is
+    //    one shift.  An element's bits are the comparisons of mag_index and
+    //    its sign, (y < 0), recomputed where each is pushed
+    float ys[kSrHalf];
+#pragma unroll
+    for (int i = 0; i < kSrHalf; ++i) ys[i] = u[i] * inv_s;
     uint32_t word[4 * B];
 #pragma unroll
-    for (int w = 0; w < 4 * B; ++w) word[w] = 0u;
+    for (int w = 4 * B - 1; w >= 0; --w) {
+      uint32_t acc = 0u;
+      int zrun = 0;
 #pragma unroll
-    for (int i = 0; i < kSrHalf; ++i) {
-      const float y = u[i] * inv_s;
-      const float a = __builtin_fabsf(y);
-      const uint32_t c = mag_index<B>(a) | (y < 0.f ? 1u << (B - 1) : 0u);
-      // element 8v + 4h + r of the group (i = 4v + r); the lane-dependent
-      // part 4h B of its bit position is applied below, as a shift of the
-      // lane's 4B-bit chunk fields
-      const int v = i >> 2, r = i & 3;
-      const int bit = 8 * B * v + B * r, w = bit >> 5, sh = bit & 31;
-      word[w] |= c << sh;
-      if (sh + B > 32) word[w + 1] |= c >> (32 - sh);
+      for (int p = 32 * w + 31; p >= 32 * w; --p) {
+        const int e = p / B, b = p - e * B;
+        if ((e & 7) >= 4) {       // the partner's element: a zero bit here
+          ++zrun;
+          continue;
+        }
+        if (zrun > 0) acc <<= zrun;
+        zrun = 0;
+        const bool bit = code_bit<B>(ys[4 * (e >> 3) + (e & 7)], b);
+        acc = push_bit(acc, bit);
+      }
+      if (zrun > 0) acc <<= zrun;
+      word[w] = acc;
     }
     // the upper lane's chunk fields sit 4B bits higher: shift its image
     // (a funnel shift across the dwords)
