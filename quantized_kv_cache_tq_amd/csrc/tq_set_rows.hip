@@ -53,6 +53,14 @@ __device__ __forceinline__ uint32_t mag_index(float a) {
   }
 }
 
+// v from the partner lane (lane ^ 1, a DPP quad permute).  Every lane's
+// source lane is valid, so the bound-control bit never acts; it is set so
+// that the exchange needs no register for an unused old value and folds into
+// the instruction that consumes it.
+__device__ __forceinline__ float from_partner(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+
 // 2 acc + bit as one add with the comparison's lane mask as its carry-in
 // (written as plain C the compiler selects the bit into a register first).
 __device__ __forceinline__ uint32_t push_bit(uint32_t acc, bool bit) {
@@ -167,7 +175,7 @@ __global__ __launch_bounds__(64 * kSrWaves) void set_rows_kernel(
       const float s01 = x[0] * x[0] + x[1] * x[1];
       const float s23 = x[2] * x[2] + x[3] * x[3];
       const float q = s01 + s23;
-      float t = q + xor_lane<1>(q);
+      float t = q + from_partner(q);
       int l = 0;
 #pragma unroll
       for (; (v >> l) & 1; ++l) t = pend[l] + t;
@@ -181,7 +189,7 @@ __global__ __launch_bounds__(64 * kSrWaves) void set_rows_kernel(
       x[2] = a0 - a2;
       x[3] = a1 - a3;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) x[k] = __builtin_fmaf(xor_lane<1>(x[k]), c4, x[k]);
+      for (int k = 0; k < 4; ++k) x[k] = __builtin_fmaf(from_partner(x[k]), c4, x[k]);
     }
     const float n2 = pend[4];
     const float norm = __builtin_sqrtf(n2);                  // correctly rounded
@@ -246,7 +254,7 @@ __global__ __launch_bounds__(64 * kSrWaves) void set_rows_kernel(
       img[w] = h ? shifted : word[w];
     }
 #pragma unroll
-    for (int w = 0; w < 4 * B; ++w) img[w] |= (uint32_t)__float_as_int(xor_lane<1>(__int_as_float((int)img[w])));
+    for (int w = 0; w < 4 * B; ++w) img[w] |= (uint32_t)__float_as_int(from_partner(__int_as_float((int)img[w])));
     if (live && cell >= 0 && cell < n_cells) {
       const int64_t slot = ((int64_t)head * n_cells + cell) * n_groups_per_head + grp;
       uint8_t *dst = codes + slot * (16 * B) + 8 * B * h;     // this lane's 8B bytes (8-byte aligned)
