@@ -41,14 +41,14 @@ FP32_PEAK_TFLOPS = 157.3
 # `rocprofv3 --pmc` passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) over
 # `bench.py --no-cpu-baseline --only decode,copy --steps 2 --warmup 1`, each
 # scaled by what the same counter reads for the 256 MiB device copy of that
-# run (FETCH_SIZE reads 131087.6 KiB for 262144 KiB copied: x1.99976;
+# run (FETCH_SIZE reads 131088.5 KiB for 262144 KiB copied: x1.99975;
 # WRITE_SIZE reads 262144 KiB: x1.0).  Valid only for the decode sources it
 # was taken on (sha256 of tq_decode.hip + tq_common.h); otherwise traffic is
 # reported as null.
-DECODE_TRAFFIC = {"sources_sha256": "a385a3ba7f82192d9af3758843701d176bb05371c59bae3eb6854e7b9b20906d",
+DECODE_TRAFFIC = {"sources_sha256": "fd070f310707396c9903f124b009fb4beacbc4d9ec22580359662e534590f5e8",
                   "fetch_kib": {"decode_fused_kernel": 6541.6, "decode_merge_kernel": 568.5},
                   "write_kib": {"decode_fused_kernel": 1088.0, "decode_merge_kernel": 16.0},
-                  "fetch_scale": 1.99974, "write_scale": 1.0}
+                  "fetch_scale": 1.99975, "write_scale": 1.0}
 
 
 def decode_traffic_bytes():

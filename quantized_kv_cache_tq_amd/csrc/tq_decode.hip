@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_split_kernel(
   constexpr int kBlockWords = kReuse ? (kRowWords + kPWords > kOutWords ? kRowWords + kPWords : kOutWords)
                                      : kRowWords + kPWords + kOutWords;
   // 256-byte aligned: a lookup address is the entry offset OR the lane offset
-  __shared__ __align__(256) uint32_t ptab[PairCfg<B>::WORDS];   // pair table, 64 copies
+  __shared__ __align__(256) uint32_t ptab[PairCfg<B>::WORDS];   // pair table, 32 copies
   __shared__ __align__(16) uint32_t block[kBlockWords];
   __shared__ __align__(16) float nk[GK][4][KPW * (KQ8 ? 4 : 1)];   // K norms, or 4 block scales per key
   __shared__ __align__(16) float nv[GV][4][KPW];
