@@ -32,27 +32,6 @@ constexpr int kSrHalf = kGroup / 2;         // elements per lane
 constexpr int kSrRows = 32;                 // rows (groups) per task
 constexpr int kSrTasks = 1;                 // tasks per wave
 
-// qs = #{k : a > threshold k} by binary search over the sorted thresholds:
-// each step compares with the middle threshold of the range left, chosen by
-// the earlier steps' outcomes.
-template <int B>
-__device__ __forceinline__ uint32_t mag_index(float a) {
-  if constexpr (B == 2) {
-    return a > threshold<2>(1) ? 1u : 0u;
-  } else if constexpr (B == 3) {
-    const bool c2 = a > threshold<3>(2);
-    const bool c1 = a > (c2 ? threshold<3>(3) : threshold<3>(1));
-    return (c2 ? 2u : 0u) | (c1 ? 1u : 0u);
-  } else {
-    static_assert(B == 4, "2, 3 or 4 bits");
-    const bool c4 = a > threshold<4>(4);
-    const bool c2 = a > (c4 ? threshold<4>(6) : threshold<4>(2));
-    const float t1 = c4 ? (c2 ? threshold<4>(7) : threshold<4>(5)) : (c2 ? threshold<4>(3) : threshold<4>(1));
-    const bool c1 = a > t1;
-    return (c4 ? 4u : 0u) | (c2 ? 2u : 0u) | (c1 ? 1u : 0u);
-  }
-}
-
 // v from the partner lane (lane ^ 1, a DPP quad permute).  Every lane's
 // source lane is valid, so the bound-control bit never acts; it is set so
 // that the exchange needs no register for an unused old value and folds into
@@ -71,8 +50,11 @@ __device__ __forceinline__ uint32_t push_bit(uint32_t acc, bool bit) {
   return r;
 }
 
-// Bit b of the code of y (b = B - 1: the sign; below it the magnitude
-// index of mag_index, from its comparisons, most significant first).
+// Bit b of the code of y.  b = B - 1 is the sign, (y < 0).  Below it is the
+// magnitude index qs = #{k : |y| > threshold k}, found by binary search over
+// the sorted thresholds: each bit, most significant first, compares |y| with
+// the middle threshold of the range the higher bits left (so NaN, failing
+// every comparison, takes index 0).
 template <int B>
 __device__ __forceinline__ bool code_bit(float y, int b) {
   if (b == B - 1) return y < 0.f;
@@ -219,8 +201,8 @@ __global__ __launch_bounds__(64 * kSrWaves) void set_rows_kernel(
     //    the partner's image and stores its half.  Each dword is built from
     //    its top bit down, one bit per instruction: w = 2 w + bit takes the
     //    bit as the carry-in of one add, and a run of the partner's bits is
-    //    one shift.  An element's bits are the comparisons of mag_index and
-    //    its sign, (y < 0), recomputed where each is pushed
+    //    one shift.  An element's bits are the comparisons of code_bit,
+    //    recomputed where each is pushed
     float ys[kSrHalf];
 #pragma unroll
     for (int i = 0; i < kSrHalf; ++i) ys[i] = u[i] * inv_s;
