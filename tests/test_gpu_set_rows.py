@@ -73,6 +73,37 @@ def test_adversarial_groups(bits):
     _assert_planes_equal(bits, src, np.arange(len(rows)), len(rows), "adversarial")
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_non_finite_groups(bits):
+    """Groups holding a NaN, an infinity, both infinities, or finite values
+    whose squares overflow: the norm is NaN or +inf, the scale 1/norm is 0
+    (the norm is not > 0, or 1/inf), every coordinate is 0 or NaN, so every
+    code is +level 0 (comparisons with NaN fail) and the stored norm is the
+    float16 NaN or infinity."""
+    z = np.random.default_rng(5).standard_normal(128).astype(np.float32)
+    rows = []
+    for idx, val in [((17,), np.nan), ((3,), np.inf), ((100,), -np.inf), ((5, 6), None)]:
+        r = z.copy()
+        if val is None:
+            r[5], r[6] = np.inf, -np.inf
+        else:
+            r[list(idx)] = val
+        rows.append(r)
+    rows.append(np.full(128, np.float32(3e38)))                # squares overflow: norm +inf
+    rows.append(z.copy())                                      # a finite neighbour, unaffected
+    src = np.stack(rows)[:, None, :]
+    n = len(rows)
+    gc, gn = _gpu_set_rows(bits, src, np.arange(n), n)
+    with np.errstate(all="ignore"):
+        oc, on = _oracle_set_rows(bits, src, np.arange(n), n)
+    print(f"[set_rows] non-finite bits={bits}", flush=True)
+    np.testing.assert_array_equal(gc, oc)
+    gh, oh = gn.view(np.uint16).ravel(), on.view(np.uint16).ravel()
+    nan_o = np.isnan(on.astype(np.float32).ravel())
+    assert np.array_equal(np.isnan(gn.astype(np.float32).ravel()), nan_o)
+    np.testing.assert_array_equal(gh[~nan_o], oh[~nan_o])
+
+
 def test_outlier_decode_shape_turbo3():
     """The 32K x 4-head outlier-channel cache, K and V (2 x 131072 groups)."""
     q, k, v = inputs.outlier_decode(seed=0)
