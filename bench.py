@@ -42,9 +42,10 @@ FP32_PEAK_TFLOPS = 157.3
 # `bench.py --no-cpu-baseline --only decode,copy --steps 2 --warmup 1`, each
 # scaled by what the same counter reads for the 256 MiB device copy of that
 # run (FETCH_SIZE reads 131088.5 KiB for 262144 KiB copied: x1.99975;
-# WRITE_SIZE reads 262144 KiB: x1.0).  Valid only for the decode sources it
-# was taken on (sha256 of tq_decode.hip + tq_common.h); otherwise traffic is
-# reported as null.
+# WRITE_SIZE reads 262144 KiB: x1.0).  Valid only for the decode kernels it
+# was taken on: sha256 of their sources (tq_decode.hip, tq_decode_fused4.hip,
+# tq_common.h) and of build.py, whose per-source flags shape their code;
+# otherwise traffic is reported as null.
 DECODE_TRAFFIC = {"sources_sha256": "fd070f310707396c9903f124b009fb4beacbc4d9ec22580359662e534590f5e8",
                   "fetch_kib": {"decode_fused_kernel": 6541.6, "decode_merge_kernel": 568.5},
                   "write_kib": {"decode_fused_kernel": 1088.0, "decode_merge_kernel": 16.0},
@@ -55,8 +56,8 @@ def decode_traffic_bytes():
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
     h = hashlib.sha256()
-    for f in ("tq_decode.hip", "tq_common.h"):
-        with open(os.path.join(here, "quantized_kv_cache_tq_amd", "csrc", f), "rb") as fh:
+    for f in ("csrc/tq_decode.hip", "csrc/tq_decode_fused4.hip", "csrc/tq_common.h", "build.py"):
+        with open(os.path.join(here, "quantized_kv_cache_tq_amd", f), "rb") as fh:
             h.update(fh.read())
     t = DECODE_TRAFFIC
     if h.hexdigest() != t["sources_sha256"]:

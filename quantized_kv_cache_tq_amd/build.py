@@ -19,7 +19,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIB_DIR, "libtq.so")
-SOURCES = ["tq_api.hip", "tq_set_rows.hip", "tq_decode.hip", "tq_prefill.hip", "tq_int8.hip"]
+SOURCES = ["tq_api.hip", "tq_set_rows.hip", "tq_decode.hip", "tq_decode_fused4.hip", "tq_prefill.hip",
+           "tq_int8.hip"]
 # benchmark floors (empty launch, one streaming read): not part of libtq
 FLOOR_SOURCE = "tq_floor.hip"
 FLOOR_LIB = os.path.join(LIB_DIR, "libtq_floor.so")
@@ -32,6 +33,13 @@ HIPCC_FLAGS = [
     "-fno-fast-math", "-ffp-contract=off", "-fno-gpu-rdc",
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
 ]
+# Per-source additions: the compiler's instruction-level-parallelism
+# scheduling strategy, for the kernels it measured faster on (the prefill and
+# int8 kernels, and the fused decode kernel's one-block variants, which have
+# a translation unit of their own for this: the other decode kernels measured
+# slower with it, set_rows too).
+_MAX_ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
+SOURCE_FLAGS = {"tq_decode_fused4.hip": _MAX_ILP, "tq_prefill.hip": _MAX_ILP, "tq_int8.hip": _MAX_ILP}
 
 
 def hipcc() -> str:
@@ -43,7 +51,7 @@ def hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(LIB_DIR, "obj", os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(SRC, src), "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(SRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

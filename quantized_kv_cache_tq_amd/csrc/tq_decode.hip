@@ -1381,7 +1381,21 @@ __global__ __launch_bounds__(NTH) void decode_merge_kernel(
   reinterpret_cast<float4 *>(out + (int64_t)h * dv + kGroup * og)[j] = res;
 }
 
+#ifndef TQ_DECODE_FUSED_BLOCK4_TU
 // ---------------------------------------------------------------- host side
+
+// The one-block fused variants (64-key blocks, no prefetch) are compiled in
+// tq_decode_fused4.hip, with another instruction scheduling strategy.
+#define TQ_FUSED_PARAMS                                                                                     \
+  const uint8_t *, const uint16_t *, const uint8_t *, const uint16_t *, int64_t, const int64_t *,        \
+      const int32_t *, int64_t, const void *, int, int, int, int, int, float, float, float *, int
+extern template __global__ void decode_fused_kernel<2, 4, true, false>(TQ_FUSED_PARAMS);
+extern template __global__ void decode_fused_kernel<2, 4, false, false>(TQ_FUSED_PARAMS);
+extern template __global__ void decode_fused_kernel<3, 4, true, false>(TQ_FUSED_PARAMS);
+extern template __global__ void decode_fused_kernel<3, 4, false, false>(TQ_FUSED_PARAMS);
+extern template __global__ void decode_fused_kernel<4, 4, true, false>(TQ_FUSED_PARAMS);
+extern template __global__ void decode_fused_kernel<4, 4, false, false>(TQ_FUSED_PARAMS);
+#undef TQ_FUSED_PARAMS
 
 hipError_t device_cu_count(int *n_cu) {
   static int cache[64] = {0};
@@ -1722,5 +1736,7 @@ hipError_t launch_decode(const tq_cache &k, const tq_cache &v, const int64_t *se
 #undef TQ_MERGE
   return hipGetLastError();
 }
+
+#endif  // TQ_DECODE_FUSED_BLOCK4_TU
 
 }  // namespace tq
