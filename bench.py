@@ -41,15 +41,15 @@ FP32_PEAK_TFLOPS = 157.3
 # `rocprofv3 --pmc` passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) over
 # `bench.py --no-cpu-baseline --only decode,copy --steps 2 --warmup 1`, each
 # scaled by what the same counter reads for the 256 MiB device copy of that
-# run (FETCH_SIZE reads 131088.5 KiB for 262144 KiB copied: x1.99975;
+# run (FETCH_SIZE reads 131088.8 KiB for 262144 KiB copied: x1.99974;
 # WRITE_SIZE reads 262144 KiB: x1.0).  Valid only for the decode kernels it
 # was taken on: sha256 of their sources (tq_decode.hip, tq_decode_fused4.hip,
 # tq_common.h) and of build.py, whose per-source flags shape their code;
 # otherwise traffic is reported as null.
-DECODE_TRAFFIC = {"sources_sha256": "fd070f310707396c9903f124b009fb4beacbc4d9ec22580359662e534590f5e8",
-                  "fetch_kib": {"decode_fused_kernel": 6541.6, "decode_merge_kernel": 568.5},
+DECODE_TRAFFIC = {"sources_sha256": "5a7e501239135a3fe683c41a2bc2bd856c29e853ee53a168c0b48d5233b9d8c3",
+                  "fetch_kib": {"decode_fused_kernel": 6542.3, "decode_merge_kernel": 568.5},
                   "write_kib": {"decode_fused_kernel": 1088.0, "decode_merge_kernel": 16.0},
-                  "fetch_scale": 1.99975, "write_scale": 1.0}
+                  "fetch_scale": 1.99974, "write_scale": 1.0}
 
 
 def decode_traffic_bytes():
